@@ -1,0 +1,152 @@
+"""CPU oracle for the materialised-probability SDPA forward (float64).
+
+TEST INFRASTRUCTURE ONLY. Only the tests, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package. The product (the
+HIP library and its Python binding) never imports, links or calls it, and this
+package imports nothing from the product.
+
+``sdpa_reference`` is the plain definition written out in C (``sdpa_oracle.c``):
+scores, masking, row maximum, log-sum-exp, probabilities, output, one query
+row at a time in float64. ``brute.py`` is an independent pure-Python
+implementation with exact summation used to pin it on tiny inputs.
+
+Semantics (FlagOS-OP pull request "feat: add sdpa_math operator (Ascend Triton
++ P800 exact-P/A1)", sections Overview, Implementation and Intentional
+divergences; its "P800 exact-P fast path" update for P = exp(scale*QK^T - LSE);
+cudnn-frontend pull request "[SDPA] SM80 fwd: TemplateParams kernels,
+plan-time compile, sym_int THD extents", merge-log notes on dead rows and the
+LSE layout):
+  * bool mask: True keeps a key, False removes it (score -inf);
+  * additive mask: added to the scaled score;
+  * causal: top-left, key j is removed for query i when j > i;
+  * causal together with a mask is an error; Hq not a multiple of Hkv is an
+    error; Hq != Hkv without ``enable_gqa`` is an error;
+  * a row with every key removed has P = 0, O = 0 and LSE = -inf.
+
+Every function here is pinned by ``tests/test_oracle.py`` (brute force, closed
+forms, invariants, equivalences, torch's CPU math backend on float masks).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sdpa_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle_sdpa.so")
+
+MASK_NONE, MASK_BOOL, MASK_ADD = 0, 1, 2
+
+
+def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the C oracle with gcc (float64, no FMA contraction, OpenMP)."""
+    if force or not os.path.exists(out):
+        cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared",
+               "-o", out, src, "-lm"]
+        subprocess.run(cmd, check=True)
+    return out
+
+
+_lib_cache = {}
+
+
+def load(path: str = _LIB) -> ctypes.CDLL:
+    if path in _lib_cache:
+        return _lib_cache[path]
+    if not os.path.exists(path):
+        build(force=False, out=path)
+    lib = ctypes.CDLL(path)
+    dp = ctypes.POINTER(ctypes.c_double)
+    i64 = ctypes.c_int64
+    lib.oracle_sdpa_fwd.restype = ctypes.c_int
+    lib.oracle_sdpa_fwd.argtypes = [dp, dp, dp, i64, i64, i64, i64, i64, i64, i64,
+                                    ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(i64),
+                                    ctypes.c_int, ctypes.c_double, dp, dp, dp]
+    lib.oracle_sdpa_threads.restype = ctypes.c_int
+    lib.oracle_sdpa_threads.argtypes = []
+    _lib_cache[path] = lib
+    return lib
+
+
+def threads() -> int:
+    """OpenMP threads the oracle runs with."""
+    return int(load().oracle_sdpa_threads())
+
+
+def _f64(x) -> np.ndarray:
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().to("cpu", torch.float64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _mask_array(mask, full_shape):
+    """Mask -> (kind, contiguous array, element strides over [B,Hq,Sq,Skv])."""
+    try:
+        import torch
+        if isinstance(mask, torch.Tensor):
+            mask = mask.detach().cpu()
+            mask = mask.numpy() if mask.dtype == torch.bool else mask.to(torch.float64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    mask = np.asarray(mask)
+    if mask.ndim > 4:
+        raise ValueError("mask has more than 4 dims")
+    shape = (1,) * (4 - mask.ndim) + tuple(mask.shape)
+    for got, want in zip(shape, full_shape):
+        if got != 1 and got != want:
+            raise ValueError(f"mask shape {tuple(mask.shape)} does not broadcast to {full_shape}")
+    if mask.dtype == np.bool_:
+        kind, arr = MASK_BOOL, np.ascontiguousarray(mask.reshape(shape), dtype=np.uint8)
+    else:
+        kind, arr = MASK_ADD, np.ascontiguousarray(mask.reshape(shape), dtype=np.float64)
+    strides = [0 if shape[d] == 1 else arr.strides[d] // arr.itemsize for d in range(4)]
+    return kind, arr, strides
+
+
+def sdpa_reference(q, k, v, attn_mask=None, is_causal: bool = False,
+                   scale: Optional[float] = None, enable_gqa: bool = False,
+                   lib_path: str = _LIB) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Return (O [B,Hq,Sq,Dv], P [B,Hq,Sq,Skv], LSE [B,Hq,Sq]) in float64."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, S, D]")
+    B, Hq, Sq, D = q.shape
+    Bk, Hkv, Skv, Dk = k.shape
+    Bv, Hv, Sv, Dv = v.shape
+    if (Bk, Dk) != (B, D) or (Bv, Hv, Sv) != (B, Hkv, Skv):
+        raise ValueError("q, k, v shapes disagree")
+    if Hkv == 0 or Hq % Hkv != 0:
+        raise ValueError(f"query heads {Hq} are not a multiple of key/value heads {Hkv}")
+    if Hq != Hkv and not enable_gqa:
+        raise ValueError("Hq != Hkv requires enable_gqa")
+    if is_causal and attn_mask is not None:
+        raise ValueError("is_causal and attn_mask are mutually exclusive")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    kind, marr, mstr = MASK_NONE, None, [0, 0, 0, 0]
+    if attn_mask is not None:
+        kind, marr, mstr = _mask_array(attn_mask, (B, Hq, Sq, Skv))
+    out = np.empty((B, Hq, Sq, Dv), np.float64)
+    probs = np.empty((B, Hq, Sq, Skv), np.float64)
+    lse = np.empty((B, Hq, Sq), np.float64)
+    dp = ctypes.POINTER(ctypes.c_double)
+    st = (ctypes.c_int64 * 4)(*mstr)
+    lib = load(lib_path)
+    rc = lib.oracle_sdpa_fwd(q.ctypes.data_as(dp), k.ctypes.data_as(dp), v.ctypes.data_as(dp),
+                             B, Hq, Hkv, Sq, Skv, D, Dv, kind,
+                             None if marr is None else marr.ctypes.data_as(ctypes.c_void_p),
+                             st, int(bool(is_causal)), float(scale),
+                             out.ctypes.data_as(dp), probs.ctypes.data_as(dp), lse.ctypes.data_as(dp))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the call (code {rc})")
+    return out, probs, lse

@@ -1,0 +1,146 @@
+/*
+ * CPU oracle for the materialised-probability scaled-dot-product attention
+ * forward: returns the output O, the full probability map P and the row
+ * log-sum-exp LSE, in float64.
+ *
+ * TEST INFRASTRUCTURE ONLY. This file is the checker, not the product: only
+ * the tests, the smoke check and the benchmark's CPU-baseline leg may load it.
+ * It shares no code, header or constant with the HIP library.
+ *
+ * What it computes (the plain definition, one query row at a time, no
+ * blocking, no fusion, no online rescaling):
+ *
+ *   s_j   = scale * sum_d q[d] * k_{h'}[j][d]        j = 0 .. Skv-1
+ *   s_j   = -inf  where a causal (top-left, j > i) or boolean (False) mask
+ *                 removes key j; s_j += mask[i][j] for an additive mask
+ *   m     = max_j s_j
+ *   dead row (m == -inf):  P[i][:] = 0, O[i][:] = 0, LSE[i] = -inf
+ *   else:  LSE = m + log(sum_j exp(s_j - m)),  P_j = exp(s_j - LSE),
+ *          O[i][:] = sum_j P_j * v_{h'}[j][:]
+ *   with h' = h / (Hq / Hkv) (contiguous groups of query heads share a KV head)
+ *
+ * Passages followed:
+ *  - FlagOS-OP pull request "feat: add sdpa_math operator (Ascend Triton +
+ *    P800 exact-P/A1)", Overview: the math backend returns (out, attn_probs);
+ *    Implementation: a fully-masked row gives P = O = 0, a head count that
+ *    does not divide is an error, causal and an explicit mask are exclusive;
+ *    Intentional divergences: a boolean mask removes keys with -inf;
+ *    "P800 exact-P fast path" update: P = exp(scale * QK^T - LSE) with the
+ *    row-wise LSE.
+ *  - cudnn-frontend pull request "[SDPA] SM80 fwd: TemplateParams kernels,
+ *    plan-time compile, sym_int THD extents", merge-log notes: a dead row
+ *    reports LSE = -inf and O = 0; LSE is float32 laid out (B, H, S).
+ *
+ * Inputs are contiguous float64 arrays (the caller upcasts the exact
+ * dtype-rounded values the GPU receives):
+ *   q [B,Hq,Sq,D], k [B,Hkv,Skv,D], v [B,Hkv,Skv,Dv]
+ *   mask: NULL, or uint8 (bool kind) / float64 (additive kind) addressed with
+ *         mask_strides[4] in elements over the logical [B,Hq,Sq,Skv] index
+ *         (a stride of 0 broadcasts that dimension)
+ * Outputs (contiguous float64): out [B,Hq,Sq,Dv], probs [B,Hq,Sq,Skv],
+ *   lse [B,Hq,Sq].
+ * Returns 0 on success, 1 when Hq is not a multiple of Hkv, 2 when causal is
+ * combined with a mask, 3 for a bad mask kind.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_MASK_NONE 0
+#define ORACLE_MASK_BOOL 1
+#define ORACLE_MASK_ADD 2
+
+int oracle_sdpa_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+int oracle_sdpa_fwd(const double* q, const double* k, const double* v,
+                    int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv,
+                    int64_t D, int64_t Dv,
+                    int mask_kind, const void* mask, const int64_t* mask_strides,
+                    int is_causal, double scale,
+                    double* out, double* probs, double* lse)
+{
+    if (Hkv <= 0 || Hq % Hkv != 0)
+        return 1;
+    if (is_causal && mask_kind != ORACLE_MASK_NONE)
+        return 2;
+    if (mask_kind != ORACLE_MASK_NONE && mask_kind != ORACLE_MASK_BOOL &&
+        mask_kind != ORACLE_MASK_ADD)
+        return 3;
+
+    const int64_t group = Hq / Hkv;
+    const int64_t nrows = B * Hq * Sq;
+
+#pragma omp parallel for schedule(dynamic, 8)
+    for (int64_t row = 0; row < nrows; ++row) {
+        const int64_t i = row % Sq;
+        const int64_t h = (row / Sq) % Hq;
+        const int64_t b = row / (Sq * Hq);
+        const int64_t hk = h / group;
+
+        const double* qi = q + row * D;
+        const double* kh = k + (b * Hkv + hk) * Skv * D;
+        const double* vh = v + (b * Hkv + hk) * Skv * Dv;
+        double* p = probs + row * Skv; /* holds the scores until normalised */
+        double* o = out + row * Dv;
+
+        /* scores, masking, running maximum */
+        double m = -INFINITY;
+        for (int64_t j = 0; j < Skv; ++j) {
+            double dot = 0.0;
+            for (int64_t d = 0; d < D; ++d)
+                dot += qi[d] * kh[j * D + d];
+            double s = scale * dot;
+            if (is_causal && j > i) {
+                s = -INFINITY;
+            } else if (mask_kind != ORACLE_MASK_NONE) {
+                const int64_t off = b * mask_strides[0] + h * mask_strides[1] +
+                                    i * mask_strides[2] + j * mask_strides[3];
+                if (mask_kind == ORACLE_MASK_BOOL) {
+                    if (((const uint8_t*)mask)[off] == 0)
+                        s = -INFINITY;
+                } else {
+                    s += ((const double*)mask)[off];
+                }
+            }
+            p[j] = s;
+            if (s > m)
+                m = s;
+        }
+
+        if (m == -INFINITY) { /* every key removed (or no keys at all) */
+            for (int64_t j = 0; j < Skv; ++j)
+                p[j] = 0.0;
+            for (int64_t d = 0; d < Dv; ++d)
+                o[d] = 0.0;
+            lse[row] = -INFINITY;
+            continue;
+        }
+
+        double l = 0.0;
+        for (int64_t j = 0; j < Skv; ++j)
+            l += exp(p[j] - m);
+        const double L = m + log(l);
+        lse[row] = L;
+
+        for (int64_t j = 0; j < Skv; ++j)
+            p[j] = exp(p[j] - L);
+
+        for (int64_t d = 0; d < Dv; ++d) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < Skv; ++j)
+                acc += p[j] * vh[j * Dv + d];
+            o[d] = acc;
+        }
+    }
+    return 0;
+}
