@@ -1,0 +1,186 @@
+"""Benchmark of the materialised-probability SDPA forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step = one ``sdpa_math_fwd`` call (validation, path choice, kernel launch)
+on the 2k-token, head-dim-128, causal bf16 prefill workload (B=2, H=16,
+Sq=Skv=2048), inputs resident in HBM. Prints one JSON line on stdout;
+progress goes to stderr.
+
+Accounting (the FlagOS-OP page's perf-gate convention, Validation table):
+  flops = 2 * B * Hq * Sq * Skv * (D + Dv), halved when causal
+  bytes = P + Q + K + V + O + LSE (+ mask), each once; P counts in full
+          (its causal upper triangle is written as zeros).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "ms, effective TFLOPS and P-write GB/s for SDPA fwd (out,P) prefill 2k D128 fp16"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
+ELT = {"f32": 4, "f16": 2, "bf16": 2}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_flops(B, Hq, Sq, Skv, D, Dv, causal):
+    f = 2.0 * B * Hq * Sq * Skv * (D + Dv)
+    return f / 2 if causal else f
+
+
+def algorithmic_bytes(w, mask_bytes=0):
+    e = ELT[w.dtype]
+    q = w.B * w.Hq * w.Sq * w.D * e
+    k = w.B * w.Hkv * w.Skv * w.D * e
+    v = w.B * w.Hkv * w.Skv * w.dv * e
+    o = w.B * w.Hq * w.Sq * w.dv * e
+    p = w.B * w.Hq * w.Sq * w.Skv * e
+    lse = w.B * w.Hq * w.Sq * 4
+    return {"total": q + k + v + o + p + lse + mask_bytes, "p": p}
+
+
+def time_gpu(w, steps, warmup, path="auto"):
+    import torch
+
+    import sdpa_forward_materialised_amd as S
+    import sdpa_workloads as W
+
+    dev = torch.device("cuda:0")
+    inp = W.make_inputs(w)
+    q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
+    m = None if inp["mask"] is None else inp["mask"].to(dev)
+    mask_bytes = 0 if m is None else m.numel() * m.element_size()
+    B, Hq, Sq, D = q.shape
+    Skv, Dv = k.shape[2], v.shape[3]
+    # preallocated outputs: the timed region is the forward alone
+    O = torch.empty(B, Hq, Sq, Dv, dtype=q.dtype, device=dev)
+    P = torch.empty(B, Hq, Sq, Skv, dtype=q.dtype, device=dev)
+    L = torch.empty(B, Hq, Sq, dtype=torch.float32, device=dev)
+    out = (O, P, L)
+    chosen, tiles, tiles64 = S.plan(q, k, v, m, w.causal, w.gqa)
+    for _ in range(warmup):
+        S.fwd(q, k, v, m, w.causal, w.scale, w.gqa, path=path, out=out)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        S.fwd(q, k, v, m, w.causal, w.scale, w.gqa, path=path, out=out)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / steps
+    return {"ms": ms, "wall_ms": wall * 1e3 / steps, "mask_bytes": mask_bytes,
+            "path": path if path != "auto" else chosen, "tiles_per_bh": tiles, "tiles64_per_bh": tiles64}
+
+
+def cpu_baseline(w, budget_s=15.0):
+    """The float64 oracle on whole (batch, head) slices of the same workload,
+    as many as fit in about ``budget_s`` seconds of host time."""
+    import oracle
+    import sdpa_workloads as W
+
+    inp = W.make_inputs(w)
+    g = w.Hq // w.Hkv
+    done, t_used = 0, 0.0
+    heads = [(b, h) for b in range(w.B) for h in range(w.Hq)]
+    for b, h in heads:
+        hk = h // g
+        qs, ks, vs = inp["q"][b:b + 1, h:h + 1], inp["k"][b:b + 1, hk:hk + 1], inp["v"][b:b + 1, hk:hk + 1]
+        ms = None
+        if inp["mask"] is not None:
+            mm = inp["mask"]
+            ms = (mm[b:b + 1] if mm.shape[0] > 1 else mm)
+            ms = ms[:, h:h + 1] if ms.shape[1] > 1 else ms
+        t0 = time.perf_counter()
+        oracle.sdpa_reference(qs, ks, vs, ms, w.causal, w.scale, False)
+        t_used += time.perf_counter() - t0
+        done += 1
+        if t_used >= budget_s:
+            break
+    flops = algorithmic_flops(1, done, w.Sq, w.Skv, w.D, w.dv, w.causal)
+    return {"value": flops / t_used / 1e12, "unit": "TFLOPS", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{done} of {len(heads)} (batch, head) slices of {w.name}, float64, "
+                      f"{t_used:.1f} s ({t_used / done * 1e3:.0f} ms per slice)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--path", default="auto", choices=["auto", "fused", "twopass"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fp16", action="store_true", help="skip the same-shape fp16 line")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch  # noqa: F401
+
+    import sdpa_workloads as W
+
+    w = W.BY_NAME["prefill_2k_d128_bf16_causal"]
+    log(f"[bench] {w.describe()} steps={args.steps} warmup={args.warmup}")
+    r = time_gpu(w, args.steps, args.warmup, args.path)
+    flops = algorithmic_flops(w.B, w.Hq, w.Sq, w.Skv, w.D, w.dv, w.causal)
+    by = algorithmic_bytes(w, r["mask_bytes"])
+    tflops = flops / (r["ms"] * 1e-3) / 1e12
+    achieved = by["total"] / (r["ms"] * 1e-3) / 1e9
+    p_gbps = by["p"] / (r["ms"] * 1e-3) / 1e9
+    log(f"[bench] bf16: {r['ms']:.4f} ms/step, {tflops:.1f} TFLOPS, {achieved:.0f} GB/s, P {p_gbps:.0f} GB/s")
+
+    extra = {}
+    if not args.no_fp16:
+        w16 = W.Workload("prefill_2k_d128_f16_causal", "f16", 2, 16, 16, 2048, 2048, 128, True, "none", 3)
+        r16 = time_gpu(w16, args.steps, args.warmup, args.path)
+        extra["fp16_same_shape"] = {"ms": round(r16["ms"], 5),
+                                    "tflops": round(flops / (r16["ms"] * 1e-3) / 1e12, 2),
+                                    "p_write_gbps": round(by["p"] / (r16["ms"] * 1e-3) / 1e9, 1)}
+        log(f"[bench] fp16: {r16['ms']:.4f} ms/step")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the float64 oracle on the host")
+        cpu = cpu_baseline(w)
+        log(f"[bench] cpu baseline: {cpu}")
+
+    line = {
+        "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["ms"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Sq": w.Sq, "Skv": w.Skv,
+                   "D": w.D, "causal": w.causal, "path": r["path"], "tiles_per_bh": r["tiles_per_bh"],
+                   "tiles64_per_bh": r["tiles64_per_bh"]},
+        "p_write_gbps": round(p_gbps, 1),
+        "effective_tflops_frac_of_mfma_peak": round(tflops / MFMA_PEAK_TFLOPS[w.dtype], 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "sdpa_twopass_kernel" if r["path"] == "twopass" else "sdpa_fused_kernel",
+                     "bytes_per_launch": by["total"]},
+        "cpu_baseline": cpu,
+        "wall_ms_per_step": round(r["wall_ms"], 5),
+    }
+    line.update(extra)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,156 @@
+/*
+ * sdpa_math — materialised-probability scaled-dot-product attention forward
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * One call returns the attention output O, the full probability map P and
+ * the float32 row log-sum-exp LSE. This is the math-backend contract of the
+ * FlagOS-OP pull request "feat: add sdpa_math operator (Ascend Triton + P800
+ * exact-P/A1)" (Overview: the operator returns (out, attn_probs) for callers
+ * that must see the probabilities), with the row-wise LSE of its "P800
+ * exact-P fast path" update (P = exp(scale * Q K^T - LSE)).
+ *
+ * For every batch b, query head h, query row i and key j, with
+ * g = Hq / Hkv and kv head h' = h / g:
+ *   s_ij = scale * sum_d Q[b,h,i,d] * K[b,h',j,d]
+ *   s_ij = -inf  if causal and j > i (top-left alignment), or if a boolean
+ *                mask holds False at (b,h,i,j); s_ij += mask[b,h,i,j] for an
+ *                additive mask (masks broadcast over size-1 dimensions)
+ *   LSE_i  = log sum_j exp(s_ij)            (-inf when every key is removed)
+ *   P_ij   = exp(s_ij - LSE_i)              (0 on rows whose LSE is -inf)
+ *   O_i    = sum_j P_ij * V[b,h',j,:]       (0 on rows whose LSE is -inf)
+ * Semantics fixed by that page's Implementation section (fully-masked rows
+ * give P = O = 0, head counts that do not divide are an error, causal and an
+ * explicit mask are exclusive) and its Intentional-divergences section (a
+ * boolean mask removes keys with -inf). Dead rows report LSE = -inf and LSE is
+ * laid out [B, H, S] in float32, as the cudnn-frontend pull request "[SDPA]
+ * SM80 fwd: TemplateParams kernels, plan-time compile, sym_int THD extents"
+ * records in its merge-log notes.
+ *
+ * Numerics: scores, row statistics and the P·V accumulation run in float32;
+ * P is rounded to the output dtype with round-to-nearest-even and O is
+ * accumulated from exactly those rounded values (O = P_stored · V up to
+ * float32 summation), then rounded the same way.
+ */
+#ifndef SDPA_MATH_H
+#define SDPA_MATH_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SDPA_MATH_VERSION 1
+
+typedef enum {
+    SDPA_F32 = 0,
+    SDPA_F16 = 1,
+    SDPA_BF16 = 2,
+    SDPA_BOOL = 3 /* one byte per element, 0 = False */
+} sdpa_dtype_t;
+
+/*
+ * A strided view of device memory. `ndim` is 4 for q, k, v, out, probs and
+ * the mask (a mask of fewer dims is passed right-aligned with leading size-1
+ * dims), and 3 for lse. Sizes and strides are in ELEMENTS; a size-1 dim may
+ * have any stride. The library never takes ownership of `data`.
+ */
+typedef struct {
+    void* data;
+    int32_t dtype; /* sdpa_dtype_t */
+    int32_t ndim;
+    int64_t sizes[4];
+    int64_t strides[4];
+} sdpa_tensor_t;
+
+typedef enum {
+    SDPA_OK = 0,
+    SDPA_ERR_INVALID_ARG = 1, /* shapes, dtypes, null pointers, semantic rule broken */
+    SDPA_ERR_UNSUPPORTED = 2, /* valid call this build does not implement (layout, head dim) */
+    SDPA_ERR_HIP = 3          /* the HIP runtime reported an error at launch */
+} sdpa_status_t;
+
+typedef enum {
+    SDPA_PATH_AUTO = 0,    /* choose by the number of score tiles (see sdpa_math_plan) */
+    SDPA_PATH_FUSED = 1,   /* one sweep over the keys; scores stay on chip */
+    SDPA_PATH_TWOPASS = 2  /* row statistics sweep, then a probability/output sweep */
+} sdpa_path_t;
+
+/*
+ * sdpa_math_fwd — enqueue the forward on `hip_stream` (a hipStream_t; NULL =
+ * the null stream) and return without synchronising.
+ *
+ * q      [B, Hq, Sq, D]   f32 | f16 | bf16
+ * k      [B, Hkv, Skv, D] same dtype as q
+ * v      [B, Hkv, Skv, Dv] same dtype as q; Dv == D in this version
+ * mask   NULL, or a bool or q-dtype tensor broadcastable to [B, Hq, Sq, Skv]
+ *        (bool: True keeps the key; float: added to the scaled score)
+ * is_causal  nonzero for the top-left causal mask (exclusive with `mask`)
+ * scale  multiplier of Q K^T (the Python layer passes 1/sqrt(D) by default,
+ *        as the cudnn-frontend merge-log notes resolve a missing scale)
+ * enable_gqa nonzero lets Hq be a multiple of Hkv; query head h then reads
+ *        kv head h / (Hq / Hkv)
+ * out    [B, Hq, Sq, Dv] q dtype     (written)
+ * probs  [B, Hq, Sq, Skv] q dtype    (written in full, zeros included)
+ * lse    [B, Hq, Sq] f32             (written)
+ *
+ * Layout: every tensor needs stride 1 in its last dim (a broadcast mask may
+ * use stride 0 there); q, k, v need a 16-byte-aligned base and strides that
+ * are multiples of 16 bytes (the operand contract of the cudnn-frontend page,
+ * merge-log note on dense operands). Outputs may be uninitialised.
+ * Ownership: the caller allocates every buffer; the library allocates no
+ * device memory, keeps no device state between calls, never synchronises and
+ * never reads device data on the host. Calls on different streams may run
+ * concurrently.
+ * Errors: validation runs before any launch; on error nothing is enqueued and
+ * sdpa_math_last_error() describes the problem. Head dims 32, 64 and 128 are
+ * implemented; others give SDPA_ERR_UNSUPPORTED. An empty problem (B*Hq*Sq
+ * == 0) is SDPA_OK with nothing launched; Skv == 0 yields O = 0, LSE = -inf.
+ */
+sdpa_status_t sdpa_math_fwd(const sdpa_tensor_t* q, const sdpa_tensor_t* k,
+                            const sdpa_tensor_t* v, const sdpa_tensor_t* mask,
+                            int is_causal, float scale, int enable_gqa,
+                            sdpa_tensor_t* out, sdpa_tensor_t* probs, sdpa_tensor_t* lse,
+                            void* hip_stream);
+
+/*
+ * sdpa_math_fwd_path — sdpa_math_fwd with the path forced (SDPA_PATH_AUTO
+ * behaves exactly like sdpa_math_fwd). A forced path the shape cannot take
+ * (the fused path needs every processed key row of a query block to fit on
+ * chip) returns SDPA_ERR_UNSUPPORTED. Both paths compute the same values.
+ */
+sdpa_status_t sdpa_math_fwd_path(const sdpa_tensor_t* q, const sdpa_tensor_t* k,
+                                 const sdpa_tensor_t* v, const sdpa_tensor_t* mask,
+                                 int is_causal, float scale, int enable_gqa,
+                                 sdpa_tensor_t* out, sdpa_tensor_t* probs, sdpa_tensor_t* lse,
+                                 void* hip_stream, int path);
+
+/*
+ * sdpa_math_plan — validate the shapes exactly as sdpa_math_fwd would and
+ * report, without launching anything:
+ *   *path         the path SDPA_PATH_AUTO resolves to
+ *   *tiles_per_bh score tiles one (batch, head) processes with this
+ *                 library's tiling, after causal truncation
+ *   *tiles_64     the same count in 64x64 tiles (the unit of the FlagOS-OP
+ *                 page's fused-vs-two-stage rule, single-kernel fusion update)
+ * out/probs/lse may be NULL here. Any output pointer may be NULL.
+ * The environment variable SDPA_MATH_PATH=auto|fused|twopass forces the
+ * automatic choice; SDPA_MATH_FUSED_MAX_TILES=<n> moves its threshold.
+ */
+sdpa_status_t sdpa_math_plan(const sdpa_tensor_t* q, const sdpa_tensor_t* k,
+                             const sdpa_tensor_t* v, const sdpa_tensor_t* mask,
+                             int is_causal, int enable_gqa,
+                             int32_t* path, int64_t* tiles_per_bh, int64_t* tiles_64);
+
+/* Message of the last failed call on this thread ("" if none). Valid until
+ * the next call on the same thread. */
+const char* sdpa_math_last_error(void);
+
+/* SDPA_MATH_VERSION of the loaded library. */
+int sdpa_math_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDPA_MATH_H */

@@ -1,0 +1,13 @@
+"""MI355X-native materialised-probability SDPA forward.
+
+``fwd(q, k, v, attn_mask=None, is_causal=False, scale=None, enable_gqa=False)``
+returns ``(O, P, LSE)``: the attention output, the full probability map and
+the float32 row log-sum-exp, computed by hand-written gfx950 HIP kernels in
+``libsdpa_math.so`` (C ABI declared in ``include/sdpa_math.h``). This package
+is argument marshalling only; torch supplies device memory and streams.
+"""
+
+from ._binding import (EXPORTS, LIB_PATH, PATHS, fwd, last_error, load_library, plan,  # noqa: F401
+                       version)
+
+__all__ = ["fwd", "plan", "version", "last_error", "load_library", "LIB_PATH", "PATHS", "EXPORTS"]

@@ -1,0 +1,179 @@
+"""ctypes binding of libsdpa_math.so (argument marshalling only).
+
+Every step of the forward runs in the HIP library; this module only turns
+torch tensors into ``sdpa_tensor_t`` descriptors, allocates the outputs with
+torch's caching allocator and passes torch's current stream. There is no
+fallback: if the library is missing or the device is not a GPU, calls fail.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsdpa_math.so")
+
+SDPA_F32, SDPA_F16, SDPA_BF16, SDPA_BOOL = 0, 1, 2, 3
+PATH_AUTO, PATH_FUSED, PATH_TWOPASS = 0, 1, 2
+PATHS = {"auto": PATH_AUTO, "fused": PATH_FUSED, "twopass": PATH_TWOPASS}
+PATH_NAMES = {v: k for k, v in PATHS.items()}
+
+_DTYPES = {torch.float32: SDPA_F32, torch.float16: SDPA_F16, torch.bfloat16: SDPA_BF16,
+           torch.bool: SDPA_BOOL}
+
+EXPORTS = ("sdpa_math_fwd", "sdpa_math_fwd_path", "sdpa_math_plan", "sdpa_math_last_error",
+           "sdpa_math_version")
+
+
+class SdpaTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("sizes", ctypes.c_int64 * 4), ("strides", ctypes.c_int64 * 4)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m sdpa_forward_materialised_amd.build` "
+                           "(there is no CPU fallback)")
+    lib = ctypes.CDLL(path)
+    T = ctypes.POINTER(SdpaTensor)
+    lib.sdpa_math_fwd.restype = ctypes.c_int
+    lib.sdpa_math_fwd.argtypes = [T, T, T, T, ctypes.c_int, ctypes.c_float, ctypes.c_int, T, T, T, ctypes.c_void_p]
+    lib.sdpa_math_fwd_path.restype = ctypes.c_int
+    lib.sdpa_math_fwd_path.argtypes = lib.sdpa_math_fwd.argtypes + [ctypes.c_int]
+    lib.sdpa_math_plan.restype = ctypes.c_int
+    lib.sdpa_math_plan.argtypes = [T, T, T, T, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int32),
+                                   ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
+    lib.sdpa_math_last_error.restype = ctypes.c_char_p
+    lib.sdpa_math_last_error.argtypes = []
+    lib.sdpa_math_version.restype = ctypes.c_int
+    lib.sdpa_math_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _desc(t: Optional[torch.Tensor], ndim: int) -> Optional[SdpaTensor]:
+    if t is None:
+        return None
+    if t.dim() > ndim:
+        raise ValueError(f"expected at most {ndim} dims, got {t.dim()}")
+    while t.dim() < ndim:  # right-align (a mask may have fewer dims)
+        t = t.unsqueeze(0)
+    if t.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {t.dtype}")
+    d = SdpaTensor()
+    d.data = t.data_ptr() if t.numel() > 0 else None
+    d.dtype = _DTYPES[t.dtype]
+    d.ndim = ndim
+    for i in range(ndim):
+        d.sizes[i] = t.shape[i]
+        d.strides[i] = t.stride(i)
+    return d
+
+
+def _ref(d: Optional[SdpaTensor]):
+    return None if d is None else ctypes.byref(d)
+
+
+def _raise(code: int, lib) -> None:
+    msg = lib.sdpa_math_last_error().decode()
+    if code == 1:
+        raise ValueError(msg)
+    if code == 2:
+        raise NotImplementedError(msg)
+    raise RuntimeError(f"sdpa_math: {msg}")
+
+
+def _check_devices(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("sdpa_math runs on the GPU only: every tensor must be a cuda tensor")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"tensors on different devices ({dev} and {t.device})")
+    return dev
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, attn_mask: Optional[torch.Tensor] = None,
+        is_causal: bool = False, scale: Optional[float] = None, enable_gqa: bool = False,
+        path: str = "auto", out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None
+        ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Return (O [B,Hq,Sq,Dv], P [B,Hq,Sq,Skv], LSE [B,Hq,Sq] float32).
+
+    ``scale=None`` means 1/sqrt(D). ``path`` is "auto", "fused" or "twopass".
+    ``out`` may pass preallocated (O, P, LSE) buffers (any strides with a
+    contiguous last dim); by default P and O share one allocation.
+    """
+    lib = load_library()
+    dev = _check_devices(q, k, v, attn_mask)
+    if path not in PATHS:
+        raise ValueError(f"path must be one of {sorted(PATHS)}")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, S, D]")
+    B, Hq, Sq, D = q.shape
+    Skv, Dv = k.shape[2], v.shape[3]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D) if D > 0 else 1.0
+    if out is None:
+        n_p = B * Hq * Sq * Skv
+        n_o = B * Hq * Sq * Dv
+        pad = (-n_p) % 64  # keep O 128-byte aligned behind P
+        buf = torch.empty(n_p + pad + n_o, dtype=q.dtype, device=dev)
+        P = buf[:n_p].view(B, Hq, Sq, Skv)
+        O = buf[n_p + pad:].view(B, Hq, Sq, Dv)
+        L = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
+    else:
+        O, P, L = out
+        _check_devices(q, O, P, L)
+    dq, dk, dv = _desc(q, 4), _desc(k, 4), _desc(v, 4)
+    dm = _desc(attn_mask, 4)
+    do, dp, dl = _desc(O, 4), _desc(P, 4), _desc(L, 3)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = lib.sdpa_math_fwd_path(_ref(dq), _ref(dk), _ref(dv), _ref(dm), int(bool(is_causal)),
+                                    float(scale), int(bool(enable_gqa)), _ref(do), _ref(dp), _ref(dl),
+                                    ctypes.c_void_p(stream), PATHS[path])
+    if rc != 0:
+        _raise(rc, lib)
+    return O, P, L
+
+
+def plan(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, attn_mask: Optional[torch.Tensor] = None,
+         is_causal: bool = False, enable_gqa: bool = False):
+    """Validate like ``fwd`` and return (path name, tiles per (b,h), 64x64 tiles per (b,h)).
+
+    Reads only shapes, strides, dtypes and pointers; works on CPU tensors too.
+    """
+    lib = load_library()
+    path = ctypes.c_int32(-1)
+    tiles = ctypes.c_int64(-1)
+    tiles64 = ctypes.c_int64(-1)
+    rc = lib.sdpa_math_plan(_ref(_desc(q, 4)), _ref(_desc(k, 4)), _ref(_desc(v, 4)),
+                            _ref(_desc(attn_mask, 4)), int(bool(is_causal)), int(bool(enable_gqa)),
+                            ctypes.byref(path), ctypes.byref(tiles), ctypes.byref(tiles64))
+    if rc != 0:
+        _raise(rc, lib)
+    return PATH_NAMES[path.value], tiles.value, tiles64.value
+
+
+def version() -> int:
+    return int(load_library().sdpa_math_version())
+
+
+def last_error() -> str:
+    return load_library().sdpa_math_last_error().decode()

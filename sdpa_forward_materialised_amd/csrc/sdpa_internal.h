@@ -1,0 +1,57 @@
+// Internal interface between the host side (validation, planning, C ABI) and
+// the gfx950 kernels. Not installed; the public interface is include/sdpa_math.h.
+#pragma once
+
+#include <cstdint>
+
+namespace sdpa {
+
+enum MaskKind : int { MASK_NONE = 0, MASK_BOOL = 1, MASK_ADD = 2 };
+enum Dtype : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_BOOL = 3 };
+
+// Everything a kernel needs, passed by value. Strides are in elements and
+// ordered (batch, head, row); the last dim is contiguous. Mask strides cover
+// the logical [B, Hq, Sq, Skv] index, 0 on broadcast dims.
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* mask;
+    void* o;
+    void* p;
+    float* lse;
+    int64_t q_s[3], k_s[3], v_s[3], o_s[3], p_s[3], l_s[3];
+    int64_t m_s[4];
+    int B, Hq, Hkv, Sq, Skv, group;
+    int causal;
+    int mask_vec;    // mask rows can be read with aligned vector loads
+    int p_vec;       // P rows can be written with aligned 16-byte stores
+    int o_vec;       // O rows likewise
+    float scale_log2;  // scale * log2(e): scores live in the base-2 domain
+    int n_qblk;      // query blocks per (batch, head)
+    int n_blocks;    // workgroups in the grid
+    int keys_per_wave;  // fused path: key range of one wave
+};
+
+// Launch configuration chosen on the host for one call.
+struct Plan {
+    int path;        // 1 fused, 2 two-pass
+    int waves;       // waves per workgroup
+    int q_rows;      // query rows per workgroup
+    int n_qblk;
+    int64_t grid;
+    int keys_per_wave;  // fused only
+    int64_t tiles_per_bh;
+    int64_t tiles_64;
+};
+
+// Kernel launchers (sdpa_kernels.hip). Return a hipError_t as int.
+int launch_twopass(int dtype, int D, int mask_kind, int waves, const FwdArgs& a, void* stream);
+int launch_fused(int dtype, int D, int mask_kind, int waves, const FwdArgs& a, void* stream);
+
+// Largest key range the fused path keeps on chip per wave.
+constexpr int FUSED_MAX_KEYS_PER_WAVE = 256;
+constexpr int FUSED_MAX_WAVES = 8;
+constexpr int TILE_N = 64;  // keys per score tile
+
+}  // namespace sdpa

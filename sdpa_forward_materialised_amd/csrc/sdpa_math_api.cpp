@@ -1,0 +1,360 @@
+// Host side of the sdpa_math C ABI: argument validation, shape resolution,
+// the tile-count path choice and the kernel launch. No device memory is
+// allocated here, nothing is synchronised and no device data is read.
+
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "sdpa_internal.h"
+#include "sdpa_math.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+sdpa_status_t fail(sdpa_status_t st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+int64_t elt_size(int dtype) {
+    switch (dtype) {
+        case SDPA_F32: return 4;
+        case SDPA_F16:
+        case SDPA_BF16: return 2;
+        case SDPA_BOOL: return 1;
+        default: return 0;
+    }
+}
+
+const char* dtype_name(int dtype) {
+    switch (dtype) {
+        case SDPA_F32: return "f32";
+        case SDPA_F16: return "f16";
+        case SDPA_BF16: return "bf16";
+        case SDPA_BOOL: return "bool";
+        default: return "?";
+    }
+}
+
+int64_t numel(const sdpa_tensor_t* t) {
+    int64_t n = 1;
+    for (int d = 0; d < t->ndim; ++d) n *= t->sizes[d];
+    return n;
+}
+
+// Effective stride: a size-1 dim never advances, whatever stride it carries.
+int64_t eff_stride(const sdpa_tensor_t* t, int d) { return t->sizes[d] == 1 ? 0 : t->strides[d]; }
+
+// True when every row start (all dims but the last) is `align`-byte aligned.
+bool rows_aligned(const sdpa_tensor_t* t, int64_t align) {
+    const int64_t es = elt_size(t->dtype);
+    if (reinterpret_cast<uintptr_t>(t->data) % align) return false;
+    for (int d = 0; d + 1 < t->ndim; ++d)
+        if ((eff_stride(t, d) * es) % align) return false;
+    return true;
+}
+
+struct Shape {
+    int64_t B, Hq, Hkv, Sq, Skv, D, Dv;
+    int dtype;
+    int mask_kind;
+};
+
+sdpa_status_t check_tensor(const sdpa_tensor_t* t, const char* name, int ndim) {
+    if (!t) return fail(SDPA_ERR_INVALID_ARG, "%s is NULL", name);
+    if (t->ndim != ndim) return fail(SDPA_ERR_INVALID_ARG, "%s must have %d dims, got %d", name, ndim, t->ndim);
+    for (int d = 0; d < ndim; ++d)
+        if (t->sizes[d] < 0) return fail(SDPA_ERR_INVALID_ARG, "%s has a negative size", name);
+    if (elt_size(t->dtype) == 0) return fail(SDPA_ERR_INVALID_ARG, "%s has an unknown dtype %d", name, t->dtype);
+    if (numel(t) > 0 && t->data == nullptr) return fail(SDPA_ERR_INVALID_ARG, "%s has no data pointer", name);
+    if (numel(t) > 0 && t->sizes[ndim - 1] > 1 && t->strides[ndim - 1] != 1)
+        return fail(SDPA_ERR_UNSUPPORTED, "%s must be contiguous in its last dim (stride %lld)", name,
+                    (long long)t->strides[ndim - 1]);
+    return SDPA_OK;
+}
+
+sdpa_status_t check_dims(const sdpa_tensor_t* t, const char* name, const int64_t* want, int ndim) {
+    for (int d = 0; d < ndim; ++d)
+        if (t->sizes[d] != want[d]) {
+            return fail(SDPA_ERR_INVALID_ARG, "%s dim %d is %lld, expected %lld", name, d, (long long)t->sizes[d],
+                        (long long)want[d]);
+        }
+    return SDPA_OK;
+}
+
+sdpa_status_t validate_inputs(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_tensor_t* v,
+                              const sdpa_tensor_t* mask, int is_causal, int enable_gqa, Shape* sh) {
+    sdpa_status_t st;
+    if ((st = check_tensor(q, "q", 4)) || (st = check_tensor(k, "k", 4)) || (st = check_tensor(v, "v", 4)))
+        return st;
+    if (q->dtype != SDPA_F32 && q->dtype != SDPA_F16 && q->dtype != SDPA_BF16)
+        return fail(SDPA_ERR_INVALID_ARG, "q dtype %s is not f32, f16 or bf16", dtype_name(q->dtype));
+    if (k->dtype != q->dtype || v->dtype != q->dtype)
+        return fail(SDPA_ERR_INVALID_ARG, "q, k, v dtypes differ (%s, %s, %s)", dtype_name(q->dtype),
+                    dtype_name(k->dtype), dtype_name(v->dtype));
+    sh->B = q->sizes[0];
+    sh->Hq = q->sizes[1];
+    sh->Sq = q->sizes[2];
+    sh->D = q->sizes[3];
+    sh->Hkv = k->sizes[1];
+    sh->Skv = k->sizes[2];
+    sh->Dv = v->sizes[3];
+    sh->dtype = q->dtype;
+    if (k->sizes[0] != sh->B || v->sizes[0] != sh->B)
+        return fail(SDPA_ERR_INVALID_ARG, "batch sizes differ: q %lld, k %lld, v %lld", (long long)sh->B,
+                    (long long)k->sizes[0], (long long)v->sizes[0]);
+    if (v->sizes[1] != sh->Hkv || v->sizes[2] != sh->Skv)
+        return fail(SDPA_ERR_INVALID_ARG, "k and v disagree on heads or length");
+    if (k->sizes[3] != sh->D)
+        return fail(SDPA_ERR_INVALID_ARG, "q and k head dims differ (%lld vs %lld)", (long long)sh->D,
+                    (long long)k->sizes[3]);
+    if (sh->Hkv <= 0 || sh->Hq % sh->Hkv != 0)
+        return fail(SDPA_ERR_INVALID_ARG, "query heads (%lld) are not a multiple of key/value heads (%lld)",
+                    (long long)sh->Hq, (long long)sh->Hkv);
+    if (sh->Hq != sh->Hkv && !enable_gqa)
+        return fail(SDPA_ERR_INVALID_ARG, "Hq (%lld) != Hkv (%lld) needs enable_gqa", (long long)sh->Hq,
+                    (long long)sh->Hkv);
+    sh->mask_kind = sdpa::MASK_NONE;
+    if (mask) {
+        if (is_causal) return fail(SDPA_ERR_INVALID_ARG, "is_causal and an explicit mask are mutually exclusive");
+        if (mask->ndim != 4) return fail(SDPA_ERR_INVALID_ARG, "mask must be passed with 4 dims (right-aligned)");
+        for (int d = 0; d < 4; ++d)
+            if (mask->sizes[d] < 0) return fail(SDPA_ERR_INVALID_ARG, "mask has a negative size");
+        const int64_t full[4] = {sh->B, sh->Hq, sh->Sq, sh->Skv};
+        for (int d = 0; d < 4; ++d)
+            if (mask->sizes[d] != 1 && mask->sizes[d] != full[d])
+                return fail(SDPA_ERR_INVALID_ARG, "mask dim %d (%lld) does not broadcast to %lld", d,
+                            (long long)mask->sizes[d], (long long)full[d]);
+        if (mask->dtype == SDPA_BOOL) sh->mask_kind = sdpa::MASK_BOOL;
+        else if (mask->dtype == q->dtype) sh->mask_kind = sdpa::MASK_ADD;
+        else
+            return fail(SDPA_ERR_INVALID_ARG, "mask dtype %s must be bool or the query dtype %s",
+                        dtype_name(mask->dtype), dtype_name(q->dtype));
+        if (numel(mask) > 0 && !mask->data) return fail(SDPA_ERR_INVALID_ARG, "mask has no data pointer");
+    }
+    if (sh->Sq > INT32_MAX || sh->Skv > INT32_MAX || sh->B > INT32_MAX || sh->Hq > INT32_MAX)
+        return fail(SDPA_ERR_UNSUPPORTED, "sizes beyond 2^31 are not supported");
+    if (sh->D != 32 && sh->D != 64 && sh->D != 128)
+        return fail(SDPA_ERR_UNSUPPORTED, "head dim %lld is not implemented (32, 64, 128)", (long long)sh->D);
+    if (sh->Dv != sh->D)
+        return fail(SDPA_ERR_UNSUPPORTED, "value head dim %lld != query head dim %lld is not implemented",
+                    (long long)sh->Dv, (long long)sh->D);
+    const sdpa_tensor_t* in[3] = {q, k, v};
+    const char* names[3] = {"q", "k", "v"};
+    for (int i = 0; i < 3; ++i)
+        if (numel(in[i]) > 0 && !rows_aligned(in[i], 16))
+            return fail(SDPA_ERR_UNSUPPORTED, "%s needs a 16-byte aligned base and 16-byte multiple strides", names[i]);
+    return SDPA_OK;
+}
+
+sdpa_status_t validate_outputs(const Shape& sh, const sdpa_tensor_t* out, const sdpa_tensor_t* probs,
+                               const sdpa_tensor_t* lse) {
+    sdpa_status_t st;
+    if ((st = check_tensor(out, "out", 4)) || (st = check_tensor(probs, "probs", 4)) ||
+        (st = check_tensor(lse, "lse", 3)))
+        return st;
+    if (out->dtype != sh.dtype || probs->dtype != sh.dtype)
+        return fail(SDPA_ERR_INVALID_ARG, "out and probs must have the query dtype %s", dtype_name(sh.dtype));
+    if (lse->dtype != SDPA_F32) return fail(SDPA_ERR_INVALID_ARG, "lse must be f32");
+    const int64_t wo[4] = {sh.B, sh.Hq, sh.Sq, sh.Dv};
+    const int64_t wp[4] = {sh.B, sh.Hq, sh.Sq, sh.Skv};
+    const int64_t wl[3] = {sh.B, sh.Hq, sh.Sq};
+    if ((st = check_dims(out, "out", wo, 4)) || (st = check_dims(probs, "probs", wp, 4)) ||
+        (st = check_dims(lse, "lse", wl, 3)))
+        return st;
+    return SDPA_OK;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Score tiles one (batch, head) processes with `rows` query rows per block
+// and 64 keys per tile, after top-left causal truncation.
+int64_t count_tiles(int64_t Sq, int64_t Skv, bool causal, int64_t rows) {
+    const int64_t ktiles = cdiv(Skv, sdpa::TILE_N);
+    if (!causal) return cdiv(Sq, rows) * ktiles;
+    int64_t total = 0;
+    for (int64_t r0 = 0; r0 < Sq; r0 += rows) {
+        const int64_t last = std::min(Sq, r0 + rows);  // keys j < last are reachable
+        total += cdiv(std::min(Skv, last), sdpa::TILE_N);
+    }
+    return total;
+}
+
+// Default fused-path ceiling in 64x64 tiles per (batch, head); the FlagOS-OP
+// page settled on 56 for its hardware, this value is re-measured on MI355X.
+constexpr int64_t kFusedMaxTiles64 = 56;
+
+int env_path() {
+    const char* e = std::getenv("SDPA_MATH_PATH");
+    if (!e) return SDPA_PATH_AUTO;
+    if (!std::strcmp(e, "fused")) return SDPA_PATH_FUSED;
+    if (!std::strcmp(e, "twopass")) return SDPA_PATH_TWOPASS;
+    return SDPA_PATH_AUTO;
+}
+
+int64_t env_max_tiles() {
+    const char* e = std::getenv("SDPA_MATH_FUSED_MAX_TILES");
+    if (!e || !*e) return kFusedMaxTiles64;
+    return std::strtoll(e, nullptr, 10);
+}
+
+// Fused path: one workgroup = 32 query rows, keys split over up to 8 waves,
+// each keeping at most FUSED_MAX_KEYS_PER_WAVE scores on chip.
+bool fused_config(const Shape& sh, bool causal, int* waves, int* keys_per_wave) {
+    const int64_t keys = causal ? std::min(sh.Skv, sh.Sq) : sh.Skv;
+    for (int w = 1; w <= sdpa::FUSED_MAX_WAVES; w *= 2) {
+        const int64_t kpw = cdiv(cdiv(keys, w), 32) * 32;
+        if (kpw <= sdpa::FUSED_MAX_KEYS_PER_WAVE) {
+            *waves = w;
+            *keys_per_wave = (int)std::max<int64_t>(kpw, 32);
+            return true;
+        }
+    }
+    return false;
+}
+
+bool fused_available() { return false; }  // the fused kernel is not built yet
+
+sdpa_status_t make_plan(const Shape& sh, bool causal, int forced, sdpa::Plan* p) {
+    p->tiles_64 = count_tiles(sh.Sq, sh.Skv, causal, 64);
+    int fw = 0, fk = 0;
+    const bool fused_ok = fused_available() && fused_config(sh, causal, &fw, &fk);
+    int path = forced;
+    if (path == SDPA_PATH_AUTO) path = env_path();
+    if (path == SDPA_PATH_AUTO) path = (fused_ok && p->tiles_64 <= env_max_tiles()) ? SDPA_PATH_FUSED : SDPA_PATH_TWOPASS;
+    if (path == SDPA_PATH_FUSED && !fused_ok)
+        return fail(SDPA_ERR_UNSUPPORTED, "the fused path cannot take this shape (keys beyond %d per wave x %d waves)",
+                    sdpa::FUSED_MAX_KEYS_PER_WAVE, sdpa::FUSED_MAX_WAVES);
+    p->path = path;
+    if (path == SDPA_PATH_FUSED) {
+        p->waves = fw;
+        p->keys_per_wave = fk;
+        p->q_rows = 32;
+    } else {
+        // Four waves (128 rows) share each staged K/V tile; drop to two when
+        // that leaves fewer than two workgroups per compute unit.
+        const int64_t bh = sh.B * sh.Hq;
+        p->waves = (bh * cdiv(sh.Sq, 128) >= 512) ? 4 : 2;
+        p->keys_per_wave = 0;
+        p->q_rows = 32 * p->waves;
+    }
+    p->n_qblk = (int)cdiv(sh.Sq, p->q_rows);
+    p->grid = sh.B * sh.Hq * p->n_qblk;
+    p->tiles_per_bh = count_tiles(sh.Sq, sh.Skv, causal, p->q_rows);
+    if (p->grid > INT32_MAX) return fail(SDPA_ERR_UNSUPPORTED, "grid too large");
+    return SDPA_OK;
+}
+
+void fill_strides3(const sdpa_tensor_t* t, int64_t* s) {
+    for (int d = 0; d < 3; ++d) s[d] = eff_stride(t, d);
+}
+
+sdpa_status_t run(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_tensor_t* v, const sdpa_tensor_t* mask,
+                  int is_causal, float scale, int enable_gqa, sdpa_tensor_t* out, sdpa_tensor_t* probs,
+                  sdpa_tensor_t* lse, void* stream, int path) {
+    g_last_error.clear();
+    if (path < SDPA_PATH_AUTO || path > SDPA_PATH_TWOPASS) return fail(SDPA_ERR_INVALID_ARG, "unknown path %d", path);
+    Shape sh;
+    sdpa_status_t st = validate_inputs(q, k, v, mask, is_causal, enable_gqa, &sh);
+    if (st) return st;
+    if ((st = validate_outputs(sh, out, probs, lse))) return st;
+    if (!std::isfinite(scale)) return fail(SDPA_ERR_INVALID_ARG, "scale must be finite");
+    if (sh.B * sh.Hq * sh.Sq == 0) return SDPA_OK;
+    sdpa::Plan plan;
+    if ((st = make_plan(sh, is_causal != 0, path, &plan))) return st;
+
+    sdpa::FwdArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.q = q->data;
+    a.k = k->data;
+    a.v = v->data;
+    a.mask = mask ? mask->data : nullptr;
+    a.o = out->data;
+    a.p = probs->data;
+    a.lse = static_cast<float*>(lse->data);
+    fill_strides3(q, a.q_s);
+    fill_strides3(k, a.k_s);
+    fill_strides3(v, a.v_s);
+    fill_strides3(out, a.o_s);
+    fill_strides3(probs, a.p_s);
+    for (int d = 0; d < 3; ++d) a.l_s[d] = eff_stride(lse, d);
+    if (mask)
+        for (int d = 0; d < 4; ++d) a.m_s[d] = eff_stride(mask, d);
+    a.B = (int)sh.B;
+    a.Hq = (int)sh.Hq;
+    a.Hkv = (int)sh.Hkv;
+    a.Sq = (int)sh.Sq;
+    a.Skv = (int)sh.Skv;
+    a.group = (int)(sh.Hq / sh.Hkv);
+    a.causal = is_causal ? 1 : 0;
+    const int64_t mvec_align = sh.mask_kind == sdpa::MASK_BOOL ? 8 : 16;
+    a.mask_vec = mask && a.m_s[3] == 1 && rows_aligned(mask, mvec_align) ? 1 : 0;
+    a.p_vec = rows_aligned(probs, 16) ? 1 : 0;
+    a.o_vec = rows_aligned(out, 16) ? 1 : 0;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.n_qblk = plan.n_qblk;
+    a.n_blocks = (int)plan.grid;
+    a.keys_per_wave = plan.keys_per_wave;
+
+    const int D = (int)sh.D;
+    int err = plan.path == SDPA_PATH_FUSED
+                  ? sdpa::launch_fused(sh.dtype, D, sh.mask_kind, plan.waves, a, stream)
+                  : sdpa::launch_twopass(sh.dtype, D, sh.mask_kind, plan.waves, a, stream);
+    if (err != 0)
+        return fail(SDPA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(static_cast<hipError_t>(err)));
+    if (std::getenv("SDPA_MATH_DEBUG"))
+        std::fprintf(stderr, "sdpa_math: path=%s waves=%d grid=%lld tiles/bh=%lld tiles64/bh=%lld\n",
+                     plan.path == SDPA_PATH_FUSED ? "fused" : "twopass", plan.waves, (long long)plan.grid,
+                     (long long)plan.tiles_per_bh, (long long)plan.tiles_64);
+    return SDPA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sdpa_status_t sdpa_math_fwd(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_tensor_t* v,
+                            const sdpa_tensor_t* mask, int is_causal, float scale, int enable_gqa,
+                            sdpa_tensor_t* out, sdpa_tensor_t* probs, sdpa_tensor_t* lse, void* hip_stream) {
+    return run(q, k, v, mask, is_causal, scale, enable_gqa, out, probs, lse, hip_stream, SDPA_PATH_AUTO);
+}
+
+sdpa_status_t sdpa_math_fwd_path(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_tensor_t* v,
+                                 const sdpa_tensor_t* mask, int is_causal, float scale, int enable_gqa,
+                                 sdpa_tensor_t* out, sdpa_tensor_t* probs, sdpa_tensor_t* lse, void* hip_stream,
+                                 int path) {
+    return run(q, k, v, mask, is_causal, scale, enable_gqa, out, probs, lse, hip_stream, path);
+}
+
+sdpa_status_t sdpa_math_plan(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_tensor_t* v,
+                             const sdpa_tensor_t* mask, int is_causal, int enable_gqa, int32_t* path,
+                             int64_t* tiles_per_bh, int64_t* tiles_64) {
+    g_last_error.clear();
+    Shape sh;
+    sdpa_status_t st = validate_inputs(q, k, v, mask, is_causal, enable_gqa, &sh);
+    if (st) return st;
+    sdpa::Plan plan;
+    if ((st = make_plan(sh, is_causal != 0, SDPA_PATH_AUTO, &plan))) return st;
+    if (path) *path = plan.path;
+    if (tiles_per_bh) *tiles_per_bh = plan.tiles_per_bh;
+    if (tiles_64) *tiles_64 = plan.tiles_64;
+    return SDPA_OK;
+}
+
+const char* sdpa_math_last_error(void) { return g_last_error.c_str(); }
+
+int sdpa_math_version(void) { return SDPA_MATH_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,85 @@
+"""Shared helpers for GPU-vs-oracle parity checks (test code only)."""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import oracle
+
+# Max-abs bounds on O and P per compute dtype (the pages' f32/f16/bf16 bar),
+# and on LSE (float32 row statistics from dtype-exact inputs).
+TOL_OP = {torch.float32: 1e-5, torch.float16: 2e-3, torch.bfloat16: 8e-3}
+TOL_LSE = {torch.float32: 1e-5, torch.float16: 1e-4, torch.bfloat16: 1e-4}
+
+# An oracle probability this small may legitimately come back as 0: below half
+# the smallest subnormal of the output dtype it rounds to 0, and the kernel's
+# float32 exp2 does not produce float32 subnormals.
+UNDERFLOW = {torch.float32: 2.0 ** -126, torch.float16: 2.0 ** -25, torch.bfloat16: 2.0 ** -126}
+
+
+def poisoned_outputs(B, Hq, Sq, Skv, Dv, dtype, device):
+    """Output buffers filled with NaN so that an unwritten element cannot pass."""
+    O = torch.full((B, Hq, Sq, Dv), float("nan"), dtype=dtype, device=device)
+    P = torch.full((B, Hq, Sq, Skv), float("nan"), dtype=dtype, device=device)
+    L = torch.full((B, Hq, Sq), float("nan"), dtype=torch.float32, device=device)
+    return O, P, L
+
+
+def compare(O, P, L, ref, dtype, label=""):
+    """Element-by-element comparison against the float64 oracle.
+
+    Returns a dict of the observed errors; raises AssertionError on failure.
+    """
+    ro, rp, rl = ref
+    o = O.detach().cpu().double().numpy()
+    p = P.detach().cpu().double().numpy()
+    lse = L.detach().cpu().double().numpy()
+    assert o.shape == ro.shape and p.shape == rp.shape and lse.shape == rl.shape, label
+    assert not np.isnan(o).any(), f"{label}: NaN in O"
+    assert not np.isnan(p).any(), f"{label}: NaN in P"
+    assert not np.isnan(lse).any(), f"{label}: NaN in LSE"
+    err_o = float(np.abs(o - ro).max()) if o.size else 0.0
+    err_p = float(np.abs(p - rp).max()) if p.size else 0.0
+    tol = TOL_OP[dtype]
+    assert err_o <= tol, f"{label}: max|dO| = {err_o:.3e} > {tol} (max|O_ref| = {np.abs(ro).max():.3f})"
+    assert err_p <= tol, f"{label}: max|dP| = {err_p:.3e} > {tol}"
+    # dead rows: LSE exactly -inf; live rows within tolerance
+    dead = np.isneginf(rl)
+    assert np.array_equal(np.isneginf(lse), dead), f"{label}: dead-row pattern of LSE differs"
+    err_l = float(np.abs(lse[~dead] - rl[~dead]).max()) if (~dead).any() else 0.0
+    assert err_l <= TOL_LSE[dtype], f"{label}: max|dLSE| = {err_l:.3e}"
+    # masked-position pattern of P: bit-exact +0.0 where the oracle is exactly 0
+    if P.numel():
+        bits = P.detach().cpu().contiguous().view(torch.int16 if P.element_size() == 2 else torch.int32)
+        zero_bits = (bits == 0).numpy()
+        ref_zero = rp == 0
+        assert np.array_equal(zero_bits & ref_zero, ref_zero), f"{label}: a removed position is not +0.0"
+        unexpected = zero_bits & ~ref_zero & (rp >= UNDERFLOW[dtype])
+        assert not unexpected.any(), f"{label}: {int(unexpected.sum())} live positions came back as 0"
+    return {"err_o": err_o, "err_p": err_p, "err_lse": err_l, "max_abs_o_ref": float(np.abs(ro).max()) if ro.size else 0.0}
+
+
+def run_oracle(q, k, v, mask, causal, scale, gqa):
+    return oracle.sdpa_reference(q, k, v, mask, causal, scale, gqa)
+
+
+def head_slice(q, k, v, mask, b, h):
+    """Inputs restricted to batch b, query head h (and the KV head it reads)."""
+    g = q.shape[1] // k.shape[1]
+    hk = h // g
+    qs, ks, vs = q[b:b + 1, h:h + 1], k[b:b + 1, hk:hk + 1], v[b:b + 1, hk:hk + 1]
+    ms = None
+    if mask is not None:
+        m4 = mask
+        while m4.dim() < 4:
+            m4 = m4.unsqueeze(0)
+        mb = m4[b:b + 1] if m4.shape[0] > 1 else m4
+        ms = mb[:, h:h + 1] if mb.shape[1] > 1 else mb
+    return qs, ks, vs, ms
+
+
+def default_scale(D):
+    return 1.0 / math.sqrt(D)

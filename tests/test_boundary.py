@@ -1,0 +1,116 @@
+"""The C-ABI boundary on the CPU: the library loads, exports what the header
+declares, validates arguments before touching the GPU, and counts score tiles
+the way the FlagOS-OP page's path rule does (values printed on that page)."""
+
+import ctypes
+import json
+import os
+import re
+
+import pytest
+import torch
+
+import sdpa_forward_materialised_amd as S
+from sdpa_forward_materialised_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def _declared_functions():
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for fn in os.listdir(inc):
+        if not fn.endswith(".h"):
+            continue
+        text = open(os.path.join(inc, fn)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w \*]*?\b(sdpa_\w+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = S.load_library()
+    declared = _declared_functions()
+    assert {"sdpa_math_fwd", "sdpa_math_fwd_path", "sdpa_math_plan", "sdpa_math_last_error",
+            "sdpa_math_version"} <= declared
+    for name in declared:
+        assert hasattr(lib, name), f"{name} declared in include/ but not exported"
+    assert S.version() == 1
+
+
+def test_tile_counts_match_page_values():
+    g = json.load(open(os.path.join(GOLDEN, "page_tile_counts.json")))
+    for case in g["cases"]:
+        q = torch.zeros(1, 1, case["Sq"], 64, dtype=torch.float16)
+        k = torch.zeros(1, 1, case["Skv"], 64, dtype=torch.float16)
+        _, _, t64 = S.plan(q, k, k, is_causal=case["causal"])
+        assert t64 == case["tiles"], case["cite"]
+
+
+def _z(*shape, dtype=torch.float16):
+    return torch.zeros(*shape, dtype=dtype)
+
+
+@pytest.mark.parametrize("args,exc,frag", [
+    ((_z(1, 3, 8, 64), _z(1, 2, 8, 64), _z(1, 2, 8, 64)), ValueError, "not a multiple"),
+    ((_z(1, 4, 8, 64), _z(1, 2, 8, 64), _z(1, 2, 8, 64), None, False, False), ValueError, "enable_gqa"),
+    ((_z(1, 2, 8, 64), _z(1, 2, 8, 64), _z(1, 2, 8, 64), torch.ones(8, 8, dtype=torch.bool), True), ValueError,
+     "mutually exclusive"),
+    ((_z(1, 2, 8, 64), _z(1, 2, 8, 64), _z(1, 2, 8, 64), torch.ones(3, 8, dtype=torch.bool)), ValueError,
+     "broadcast"),
+    ((_z(1, 2, 8, 64), _z(1, 2, 8, 64), _z(1, 2, 8, 64), torch.ones(8, 8, dtype=torch.float32)), ValueError,
+     "mask dtype"),
+    ((_z(1, 2, 8, 64), _z(1, 2, 8, 64, dtype=torch.bfloat16), _z(1, 2, 8, 64)), ValueError, "dtypes differ"),
+    ((_z(2, 2, 8, 64), _z(1, 2, 8, 64), _z(1, 2, 8, 64)), ValueError, "batch"),
+    ((_z(1, 2, 8, 48), _z(1, 2, 8, 48), _z(1, 2, 8, 48)), NotImplementedError, "head dim"),
+    ((_z(1, 2, 8, 64), _z(1, 2, 8, 64), _z(1, 2, 8, 32)), NotImplementedError, "value head dim"),
+    ((_z(1, 2, 8, 128)[..., ::2], _z(1, 2, 8, 64), _z(1, 2, 8, 64)), NotImplementedError, "last dim"),
+    ((_z(1, 2, 8, 65)[..., 1:], _z(1, 2, 8, 64), _z(1, 2, 8, 64)), NotImplementedError, "aligned"),
+    ((_z(1, 2, 8, 64, dtype=torch.int32),) * 3, ValueError, "unsupported dtype"),
+])
+def test_validation_errors(args, exc, frag):
+    full = list(args) + [None, False, True][len(args) - 3:]
+    q, k, v, m, causal, gqa = full[:6]
+    with pytest.raises(exc) as ei:
+        S.plan(q, k, v, m, causal, gqa)
+    assert frag in str(ei.value)
+
+
+def test_fwd_rejects_bad_outputs_before_launch():
+    """Output descriptors are checked on the host; nothing reaches the GPU."""
+    lib = S.load_library()
+    q = _z(1, 2, 8, 64)
+    o, p, lse = _z(1, 2, 8, 64), _z(1, 2, 8, 9), torch.zeros(1, 2, 8)
+    d = [B._desc(t, 4) for t in (q, q, q, o, p)] + [B._desc(lse, 3)]
+    rc = lib.sdpa_math_fwd(ctypes.byref(d[0]), ctypes.byref(d[1]), ctypes.byref(d[2]), None, 0, 0.125, 0,
+                           ctypes.byref(d[3]), ctypes.byref(d[4]), ctypes.byref(d[5]), None)
+    assert rc == 1 and "probs dim 3" in S.last_error()
+    lse16 = B._desc(torch.zeros(1, 2, 8, dtype=torch.float16), 3)
+    p_ok = B._desc(_z(1, 2, 8, 8), 4)
+    rc = lib.sdpa_math_fwd(ctypes.byref(d[0]), ctypes.byref(d[1]), ctypes.byref(d[2]), None, 0, 0.125, 0,
+                           ctypes.byref(d[3]), ctypes.byref(p_ok), ctypes.byref(lse16), None)
+    assert rc == 1 and "lse must be f32" in S.last_error()
+    rc = lib.sdpa_math_fwd(None, ctypes.byref(d[1]), ctypes.byref(d[2]), None, 0, 0.125, 0,
+                           ctypes.byref(d[3]), ctypes.byref(p_ok), ctypes.byref(d[5]), None)
+    assert rc == 1 and "q is NULL" in S.last_error()
+    rc = lib.sdpa_math_fwd_path(ctypes.byref(d[0]), ctypes.byref(d[1]), ctypes.byref(d[2]), None, 0, 0.125, 0,
+                                ctypes.byref(d[3]), ctypes.byref(p_ok), ctypes.byref(d[5]), None, 7)
+    assert rc == 1 and "unknown path" in S.last_error()
+
+
+def test_binding_refuses_cpu_tensors():
+    q = _z(1, 2, 8, 64)
+    with pytest.raises(ValueError, match="GPU only"):
+        S.fwd(q, q, q)
+
+
+def test_plan_reports_paths_and_tiles():
+    q = _z(2, 16, 2048, 128, dtype=torch.bfloat16)
+    path, tiles, t64 = S.plan(q, q, q, is_causal=True)
+    assert t64 == 528 and path == "twopass"
+    q = _z(4, 32, 1024, 128)
+    k = _z(4, 8, 1024, 128)
+    m = torch.ones(4, 1, 1024, 1024, dtype=torch.bool)
+    assert S.plan(q, k, k, m, False, True)[2] == 256

@@ -1,0 +1,203 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Every case pre-poisons the outputs with NaN, runs ``sdpa_math_fwd_path`` on
+the MI355X, and compares O, P and LSE element by element with the oracle on
+the same seeded inputs (max-abs bounds per dtype, +0.0 bit pattern at every
+removed position, LSE = -inf exactly on dead rows).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import sdpa_workloads as W
+from parity import compare, head_slice, poisoned_outputs, run_oracle
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+PATHS = ["twopass"]
+
+
+def _lib():
+    import sdpa_forward_materialised_amd as S
+    S.load_library()
+    return S
+
+
+def _run(c, path, scale=None, gqa=None, label=""):
+    S = _lib()
+    q, k, v, m = c["q"], c["k"], c["v"], c["mask"]
+    B, Hq, Sq, D = q.shape
+    Skv, Dv = k.shape[2], v.shape[3]
+    if gqa is None:
+        gqa = q.shape[1] != k.shape[1]
+    out = poisoned_outputs(B, Hq, Sq, Skv, Dv, q.dtype, DEV)
+    print(f"[case] {label} path={path} shape={tuple(q.shape)}x{tuple(k.shape)} mask="
+          f"{None if m is None else (tuple(m.shape), m.dtype)} causal={c['causal']}", flush=True)
+    gm = None if m is None else m.to(DEV)
+    O, P, L = S.fwd(q.to(DEV), k.to(DEV), v.to(DEV), gm, c["causal"], scale, gqa, path=path, out=out)
+    torch.cuda.synchronize()
+    return O, P, L
+
+
+def _check(c, path, scale=None, label=""):
+    O, P, L = _run(c, path, scale, label=label)
+    gqa = c["q"].shape[1] != c["k"].shape[1]
+    ref = run_oracle(c["q"], c["k"], c["v"], c["mask"], c["causal"], scale, gqa)
+    return compare(O, P, L, ref, c["q"].dtype, label)
+
+
+# ------------------------------------------------------------ small cases, full oracle
+
+SMALL = [
+    # (label, make_case kwargs)
+    ("f16-d64-causal-ragged", dict(seed=101, dtype="f16", B=2, Hq=3, Hkv=3, Sq=150, Skv=150, D=64, causal=True)),
+    ("bf16-d128-causal-sq<skv", dict(seed=102, dtype="bf16", B=1, Hq=2, Hkv=2, Sq=70, Skv=200, D=128, causal=True)),
+    ("bf16-d128-causal-sq>skv", dict(seed=103, dtype="bf16", B=1, Hq=2, Hkv=2, Sq=200, Skv=70, D=128, causal=True)),
+    ("f32-d32-causal", dict(seed=104, dtype="f32", B=1, Hq=2, Hkv=2, Sq=64, Skv=64, D=32, causal=True)),
+    ("f32-d64-nomask-ragged", dict(seed=105, dtype="f32", B=2, Hq=2, Hkv=2, Sq=77, Skv=131, D=64)),
+    ("f32-d128-bool", dict(seed=106, dtype="f32", B=1, Hq=2, Hkv=1, Sq=96, Skv=100, D=128, mask="bool")),
+    ("f16-d32-bool-bcast", dict(seed=107, dtype="f16", B=2, Hq=4, Hkv=2, Sq=65, Skv=129, D=32, mask="bool",
+                                mask_shape=(1, 1, 65, 129))),
+    ("f16-d128-keypad", dict(seed=108, dtype="f16", B=2, Hq=8, Hkv=2, Sq=128, Skv=192, D=128, mask="bool",
+                             mask_shape=(2, 1, 1, 192), p=0.3)),
+    ("bf16-d64-add", dict(seed=109, dtype="bf16", B=2, Hq=2, Hkv=2, Sq=100, Skv=300, D=64, mask="add", p=0.1)),
+    ("f16-d64-neginf-heads", dict(seed=110, dtype="f16", B=1, Hq=4, Hkv=4, Sq=33, Skv=1152, D=64, mask="neginf",
+                                  mask_shape=(1, 4, 33, 1152))),
+    ("f32-d32-add-bcast-key", dict(seed=111, dtype="f32", B=2, Hq=2, Hkv=2, Sq=40, Skv=90, D=32, mask="add",
+                                   mask_shape=(90,), p=0.2)),
+    ("bf16-d32-single", dict(seed=112, dtype="bf16", B=1, Hq=1, Hkv=1, Sq=1, Skv=1, D=32)),
+    ("f16-d128-decode-row", dict(seed=113, dtype="f16", B=3, Hq=8, Hkv=8, Sq=1, Skv=1025, D=128)),
+    ("f16-d64-odd-skv", dict(seed=114, dtype="f16", B=1, Hq=2, Hkv=2, Sq=50, Skv=37, D=64, mask="bool")),
+]
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("label,spec", SMALL, ids=[s[0] for s in SMALL])
+def test_small_cases(label, spec, path):
+    c = W.make_case(**spec)
+    _check(c, path, label=label)
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_fully_masked_rows(path):
+    c = W.make_case(120, "f16", 2, 4, 2, 96, 160, 64, mask="bool", mask_shape=(2, 4, 96, 160), p=0.2)
+    c["mask"][0, 1, 5, :] = False
+    c["mask"][1, 3, 40:72, :] = False
+    O, P, L = _run(c, path, label="dead rows")
+    assert torch.all(P[0, 1, 5] == 0) and torch.all(O[0, 1, 5] == 0)
+    assert torch.isneginf(L[0, 1, 5]) and torch.isneginf(L[1, 3, 40:72]).all()
+    ref = run_oracle(c["q"], c["k"], c["v"], c["mask"], False, None, True)
+    compare(O, P, L, ref, torch.float16, "dead rows")
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_explicit_scale_and_strided_inputs(path):
+    # physical [B, S, H, D] viewed as logical [B, H, S, D]: only the last dim is dense
+    c = W.make_case(121, "bf16", 2, 4, 4, 80, 96, 64, causal=True)
+    for key in ("q", "k", "v"):
+        c[key] = c[key].transpose(1, 2).contiguous().transpose(1, 2)
+    _check(c, path, scale=0.05, label="strided scale=0.05")
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_gqa_matches_repeated_kv_bitwise(path):
+    c = W.make_case(122, "f16", 2, 8, 2, 70, 130, 64, mask="bool", mask_shape=(2, 1, 70, 130))
+    S = _lib()
+    q, k, v, m = (c[x].to(DEV) for x in ("q", "k", "v", "mask"))
+    a = S.fwd(q, k, v, m, False, None, True, path=path)
+    b = S.fwd(q, k.repeat_interleave(4, 1).contiguous(), v.repeat_interleave(4, 1).contiguous(), m, False, None,
+              False, path=path)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_deterministic(path):
+    c = W.make_case(123, "bf16", 1, 4, 4, 200, 200, 128, causal=True)
+    S = _lib()
+    q, k, v = (c[x].to(DEV) for x in ("q", "k", "v"))
+    a = S.fwd(q, k, v, None, True, path=path)
+    b = S.fwd(q, k, v, None, True, path=path)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_degenerate_shapes():
+    S = _lib()
+    q = torch.randn(2, 2, 0, 64, device=DEV, dtype=torch.float16)
+    k = torch.randn(2, 2, 10, 64, device=DEV, dtype=torch.float16)
+    O, P, L = S.fwd(q, k, k)
+    assert O.shape == (2, 2, 0, 64) and P.shape == (2, 2, 0, 10) and L.shape == (2, 2, 0)
+    # no keys at all: O = 0, LSE = -inf
+    q = torch.randn(1, 2, 5, 32, device=DEV, dtype=torch.bfloat16)
+    k = torch.randn(1, 2, 0, 32, device=DEV, dtype=torch.bfloat16)
+    out = poisoned_outputs(1, 2, 5, 0, 32, torch.bfloat16, DEV)
+    O, P, L = S.fwd(q, k, k, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(O == 0) and torch.isneginf(L).all() and P.numel() == 0
+
+
+def test_errors_leave_outputs_untouched():
+    S = _lib()
+    q = torch.randn(1, 3, 8, 64, device=DEV, dtype=torch.float16)
+    k = torch.randn(1, 2, 8, 64, device=DEV, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        S.fwd(q, k, k, enable_gqa=True)
+    q = torch.randn(1, 2, 8, 48, device=DEV, dtype=torch.float16)
+    with pytest.raises(NotImplementedError):
+        S.fwd(q, q, q)
+    q = torch.randn(1, 2, 8, 64, device=DEV, dtype=torch.float16)
+    m = torch.ones(8, 8, dtype=torch.bool, device=DEV)
+    with pytest.raises(ValueError):
+        S.fwd(q, q, q, m, is_causal=True)
+
+
+# ------------------------------------------------------------ the five workloads
+
+def _workload_case(w):
+    inp = W.make_inputs(w)
+    inp["causal"] = w.causal
+    return inp
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("w", [w for w in W.WORKLOADS if w.name.startswith(("tiny", "decode"))],
+                         ids=lambda w: w.name)
+def test_workload_full_oracle(w, path):
+    """Workloads the oracle finishes in seconds: every output element checked."""
+    c = _workload_case(w)
+    r = _check(c, path, scale=w.scale, label=w.name)
+    print(f"[result] {w.name} {path} {r}", flush=True)
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("w", [w for w in W.WORKLOADS if w.name.startswith(("prefill", "gqa"))],
+                         ids=lambda w: w.name)
+def test_workload_full_size(w, path):
+    """Full-size workloads: sampled (batch, head) slices against the oracle,
+    plus properties of the whole output that hold at any size."""
+    c = _workload_case(w)
+    O, P, L = _run(c, path, scale=w.scale, label=w.name)
+    dt = c["q"].dtype
+    # sampled heads, every element of each
+    picks = [(0, 0), (w.B - 1, w.Hq - 1), (w.B // 2, w.Hq // 2 + 1)]
+    for b, h in picks:
+        qs, ks, vs, ms = head_slice(c["q"], c["k"], c["v"], c["mask"], b, h)
+        ref = run_oracle(qs, ks, vs, ms, w.causal, w.scale, False)
+        r = compare(O[b:b + 1, h:h + 1], P[b:b + 1, h:h + 1], L[b:b + 1, h:h + 1], ref, dt, f"{w.name} b{b} h{h}")
+        print(f"[result] {w.name} {path} b={b} h={h} {r}", flush=True)
+    # whole-output properties
+    assert not torch.isnan(O).any() and not torch.isnan(P).any() and not torch.isnan(L).any()
+    rows = P.float().sum(-1)
+    dead = torch.isneginf(L)
+    assert torch.allclose(rows[~dead], torch.ones_like(rows[~dead]), atol=1e-2)
+    assert torch.all(rows[dead] == 0)
+    if w.causal:
+        upper = torch.ones(w.Sq, w.Skv, dtype=torch.bool, device=DEV).triu(1)
+        assert torch.all(P[:, :, upper] == 0)
+    if w.mask == "keypad_bool":
+        assert dead[0, :, :8].all() and (dead.sum().item() == 8 * w.Hq)
