@@ -31,6 +31,10 @@ struct FwdArgs {
     int n_qblk;      // query blocks per (batch, head)
     int n_blocks;    // workgroups in the grid
     int keys_per_wave;  // fused path: key range of one wave
+    int sched;       // workgroup order: 0 head-major, 1 heavy/light pairs per XCD (causal)
+    // Byte extent of one (batch, head) slice of each tensor (< 2^31); the
+    // kernels address every tensor through a buffer descriptor of this size.
+    uint32_t q_ext, k_ext, v_ext, o_ext, p_ext, m_ext, l_ext;
 };
 
 // Launch configuration chosen on the host for one call.
@@ -45,9 +49,14 @@ struct Plan {
     int64_t tiles_64;
 };
 
-// Kernel launchers (sdpa_kernels.hip). Return a hipError_t as int.
-int launch_twopass(int dtype, int D, int mask_kind, int waves, const FwdArgs& a, void* stream);
-int launch_fused(int dtype, int D, int mask_kind, int waves, const FwdArgs& a, void* stream);
+// Kernel launchers, one translation unit per dtype. `vec` selects the
+// variant with 16-byte row stores and vector mask loads (rows aligned, Skv a
+// multiple of 8, mask contiguous in its last dim); the other variant handles
+// any layout element by element. Return a hipError_t as int.
+int launch_twopass_f32(int D, int mask_kind, int waves, bool vec, const FwdArgs& a, void* stream);
+int launch_twopass_f16(int D, int mask_kind, int waves, bool vec, const FwdArgs& a, void* stream);
+int launch_twopass_bf16(int D, int mask_kind, int waves, bool vec, const FwdArgs& a, void* stream);
+int launch_fused(int dtype, int D, int mask_kind, int waves, bool vec, const FwdArgs& a, void* stream);
 
 // Largest key range the fused path keeps on chip per wave.
 constexpr int FUSED_MAX_KEYS_PER_WAVE = 256;

@@ -247,6 +247,10 @@ sdpa_status_t make_plan(const Shape& sh, bool causal, int forced, sdpa::Plan* p)
         // that leaves fewer than two workgroups per compute unit.
         const int64_t bh = sh.B * sh.Hq;
         p->waves = (bh * cdiv(sh.Sq, 128) >= 512) ? 4 : 2;
+        if (const char* e = std::getenv("SDPA_MATH_TP_WAVES")) {
+            const int wv = std::atoi(e);
+            if (wv == 2 || wv == 4) p->waves = wv;
+        }
         p->keys_per_wave = 0;
         p->q_rows = 32 * p->waves;
     }
@@ -299,24 +303,62 @@ sdpa_status_t run(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_ten
     a.Skv = (int)sh.Skv;
     a.group = (int)(sh.Hq / sh.Hkv);
     a.causal = is_causal ? 1 : 0;
-    const int64_t mvec_align = sh.mask_kind == sdpa::MASK_BOOL ? 8 : 16;
-    a.mask_vec = mask && a.m_s[3] == 1 && rows_aligned(mask, mvec_align) ? 1 : 0;
+    const int64_t es = elt_size(sh.dtype);
+    const int64_t me = sh.mask_kind == sdpa::MASK_BOOL ? 1 : es;
+    a.mask_vec = mask && a.m_s[3] == 1 && rows_aligned(mask, me == 1 ? 8 : 16) ? 1 : 0;
     a.p_vec = rows_aligned(probs, 16) ? 1 : 0;
     a.o_vec = rows_aligned(out, 16) ? 1 : 0;
+    const bool vec = a.p_vec && a.o_vec && sh.Skv % 8 == 0 && (!mask || a.mask_vec);
     a.scale_log2 = scale * 1.4426950408889634f;
     a.n_qblk = plan.n_qblk;
     a.n_blocks = (int)plan.grid;
     a.keys_per_wave = plan.keys_per_wave;
+    a.sched = 0;
+    if (is_causal && plan.grid % 8 == 0) {
+        const int64_t per = plan.grid / 8;
+        if (per % plan.n_qblk == 0 && per % 2 == 0) a.sched = 1;
+    }
+    if (const char* e = std::getenv("SDPA_MATH_SCHED")) {
+        if (*e == '0') a.sched = 0;
+    }
+
+    // byte extent of one (batch, head) slice of each tensor
+    int64_t ext[7];
+    ext[0] = ((sh.Sq - 1) * a.q_s[2] + sh.D) * es;
+    ext[1] = sh.Skv > 0 ? ((sh.Skv - 1) * a.k_s[2] + sh.D) * es : 0;
+    ext[2] = sh.Skv > 0 ? ((sh.Skv - 1) * a.v_s[2] + sh.Dv) * es : 0;
+    ext[3] = ((sh.Sq - 1) * a.o_s[2] + sh.Dv) * es;
+    ext[4] = ((sh.Sq - 1) * a.p_s[2] + sh.Skv) * es;
+    ext[5] = (mask && sh.Skv > 0) ? ((sh.Sq - 1) * a.m_s[2] + (sh.Skv - 1) * a.m_s[3] + 1) * me : 0;
+    ext[6] = ((sh.Sq - 1) * a.l_s[2] + 1) * 4;
+    for (int i = 0; i < 7; ++i)
+        if (ext[i] < 0 || ext[i] >= (int64_t(1) << 31))
+            return fail(SDPA_ERR_UNSUPPORTED, "one (batch, head) slice spans 2 GiB or more");
+    a.q_ext = (uint32_t)ext[0];
+    a.k_ext = (uint32_t)ext[1];
+    a.v_ext = (uint32_t)ext[2];
+    a.o_ext = (uint32_t)ext[3];
+    a.p_ext = (uint32_t)ext[4];
+    a.m_ext = (uint32_t)ext[5];
+    a.l_ext = (uint32_t)ext[6];
 
     const int D = (int)sh.D;
-    int err = plan.path == SDPA_PATH_FUSED
-                  ? sdpa::launch_fused(sh.dtype, D, sh.mask_kind, plan.waves, a, stream)
-                  : sdpa::launch_twopass(sh.dtype, D, sh.mask_kind, plan.waves, a, stream);
+    int err;
+    if (plan.path == SDPA_PATH_FUSED) {
+        err = sdpa::launch_fused(sh.dtype, D, sh.mask_kind, plan.waves, vec, a, stream);
+    } else if (sh.dtype == SDPA_BF16) {
+        err = sdpa::launch_twopass_bf16(D, sh.mask_kind, plan.waves, vec, a, stream);
+    } else if (sh.dtype == SDPA_F16) {
+        err = sdpa::launch_twopass_f16(D, sh.mask_kind, plan.waves, vec, a, stream);
+    } else {
+        err = sdpa::launch_twopass_f32(D, sh.mask_kind, plan.waves, vec, a, stream);
+    }
     if (err != 0)
         return fail(SDPA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(static_cast<hipError_t>(err)));
     if (std::getenv("SDPA_MATH_DEBUG"))
-        std::fprintf(stderr, "sdpa_math: path=%s waves=%d grid=%lld tiles/bh=%lld tiles64/bh=%lld\n",
-                     plan.path == SDPA_PATH_FUSED ? "fused" : "twopass", plan.waves, (long long)plan.grid,
+        std::fprintf(stderr, "sdpa_math: path=%s waves=%d vec=%d sched=%d grid=%lld tiles/bh=%lld tiles64/bh=%lld\n",
+                     plan.path == SDPA_PATH_FUSED ? "fused" : "twopass", plan.waves, vec ? 1 : 0, a.sched,
+                     (long long)plan.grid,
                      (long long)plan.tiles_per_bh, (long long)plan.tiles_64);
     return SDPA_OK;
 }

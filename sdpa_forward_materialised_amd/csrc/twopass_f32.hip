@@ -1,0 +1,10 @@
+// Two-sweep kernel instantiations for f32 inputs.
+#include "twopass.h"
+
+namespace sdpa {
+
+int launch_twopass_f32(int D, int mask_kind, int waves, bool vec, const FwdArgs& a, void* stream) {
+    return launch_twopass_t<float>(D, mask_kind, waves, vec, a, stream);
+}
+
+}  // namespace sdpa
