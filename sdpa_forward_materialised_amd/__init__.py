@@ -8,6 +8,6 @@ is argument marshalling only; torch supplies device memory and streams.
 """
 
 from ._binding import (EXPORTS, LIB_PATH, PATHS, fwd, last_error, load_library, plan,  # noqa: F401
-                       version)
+                       probe_copy, probe_fill, version)
 
 __all__ = ["fwd", "plan", "version", "last_error", "load_library", "LIB_PATH", "PATHS", "EXPORTS"]

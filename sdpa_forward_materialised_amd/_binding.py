@@ -27,7 +27,7 @@ _DTYPES = {torch.float32: SDPA_F32, torch.float16: SDPA_F16, torch.bfloat16: SDP
            torch.bool: SDPA_BOOL}
 
 EXPORTS = ("sdpa_math_fwd", "sdpa_math_fwd_path", "sdpa_math_plan", "sdpa_math_last_error",
-           "sdpa_math_version")
+           "sdpa_math_version", "sdpa_probe_fill", "sdpa_probe_copy")
 
 
 class SdpaTensor(ctypes.Structure):
@@ -59,6 +59,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sdpa_math_last_error.argtypes = []
     lib.sdpa_math_version.restype = ctypes.c_int
     lib.sdpa_math_version.argtypes = []
+    lib.sdpa_probe_fill.restype = ctypes.c_int
+    lib.sdpa_probe_fill.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint32, ctypes.c_void_p]
+    lib.sdpa_probe_copy.restype = ctypes.c_int
+    lib.sdpa_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     _lib = lib
     return lib
 
@@ -169,6 +173,31 @@ def plan(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, attn_mask: Optional[
     if rc != 0:
         _raise(rc, lib)
     return PATH_NAMES[path.value], tiles.value, tiles64.value
+
+
+def probe_fill(dst: torch.Tensor, value: int = 0) -> None:
+    """Streaming write of `dst` (whole tensor) with the library's fill kernel."""
+    lib = load_library()
+    _check_devices(dst)
+    with torch.cuda.device(dst.device):
+        rc = lib.sdpa_probe_fill(ctypes.c_void_p(dst.data_ptr()), dst.numel() * dst.element_size(), value,
+                                 ctypes.c_void_p(torch.cuda.current_stream(dst.device).cuda_stream))
+    if rc != 0:
+        raise RuntimeError(f"sdpa_probe_fill failed with hip error {rc}")
+
+
+def probe_copy(dst: torch.Tensor, src: torch.Tensor) -> None:
+    """Streaming copy src -> dst (same byte size) with the library's copy kernel."""
+    lib = load_library()
+    _check_devices(dst, src)
+    nbytes = dst.numel() * dst.element_size()
+    if nbytes != src.numel() * src.element_size():
+        raise ValueError("probe_copy needs equal byte sizes")
+    with torch.cuda.device(dst.device):
+        rc = lib.sdpa_probe_copy(ctypes.c_void_p(dst.data_ptr()), ctypes.c_void_p(src.data_ptr()), nbytes,
+                                 ctypes.c_void_p(torch.cuda.current_stream(dst.device).cuda_stream))
+    if rc != 0:
+        raise RuntimeError(f"sdpa_probe_copy failed with hip error {rc}")
 
 
 def version() -> int:

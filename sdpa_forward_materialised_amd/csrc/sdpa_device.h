@@ -57,7 +57,15 @@ __device__ __forceinline__ uint32_t pred(bool ok, uint32_t off) { return ok ? of
 
 __device__ __forceinline__ u32x4 ld128(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0); }
 __device__ __forceinline__ u32x2 ld64(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0); }
-__device__ __forceinline__ void st128(rsrc_t r, uint32_t off, u32x4 v) { __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0); }
+// A 16-byte store reads its data registers after issue; the following
+// instruction must not rewrite them. The s_nop below (two wait states) both
+// supplies that wait and keeps the data registers allocated across it (the
+// register allocator was seen reusing them in the very next instruction).
+__device__ __forceinline__ void st128s(rsrc_t r, uint32_t voff, uint32_t soff, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, 0);
+    asm volatile("s_nop 1" ::"v"(v));
+}
+__device__ __forceinline__ void st128(rsrc_t r, uint32_t off, u32x4 v) { st128s(r, off, 0, v); }
 
 // ---------------------------------------------------------------- element traits
 
@@ -102,6 +110,7 @@ template <> struct Tr<float> {
 // 16-byte chunk <-> operand vector
 template <typename T>
 __device__ __forceinline__ typename Tr<T>::vec as_vec(u32x4 x) {
+    static_assert(sizeof(T) == 2, "16-byte operand vectors are 16-bit elements");
     return __builtin_bit_cast(typename Tr<T>::vec, x);
 }
 

@@ -227,7 +227,23 @@ bool fused_config(const Shape& sh, bool causal, int* waves, int* keys_per_wave) 
 
 bool fused_available() { return false; }  // the fused kernel is not built yet
 
-sdpa_status_t make_plan(const Shape& sh, bool causal, int forced, sdpa::Plan* p) {
+// True when the 16-byte variant of the two-pass kernel can run: probability
+// and output rows 16-byte aligned (null: the default dense outputs), Skv a
+// multiple of 8, and a mask (if any) contiguous along the keys with 16-byte
+// aligned rows and whole 16-byte chunks.
+bool staged_layout(const Shape& sh, const sdpa_tensor_t* mask, const sdpa_tensor_t* out,
+                   const sdpa_tensor_t* probs) {
+    if (sh.Skv % 8) return false;
+    if (out && !rows_aligned(out, 16)) return false;
+    if (probs && !rows_aligned(probs, 16)) return false;
+    if (mask) {
+        const int64_t me = sh.mask_kind == sdpa::MASK_BOOL ? 1 : elt_size(sh.dtype);
+        if (eff_stride(mask, 3) != 1 || !rows_aligned(mask, 16) || sh.Skv % (16 / me)) return false;
+    }
+    return true;
+}
+
+sdpa_status_t make_plan(const Shape& sh, bool causal, int forced, bool vec, sdpa::Plan* p) {
     p->tiles_64 = count_tiles(sh.Sq, sh.Skv, causal, 64);
     int fw = 0, fk = 0;
     const bool fused_ok = fused_available() && fused_config(sh, causal, &fw, &fk);
@@ -243,14 +259,21 @@ sdpa_status_t make_plan(const Shape& sh, bool causal, int forced, sdpa::Plan* p)
         p->keys_per_wave = fk;
         p->q_rows = 32;
     } else {
-        // Four waves (128 rows) share each staged K/V tile; drop to two when
-        // that leaves fewer than two workgroups per compute unit.
+        // Several compute waves share each staged K/V tile; drop to two when
+        // that leaves fewer than two workgroups per compute unit. 128-wide
+        // heads need about 256 VGPRs per compute wave (two waves per SIMD):
+        // three compute waves plus the loader wave fill a CU with two
+        // workgroups. Narrower heads fit 168 VGPRs and take four.
         const int64_t bh = sh.B * sh.Hq;
-        p->waves = (bh * cdiv(sh.Sq, 128) >= 512) ? 4 : 2;
+        const int wide = sh.D == 128 ? 3 : 4;
+        p->waves = (bh * cdiv(sh.Sq, 32 * wide) >= 512) ? wide : 2;
         if (const char* e = std::getenv("SDPA_MATH_TP_WAVES")) {
             const int wv = std::atoi(e);
-            if (wv == 2 || wv == 4) p->waves = wv;
+            if (wv >= 2 && wv <= wide) p->waves = wv;
         }
+        // float32 128-wide tiles only fit LDS with two compute waves; the
+        // element-wise variant is built with two only
+        if ((sh.dtype == SDPA_F32 && sh.D == 128) || !vec) p->waves = 2;
         p->keys_per_wave = 0;
         p->q_rows = 32 * p->waves;
     }
@@ -261,8 +284,12 @@ sdpa_status_t make_plan(const Shape& sh, bool causal, int forced, sdpa::Plan* p)
     return SDPA_OK;
 }
 
+// Strides (batch, head, row) in elements. A size-1 batch or head dim never
+// advances (stride 0); a single row gets the row length as its pitch so that
+// rows past the end fall outside the per-(batch, head) buffer descriptor.
 void fill_strides3(const sdpa_tensor_t* t, int64_t* s) {
-    for (int d = 0; d < 3; ++d) s[d] = eff_stride(t, d);
+    for (int d = 0; d < 2; ++d) s[d] = eff_stride(t, d);
+    s[2] = t->sizes[2] == 1 ? t->sizes[3] : t->strides[2];
 }
 
 sdpa_status_t run(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_tensor_t* v, const sdpa_tensor_t* mask,
@@ -276,8 +303,9 @@ sdpa_status_t run(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_ten
     if ((st = validate_outputs(sh, out, probs, lse))) return st;
     if (!std::isfinite(scale)) return fail(SDPA_ERR_INVALID_ARG, "scale must be finite");
     if (sh.B * sh.Hq * sh.Sq == 0) return SDPA_OK;
+    const bool vec = staged_layout(sh, mask, out, probs);
     sdpa::Plan plan;
-    if ((st = make_plan(sh, is_causal != 0, path, &plan))) return st;
+    if ((st = make_plan(sh, is_causal != 0, path, vec, &plan))) return st;
 
     sdpa::FwdArgs a;
     std::memset(&a, 0, sizeof a);
@@ -305,10 +333,9 @@ sdpa_status_t run(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_ten
     a.causal = is_causal ? 1 : 0;
     const int64_t es = elt_size(sh.dtype);
     const int64_t me = sh.mask_kind == sdpa::MASK_BOOL ? 1 : es;
-    a.mask_vec = mask && a.m_s[3] == 1 && rows_aligned(mask, me == 1 ? 8 : 16) ? 1 : 0;
-    a.p_vec = rows_aligned(probs, 16) ? 1 : 0;
-    a.o_vec = rows_aligned(out, 16) ? 1 : 0;
-    const bool vec = a.p_vec && a.o_vec && sh.Skv % 8 == 0 && (!mask || a.mask_vec);
+    a.mask_vec = vec && mask;
+    a.p_vec = vec;
+    a.o_vec = vec;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.n_qblk = plan.n_qblk;
     a.n_blocks = (int)plan.grid;
@@ -332,8 +359,8 @@ sdpa_status_t run(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_ten
     ext[5] = (mask && sh.Skv > 0) ? ((sh.Sq - 1) * a.m_s[2] + (sh.Skv - 1) * a.m_s[3] + 1) * me : 0;
     ext[6] = ((sh.Sq - 1) * a.l_s[2] + 1) * 4;
     for (int i = 0; i < 7; ++i)
-        if (ext[i] < 0 || ext[i] >= (int64_t(1) << 31))
-            return fail(SDPA_ERR_UNSUPPORTED, "one (batch, head) slice spans 2 GiB or more");
+        if (ext[i] < 0 || ext[i] >= (int64_t(1) << 30))
+            return fail(SDPA_ERR_UNSUPPORTED, "one (batch, head) slice spans 1 GiB or more");
     a.q_ext = (uint32_t)ext[0];
     a.k_ext = (uint32_t)ext[1];
     a.v_ext = (uint32_t)ext[2];
@@ -388,7 +415,8 @@ sdpa_status_t sdpa_math_plan(const sdpa_tensor_t* q, const sdpa_tensor_t* k, con
     sdpa_status_t st = validate_inputs(q, k, v, mask, is_causal, enable_gqa, &sh);
     if (st) return st;
     sdpa::Plan plan;
-    if ((st = make_plan(sh, is_causal != 0, SDPA_PATH_AUTO, &plan))) return st;
+    if ((st = make_plan(sh, is_causal != 0, SDPA_PATH_AUTO, staged_layout(sh, mask, nullptr, nullptr), &plan)))
+        return st;
     if (path) *path = plan.path;
     if (tiles_per_bh) *tiles_per_bh = plan.tiles_per_bh;
     if (tiles_64) *tiles_64 = plan.tiles_64;

@@ -11,14 +11,17 @@
 // kernels). Unlike the page's two-stage Triton path, P is never read back:
 // P·V is accumulated in the pass that writes it.
 //
-// One workgroup = NW waves x 32 query rows of one (batch, query head). Each
-// 64-key tile of K (both sweeps) and V^T (sweep 2) is staged through LDS once
-// and shared by all waves; tiles are double-buffered with the next one
-// prefetched into registers while the current one is consumed, so one
-// barrier per tile suffices. Every global access goes through a buffer
-// descriptor with out-of-range lanes predicated off (no branches), all loads
-// a tile needs are issued before the previous tile's probability stores, and
-// the causal zero region is written after the last tile.
+// Workgroup = NW compute waves (32 query rows each, one (batch, query head))
+// plus one loader wave. The loader wave copies each 64-key tile of K (and of
+// V and the mask in sweep 2) from global memory straight into LDS with
+// buffer-to-LDS loads, double-buffered, one barrier per tile. The compute
+// waves issue no global loads inside the loops, so their probability stores
+// are never waited for: on this hardware a wait for a load also waits for
+// every store issued before it, and the probability map is most of the
+// traffic. The LDS tile layouts make every operand read a per-lane base plus
+// a constant offset, free of bank conflicts; the V^T operand of
+// O^T += V^T P^T is read with the gfx950 transposing LDS read
+// (ds_read_b64_tr_b16).
 
 #pragma once
 
@@ -26,124 +29,179 @@
 
 namespace sdpa {
 
-// Mask bits for the 64 keys of one tile, fetched one tile ahead.
-template <typename T, int MASK, bool VEC>
-struct MaskPrefetch {
-    __device__ __forceinline__ void load(const FwdArgs&, rsrc_t, uint32_t, int, int) {}
-    __device__ __forceinline__ void get(const FwdArgs&, rsrc_t, uint32_t, int, int, int, float*) const {}
-};
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) void lds_void;
 
-// Vectorised masks: per lane 4 runs of 8 keys (2 blocks x 2 runs).
-template <typename T, int MASK>
-struct MaskPrefetch<T, MASK, true> {
-    static constexpr int ME = MASK == MASK_BOOL ? 1 : (int)sizeof(T);
-    static constexpr int NCH = MASK == MASK_NONE ? 0 : (ME == 4 ? 8 : 4);  // 16-byte chunks (bool: 8 bytes)
-    u32x4 raw[NCH > 0 ? NCH : 1];
+// Transposing LDS read: within each 16-lane group, output lane 4a+b receives
+// element b of the 4-element reads made by source lanes 4j+a, j = 0..3.
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p));
+}
 
-    __device__ __forceinline__ void load(const FwdArgs& a, rsrc_t mr, uint32_t row_off, int k0, int hf) {
-        if constexpr (MASK != MASK_NONE) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int j = k0 + 32 * (q >> 1) + 16 * (q & 1) + 8 * hf;
-                const uint32_t off = pred(j < a.Skv, row_off + (uint32_t)j * ME);
-                if constexpr (ME == 1) {
-                    const u32x2 w = ld64(mr, off);
-                    raw[q] = u32x4{w[0], w[1], 0u, 0u};
-                } else if constexpr (ME == 2) {
-                    raw[q] = ld128(mr, off);
-                } else {
-                    raw[2 * q] = ld128(mr, off);
-                    raw[2 * q + 1] = ld128(mr, off == OOB ? OOB : off + 16);
-                }
-            }
-        }
-    }
-    // decoded terms for block kb (16 values in accumulator-register order)
-    __device__ __forceinline__ void get(const FwdArgs&, rsrc_t, uint32_t, int, int, int kb, float* out) const {
-        if constexpr (MASK != MASK_NONE) {
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const int q = 2 * kb + c;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    float v;
-                    if constexpr (MASK == MASK_BOOL) {
-                        v = ((raw[q][e >> 2] >> (8 * (e & 3))) & 0xffu) ? 1.0f : 0.0f;
-                    } else if constexpr (ME == 2) {
-                        v = Tr<T>::to_f((raw[q][e >> 1] >> (16 * (e & 1))) & 0xffffu) * LOG2E;
-                    } else {
-                        v = __builtin_bit_cast(float, raw[2 * q + (e >> 2)][e & 3]) * LOG2E;
-                    }
-                    out[8 * c + e] = v;
-                }
-            }
-        }
-    }
-};
+// vmcnt(0) only (expcnt and lgkmcnt left at their maxima)
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// Element-wise masks (any layout): read when needed.
-template <typename T, int MASK>
-struct MaskPrefetch<T, MASK, false> {
-    __device__ __forceinline__ void load(const FwdArgs&, rsrc_t, uint32_t, int, int) {}
-    __device__ __forceinline__ void get(const FwdArgs& a, rsrc_t mr, uint32_t row_off, int k0, int hf, int kb,
-                                        float* out) const {
-        if constexpr (MASK != MASK_NONE) load_mask16<T, MASK, false>(a, mr, row_off, k0 + 32 * kb, hf, out);
+template <typename T, int D, int NW, int MASK, bool VEC>
+struct TwoPassCfg {
+    static constexpr int SZ = (int)sizeof(T);
+    static constexpr int QB = 32 * NW;            // query rows per workgroup
+    static constexpr int ROWB = D * SZ;           // bytes per K/V row
+    static constexpr int CPR = ROWB / 16;         // 16-byte chunks per K/V row
+    static constexpr int RPI = 64 / CPR;          // tile rows per buffer-to-LDS instruction
+    static constexpr int NI = BN / RPI;           // instructions per K (or V) tile
+    static constexpr int RPB = ROWB >= 256 ? 1 : 256 / ROWB;  // rows per 64-bank span
+    static constexpr int TILEB = BN * ROWB;       // bytes per K (or V) tile
+    static constexpr int ME = MASK == MASK_BOOL ? 1 : SZ;
+    static constexpr bool MLDS = MASK != MASK_NONE && VEC;  // mask tiles staged in LDS
+    static constexpr int MROWB = BN * ME;         // bytes per mask tile row
+    static constexpr int MCPR = MROWB / 16;
+    static constexpr int MRPI = 64 / MCPR;
+    static constexpr int MNI = QB / MRPI;
+    static constexpr int MTILEB = MLDS ? QB * MROWB : 0;
+    static constexpr int LDS_BYTES = 2 * (2 * TILEB + MTILEB);
+    static_assert(LDS_BYTES <= 160 * 1024, "tile buffers exceed the 160 KB LDS of a compute unit");
+    // LDS tile layouts, in 16-byte chunk positions. Every operand read is a
+    // per-lane base plus a compile-time offset, and free of bank conflicts:
+    //  K: per 32-row block, per chunk pair: 32 rows of the even chunk, then
+    //     32 rows of the odd chunk (a lane reads row r, chunk 2c + h at r + 32h
+    //     + 64c: 16 consecutive rows hit 16 distinct bank groups);
+    //  V: per 16-row block, per group of 4 chunks: row-major 16 x 4 (the
+    //     transposing read takes 4 rows x 2 chunks per 16-lane group, which
+    //     land on 8 distinct bank groups).
+    static __device__ __forceinline__ int pos_k(int row, int chunk) {
+        return (row >> 5) * (32 * CPR) + (chunk >> 1) * 64 + (row & 31) + 32 * (chunk & 1);
     }
+    static __device__ __forceinline__ int pos_v(int row, int chunk) {
+        return (row >> 4) * (16 * CPR) + (chunk >> 2) * 64 + 4 * (row & 15) + (chunk & 3);
+    }
+    static_assert(CPR % 4 == 0, "tile layouts need a multiple of 4 chunks per row");
 };
 
 template <typename T, int D, int NW, int MASK, bool VEC>
-__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(2)))
+__global__ __attribute__((amdgpu_flat_work_group_size((NW + 1) * 64, (NW + 1) * 64),
+                          amdgpu_waves_per_eu(NW >= 4 ? 3 : 2)))
 void sdpa_twopass_kernel(const FwdArgs a) {
+    using C = TwoPassCfg<T, D, NW, MASK, VEC>;
     using TR = Tr<T>;
     using vec = typename TR::vec;
-    constexpr int SZ = (int)sizeof(T);
+    constexpr int SZ = C::SZ;
     constexpr int KH = TR::KH;
     constexpr int KSTEP = 2 * KH;
     constexpr int NKS = D / KSTEP;           // MFMAs per 32x32 score block
-    constexpr int NT = NW * 64;
-    constexpr int QB = 32 * NW;
-    constexpr int E16 = 16 / SZ;             // elements per 16-byte chunk
-    constexpr int KLD = D + E16;             // LDS row pitch of a K tile (padded)
-    constexpr int VLD = BN + E16;            // LDS row pitch of a V^T tile (padded)
-    constexpr int CPR = D / E16;             // 16-byte chunks per K/V row
-    constexpr int KCH = (BN * CPR + NT - 1) / NT;        // K chunks per thread
-    constexpr int NVI = (BN / 4) * CPR;                  // V items: 4 keys x one chunk
-    constexpr int VIT = (NVI + NT - 1) / NT;             // V items per thread
+    constexpr int QB = C::QB;
     constexpr int ND = D / 32;               // 32-wide head-dim chunks of O^T
-    constexpr int ME = MASK == MASK_BOOL ? 1 : SZ;
+    constexpr int ME = C::ME;
 
-    __shared__ __attribute__((aligned(16))) T k_lds[2][BN * KLD];
-    __shared__ __attribute__((aligned(16))) T vt_lds[2][D * VLD];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS_BYTES];
+    auto kbuf = [&](int b) -> uint8_t* { return smem + b * C::TILEB; };
+    auto vbuf = [&](int b) -> uint8_t* { return smem + 2 * C::TILEB + b * C::TILEB; };
+    auto mbuf = [&](int b) -> uint8_t* { return smem + 4 * C::TILEB + b * C::MTILEB; };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar
     const int n = lane & 31;
     const int hf = lane >> 5;
 
     const Work w = decode_block(blockIdx.x, a);
     const int hk = w.hq / a.group;
     const int q0 = w.qblk * QB;
+    const int kend = a.causal ? min(a.Skv, q0 + QB) : a.Skv;
+    const int ntiles = (kend + BN - 1) / BN;
+
+    const rsrc_t kr = make_rsrc(static_cast<const T*>(a.k) + w.b * a.k_s[0] + hk * a.k_s[1], a.k_ext);
+    const rsrc_t vr = make_rsrc(static_cast<const T*>(a.v) + w.b * a.v_s[0] + hk * a.v_s[1], a.v_ext);
+    rsrc_t mr = kr;
+    if constexpr (MASK != MASK_NONE)
+        mr = make_rsrc(static_cast<const uint8_t*>(a.mask) + (w.b * a.m_s[0] + w.hq * a.m_s[1]) * ME, a.m_ext);
+    const uint32_t krow_bytes = (uint32_t)(a.k_s[2] * SZ);
+    const uint32_t vrow_bytes = (uint32_t)(a.v_s[2] * SZ);
+
+    // ======================================================== loader wave
+    if (wave == NW) {
+        // instruction j of a tile fills chunk positions [64 j, 64 j + 64): lane
+        // l fetches the (row, chunk) that the layout puts at position 64 j + l
+        auto dma_k = [&](uint8_t* dst, int t) {
+            const uint32_t so = (uint32_t)(t * BN) * krow_bytes;
+#pragma unroll
+            for (int j = 0; j < C::CPR; ++j) {
+                const int row = 32 * (j / (C::CPR / 2)) + (lane & 31);
+                const int chunk = 2 * (j % (C::CPR / 2)) + (lane >> 5);
+                const uint32_t vo = pred(t * BN + row < a.Skv, row * krow_bytes + (uint32_t)(chunk * 16));
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(dst + j * 1024), 16, vo, so, 0, 0);
+            }
+        };
+        auto dma_v = [&](uint8_t* dst, int t) {
+            const uint32_t so = (uint32_t)(t * BN) * vrow_bytes;
+#pragma unroll
+            for (int j = 0; j < C::CPR; ++j) {
+                const int row = 16 * (j / (C::CPR / 4)) + (lane >> 2);
+                const int chunk = 4 * (j % (C::CPR / 4)) + (lane & 3);
+                const uint32_t vo = pred(t * BN + row < a.Skv, row * vrow_bytes + (uint32_t)(chunk * 16));
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(dst + j * 1024), 16, vo, so, 0, 0);
+            }
+        };
+        auto dma_m = [&](int t, int b) {
+            if constexpr (C::MLDS) {
+                const int mrow = lane / C::MCPR, mch = lane % C::MCPR;
+#pragma unroll
+                for (int j = 0; j < C::MNI; ++j) {
+                    const int row = j * C::MRPI + mrow;  // query row q0 + row
+                    // whole 16-byte chunks only: Skv is a multiple of the keys per chunk here
+                    const uint32_t vo = pred(q0 + row < a.Sq && t * BN + mch * (16 / ME) < a.Skv,
+                                             (uint32_t)((int64_t)(q0 + row) * a.m_s[2] * ME) + (uint32_t)(mch * 16));
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(mr, (lds_void*)(mbuf(b) + j * 1024), 16, vo,
+                                                             (uint32_t)(t * BN * ME), 0, 0);
+                }
+            }
+        };
+        // sweep 1: K (+ mask)
+        if (ntiles > 0) {
+            dma_k(kbuf(0), 0);
+            dma_m(0, 0);
+            wait_vmem();
+        }
+        __syncthreads();
+        for (int t = 0; t < ntiles; ++t) {
+            if (t + 1 < ntiles) {
+                dma_k(kbuf((t + 1) & 1), t + 1);
+                dma_m(t + 1, (t + 1) & 1);
+                wait_vmem();
+            }
+            __syncthreads();
+        }
+        // sweep 2: K, V (+ mask)
+        if (ntiles > 0) {
+            dma_k(kbuf(0), 0);
+            dma_v(vbuf(0), 0);
+            dma_m(0, 0);
+            wait_vmem();
+        }
+        __syncthreads();
+        for (int t = 0; t < ntiles; ++t) {
+            if (t + 1 < ntiles) {
+                dma_k(kbuf((t + 1) & 1), t + 1);
+                dma_v(vbuf((t + 1) & 1), t + 1);
+                dma_m(t + 1, (t + 1) & 1);
+                wait_vmem();
+            }
+            __syncthreads();
+        }
+        return;
+    }
+
+    // ======================================================== compute waves
     const int qw = q0 + 32 * wave;
     const int qi = qw + n;
     const bool row_ok = qi < a.Sq;
 
-    const int kend = a.causal ? min(a.Skv, q0 + QB) : a.Skv;
-    const int ntiles = (kend + BN - 1) / BN;
-
     const rsrc_t qr = make_rsrc(static_cast<const T*>(a.q) + w.b * a.q_s[0] + w.hq * a.q_s[1], a.q_ext);
-    const rsrc_t kr = make_rsrc(static_cast<const T*>(a.k) + w.b * a.k_s[0] + hk * a.k_s[1], a.k_ext);
-    const rsrc_t vr = make_rsrc(static_cast<const T*>(a.v) + w.b * a.v_s[0] + hk * a.v_s[1], a.v_ext);
     const rsrc_t pr = make_rsrc(static_cast<T*>(a.p) + w.b * a.p_s[0] + w.hq * a.p_s[1], a.p_ext);
     const rsrc_t orr = make_rsrc(static_cast<T*>(a.o) + w.b * a.o_s[0] + w.hq * a.o_s[1], a.o_ext);
     const rsrc_t lr = make_rsrc(a.lse + w.b * a.l_s[0] + w.hq * a.l_s[1], a.l_ext);
-    rsrc_t mr = kr;
-    uint32_t mrow_off = 0;
-    if constexpr (MASK != MASK_NONE) {
-        mr = make_rsrc(static_cast<const uint8_t*>(a.mask) + (w.b * a.m_s[0] + w.hq * a.m_s[1]) * ME, a.m_ext);
-        mrow_off = (uint32_t)((int64_t)(row_ok ? qi : 0) * a.m_s[2] * ME);
-    }
-    const uint32_t prow_off = (uint32_t)((int64_t)(row_ok ? qi : 0) * a.p_s[2] * SZ);
+    // byte offset of this lane's P row (past the descriptor when the row is out of range)
+    const uint32_t prow = pred(row_ok, (uint32_t)((int64_t)(row_ok ? qi : 0) * a.p_s[2] * SZ));
 
     // Q fragments (B operand): lane (n, h) holds Q[qi][c*KSTEP + h*KH .. +KH)
     vec qf[NKS];
@@ -152,156 +210,125 @@ void sdpa_twopass_kernel(const FwdArgs a) {
 #pragma unroll
         for (int c = 0; c < NKS; ++c) {
             const uint32_t off = pred(row_ok, qoff + (uint32_t)((c * KSTEP + hf * KH) * SZ));
-            if constexpr (SZ == 2) qf[c] = as_vec<T>(ld128(qr, off));
+            if constexpr (sizeof(T) == 2) qf[c] = as_vec<T>(ld128(qr, off));
             else qf[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(qr, off, 0, 0));
         }
     }
 
-    // ---- tile staging (registers -> LDS)
-    u32x4 kreg[KCH];
-    u32x4 vreg[VIT][4];
-    MaskPrefetch<T, MASK, VEC> mpre;  // mask bits of the tile after the staged one
+    // K operand (A) of S^T block kb, k-step c: lane (m, h) reads row 32kb +
+    // swap23(m), elements c*KSTEP + h*KH .. +KH
+    const int kr0 = swap23(n);
+    auto k_operand = [&](const uint8_t* kt, int kb, int c) -> vec {
+        const int row = 32 * kb + kr0;
+        const int elem = c * KSTEP + hf * KH;
+        const uint8_t* p = kt + C::pos_k(row, elem * SZ / 16) * 16 + ((elem * SZ) & 15);
+        if constexpr (sizeof(T) == 2) return as_vec<T>(*reinterpret_cast<const u32x4*>(p));
+        else return *reinterpret_cast<const float*>(p);
+    };
+    // S^T of 32-key block kb (one MFMA chain over the head dim)
+    auto qk_block = [&](const uint8_t* kt, int kb) -> f32x16 {
+        f32x16 acc = {};
+#pragma unroll
+        for (int c = 0; c < NKS; ++c) acc = TR::mfma(k_operand(kt, kb, c), qf[c], acc);
+        return acc;
+    };
 
-    auto load_k = [&](int t) {
-        const int k0 = t * BN;
+    // mask terms of register r of block kb: keep flag (bool) or base-2 additive term
+    auto mask_terms = [&](const uint8_t* mt, int k0, int kb, float* mv) {
+        if constexpr (MASK == MASK_NONE) {
+            return;
+        } else if constexpr (C::MLDS) {
+            const uint8_t* base = mt + (32 * wave + n) * C::MROWB;
 #pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int c = tid + i * NT;
-            const int row = c / CPR, ch = c - (c / CPR) * CPR;
-            const bool ok = (c < BN * CPR) && (k0 + row < a.Skv);
-            kreg[i] = ld128(kr, pred(ok, (uint32_t)((int64_t)(k0 + row) * a.k_s[2] * SZ) + (uint32_t)(ch * 16)));
-        }
-    };
-    auto store_k = [&](int buf) {
+            for (int c = 0; c < 2; ++c) {
+                const int jrel = 32 * kb + 16 * c + 8 * hf;
+                if constexpr (ME == 1) {
+                    const u32x2 wv = *reinterpret_cast<const u32x2*>(base + jrel);
 #pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int c = tid + i * NT;
-            if (KCH * NT == BN * CPR || c < BN * CPR) {
-                const int row = c / CPR, ch = c - (c / CPR) * CPR;
-                *reinterpret_cast<u32x4*>(&k_lds[buf][row * KLD + ch * E16]) = kreg[i];
-            }
-        }
-    };
-    auto load_v = [&](int t) {
-        const int k0 = t * BN;
+                    for (int e = 0; e < 8; ++e) mv[8 * c + e] = ((wv[e >> 2] >> (8 * (e & 3))) & 0xffu) ? 1.0f : 0.0f;
+                } else if constexpr (ME == 2) {
+                    const u32x4 wv = *reinterpret_cast<const u32x4*>(base + jrel * 2);
 #pragma unroll
-        for (int i = 0; i < VIT; ++i) {
-            const int it = tid + i * NT;
-            const int kg = it / CPR, ch = it - (it / CPR) * CPR;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = k0 + 4 * kg + r;
-                const bool ok = (VIT * NT == NVI || it < NVI) && key < a.Skv;
-                vreg[i][r] = ld128(vr, pred(ok, (uint32_t)((int64_t)key * a.v_s[2] * SZ) + (uint32_t)(ch * 16)));
-            }
-        }
-    };
-    auto store_vt = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < VIT; ++i) {
-            const int it = tid + i * NT;
-            if (VIT * NT == NVI || it < NVI) {
-                const int kg = it / CPR, ch = it - (it / CPR) * CPR;
-                if constexpr (SZ == 2) {
-                    // 8 head-dim rows, each receiving 4 consecutive keys (8 bytes)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int wd = e >> 1;
-                        const uint32_t x0 = vreg[i][0][wd], x1 = vreg[i][1][wd];
-                        const uint32_t x2 = vreg[i][2][wd], x3 = vreg[i][3][wd];
-                        uint32_t lo, hi;
-                        if (e & 1) {
-                            lo = (x0 >> 16) | (x1 & 0xffff0000u);
-                            hi = (x2 >> 16) | (x3 & 0xffff0000u);
-                        } else {
-                            lo = (x0 & 0xffffu) | (x1 << 16);
-                            hi = (x2 & 0xffffu) | (x3 << 16);
-                        }
-                        *reinterpret_cast<u32x2*>(&vt_lds[buf][(ch * 8 + e) * VLD + 4 * kg]) = u32x2{lo, hi};
-                    }
+                    for (int e = 0; e < 8; ++e) mv[8 * c + e] = Tr<T>::to_f((wv[e >> 1] >> (16 * (e & 1))) & 0xffffu) * LOG2E;
                 } else {
+                    const u32x4 w0 = *reinterpret_cast<const u32x4*>(base + jrel * 4);
+                    const u32x4 w1 = *reinterpret_cast<const u32x4*>(base + jrel * 4 + 16);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        *reinterpret_cast<u32x4*>(&vt_lds[buf][(ch * 4 + e) * VLD + 4 * kg]) =
-                            u32x4{vreg[i][0][e], vreg[i][1][e], vreg[i][2][e], vreg[i][3][e]};
+                    for (int e = 0; e < 4; ++e) {
+                        mv[8 * c + e] = __builtin_bit_cast(float, w0[e]) * LOG2E;
+                        mv[8 * c + 4 + e] = __builtin_bit_cast(float, w1[e]) * LOG2E;
+                    }
                 }
             }
+        } else {
+            // element-wise reads for layouts the staged path cannot take
+            load_mask16<T, MASK, false>(a, mr, (uint32_t)((int64_t)(row_ok ? qi : 0) * a.m_s[2] * ME), k0 + 32 * kb,
+                                        hf, mv);
         }
     };
 
-    // S^T of both 32-key blocks of the staged tile for this wave's queries
-    // (two independent MFMA chains, interleaved to cover their latency).
-    auto qk_tile = [&](int buf, f32x16* acc) {
-        acc[0] = f32x16{};
-        acc[1] = f32x16{};
-        const T* k0row = &k_lds[buf][swap23(n) * KLD + hf * KH];
-        const T* k1row = k0row + 32 * KLD;
+    // Base-2 scaled, masked scores t[r] of one block. `edge`: the block may
+    // hold keys past Skv or past this wave's causal diagonal.
+    auto scores = [&](const f32x16& acc, const float* mv, int kb, int k0, bool edge, float* t) {
+        const int jb = k0 + 32 * kb;
+        // register r holds key jb + kk(hf, r); it is dropped when kk(hf, r) > lim
+        const int lim = edge ? min(a.Skv - 1 - jb, a.causal ? qi - jb : 0x7fffffff) : 0x7fffffff;
 #pragma unroll
-        for (int c = 0; c < NKS; ++c) {
-            vec a0, a1;
-            if constexpr (SZ == 2) {
-                a0 = as_vec<T>(*reinterpret_cast<const u32x4*>(k0row + c * KSTEP));
-                a1 = as_vec<T>(*reinterpret_cast<const u32x4*>(k1row + c * KSTEP));
+        for (int r = 0; r < 16; ++r) {
+            float x;
+            bool drop = false;
+            if constexpr (MASK == MASK_ADD) {
+                x = __builtin_fmaf(acc[r], a.scale_log2, mv[r]);
             } else {
-                a0 = k0row[c * KSTEP];
-                a1 = k1row[c * KSTEP];
+                x = acc[r] * a.scale_log2;
+                if constexpr (MASK == MASK_BOOL) drop = mv[r] == 0.0f;
             }
-            acc[0] = TR::mfma(a0, qf[c], acc[0]);
-            acc[1] = TR::mfma(a1, qf[c], acc[1]);
+            if (edge) drop = drop || kk(hf, r) > lim;
+            t[r] = drop ? -INFINITY : x;
         }
     };
 
     // ---------------- sweep 1: row maximum and sum (base 2)
-    // Loop shape: compute tile t from LDS buffer t&1, then stage tile t+1
-    // (already in registers) into the other buffer, barrier, and prefetch
-    // tile t+2. Every path into the LDS writes then has the same memory ops
-    // in flight (the prefetch, then this tile's stores), so the counter wait
-    // there never covers the probability stores.
     float m_run = -INFINITY, l_run = 0.0f;
-    MaskPrefetch<T, MASK, VEC> mcur;
-    if (ntiles > 0) {
-        load_k(0);
-        mpre.load(a, mr, mrow_off, 0, hf);
-        store_k(0);
-        mcur = mpre;
-        __syncthreads();
-        const int t1 = min(1, ntiles - 1);
-        load_k(t1);
-        mpre.load(a, mr, mrow_off, t1 * BN, hf);
-    }
+    __syncthreads();  // tile 0 staged
     for (int t = 0; t < ntiles; ++t) {
         const int k0 = t * BN;
         const int buf = t & 1;
         if (!(a.causal && k0 > qw + 31)) {  // else: whole tile above this wave's diagonal
             const bool edge = (k0 + BN > a.Skv) || (a.causal && k0 + BN - 1 > qw);
-            f32x16 acc2[2];
-            qk_tile(buf, acc2);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                float mv[16];
-                mcur.get(a, mr, mrow_off, k0, hf, kb, mv);
-                float tt[16];
-                if (edge) scores16<MASK>(a, acc2[kb], mv, k0 + 32 * kb, hf, qi, true, tt);
-                else scores16<MASK>(a, acc2[kb], mv, k0 + 32 * kb, hf, qi, false, tt);
-                float mt = tt[0];
+                const f32x16 acc = qk_block(kbuf(buf), kb);
+                float sum = 0.0f;
+                if (MASK == MASK_NONE && !edge && a.scale_log2 > 0.0f) {
+                    // max on the raw scores (the scale is positive), then one fma per exponent
+                    float mx = acc[0];
 #pragma unroll
-                for (int r = 1; r < 16; ++r) mt = fmaxf(mt, tt[r]);
-                const float mn = fmaxf(m_run, mt);
-                if (mn != -INFINITY) {
-                    float sum = 0.0f;
+                    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, acc[r]);
+                    const float mn = fmaxf(m_run, mx * a.scale_log2);
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) sum += fast_exp2(tt[r] - mn);
+                    for (int r = 0; r < 16; ++r) sum += fast_exp2(__builtin_fmaf(acc[r], a.scale_log2, -mn));
                     l_run = l_run * fast_exp2(m_run - mn) + sum;
                     m_run = mn;
+                } else {
+                    float mv[16];
+                    mask_terms(mbuf(buf), k0, kb, mv);
+                    float tt[16];
+                    scores(acc, mv, kb, k0, edge, tt);
+                    float mt = tt[0];
+#pragma unroll
+                    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, tt[r]);
+                    const float mn = fmaxf(m_run, mt);
+                    if (mn != -INFINITY) {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) sum += fast_exp2(tt[r] - mn);
+                        l_run = l_run * fast_exp2(m_run - mn) + sum;
+                        m_run = mn;
+                    }
                 }
             }
         }
-        store_k(buf ^ 1);
-        mcur = mpre;
-        __syncthreads();
-        const int t2 = min(t + 2, ntiles - 1);
-        load_k(t2);
-        mpre.load(a, mr, mrow_off, t2 * BN, hf);
+        __syncthreads();  // tile t consumed, tile t+1 staged
     }
     {  // the two half-waves holding the same query row
         const float m_o = __shfl_xor(m_run, 32);
@@ -313,6 +340,7 @@ void sdpa_twopass_kernel(const FwdArgs a) {
         }
     }
     const bool dead = (m_run == -INFINITY);
+    // dead rows: lse2 = +inf makes every probability exp2(-inf) = +0
     const float lse2 = dead ? INFINITY : m_run + __log2f(l_run);
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, dead ? -INFINITY : lse2 * LN2), lr,
                                           pred(row_ok && hf == 0, (uint32_t)((int64_t)(row_ok ? qi : 0) * a.l_s[2] * 4)),
@@ -323,75 +351,105 @@ void sdpa_twopass_kernel(const FwdArgs a) {
 #pragma unroll
     for (int d = 0; d < ND; ++d) oacc[d] = f32x16{};
 
-    __syncthreads();  // sweep 1 readers are done with both LDS buffers
-    if (ntiles > 0) {
-        load_k(0);
-        load_v(0);
-        mpre.load(a, mr, mrow_off, 0, hf);
-        store_k(0);
-        store_vt(0);
-        mcur = mpre;
-        __syncthreads();
-        const int t1 = min(1, ntiles - 1);
-        load_k(t1);
-        load_v(t1);
-        mpre.load(a, mr, mrow_off, t1 * BN, hf);
-    }
+    // Transposing-read address for the V^T operand: as source lane s = lane %
+    // 16 of group g = lane / 16 this lane reads 4 head-dim columns of key row
+    // 8(g/2) + s/4 (+ 4 for the second read); the column group is permuted
+    // (bits 0 and 1 of s exchanged) so that output lane i receives head-dim
+    // column swap23(i) of its half of a 32-wide chunk.
+    const int trg = lane >> 4, trs = lane & 15;
+    const int tr_sig = ((trs & 1) << 1) | ((trs >> 1) & 1);
+    const int tr_row = 8 * (trg >> 1) + (trs >> 2);
+    const int tr_col = 16 * (trg & 1) + 4 * tr_sig;
+    auto v_operand = [&](const uint8_t* vt, int key0, int d) -> vec {
+        if constexpr (sizeof(T) == 2) {
+            // rows key0 + tr_row and key0 + tr_row + 4, columns 32d + tr_col .. +3
+            u32x2 half[2];
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int row = key0 + tr_row + 4 * r;
+                const int col = 32 * d + tr_col;
+                half[r] = lds_read_tr16(vt + C::pos_v(row, col * SZ / 16) * 16 + ((col * SZ) & 15));
+            }
+            return __builtin_bit_cast(vec, u32x4{half[0][0], half[0][1], half[1][0], half[1][1]});
+        } else {
+            return vec{};
+        }
+    };
+
+    // store of 8 probabilities (one run) of block kb, run c
+    auto store_run = [&](int k0, int kb, int c, bool edge, const float* x) {
+        const int jrel = 32 * kb + 16 * c + 8 * hf;
+        if constexpr (VEC) {
+            uint32_t vo = prow + (uint32_t)(jrel * SZ);
+            if (edge) vo = pred(k0 + jrel < a.Skv, vo);
+            if constexpr (sizeof(T) == 2) {
+                st128s(pr, vo, (uint32_t)(k0 * SZ), __builtin_bit_cast(u32x4, Tr<T>::cvt8(x)));
+            } else {
+                st128s(pr, vo, (uint32_t)(k0 * SZ),
+                       u32x4{__builtin_bit_cast(uint32_t, x[0]), __builtin_bit_cast(uint32_t, x[1]),
+                             __builtin_bit_cast(uint32_t, x[2]), __builtin_bit_cast(uint32_t, x[3])});
+                st128s(pr, vo == OOB ? OOB : vo + 16, (uint32_t)(k0 * SZ),
+                       u32x4{__builtin_bit_cast(uint32_t, x[4]), __builtin_bit_cast(uint32_t, x[5]),
+                             __builtin_bit_cast(uint32_t, x[6]), __builtin_bit_cast(uint32_t, x[7])});
+            }
+        } else {
+            store8<T, false>(pr, row_ok ? prow : 0u, row_ok, k0 + jrel, a.Skv, x);
+        }
+    };
+
+    __syncthreads();  // tile 0 staged
     for (int t = 0; t < ntiles; ++t) {
         const int k0 = t * BN;
         const int buf = t & 1;
+        const bool edge = (k0 + BN > a.Skv) || (a.causal && k0 + BN - 1 > qw);
         if (a.causal && k0 > qw + 31) {
             // whole tile above this wave's diagonal: P is zero, O unchanged
             const float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-            for (int c = 0; c < 4; ++c) store8<T, VEC>(pr, prow_off, row_ok, k0 + 16 * c + 8 * hf, a.Skv, z);
+            for (int q = 0; q < 4; ++q) store_run(k0, q >> 1, q & 1, edge, z);
         } else {
-            const bool edge = (k0 + BN > a.Skv) || (a.causal && k0 + BN - 1 > qw);
-            f32x16 acc2[2];
-            qk_tile(buf, acc2);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                float mv[16];
-                mcur.get(a, mr, mrow_off, k0, hf, kb, mv);
-                float tt[16];
-                if (edge) scores16<MASK>(a, acc2[kb], mv, k0 + 32 * kb, hf, qi, true, tt);
-                else scores16<MASK>(a, acc2[kb], mv, k0 + 32 * kb, hf, qi, false, tt);
+                const f32x16 acc = qk_block(kbuf(buf), kb);
                 float p[16];
+                if (MASK == MASK_NONE && !edge) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) p[r] = fast_exp2(tt[r] - lse2);
-                store8<T, VEC>(pr, prow_off, row_ok, k0 + 32 * kb + 8 * hf, a.Skv, p);
-                store8<T, VEC>(pr, prow_off, row_ok, k0 + 32 * kb + 16 + 8 * hf, a.Skv, p + 8);
-                if constexpr (SZ == 2) {
+                    for (int r = 0; r < 16; ++r) p[r] = fast_exp2(__builtin_fmaf(acc[r], a.scale_log2, -lse2));
+                } else {
+                    float mv[16];
+                    mask_terms(mbuf(buf), k0, kb, mv);
+                    float tt[16];
+                    scores(acc, mv, kb, k0, edge, tt);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) p[r] = fast_exp2(tt[r] - lse2);
+                }
+                if constexpr (sizeof(T) == 2) {
 #pragma unroll
                     for (int c2 = 0; c2 < 2; ++c2) {
                         const vec pv = TR::cvt8(p + 8 * c2);
+                        store_run(k0, kb, c2, edge, p + 8 * c2);
 #pragma unroll
-                        for (int d = 0; d < ND; ++d) {
-                            const vec va = as_vec<T>(*reinterpret_cast<const u32x4*>(
-                                &vt_lds[buf][(32 * d + swap23(n)) * VLD + 32 * kb + 16 * c2 + 8 * hf]));
-                            oacc[d] = TR::mfma(va, pv, oacc[d]);
-                        }
+                        for (int d = 0; d < ND; ++d)
+                            oacc[d] = TR::mfma(v_operand(vbuf(buf), 32 * kb + 16 * c2, d), pv, oacc[d]);
                     }
                 } else {
+                    store_run(k0, kb, 0, edge, p);
+                    store_run(k0, kb, 1, edge, p + 8);
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
+                        const int row = 32 * kb + kk(hf, r);
 #pragma unroll
                         for (int d = 0; d < ND; ++d) {
-                            const float va = vt_lds[buf][(32 * d + swap23(n)) * VLD + 32 * kb + kk(hf, r)];
+                            const int col = 32 * d + swap23(n);
+                            const float va = *reinterpret_cast<const float*>(
+                                vbuf(buf) + C::pos_v(row, col * SZ / 16) * 16 + ((col * SZ) & 15));
                             oacc[d] = TR::mfma(va, p[r], oacc[d]);
                         }
                     }
                 }
             }
         }
-        store_k(buf ^ 1);
-        store_vt(buf ^ 1);
-        mcur = mpre;
-        __syncthreads();
-        const int t2 = min(t + 2, ntiles - 1);
-        load_k(t2);
-        load_v(t2);
-        mpre.load(a, mr, mrow_off, t2 * BN, hf);
+        __syncthreads();  // tile t consumed, tile t+1 staged
     }
 
     // ---------------- O: lane (n, h) holds O[qi][32d + 8h ..+8) and [32d + 16 + 8h ..+8)
@@ -413,7 +471,7 @@ void sdpa_twopass_kernel(const FwdArgs a) {
 
 template <typename T, int D, int NW, bool VEC>
 static int launch_twopass_mask(int mask_kind, const FwdArgs& a, hipStream_t s) {
-    dim3 grid(a.n_blocks), block(NW * 64);
+    dim3 grid(a.n_blocks), block((NW + 1) * 64);
     switch (mask_kind) {
         case MASK_NONE: hipLaunchKernelGGL((sdpa_twopass_kernel<T, D, NW, MASK_NONE, VEC>), grid, block, 0, s, a); break;
         case MASK_BOOL: hipLaunchKernelGGL((sdpa_twopass_kernel<T, D, NW, MASK_BOOL, VEC>), grid, block, 0, s, a); break;
@@ -424,14 +482,21 @@ static int launch_twopass_mask(int mask_kind, const FwdArgs& a, hipStream_t s) {
 }
 
 // Element-wise layouts only need correctness: they get one two-wave shape.
+// 128-wide heads take at most three compute waves (register budget); float32
+// 128-wide tiles are twice as large: two compute waves keep them within LDS.
 template <typename T>
 static int launch_twopass_t(int D, int mask_kind, int waves, bool vec, const FwdArgs& a, void* stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-#define SDPA_TP_DIM(DD)                                                                   \
-    case DD:                                                                              \
-        if (!vec) return launch_twopass_mask<T, DD, 2, false>(mask_kind, a, s);           \
-        if (waves == 4) return launch_twopass_mask<T, DD, 4, true>(mask_kind, a, s);      \
-        if (waves == 2) return launch_twopass_mask<T, DD, 2, true>(mask_kind, a, s);      \
+#define SDPA_TP_DIM(DD)                                                                     \
+    case DD:                                                                                \
+        if (!vec) return launch_twopass_mask<T, DD, 2, false>(mask_kind, a, s);             \
+        if constexpr (DD < 128) {                                                           \
+            if (waves == 4) return launch_twopass_mask<T, DD, 4, true>(mask_kind, a, s);    \
+        }                                                                                   \
+        if constexpr (sizeof(T) == 2 || DD < 128) {                                          \
+            if (waves == 3) return launch_twopass_mask<T, DD, 3, true>(mask_kind, a, s);    \
+        }                                                                                   \
+        if (waves == 2 || waves == 4) return launch_twopass_mask<T, DD, 2, true>(mask_kind, a, s); \
         return (int)hipErrorInvalidValue;
     switch (D) {
         SDPA_TP_DIM(32)

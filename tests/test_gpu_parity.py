@@ -82,6 +82,28 @@ def test_small_cases(label, spec, path):
     _check(c, path, label=label)
 
 
+# Every compute-wave count the kernel is built for (the count is a tuning
+# knob read at each call; 128-wide heads take at most three).
+WAVE_CASES = [
+    ("bf16-d128-causal", dict(seed=130, dtype="bf16", B=1, Hq=2, Hkv=2, Sq=300, Skv=300, D=128, causal=True)),
+    ("f16-d64-bool-staged", dict(seed=131, dtype="f16", B=1, Hq=2, Hkv=1, Sq=257, Skv=320, D=64, mask="bool", p=0.2)),
+    ("bf16-d32-add-staged", dict(seed=132, dtype="bf16", B=2, Hq=1, Hkv=1, Sq=200, Skv=136, D=32, mask="add", p=0.1)),
+    ("f16-d128-causal-skv-ragged", dict(seed=133, dtype="f16", B=1, Hq=2, Hkv=2, Sq=190, Skv=250, D=128,
+                                        causal=True)),
+    ("f32-d64-causal", dict(seed=134, dtype="f32", B=1, Hq=2, Hkv=2, Sq=160, Skv=160, D=64, causal=True)),
+]
+
+
+@pytest.mark.parametrize("waves", [2, 3, 4])
+@pytest.mark.parametrize("label,spec", WAVE_CASES, ids=[s[0] for s in WAVE_CASES])
+def test_compute_wave_counts(label, spec, waves, monkeypatch):
+    if spec["D"] == 128 and waves > 3:
+        pytest.skip("128-wide heads take at most three compute waves")
+    monkeypatch.setenv("SDPA_MATH_TP_WAVES", str(waves))
+    c = W.make_case(**spec)
+    _check(c, "twopass", label=f"{label} waves={waves}")
+
+
 @pytest.mark.parametrize("path", PATHS)
 def test_fully_masked_rows(path):
     c = W.make_case(120, "f16", 2, 4, 2, 96, 160, 64, mask="bool", mask_shape=(2, 4, 96, 160), p=0.2)
