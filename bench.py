@@ -89,9 +89,83 @@ def time_gpu(w, steps, warmup, path="auto"):
             "path": path if path != "auto" else chosen, "tiles_per_bh": tiles, "tiles64_per_bh": tiles64}
 
 
-def cpu_baseline(w, budget_s=15.0):
+# Sources whose change invalidates a stored counter measurement of the kernel.
+KERNEL_SOURCES = ["sdpa_device.h", "sdpa_internal.h", "twopass.h", "twopass_bf16.hip", "sdpa_math_api.cpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sdpa_twopass_kernel.prefill_2k_d128_bf16_causal.traffic.txt")
+
+
+def kernel_source_hash():
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "sdpa_forward_materialised_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic():
+    """HBM bytes per launch from the committed counter summary, or None when
+    it is missing or was taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            kv = dict(ln.split(":", 1) for ln in fh if ":" in ln and not ln.startswith("#"))
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return int(kv["traffic_bytes_per_launch"])
+
+
+def probe_copy(mib, steps, warmup):
+    """Time the library's streaming copy kernel over `mib` MiB (counter calibration)."""
+    import torch
+
+    import sdpa_forward_materialised_amd as S
+
+    n = mib << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(warmup):
+        S.probe_copy(dst, src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        S.probe_copy(dst, src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    assert torch.equal(dst, src)
+    return {"probe": "copy", "bytes_read": n, "bytes_written": n, "ms": round(ms, 5),
+            "gbps": round(2 * n / (ms * 1e-3) / 1e9, 1), "steps": steps}
+
+
+def all_configs(steps, warmup, path):
+    """Every seeded workload: time, effective TFLOPS, P-write GB/s and the
+    fraction of the HBM roofline each reaches."""
+    import sdpa_workloads as W
+
+    rows = []
+    for w in W.WORKLOADS:
+        r = time_gpu(w, steps, warmup, path)
+        by = algorithmic_bytes(w, r["mask_bytes"])
+        sec = r["ms"] * 1e-3
+        fl = algorithmic_flops(w.B, w.Hq, w.Sq, w.Skv, w.D, w.dv, w.causal)
+        rows.append({"workload": w.name, "dtype": w.dtype, "path": r["path"], "ms": round(r["ms"], 5),
+                     "tflops": round(fl / sec / 1e12, 2), "p_write_gbps": round(by["p"] / sec / 1e9, 1),
+                     "hbm_gbps": round(by["total"] / sec / 1e9, 1),
+                     "hbm_frac": round(by["total"] / sec / 1e9 / HBM_PEAK_GBPS, 4),
+                     "mfma_frac": round(fl / sec / 1e12 / MFMA_PEAK_TFLOPS[w.dtype], 4)})
+        log(f"[bench] {w.name}: {r['ms']:.4f} ms, {rows[-1]['hbm_frac'] * 100:.1f}% of HBM roofline")
+    return rows
+
+
+def cpu_baseline(w, budget_s=12.0):
     """The float64 oracle on whole (batch, head) slices of the same workload,
-    as many as fit in about ``budget_s`` seconds of host time."""
+    taken in order (and again from the start once all were done) until about
+    ``budget_s`` seconds of host time are used."""
     import oracle
     import sdpa_workloads as W
 
@@ -99,7 +173,8 @@ def cpu_baseline(w, budget_s=15.0):
     g = w.Hq // w.Hkv
     done, t_used = 0, 0.0
     heads = [(b, h) for b in range(w.B) for h in range(w.Hq)]
-    for b, h in heads:
+    while t_used < budget_s:
+        b, h = heads[done % len(heads)]
         hk = h // g
         qs, ks, vs = inp["q"][b:b + 1, h:h + 1], inp["k"][b:b + 1, hk:hk + 1], inp["v"][b:b + 1, hk:hk + 1]
         ms = None
@@ -111,11 +186,9 @@ def cpu_baseline(w, budget_s=15.0):
         oracle.sdpa_reference(qs, ks, vs, ms, w.causal, w.scale, False)
         t_used += time.perf_counter() - t0
         done += 1
-        if t_used >= budget_s:
-            break
     flops = algorithmic_flops(1, done, w.Sq, w.Skv, w.D, w.dv, w.causal)
     return {"value": flops / t_used / 1e12, "unit": "TFLOPS", "cores": oracle.threads(), "kind": "oracle",
-            "sample": f"{done} of {len(heads)} (batch, head) slices of {w.name}, float64, "
+            "sample": f"{done} (batch, head) slices of {w.name} (it has {len(heads)}), float64, "
                       f"{t_used:.1f} s ({t_used / done * 1e3:.0f} ms per slice)"}
 
 
@@ -127,6 +200,9 @@ def main():
     ap.add_argument("--path", default="auto", choices=["auto", "fused", "twopass"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp16", action="store_true", help="skip the same-shape fp16 line")
+    ap.add_argument("--no-configs", action="store_true", help="skip the table over every seeded workload")
+    ap.add_argument("--probe-copy-mib", type=int, default=0,
+                    help="only time the streaming copy kernel over this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -135,6 +211,10 @@ def main():
     import torch  # noqa: F401
 
     import sdpa_workloads as W
+
+    if args.probe_copy_mib:
+        print(json.dumps(probe_copy(args.probe_copy_mib, args.steps, args.warmup)), flush=True)
+        return
 
     w = W.BY_NAME["prefill_2k_d128_bf16_causal"]
     log(f"[bench] {w.describe()} steps={args.steps} warmup={args.warmup}")
@@ -155,6 +235,9 @@ def main():
                                     "p_write_gbps": round(by["p"] / (r16["ms"] * 1e-3) / 1e9, 1)}
         log(f"[bench] fp16: {r16['ms']:.4f} ms/step")
 
+    if not args.no_configs:
+        extra["configs"] = all_configs(min(args.steps, 20), min(args.warmup, 3), args.path)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the float64 oracle on the host")
@@ -172,7 +255,7 @@ def main():
         "p_write_gbps": round(p_gbps, 1),
         "effective_tflops_frac_of_mfma_peak": round(tflops / MFMA_PEAK_TFLOPS[w.dtype], 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": stored_traffic(),
                      "kernel": "sdpa_twopass_kernel" if r["path"] == "twopass" else "sdpa_fused_kernel",
                      "bytes_per_launch": by["total"]},
         "cpu_baseline": cpu,

@@ -340,13 +340,15 @@ sdpa_status_t run(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_ten
     a.n_qblk = plan.n_qblk;
     a.n_blocks = (int)plan.grid;
     a.keys_per_wave = plan.keys_per_wave;
+    // Workgroup order: head-major with the heaviest causal blocks first
+    // (measured fastest); SDPA_MATH_SCHED=1 pairs heavy and light causal
+    // blocks on each XCD instead, where the grid splits evenly.
     a.sched = 0;
-    if (is_causal && plan.grid % 8 == 0) {
-        const int64_t per = plan.grid / 8;
-        if (per % plan.n_qblk == 0 && per % 2 == 0) a.sched = 1;
-    }
     if (const char* e = std::getenv("SDPA_MATH_SCHED")) {
-        if (*e == '0') a.sched = 0;
+        if (*e == '1' && is_causal && plan.grid % 8 == 0) {
+            const int64_t per = plan.grid / 8;
+            if (per % plan.n_qblk == 0 && per % 2 == 0) a.sched = 1;
+        }
     }
 
     // byte extent of one (batch, head) slice of each tensor
