@@ -142,6 +142,52 @@ def probe_copy(mib, steps, warmup):
             "gbps": round(2 * n / (ms * 1e-3) / 1e9, 1), "steps": steps}
 
 
+def threshold_sweep(reps=15, warmup=3):
+    """Both paths on a grid of shapes (fp16, B=4, H=16; D 64/128; causal or
+    not; Sq 32..1024; Skv 128..2048): one JSON line per shape with the event
+    time per call of each path (None where the fused path cannot take the
+    shape). Run under ``rocprofv3 --kernel-trace`` for kernel-only times: the
+    dispatches come in order, ``warmup + reps`` per shape and path."""
+    import torch
+
+    import sdpa_forward_materialised_amd as S
+
+    dev = "cuda:0"
+    g = torch.Generator(device="cpu").manual_seed(0)
+    BH = (4, 16)
+    for D in (64, 128):
+        for causal in (False, True):
+            for Sq in (32, 64, 128, 256, 512, 1024):
+                for Skv in (128, 256, 512, 1024, 2048):
+                    if causal and Skv < Sq:
+                        continue
+                    q = torch.randn(*BH, Sq, D, generator=g).to(dev, torch.float16)
+                    k = torch.randn(*BH, Skv, D, generator=g).to(dev, torch.float16)
+                    v = torch.randn(*BH, Skv, D, generator=g).to(dev, torch.float16)
+                    out = (torch.empty_like(q), torch.empty(*BH, Sq, Skv, device=dev, dtype=torch.float16),
+                           torch.empty(*BH, Sq, device=dev))
+                    auto, _, t64 = S.plan(q, k, v, None, causal)
+                    res = {"D": D, "causal": causal, "Sq": Sq, "Skv": Skv, "tiles64": t64, "auto": auto}
+                    for path in ("twopass", "fused"):
+                        def call():
+                            S.fwd(q, k, v, None, causal, None, False, path=path, out=out)
+                        try:
+                            for _ in range(warmup):
+                                call()
+                        except NotImplementedError:
+                            res[path + "_us"] = None
+                            continue
+                        torch.cuda.synchronize()
+                        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                        e0.record()
+                        for _ in range(reps):
+                            call()
+                        e1.record()
+                        torch.cuda.synchronize()
+                        res[path + "_us"] = round(e0.elapsed_time(e1) / reps * 1e3, 2)
+                    print(json.dumps(res), flush=True)
+
+
 def all_configs(steps, warmup, path):
     """Every seeded workload: time, effective TFLOPS, P-write GB/s and the
     fraction of the HBM roofline each reaches."""
@@ -201,6 +247,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp16", action="store_true", help="skip the same-shape fp16 line")
     ap.add_argument("--no-configs", action="store_true", help="skip the table over every seeded workload")
+    ap.add_argument("--threshold-sweep", action="store_true",
+                    help="only time both paths over a grid of shapes (fused/two-pass switch)")
     ap.add_argument("--probe-copy-mib", type=int, default=0,
                     help="only time the streaming copy kernel over this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -212,6 +260,9 @@ def main():
 
     import sdpa_workloads as W
 
+    if args.threshold_sweep:
+        threshold_sweep()
+        return
     if args.probe_copy_mib:
         print(json.dumps(probe_copy(args.probe_copy_mib, args.steps, args.warmup)), flush=True)
         return

@@ -1,8 +1,371 @@
-// Fused single-sweep kernel (scores kept on chip). Not built yet.
+// Fused single-sweep kernel for shapes with few score tiles.
+//
+// FlagOS-OP pull request "feat: add sdpa_math operator (Ascend Triton + P800
+// exact-P/A1)", single-kernel fusion and threshold sections: when a row block
+// has few score tiles, one launch that keeps the block's scores on chip
+// computes Q K^T once (the two-sweep kernel computes it twice) and reads the
+// mask once. The math is the same as the two-sweep kernel's: exact row
+// maximum and sum, LSE, P = exp(scale*QK^T - LSE) rounded to the dtype, and
+// O accumulated from the rounded P ("P800 exact-P fast path" update).
+//
+// Workgroup = 32 query rows of one (batch, head) and NW waves (1..8); wave w
+// owns keys [w*kpw, (w+1)*kpw) and holds their scores (S^T blocks of 32 keys,
+// the same MFMA layout as the two-sweep kernel) in registers. Row maximum and
+// sum are combined across waves through LDS. Each wave then stages its own V
+// rows in LDS by buffer-to-LDS loads and accumulates a partial O^T; the
+// partials are summed through LDS. Every global load (Q, K, mask, V) is
+// issued before the first store, so no wait ever covers a store.
+
 #include "sdpa_device.h"
 
 namespace sdpa {
 
-int launch_fused(int, int, int, int, bool, const FwdArgs&, void*) { return (int)hipErrorNotSupported; }
+namespace {
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ u32x2 lds_tr16(const void* p) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p));
+}
+
+// vmcnt(0) only
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// lgkmcnt(0) only
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Largest number of 32-key score blocks one wave keeps in registers.
+template <int D>
+constexpr int fused_max_blocks() {
+    return D == 128 ? FUSED_MAX_KEYS_PER_WAVE_D128 / 32 : FUSED_MAX_KEYS_PER_WAVE / 32;
+}
+
+// Bytes of dynamic LDS for `nw` waves: per wave a 32-row V block or, later, a
+// 32 x (D + 4) float partial O^T; then the row max and sum of every wave.
+template <typename T, int D>
+constexpr int fused_lds_bytes(int nw) {
+    return nw * 32 * (D + 4) * 4 + 2 * nw * 32 * 4;
+}
+
+template <typename T, int D, int MASK, bool VEC>
+__global__ __attribute__((amdgpu_flat_work_group_size(64, 512)))
+void sdpa_fused_kernel(const FwdArgs a) {
+    using TR = Tr<T>;
+    using vec = typename TR::vec;
+    constexpr int SZ = (int)sizeof(T);
+    constexpr int KH = TR::KH;
+    constexpr int KSTEP = 2 * KH;
+    constexpr int NKS = D / KSTEP;
+    constexpr int ND = D / 32;
+    constexpr int ME = MASK == MASK_BOOL ? 1 : SZ;
+    constexpr int ROWB = D * SZ;
+    constexpr int CPR = ROWB / 16;
+    constexpr int NBMAX = fused_max_blocks<D>();
+    constexpr int OPITCH = D + 4;  // floats per partial-O row (padding spreads the banks)
+    static_assert(CPR % 4 == 0, "V block layout needs a multiple of 4 chunks per row");
+
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int nw = (int)(blockDim.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n = lane & 31;
+    const int hf = lane >> 5;
+    float* red_m = reinterpret_cast<float*>(smem + nw * 32 * OPITCH * 4);
+    float* red_l = red_m + nw * 32;
+    uint8_t* vblk = smem + wave * 32 * ROWB;
+
+    const Work w = decode_block(blockIdx.x, a);
+    const int hk = w.hq / a.group;
+    const int q0 = w.qblk * 32;
+    const int qi = q0 + n;
+    const bool row_ok = qi < a.Sq;
+    // keys any row of this block may keep
+    const int kend = a.causal ? min(a.Skv, q0 + 32) : a.Skv;
+    const int kpw = a.keys_per_wave;
+    const int kbase = wave * kpw;
+    const int nb = max(0, min((kend - kbase + 31) / 32, kpw / 32));
+
+    const rsrc_t qr = make_rsrc(static_cast<const T*>(a.q) + w.b * a.q_s[0] + w.hq * a.q_s[1], a.q_ext);
+    const rsrc_t kr = make_rsrc(static_cast<const T*>(a.k) + w.b * a.k_s[0] + hk * a.k_s[1], a.k_ext);
+    const rsrc_t vr = make_rsrc(static_cast<const T*>(a.v) + w.b * a.v_s[0] + hk * a.v_s[1], a.v_ext);
+    const rsrc_t pr = make_rsrc(static_cast<T*>(a.p) + w.b * a.p_s[0] + w.hq * a.p_s[1], a.p_ext);
+    const rsrc_t orr = make_rsrc(static_cast<T*>(a.o) + w.b * a.o_s[0] + w.hq * a.o_s[1], a.o_ext);
+    const rsrc_t lr = make_rsrc(a.lse + w.b * a.l_s[0] + w.hq * a.l_s[1], a.l_ext);
+    rsrc_t mr = kr;
+    if constexpr (MASK != MASK_NONE)
+        mr = make_rsrc(static_cast<const uint8_t*>(a.mask) + (w.b * a.m_s[0] + w.hq * a.m_s[1]) * ME, a.m_ext);
+    const uint32_t krow_bytes = (uint32_t)(a.k_s[2] * SZ);
+    const uint32_t vrow_bytes = (uint32_t)(a.v_s[2] * SZ);
+    const uint32_t prow = pred(row_ok, (uint32_t)((int64_t)(row_ok ? qi : 0) * a.p_s[2] * SZ));
+
+    // Q fragments (B operand): lane (n, h) holds Q[qi][c*KSTEP + h*KH .. +KH)
+    vec qf[NKS];
+    {
+        const uint32_t qoff = (uint32_t)((int64_t)(row_ok ? qi : 0) * a.q_s[2] * SZ);
+#pragma unroll
+        for (int c = 0; c < NKS; ++c) {
+            const uint32_t off = pred(row_ok, qoff + (uint32_t)((c * KSTEP + hf * KH) * SZ));
+            if constexpr (sizeof(T) == 2) qf[c] = as_vec<T>(ld128(qr, off));
+            else qf[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(qr, off, 0, 0));
+        }
+    }
+
+    // ---------------- scores of this wave's keys (base 2, masked), kept in registers
+    const int kr0 = swap23(n);
+    f32x16 s[NBMAX];
+    float m_loc = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NBMAX; ++kb) {
+        s[kb] = f32x16{};
+        if (kb < nb) {
+            const int jb = kbase + 32 * kb;
+            // A operand: K row jb + swap23(m), elements c*KSTEP + h*KH .. +KH (rows past Skv read 0)
+            const int krow = jb + kr0;
+            const uint32_t kro = pred(krow < a.Skv, (uint32_t)krow * krow_bytes);
+            f32x16 acc = {};
+#pragma unroll
+            for (int c = 0; c < NKS; ++c) {
+                const uint32_t off = kro == OOB ? OOB : kro + (uint32_t)((c * KSTEP + hf * KH) * SZ);
+                vec ka;
+                if constexpr (sizeof(T) == 2) ka = as_vec<T>(ld128(kr, off));
+                else ka = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(kr, off, 0, 0));
+                acc = TR::mfma(ka, qf[c], acc);
+            }
+            float mv[16];
+            if constexpr (MASK != MASK_NONE)
+                load_mask16<T, MASK, VEC>(a, mr, (uint32_t)((int64_t)(row_ok ? qi : 0) * a.m_s[2] * ME), jb, hf, mv);
+            const bool edge = (jb + 32 > a.Skv) || (a.causal && jb + 31 > q0);
+            float t[16];
+            scores16<MASK>(a, acc, mv, jb, hf, qi, edge, t);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                s[kb][r] = t[r];
+                m_loc = fmaxf(m_loc, t[r]);
+            }
+        }
+    }
+
+    // ---------------- row maximum and sum across the waves
+    m_loc = fmaxf(m_loc, __shfl_xor(m_loc, 32));
+    if (hf == 0) red_m[wave * 32 + n] = m_loc;
+    __syncthreads();
+    float M = -INFINITY;
+    for (int i = 0; i < nw; ++i) M = fmaxf(M, red_m[i * 32 + n]);
+    float l_loc = 0.0f;
+    if (M != -INFINITY) {
+#pragma unroll
+        for (int kb = 0; kb < NBMAX; ++kb)
+            if (kb < nb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) l_loc += fast_exp2(s[kb][r] - M);
+            }
+    }
+    l_loc += __shfl_xor(l_loc, 32);
+    if (hf == 0) red_l[wave * 32 + n] = l_loc;
+    __syncthreads();
+    float L = 0.0f;
+    for (int i = 0; i < nw; ++i) L += red_l[i * 32 + n];
+    const bool dead = (M == -INFINITY);
+    // dead rows: lse2 = +inf makes every probability exp2(-inf) = +0
+    const float lse2 = dead ? INFINITY : M + __log2f(L);
+
+    // ---------------- probabilities (rounded to the dtype) and O^T += V^T P^T
+    f32x16 oacc[ND];
+#pragma unroll
+    for (int d = 0; d < ND; ++d) oacc[d] = f32x16{};
+    vec pv[NBMAX][2];  // 16-bit: the rounded probabilities of each block, two runs of 8
+
+    // transposing-read address of the V^T operand (as in the two-sweep kernel)
+    const int trg = lane >> 4, trs = lane & 15;
+    const int tr_sig = ((trs & 1) << 1) | ((trs >> 1) & 1);
+    const int tr_row = 8 * (trg >> 1) + (trs >> 2);
+    const int tr_col = 16 * (trg & 1) + 4 * tr_sig;
+    // V block layout: 16-row x 4-chunk bricks of 16-byte chunks
+    auto pos_v = [](int row, int chunk) -> int {
+        return (row >> 4) * (16 * CPR) + (chunk >> 2) * 64 + 4 * (row & 15) + (chunk & 3);
+    };
+
+#pragma unroll
+    for (int kb = 0; kb < NBMAX; ++kb) {
+        if (kb < nb) {
+            const int jb = kbase + 32 * kb;
+            float p[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) p[r] = fast_exp2(s[kb][r] - lse2);
+            if constexpr (sizeof(T) == 2) {
+                pv[kb][0] = TR::cvt8(p);
+                pv[kb][1] = TR::cvt8(p + 8);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[kb][r] = p[r];
+            }
+            // stage V rows jb .. jb+31 of this wave (the previous block's reads are done)
+            wait_lds();
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int j = 0; j < CPR / 2; ++j) {
+                const int row = 16 * (j / (CPR / 4)) + (lane >> 2);
+                const int chunk = 4 * (j % (CPR / 4)) + (lane & 3);
+                const uint32_t vo = pred(jb + row < a.Skv, (uint32_t)(jb + row) * vrow_bytes + (uint32_t)(chunk * 16));
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vblk + j * 1024), 16, vo, 0, 0, 0);
+            }
+            wait_vmem();
+            asm volatile("" ::: "memory");
+            if constexpr (sizeof(T) == 2) {
+#pragma unroll
+                for (int c2 = 0; c2 < 2; ++c2) {
+#pragma unroll
+                    for (int d = 0; d < ND; ++d) {
+                        u32x2 h2[2];
+#pragma unroll
+                        for (int r = 0; r < 2; ++r) {
+                            const int row = 16 * c2 + tr_row + 4 * r;
+                            const int col = 32 * d + tr_col;
+                            h2[r] = lds_tr16(vblk + pos_v(row, col * SZ / 16) * 16 + ((col * SZ) & 15));
+                        }
+                        const vec va = __builtin_bit_cast(vec, u32x4{h2[0][0], h2[0][1], h2[1][0], h2[1][1]});
+                        oacc[d] = TR::mfma(va, pv[kb][c2], oacc[d]);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = kk(hf, r);
+#pragma unroll
+                    for (int d = 0; d < ND; ++d) {
+                        const int col = 32 * d + swap23(n);
+                        const float va = *reinterpret_cast<const float*>(
+                            vblk + pos_v(row, col * SZ / 16) * 16 + ((col * SZ) & 15));
+                        oacc[d] = TR::mfma(va, s[kb][r], oacc[d]);
+                    }
+                }
+            }
+        }
+    }
+
+    // ---------------- stores: P of this wave's keys, zeros past them, LSE
+#pragma unroll
+    for (int kb = 0; kb < NBMAX; ++kb) {
+        if (kb < nb) {
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) {
+                const int j = kbase + 32 * kb + 16 * c2 + 8 * hf;
+                if constexpr (sizeof(T) == 2) {
+                    const u32x4 bits = __builtin_bit_cast(u32x4, pv[kb][c2]);
+                    if constexpr (VEC) {
+                        st128(pr, pred(j < a.Skv, prow + (uint32_t)(j * SZ)), bits);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(bits[e >> 1] >> (16 * (e & 1))), pr,
+                                                                  pred(row_ok && j + e < a.Skv, prow + (uint32_t)((j + e) * SZ)),
+                                                                  0, 0);
+                    }
+                } else {
+                    float x[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[e] = s[kb][8 * c2 + e];
+                    store8<T, VEC>(pr, row_ok ? prow : 0u, row_ok, j, a.Skv, x);
+                }
+            }
+        }
+    }
+    {
+        const int c0 = min(a.Skv, kbase + 32 * nb);
+        const int c1 = wave == nw - 1 ? a.Skv : min(a.Skv, kbase + kpw);
+        zero_rows<T, VEC>(pr, a.p_s[2], q0, a.Sq, c0, c1, lane);
+    }
+    if (wave == 0)
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, dead ? -INFINITY : lse2 * LN2), lr,
+                                              pred(row_ok && hf == 0, (uint32_t)((int64_t)(row_ok ? qi : 0) * a.l_s[2] * 4)),
+                                              0, 0);
+
+    // ---------------- O: lane (n, h) holds O^T columns 32d + kk(h, r) of row n
+    if (nw == 1) {
+        const uint32_t orow = (uint32_t)((int64_t)(row_ok ? qi : 0) * a.o_s[2] * SZ);
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+            float x[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) x[r] = oacc[d][r];
+            store8<T, VEC>(orr, orow, row_ok, 32 * d + 8 * hf, D, x);
+            store8<T, VEC>(orr, orow, row_ok, 32 * d + 16 + 8 * hf, D, x + 8);
+        }
+        return;
+    }
+    __syncthreads();  // every wave is done with its V block
+    float* opart = reinterpret_cast<float*>(smem) + wave * 32 * OPITCH;
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) opart[n * OPITCH + 32 * d + kk(hf, r)] = oacc[d][r];
+    __syncthreads();
+    const float* obase = reinterpret_cast<const float*>(smem);
+    for (int i = threadIdx.x; i < 32 * (D / 8); i += nw * 64) {
+        const int row = i / (D / 8), c8 = i - row * (D / 8);
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+        for (int ww = 0; ww < nw; ++ww) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] += obase[(ww * 32 + row) * OPITCH + 8 * c8 + e];
+        }
+        const int orow_i = q0 + row;
+        const bool ok = orow_i < a.Sq;
+        store8<T, VEC>(orr, (uint32_t)((int64_t)(ok ? orow_i : 0) * a.o_s[2] * SZ), ok, 8 * c8, D, x);
+    }
+}
+
+template <typename T, int D, bool VEC>
+int launch_fused_t(int mask_kind, int waves, const FwdArgs& a, hipStream_t s) {
+    const dim3 grid(a.n_blocks), block(waves * 64);
+    const size_t lds = (size_t)fused_lds_bytes<T, D>(waves);
+#define SDPA_FUSED_LAUNCH(MK)                                                                               \
+    {                                                                                                       \
+        auto* k = sdpa_fused_kernel<T, D, MK, VEC>;                                                        \
+        if (lds > 64 * 1024) {                                                                              \
+            const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),                     \
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
+            if (e != hipSuccess) return (int)e;                                                            \
+        }                                                                                                   \
+        hipLaunchKernelGGL(k, grid, block, lds, s, a);                                                      \
+        break;                                                                                              \
+    }
+    switch (mask_kind) {
+        case MASK_NONE: SDPA_FUSED_LAUNCH(MASK_NONE)
+        case MASK_BOOL: SDPA_FUSED_LAUNCH(MASK_BOOL)
+        case MASK_ADD: SDPA_FUSED_LAUNCH(MASK_ADD)
+        default: return (int)hipErrorInvalidValue;
+    }
+#undef SDPA_FUSED_LAUNCH
+    return (int)hipGetLastError();
+}
+
+template <typename T>
+int launch_fused_dt(int D, int mask_kind, int waves, bool vec, const FwdArgs& a, hipStream_t s) {
+    switch (D) {
+        case 32: return vec ? launch_fused_t<T, 32, true>(mask_kind, waves, a, s) : launch_fused_t<T, 32, false>(mask_kind, waves, a, s);
+        case 64: return vec ? launch_fused_t<T, 64, true>(mask_kind, waves, a, s) : launch_fused_t<T, 64, false>(mask_kind, waves, a, s);
+        case 128: return vec ? launch_fused_t<T, 128, true>(mask_kind, waves, a, s) : launch_fused_t<T, 128, false>(mask_kind, waves, a, s);
+        default: return (int)hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+int launch_fused(int dtype, int D, int mask_kind, int waves, bool vec, const FwdArgs& a, void* stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (waves < 1 || waves > FUSED_MAX_WAVES || a.keys_per_wave % 32 != 0 || a.keys_per_wave <= 0)
+        return (int)hipErrorInvalidValue;
+    const int maxk = D == 128 ? FUSED_MAX_KEYS_PER_WAVE_D128 : FUSED_MAX_KEYS_PER_WAVE;
+    if (a.keys_per_wave > maxk) return (int)hipErrorInvalidValue;
+    switch (dtype) {
+        case DT_F32: return launch_fused_dt<float>(D, mask_kind, waves, vec, a, s);
+        case DT_F16: return launch_fused_dt<_Float16>(D, mask_kind, waves, vec, a, s);
+        case DT_BF16: return launch_fused_dt<__bf16>(D, mask_kind, waves, vec, a, s);
+        default: return (int)hipErrorInvalidValue;
+    }
+}
 
 }  // namespace sdpa

@@ -58,8 +58,10 @@ int launch_twopass_f16(int D, int mask_kind, int waves, bool vec, const FwdArgs&
 int launch_twopass_bf16(int D, int mask_kind, int waves, bool vec, const FwdArgs& a, void* stream);
 int launch_fused(int dtype, int D, int mask_kind, int waves, bool vec, const FwdArgs& a, void* stream);
 
-// Largest key range the fused path keeps on chip per wave.
-constexpr int FUSED_MAX_KEYS_PER_WAVE = 256;
+// Largest key range the fused path keeps on chip per wave (scores held in
+// registers: 32 rows x keys / 64 lanes floats per lane), by head dim.
+constexpr int FUSED_MAX_KEYS_PER_WAVE = 256;       // D = 32, 64
+constexpr int FUSED_MAX_KEYS_PER_WAVE_D128 = 128;  // D = 128
 constexpr int FUSED_MAX_WAVES = 8;
 constexpr int TILE_N = 64;  // keys per score tile
 

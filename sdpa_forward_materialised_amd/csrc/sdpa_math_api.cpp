@@ -192,9 +192,18 @@ int64_t count_tiles(int64_t Sq, int64_t Skv, bool causal, int64_t rows) {
     return total;
 }
 
-// Default fused-path ceiling in 64x64 tiles per (batch, head); the FlagOS-OP
-// page settled on 56 for its hardware, this value is re-measured on MI355X.
-constexpr int64_t kFusedMaxTiles64 = 56;
+// Fused-path switch. The FlagOS-OP page switches on the causal-truncated
+// count of 64x64 score tiles per (batch, head) and settled on 56 for its
+// hardware. Measured on MI355X (kernel times of both paths over D 64/128,
+// causal and not, Sq 32..1024, Skv 128..2048), the tile count alone picks
+// the fused kernel where it loses: it re-reads K and V for every 32-row
+// block, while the two-pass kernel shares them over 96-128 rows and only
+// runs out of parallelism when the query range is short. The switch is
+// therefore: fused iff Sq <= 256 rows and at most 128 tiles per (batch,
+// head) (within 1% of the per-shape best on the sweep; tile count alone at
+// its best threshold, 32, is 2% off and up to 1.96x off on single shapes).
+constexpr int64_t kFusedMaxTiles64 = 128;
+constexpr int64_t kFusedMaxRows = 256;
 
 int env_path() {
     const char* e = std::getenv("SDPA_MATH_PATH");
@@ -210,22 +219,32 @@ int64_t env_max_tiles() {
     return std::strtoll(e, nullptr, 10);
 }
 
+int64_t env_max_rows() {
+    const char* e = std::getenv("SDPA_MATH_FUSED_MAX_ROWS");
+    if (!e || !*e) return kFusedMaxRows;
+    return std::strtoll(e, nullptr, 10);
+}
+
 // Fused path: one workgroup = 32 query rows, keys split over up to 8 waves,
-// each keeping at most FUSED_MAX_KEYS_PER_WAVE scores on chip.
+// each keeping at most the per-head-dim limit of scores in registers. Waves
+// are added until a wave holds at most 128 keys (fewer registers, more waves
+// in flight) or the wave count is at its maximum.
 bool fused_config(const Shape& sh, bool causal, int* waves, int* keys_per_wave) {
     const int64_t keys = causal ? std::min(sh.Skv, sh.Sq) : sh.Skv;
+    if (keys <= 0) return false;
+    const int64_t limit = sh.D == 128 ? sdpa::FUSED_MAX_KEYS_PER_WAVE_D128 : sdpa::FUSED_MAX_KEYS_PER_WAVE;
     for (int w = 1; w <= sdpa::FUSED_MAX_WAVES; w *= 2) {
         const int64_t kpw = cdiv(cdiv(keys, w), 32) * 32;
-        if (kpw <= sdpa::FUSED_MAX_KEYS_PER_WAVE) {
+        if (kpw <= std::min<int64_t>(limit, 128) || (w == sdpa::FUSED_MAX_WAVES && kpw <= limit)) {
             *waves = w;
-            *keys_per_wave = (int)std::max<int64_t>(kpw, 32);
+            *keys_per_wave = (int)kpw;
             return true;
         }
     }
     return false;
 }
 
-bool fused_available() { return false; }  // the fused kernel is not built yet
+bool fused_available() { return true; }
 
 // True when the 16-byte variant of the two-pass kernel can run: probability
 // and output rows 16-byte aligned (null: the default dense outputs), Skv a
@@ -249,10 +268,13 @@ sdpa_status_t make_plan(const Shape& sh, bool causal, int forced, bool vec, sdpa
     const bool fused_ok = fused_available() && fused_config(sh, causal, &fw, &fk);
     int path = forced;
     if (path == SDPA_PATH_AUTO) path = env_path();
-    if (path == SDPA_PATH_AUTO) path = (fused_ok && p->tiles_64 <= env_max_tiles()) ? SDPA_PATH_FUSED : SDPA_PATH_TWOPASS;
+    if (path == SDPA_PATH_AUTO)
+        path = (fused_ok && p->tiles_64 <= env_max_tiles() && sh.Sq <= env_max_rows()) ? SDPA_PATH_FUSED
+                                                                                      : SDPA_PATH_TWOPASS;
     if (path == SDPA_PATH_FUSED && !fused_ok)
-        return fail(SDPA_ERR_UNSUPPORTED, "the fused path cannot take this shape (keys beyond %d per wave x %d waves)",
-                    sdpa::FUSED_MAX_KEYS_PER_WAVE, sdpa::FUSED_MAX_WAVES);
+        return fail(SDPA_ERR_UNSUPPORTED, "the fused path cannot take this shape (more than %d keys per wave x %d waves)",
+                    sh.D == 128 ? sdpa::FUSED_MAX_KEYS_PER_WAVE_D128 : sdpa::FUSED_MAX_KEYS_PER_WAVE,
+                    sdpa::FUSED_MAX_WAVES);
     p->path = path;
     if (path == SDPA_PATH_FUSED) {
         p->waves = fw;

@@ -114,3 +114,18 @@ def test_plan_reports_paths_and_tiles():
     k = _z(4, 8, 1024, 128)
     m = torch.ones(4, 1, 1024, 1024, dtype=torch.bool)
     assert S.plan(q, k, k, m, False, True)[2] == 256
+
+
+def test_plan_picks_fused_for_few_tiles():
+    # decode-like: 100 queries x 1152 keys is 36 tiles of 64x64 per (b, h)
+    q, k = _z(16, 8, 100, 64), _z(16, 8, 1152, 64)
+    m = torch.zeros(16, 8, 100, 1152, dtype=torch.float16)
+    assert S.plan(q, k, k, m) == ("fused", 4 * 18, 36)  # 32-row blocks x 64-key tiles
+    q = _z(1, 2, 64, 32, dtype=torch.float32)
+    assert S.plan(q, q, q, is_causal=True)[0] == "fused"
+    # many tiles: two-pass
+    q = _z(4, 8, 1024, 64)
+    assert S.plan(q, q, q, is_causal=True)[0] == "twopass"
+    # few tiles, but more keys than the fused waves hold at D=128: two-pass
+    q, k = _z(1, 2, 1, 128), _z(1, 2, 1100, 128)
+    assert S.plan(q, k, k) == ("twopass", 18, 18)

@@ -18,7 +18,7 @@ from parity import compare, head_slice, poisoned_outputs, run_oracle
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
-PATHS = ["twopass"]
+PATHS = ["twopass", "fused"]
 
 
 def _lib():
@@ -38,7 +38,12 @@ def _run(c, path, scale=None, gqa=None, label=""):
     print(f"[case] {label} path={path} shape={tuple(q.shape)}x{tuple(k.shape)} mask="
           f"{None if m is None else (tuple(m.shape), m.dtype)} causal={c['causal']}", flush=True)
     gm = None if m is None else m.to(DEV)
-    O, P, L = S.fwd(q.to(DEV), k.to(DEV), v.to(DEV), gm, c["causal"], scale, gqa, path=path, out=out)
+    try:
+        O, P, L = S.fwd(q.to(DEV), k.to(DEV), v.to(DEV), gm, c["causal"], scale, gqa, path=path, out=out)
+    except NotImplementedError as e:
+        if path == "fused":
+            pytest.skip(f"the fused path cannot take this shape: {e}")
+        raise
     torch.cuda.synchronize()
     return O, P, L
 
