@@ -281,14 +281,17 @@ sdpa_status_t make_plan(const Shape& sh, bool causal, int forced, bool vec, sdpa
         p->keys_per_wave = fk;
         p->q_rows = 32;
     } else {
-        // Several compute waves share each staged K/V tile; drop to two when
-        // that leaves fewer than two workgroups per compute unit. 128-wide
-        // heads need about 256 VGPRs per compute wave (two waves per SIMD):
-        // three compute waves plus the loader wave fill a CU with two
-        // workgroups. Narrower heads fit 168 VGPRs and take four.
+        // Three compute waves plus the loader wave: a workgroup of four waves
+        // takes one wave slot per SIMD, so two of them share a CU (a
+        // five-wave workgroup takes two slots per SIMD and runs alone).
+        // Drop to two compute waves when that leaves fewer than two
+        // workgroups per CU. Four compute waves (a tuning option) fit
+        // 16-bit inputs at every head dim and float32 at D = 32; float32
+        // takes at most three at D = 64 and two at D = 128 (its tiles are
+        // twice as large).
         const int64_t bh = sh.B * sh.Hq;
-        const int wide = sh.D == 128 ? 3 : 4;
-        p->waves = (bh * cdiv(sh.Sq, 32 * wide) >= 512) ? wide : 2;
+        const int wide = (sh.dtype != SDPA_F32 || sh.D == 32) ? 4 : 3;
+        p->waves = (bh * cdiv(sh.Sq, 96) >= 512) ? 3 : 2;
         if (const char* e = std::getenv("SDPA_MATH_TP_WAVES")) {
             const int wv = std::atoi(e);
             if (wv >= 2 && wv <= wide) p->waves = wv;

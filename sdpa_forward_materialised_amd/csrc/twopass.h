@@ -25,6 +25,8 @@
 
 #pragma once
 
+#include <type_traits>
+
 #include "sdpa_device.h"
 
 namespace sdpa {
@@ -42,9 +44,11 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
 // vmcnt(0) only (expcnt and lgkmcnt left at their maxima)
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-template <typename T, int D, int NW, int MASK, bool VEC>
+template <typename T, int D, int NW, int MASK, bool VEC, int TN>
 struct TwoPassCfg {
     static constexpr int SZ = (int)sizeof(T);
+    static constexpr int BN = TN;                 // keys per tile: 32 or 64 (one or two MFMA blocks)
+    static constexpr int NKB = TN / 32;
     static constexpr int QB = 32 * NW;            // query rows per workgroup
     static constexpr int ROWB = D * SZ;           // bytes per K/V row
     static constexpr int CPR = ROWB / 16;         // 16-byte chunks per K/V row
@@ -59,30 +63,51 @@ struct TwoPassCfg {
     static constexpr int MRPI = 64 / MCPR;
     static constexpr int MNI = QB / MRPI;
     static constexpr int MTILEB = MLDS ? QB * MROWB : 0;
-    static constexpr int LDS_BYTES = 2 * (2 * TILEB + MTILEB);
+    // Probabilities of a tile are staged per wave in LDS and written out as
+    // whole rows (the MFMA layout gives each lane two 16-byte runs of one
+    // row per 32 keys, i.e. 32-byte pieces of 32 rows per store: the costly
+    // pattern for the memory pipeline). Staged only while two workgroups
+    // still fit in one CU's LDS.
+    static constexpr int ZC = BN * SZ / 16;       // 16-byte chunks per row of a P tile
+    static constexpr int ZRPB = ZC * 16 >= 256 ? 1 : 256 / (ZC * 16);  // P rows per 64-bank span
+    static constexpr int PSTB = 32 * BN * SZ;     // bytes of one wave's staged P tile
+    static constexpr int KVM_BYTES = 2 * (2 * TILEB + MTILEB);
+    static constexpr bool PSTAGE = VEC && KVM_BYTES + NW * PSTB <= 80 * 1024;
+    static constexpr int LDS_BYTES = KVM_BYTES + (PSTAGE ? NW * PSTB : 0);
     static_assert(LDS_BYTES <= 160 * 1024, "tile buffers exceed the 160 KB LDS of a compute unit");
-    // LDS tile layouts, in 16-byte chunk positions. Every operand read is a
-    // per-lane base plus a compile-time offset, and free of bank conflicts:
-    //  K: per 32-row block, per chunk pair: 32 rows of the even chunk, then
-    //     32 rows of the odd chunk (a lane reads row r, chunk 2c + h at r + 32h
-    //     + 64c: 16 consecutive rows hit 16 distinct bank groups);
-    //  V: per 16-row block, per group of 4 chunks: row-major 16 x 4 (the
-    //     transposing read takes 4 rows x 2 chunks per 16-lane group, which
-    //     land on 8 distinct bank groups).
-    static __device__ __forceinline__ int pos_k(int row, int chunk) {
-        return (row >> 5) * (32 * CPR) + (chunk >> 1) * 64 + (row & 31) + 32 * (chunk & 1);
-    }
-    static __device__ __forceinline__ int pos_v(int row, int chunk) {
-        return (row >> 4) * (16 * CPR) + (chunk >> 2) * 64 + 4 * (row & 15) + (chunk & 3);
+    // LDS tile layouts, in 16-byte chunk positions: row-major, with the
+    // chunks of each row permuted by an XOR (chunk c of row r at position
+    // r * CPR + (c ^ f(r))). Each buffer-to-LDS instruction then fetches whole
+    // rows (a few cache lines, the cheap pattern for the memory pipeline),
+    // and the operand reads are free of bank conflicts:
+    //  K: 16 consecutive rows, one chunk each (ds_read_b128): f spreads the
+    //     rows sharing a 256-byte bank window over distinct chunk slots;
+    //  V: 4 rows x 2 chunks per 16-lane group of the transposing read, the
+    //     two groups of a cycle on the other 2 chunks: f moves whole groups
+    //     of 4 chunks.
+    static __device__ __forceinline__ int fk(int row) { return (row / RPB) & (CPR - 1); }
+    static __device__ __forceinline__ int fv(int row) { return 4 * ((row / RPB) & (CPR / 4 - 1)); }
+    static __device__ __forceinline__ int pos_k(int row, int chunk) { return row * CPR + (chunk ^ fk(row)); }
+    static __device__ __forceinline__ int pos_v(int row, int chunk) { return row * CPR + (chunk ^ fv(row)); }
+    // staged P tile: row-major, chunks XOR-permuted like K (writes: 16 rows,
+    // one chunk each; reads: whole rows)
+    static __device__ __forceinline__ int pos_p(int row, int chunk) {
+        return row * ZC + (chunk ^ ((row / ZRPB) & (ZC - 1)));
     }
     static_assert(CPR % 4 == 0, "tile layouts need a multiple of 4 chunks per row");
 };
 
-template <typename T, int D, int NW, int MASK, bool VEC>
+#ifndef SDPA_TP_WPE
+#define SDPA_TP_WPE(NW) ((NW) >= 4 ? 3 : 2)
+#endif
+
+template <typename T, int D, int NW, int MASK, bool VEC, int TN>
 __global__ __attribute__((amdgpu_flat_work_group_size((NW + 1) * 64, (NW + 1) * 64),
-                          amdgpu_waves_per_eu(NW >= 4 ? 3 : 2)))
+                          amdgpu_waves_per_eu(SDPA_TP_WPE(NW))))
 void sdpa_twopass_kernel(const FwdArgs a) {
-    using C = TwoPassCfg<T, D, NW, MASK, VEC>;
+    using C = TwoPassCfg<T, D, NW, MASK, VEC, TN>;
+    constexpr int BN = C::BN;
+    constexpr int NKB = C::NKB;
     using TR = Tr<T>;
     using vec = typename TR::vec;
     constexpr int SZ = C::SZ;
@@ -120,14 +145,15 @@ void sdpa_twopass_kernel(const FwdArgs a) {
 
     // ======================================================== loader wave
     if (wave == NW) {
-        // instruction j of a tile fills chunk positions [64 j, 64 j + 64): lane
-        // l fetches the (row, chunk) that the layout puts at position 64 j + l
+        // instruction j of a tile fills chunk positions [64 j, 64 j + 64), i.e.
+        // rows j * RPI .. +RPI: lane l fetches the chunk the layout puts at
+        // position 64 j + l
         auto dma_k = [&](uint8_t* dst, int t) {
             const uint32_t so = (uint32_t)(t * BN) * krow_bytes;
 #pragma unroll
-            for (int j = 0; j < C::CPR; ++j) {
-                const int row = 32 * (j / (C::CPR / 2)) + (lane & 31);
-                const int chunk = 2 * (j % (C::CPR / 2)) + (lane >> 5);
+            for (int j = 0; j < C::CPR * BN / 64; ++j) {
+                const int row = j * C::RPI + lane / C::CPR;
+                const int chunk = (lane % C::CPR) ^ C::fk(row);
                 const uint32_t vo = pred(t * BN + row < a.Skv, row * krow_bytes + (uint32_t)(chunk * 16));
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(dst + j * 1024), 16, vo, so, 0, 0);
             }
@@ -135,9 +161,9 @@ void sdpa_twopass_kernel(const FwdArgs a) {
         auto dma_v = [&](uint8_t* dst, int t) {
             const uint32_t so = (uint32_t)(t * BN) * vrow_bytes;
 #pragma unroll
-            for (int j = 0; j < C::CPR; ++j) {
-                const int row = 16 * (j / (C::CPR / 4)) + (lane >> 2);
-                const int chunk = 4 * (j % (C::CPR / 4)) + (lane & 3);
+            for (int j = 0; j < C::CPR * BN / 64; ++j) {
+                const int row = j * C::RPI + lane / C::CPR;
+                const int chunk = (lane % C::CPR) ^ C::fv(row);
                 const uint32_t vo = pred(t * BN + row < a.Skv, row * vrow_bytes + (uint32_t)(chunk * 16));
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(dst + j * 1024), 16, vo, so, 0, 0);
             }
@@ -271,8 +297,9 @@ void sdpa_twopass_kernel(const FwdArgs a) {
     // hold keys past Skv or past this wave's causal diagonal.
     auto scores = [&](const f32x16& acc, const float* mv, int kb, int k0, bool edge, float* t) {
         const int jb = k0 + 32 * kb;
-        // register r holds key jb + kk(hf, r); it is dropped when kk(hf, r) > lim
-        const int lim = edge ? min(a.Skv - 1 - jb, a.causal ? qi - jb : 0x7fffffff) : 0x7fffffff;
+        // register r holds key jb + kk(hf, r) = jb + 8 hf + kk(0, r); it is
+        // dropped when kk(0, r) > lim (a compile-time constant per register)
+        const int lim = edge ? min(a.Skv - 1 - jb, a.causal ? qi - jb : 0x7fffffff) - 8 * hf : 0x7fffffff;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             float x;
@@ -283,52 +310,69 @@ void sdpa_twopass_kernel(const FwdArgs a) {
                 x = acc[r] * a.scale_log2;
                 if constexpr (MASK == MASK_BOOL) drop = mv[r] == 0.0f;
             }
-            if (edge) drop = drop || kk(hf, r) > lim;
+            if (edge) drop = drop || kk(0, r) > lim;
             t[r] = drop ? -INFINITY : x;
         }
     };
 
+    // Tiles of this wave: [0, t_fast) hold only keys every row keeps (no
+    // edge), [t_fast, t_comp) reach past Skv or the causal diagonal, and
+    // [t_comp, ntiles) lie wholly above the diagonal. Each range has its own
+    // loop, so each loop body is straight-line code; every wave still meets
+    // one barrier per tile, as the loader wave does.
+    const int t_comp = a.causal ? min(ntiles, (qw + 31) / BN + 1) : ntiles;
+    const int t_fast = min(t_comp, a.causal ? min(a.Skv / BN, (qw + 1) / BN) : a.Skv / BN);
+
     // ---------------- sweep 1: row maximum and sum (base 2)
     float m_run = -INFINITY, l_run = 0.0f;
-    __syncthreads();  // tile 0 staged
-    for (int t = 0; t < ntiles; ++t) {
+    auto sweep1_tile = [&](int t, auto edge_c) {
+        constexpr bool edge = decltype(edge_c)::value;
         const int k0 = t * BN;
         const int buf = t & 1;
-        if (!(a.causal && k0 > qw + 31)) {  // else: whole tile above this wave's diagonal
-            const bool edge = (k0 + BN > a.Skv) || (a.causal && k0 + BN - 1 > qw);
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const f32x16 acc = qk_block(kbuf(buf), kb);
-                float sum = 0.0f;
-                if (MASK == MASK_NONE && !edge && a.scale_log2 > 0.0f) {
-                    // max on the raw scores (the scale is positive), then one fma per exponent
-                    float mx = acc[0];
+        for (int kb = 0; kb < NKB; ++kb) {
+            const f32x16 acc = qk_block(kbuf(buf), kb);
+            float sum = 0.0f;
+            if (MASK == MASK_NONE && !edge && a.scale_log2 > 0.0f) {
+                // max on the raw scores (the scale is positive), then one fma per exponent
+                float mx = acc[0];
 #pragma unroll
-                    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, acc[r]);
-                    const float mn = fmaxf(m_run, mx * a.scale_log2);
+                for (int r = 1; r < 16; ++r) mx = fmaxf(mx, acc[r]);
+                const float mn = fmaxf(m_run, mx * a.scale_log2);
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) sum += fast_exp2(__builtin_fmaf(acc[r], a.scale_log2, -mn));
+                for (int r = 0; r < 16; ++r) sum += fast_exp2(__builtin_fmaf(acc[r], a.scale_log2, -mn));
+                l_run = l_run * fast_exp2(m_run - mn) + sum;
+                m_run = mn;
+            } else {
+                float mv[16];
+                mask_terms(mbuf(buf), k0, kb, mv);
+                float tt[16];
+                scores(acc, mv, kb, k0, edge, tt);
+                float mt = tt[0];
+#pragma unroll
+                for (int r = 1; r < 16; ++r) mt = fmaxf(mt, tt[r]);
+                const float mn = fmaxf(m_run, mt);
+                if (mn != -INFINITY) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) sum += fast_exp2(tt[r] - mn);
                     l_run = l_run * fast_exp2(m_run - mn) + sum;
                     m_run = mn;
-                } else {
-                    float mv[16];
-                    mask_terms(mbuf(buf), k0, kb, mv);
-                    float tt[16];
-                    scores(acc, mv, kb, k0, edge, tt);
-                    float mt = tt[0];
-#pragma unroll
-                    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, tt[r]);
-                    const float mn = fmaxf(m_run, mt);
-                    if (mn != -INFINITY) {
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) sum += fast_exp2(tt[r] - mn);
-                        l_run = l_run * fast_exp2(m_run - mn) + sum;
-                        m_run = mn;
-                    }
                 }
             }
         }
-        __syncthreads();  // tile t consumed, tile t+1 staged
+    };
+    __syncthreads();  // tile 0 staged
+    {
+        int t = 0;
+        for (; t < t_fast; ++t) {
+            sweep1_tile(t, std::false_type{});
+            __syncthreads();  // tile t consumed, tile t+1 staged
+        }
+        for (; t < t_comp; ++t) {
+            sweep1_tile(t, std::true_type{});
+            __syncthreads();
+        }
+        for (; t < ntiles; ++t) __syncthreads();
     }
     {  // the two half-waves holding the same query row
         const float m_o = __shfl_xor(m_run, 32);
@@ -397,59 +441,115 @@ void sdpa_twopass_kernel(const FwdArgs a) {
         }
     };
 
-    __syncthreads();  // tile 0 staged
-    for (int t = 0; t < ntiles; ++t) {
+    uint8_t* pst = smem + C::KVM_BYTES + (C::PSTAGE ? wave * C::PSTB : 0);  // this wave's staged P tile
+    auto sweep2_tile = [&](int t, auto edge_c) {
+        constexpr bool edge = decltype(edge_c)::value;
         const int k0 = t * BN;
         const int buf = t & 1;
-        const bool edge = (k0 + BN > a.Skv) || (a.causal && k0 + BN - 1 > qw);
-        if (a.causal && k0 > qw + 31) {
-            // whole tile above this wave's diagonal: P is zero, O unchanged
-            const float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-            for (int q = 0; q < 4; ++q) store_run(k0, q >> 1, q & 1, edge, z);
-        } else {
+        for (int kb = 0; kb < NKB; ++kb) {
+            const f32x16 acc = qk_block(kbuf(buf), kb);
+            float p[16];
+            if (MASK == MASK_NONE && !edge) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const f32x16 acc = qk_block(kbuf(buf), kb);
-                float p[16];
-                if (MASK == MASK_NONE && !edge) {
+                for (int r = 0; r < 16; ++r) p[r] = fast_exp2(__builtin_fmaf(acc[r], a.scale_log2, -lse2));
+            } else {
+                float mv[16];
+                mask_terms(mbuf(buf), k0, kb, mv);
+                float tt[16];
+                scores(acc, mv, kb, k0, edge, tt);
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) p[r] = fast_exp2(__builtin_fmaf(acc[r], a.scale_log2, -lse2));
-                } else {
-                    float mv[16];
-                    mask_terms(mbuf(buf), k0, kb, mv);
-                    float tt[16];
-                    scores(acc, mv, kb, k0, edge, tt);
+                for (int r = 0; r < 16; ++r) p[r] = fast_exp2(tt[r] - lse2);
+            }
+            if constexpr (sizeof(T) == 2) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) p[r] = fast_exp2(tt[r] - lse2);
-                }
-                if constexpr (sizeof(T) == 2) {
-#pragma unroll
-                    for (int c2 = 0; c2 < 2; ++c2) {
-                        const vec pv = TR::cvt8(p + 8 * c2);
+                for (int c2 = 0; c2 < 2; ++c2) {
+                    const vec pv = TR::cvt8(p + 8 * c2);
+                    if constexpr (C::PSTAGE) {
+                        const int chunk = (32 * kb + 16 * c2 + 8 * hf) * SZ / 16;
+                        *reinterpret_cast<u32x4*>(pst + C::pos_p(n, chunk) * 16) = __builtin_bit_cast(u32x4, pv);
+                    } else {
                         store_run(k0, kb, c2, edge, p + 8 * c2);
-#pragma unroll
-                        for (int d = 0; d < ND; ++d)
-                            oacc[d] = TR::mfma(v_operand(vbuf(buf), 32 * kb + 16 * c2, d), pv, oacc[d]);
                     }
+#pragma unroll
+                    for (int d = 0; d < ND; ++d)
+                        oacc[d] = TR::mfma(v_operand(vbuf(buf), 32 * kb + 16 * c2, d), pv, oacc[d]);
+                }
+            } else {
+                if constexpr (C::PSTAGE) {
+#pragma unroll
+                    for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+                        for (int h2 = 0; h2 < 2; ++h2) {
+                            const int chunk = (32 * kb + 16 * c2 + 8 * hf) * SZ / 16 + h2;
+                            const float* x = p + 8 * c2 + 4 * h2;
+                            *reinterpret_cast<u32x4*>(pst + C::pos_p(n, chunk) * 16) =
+                                u32x4{__builtin_bit_cast(uint32_t, x[0]), __builtin_bit_cast(uint32_t, x[1]),
+                                      __builtin_bit_cast(uint32_t, x[2]), __builtin_bit_cast(uint32_t, x[3])};
+                        }
                 } else {
                     store_run(k0, kb, 0, edge, p);
                     store_run(k0, kb, 1, edge, p + 8);
+                }
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int row = 32 * kb + kk(hf, r);
+                for (int r = 0; r < 16; ++r) {
+                    const int row = 32 * kb + kk(hf, r);
 #pragma unroll
-                        for (int d = 0; d < ND; ++d) {
-                            const int col = 32 * d + swap23(n);
-                            const float va = *reinterpret_cast<const float*>(
-                                vbuf(buf) + C::pos_v(row, col * SZ / 16) * 16 + ((col * SZ) & 15));
-                            oacc[d] = TR::mfma(va, p[r], oacc[d]);
-                        }
+                    for (int d = 0; d < ND; ++d) {
+                        const int col = 32 * d + swap23(n);
+                        const float va = *reinterpret_cast<const float*>(
+                            vbuf(buf) + C::pos_v(row, col * SZ / 16) * 16 + ((col * SZ) & 15));
+                        oacc[d] = TR::mfma(va, p[r], oacc[d]);
                     }
                 }
             }
         }
-        __syncthreads();  // tile t consumed, tile t+1 staged
+        if constexpr (C::PSTAGE) {
+            // whole-row stores: instruction i covers rows i * 64 / ZC ..
+#pragma unroll
+            for (int i = 0; i < 32 * C::ZC / 64; ++i) {
+                const int row = i * (64 / C::ZC) + lane / C::ZC;
+                const int chunk = lane % C::ZC;
+                const u32x4 bits = *reinterpret_cast<const u32x4*>(pst + C::pos_p(row, chunk) * 16);
+                const int grow = qw + row, key = k0 + chunk * (16 / SZ);
+                const bool ok = grow < a.Sq && (!edge || key < a.Skv);
+                st128(pr, pred(ok, (uint32_t)((int64_t)(grow < a.Sq ? grow : 0) * a.p_s[2] * SZ) + (uint32_t)(key * SZ)),
+                      bits);
+            }
+        }
+    };
+    __syncthreads();  // tile 0 staged
+    {
+        int t = 0;
+        for (; t < t_fast; ++t) {
+            sweep2_tile(t, std::false_type{});
+            __syncthreads();  // tile t consumed, tile t+1 staged
+        }
+        for (; t < t_comp; ++t) {
+            sweep2_tile(t, std::true_type{});
+            __syncthreads();
+        }
+        // whole tiles above this wave's diagonal: P is zero, O unchanged
+        for (; t < ntiles; ++t) {
+            if constexpr (VEC) {
+                // whole-row 16-byte stores: instruction i covers rows 64 i / ZC ..
+                constexpr int ZC = BN * SZ / 16;  // 16-byte chunks per row of the tile
+#pragma unroll
+                for (int i = 0; i < 32 * ZC / 64; ++i) {
+                    const int row = qw + i * (64 / ZC) + lane / ZC;
+                    const int key = t * BN + (lane % ZC) * (16 / SZ);
+                    st128(pr, pred(row < a.Sq && key < a.Skv,
+                                   (uint32_t)((int64_t)(row < a.Sq ? row : 0) * a.p_s[2] * SZ) + (uint32_t)(key * SZ)),
+                          u32x4{0u, 0u, 0u, 0u});
+                }
+            } else {
+                const float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                const bool edge = (t + 1) * BN > a.Skv;
+#pragma unroll
+                for (int q = 0; q < 2 * NKB; ++q) store_run(t * BN, q >> 1, q & 1, edge, z);
+            }
+            __syncthreads();
+        }
     }
 
     // ---------------- O: lane (n, h) holds O[qi][32d + 8h ..+8) and [32d + 16 + 8h ..+8)
@@ -469,28 +569,33 @@ void sdpa_twopass_kernel(const FwdArgs a) {
     zero_rows<T, VEC>(pr, a.p_s[2], qw, a.Sq, ntiles * BN, a.Skv, lane);
 }
 
+#ifndef SDPA_TP_TN
+#define SDPA_TP_TN 64
+#endif
+
 template <typename T, int D, int NW, bool VEC>
 static int launch_twopass_mask(int mask_kind, const FwdArgs& a, hipStream_t s) {
+    constexpr int TN = SDPA_TP_TN;
     dim3 grid(a.n_blocks), block((NW + 1) * 64);
     switch (mask_kind) {
-        case MASK_NONE: hipLaunchKernelGGL((sdpa_twopass_kernel<T, D, NW, MASK_NONE, VEC>), grid, block, 0, s, a); break;
-        case MASK_BOOL: hipLaunchKernelGGL((sdpa_twopass_kernel<T, D, NW, MASK_BOOL, VEC>), grid, block, 0, s, a); break;
-        case MASK_ADD: hipLaunchKernelGGL((sdpa_twopass_kernel<T, D, NW, MASK_ADD, VEC>), grid, block, 0, s, a); break;
+        case MASK_NONE: hipLaunchKernelGGL((sdpa_twopass_kernel<T, D, NW, MASK_NONE, VEC, TN>), grid, block, 0, s, a); break;
+        case MASK_BOOL: hipLaunchKernelGGL((sdpa_twopass_kernel<T, D, NW, MASK_BOOL, VEC, TN>), grid, block, 0, s, a); break;
+        case MASK_ADD: hipLaunchKernelGGL((sdpa_twopass_kernel<T, D, NW, MASK_ADD, VEC, TN>), grid, block, 0, s, a); break;
         default: return (int)hipErrorInvalidValue;
     }
     return (int)hipGetLastError();
 }
 
 // Element-wise layouts only need correctness: they get one two-wave shape.
-// 128-wide heads take at most three compute waves (register budget); float32
-// 128-wide tiles are twice as large: two compute waves keep them within LDS.
+// float32 takes at most three compute waves at D = 64 (register budget) and
+// two at D = 128 (its tiles are twice as large: two waves keep them in LDS).
 template <typename T>
 static int launch_twopass_t(int D, int mask_kind, int waves, bool vec, const FwdArgs& a, void* stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 #define SDPA_TP_DIM(DD)                                                                     \
     case DD:                                                                                \
         if (!vec) return launch_twopass_mask<T, DD, 2, false>(mask_kind, a, s);             \
-        if constexpr (DD < 128) {                                                           \
+        if constexpr (sizeof(T) == 2 || DD == 32) {                                          \
             if (waves == 4) return launch_twopass_mask<T, DD, 4, true>(mask_kind, a, s);    \
         }                                                                                   \
         if constexpr (sizeof(T) == 2 || DD < 128) {                                          \
