@@ -132,7 +132,7 @@ __device__ __forceinline__ Work decode_block(int L, const FwdArgs& a) {
     const int nfull = nb & ~7;
     const int nq = a.n_qblk;
     Work w;
-    if (L < nfull) {
+    if (L < nfull && a.sched != 2) {
         const int per = nfull >> 3;
         const int x = L & 7, i = L >> 3;
         if (a.sched == 1) {
@@ -147,6 +147,17 @@ __device__ __forceinline__ Work decode_block(int L, const FwdArgs& a) {
             return w;
         }
         L = x * per + i;
+    }
+    if (a.sched == 2) {
+        // causal, heaviest first over the whole grid (longest-processing-time
+        // order): all (batch, head) slices' last blocks, then the blocks
+        // before them, ...; a slot that frees up takes the heaviest block left
+        const int nbh = a.B * a.Hq;
+        const int bh = L % nbh;
+        w.qblk = nq - 1 - L / nbh;
+        w.b = bh / a.Hq;
+        w.hq = bh - w.b * a.Hq;
+        return w;
     }
     const int bh = L / nq;
     const int r = L - bh * nq;

@@ -285,12 +285,11 @@ sdpa_status_t make_plan(const Shape& sh, bool causal, int forced, bool vec, sdpa
         // takes one wave slot per SIMD, so two of them share a CU (a
         // five-wave workgroup takes two slots per SIMD and runs alone).
         // Drop to two compute waves when that leaves fewer than two
-        // workgroups per CU. Four compute waves (a tuning option) fit
-        // 16-bit inputs at every head dim and float32 at D = 32; float32
-        // takes at most three at D = 64 and two at D = 128 (its tiles are
-        // twice as large).
+        // workgroups per CU. Four compute waves (a tuning option) fit in
+        // registers for D <= 64 (float32: D = 32); float32 takes at most
+        // two at D = 128 (its tiles are twice as large).
         const int64_t bh = sh.B * sh.Hq;
-        const int wide = (sh.dtype != SDPA_F32 || sh.D == 32) ? 4 : 3;
+        const int wide = (sh.D < 128 && (sh.dtype != SDPA_F32 || sh.D == 32)) ? 4 : 3;
         p->waves = (bh * cdiv(sh.Sq, 96) >= 512) ? 3 : 2;
         if (const char* e = std::getenv("SDPA_MATH_TP_WAVES")) {
             const int wv = std::atoi(e);
@@ -365,15 +364,19 @@ sdpa_status_t run(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_ten
     a.n_qblk = plan.n_qblk;
     a.n_blocks = (int)plan.grid;
     a.keys_per_wave = plan.keys_per_wave;
-    // Workgroup order: head-major with the heaviest causal blocks first
-    // (measured fastest); SDPA_MATH_SCHED=1 pairs heavy and light causal
-    // blocks on each XCD instead, where the grid splits evenly.
-    a.sched = 0;
+    // Workgroup order. Causal: heaviest query blocks first over the whole
+    // grid (longest-processing-time order; measured fastest). Otherwise
+    // head-major, with each XCD taking consecutive blocks (shared K/V in its
+    // L2). SDPA_MATH_SCHED=0|1|2 overrides (1: heavy and light causal blocks
+    // interleaved per XCD).
+    a.sched = is_causal ? 2 : 0;
     if (const char* e = std::getenv("SDPA_MATH_SCHED")) {
+        a.sched = 0;
         if (*e == '1' && is_causal && plan.grid % 8 == 0) {
             const int64_t per = plan.grid / 8;
             if (per % plan.n_qblk == 0 && per % 2 == 0) a.sched = 1;
         }
+        if (*e == '2' && is_causal) a.sched = 2;
     }
 
     // byte extent of one (batch, head) slice of each tensor

@@ -252,10 +252,17 @@ void sdpa_twopass_kernel(const FwdArgs a) {
         else return *reinterpret_cast<const float*>(p);
     };
     // S^T of 32-key block kb (one MFMA chain over the head dim)
+    // All K operand reads of the block are issued before its MFMA chain, so
+    // the chain does not wait on LDS latency between steps.
     auto qk_block = [&](const uint8_t* kt, int kb) -> f32x16 {
         f32x16 acc = {};
+        vec ka[NKS];
 #pragma unroll
-        for (int c = 0; c < NKS; ++c) acc = TR::mfma(k_operand(kt, kb, c), qf[c], acc);
+        for (int c = 0; c < NKS; ++c) ka[c] = k_operand(kt, kb, c);
+#pragma unroll
+        for (int c = 0; c < NKS; ++c) acc = TR::mfma(ka[c], qf[c], acc);
+        __builtin_amdgcn_sched_group_barrier(0x100, NKS, 0);  // the DS reads first
+        __builtin_amdgcn_sched_group_barrier(0x008, NKS, 0);  // then the MFMAs
         return acc;
     };
 
@@ -320,7 +327,10 @@ void sdpa_twopass_kernel(const FwdArgs a) {
     // [t_comp, ntiles) lie wholly above the diagonal. Each range has its own
     // loop, so each loop body is straight-line code; every wave still meets
     // one barrier per tile, as the loader wave does.
-    const int t_comp = a.causal ? min(ntiles, (qw + 31) / BN + 1) : ntiles;
+    // a wave whose rows all lie past Sq (the last block of a ragged Sq) only
+    // keeps the barrier count
+    const bool live = qw < a.Sq;
+    const int t_comp = !live ? 0 : a.causal ? min(ntiles, (qw + 31) / BN + 1) : ntiles;
     const int t_fast = min(t_comp, a.causal ? min(a.Skv / BN, (qw + 1) / BN) : a.Skv / BN);
 
     // ---------------- sweep 1: row maximum and sum (base 2)
@@ -462,6 +472,11 @@ void sdpa_twopass_kernel(const FwdArgs a) {
                 for (int r = 0; r < 16; ++r) p[r] = fast_exp2(tt[r] - lse2);
             }
             if constexpr (sizeof(T) == 2) {
+                vec va[2][ND];  // V^T operands of both 16-key halves, read ahead of the MFMAs
+#pragma unroll
+                for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+                    for (int d = 0; d < ND; ++d) va[c2][d] = v_operand(vbuf(buf), 32 * kb + 16 * c2, d);
 #pragma unroll
                 for (int c2 = 0; c2 < 2; ++c2) {
                     const vec pv = TR::cvt8(p + 8 * c2);
@@ -472,8 +487,7 @@ void sdpa_twopass_kernel(const FwdArgs a) {
                         store_run(k0, kb, c2, edge, p + 8 * c2);
                     }
 #pragma unroll
-                    for (int d = 0; d < ND; ++d)
-                        oacc[d] = TR::mfma(v_operand(vbuf(buf), 32 * kb + 16 * c2, d), pv, oacc[d]);
+                    for (int d = 0; d < ND; ++d) oacc[d] = TR::mfma(va[c2][d], pv, oacc[d]);
                 }
             } else {
                 if constexpr (C::PSTAGE) {
@@ -531,7 +545,9 @@ void sdpa_twopass_kernel(const FwdArgs a) {
         }
         // whole tiles above this wave's diagonal: P is zero, O unchanged
         for (; t < ntiles; ++t) {
-            if constexpr (VEC) {
+            if (!live) {
+                // nothing to store
+            } else if constexpr (VEC) {
                 // whole-row 16-byte stores: instruction i covers rows 64 i / ZC ..
                 constexpr int ZC = BN * SZ / 16;  // 16-byte chunks per row of the tile
 #pragma unroll
@@ -595,7 +611,7 @@ static int launch_twopass_t(int D, int mask_kind, int waves, bool vec, const Fwd
 #define SDPA_TP_DIM(DD)                                                                     \
     case DD:                                                                                \
         if (!vec) return launch_twopass_mask<T, DD, 2, false>(mask_kind, a, s);             \
-        if constexpr (sizeof(T) == 2 || DD == 32) {                                          \
+        if constexpr (DD < 128 && (sizeof(T) == 2 || DD == 32)) {                            \
             if (waves == 4) return launch_twopass_mask<T, DD, 4, true>(mask_kind, a, s);    \
         }                                                                                   \
         if constexpr (sizeof(T) == 2 || DD < 128) {                                          \
