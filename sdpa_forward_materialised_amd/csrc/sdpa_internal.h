@@ -57,6 +57,11 @@ int launch_twopass_f32(int D, int mask_kind, int waves, bool vec, const FwdArgs&
 int launch_twopass_f16(int D, int mask_kind, int waves, bool vec, const FwdArgs& a, void* stream);
 int launch_twopass_bf16(int D, int mask_kind, int waves, bool vec, const FwdArgs& a, void* stream);
 int launch_fused(int dtype, int D, int mask_kind, int waves, bool vec, const FwdArgs& a, void* stream);
+// Whether the two-pass kernel can run four compute waves without a loader
+// wave (16-byte layouts) for this head dim and mask kind.
+bool twopass_nl_ok_f32(int D, int mask_kind);
+bool twopass_nl_ok_f16(int D, int mask_kind);
+bool twopass_nl_ok_bf16(int D, int mask_kind);
 
 // Largest key range the fused path keeps on chip per wave (scores held in
 // registers: 32 rows x keys / 64 lanes floats per lane), by head dim.

@@ -281,23 +281,28 @@ sdpa_status_t make_plan(const Shape& sh, bool causal, int forced, bool vec, sdpa
         p->keys_per_wave = fk;
         p->q_rows = 32;
     } else {
-        // Three compute waves plus the loader wave: a workgroup of four waves
-        // takes one wave slot per SIMD, so two of them share a CU (a
-        // five-wave workgroup takes two slots per SIMD and runs alone).
-        // Drop to two compute waves when that leaves fewer than two
-        // workgroups per CU. Four compute waves (a tuning option) fit in
-        // registers for D <= 64 (float32: D = 32); float32 takes at most
-        // two at D = 128 (its tiles are twice as large).
+        // Workgroups of four waves take one wave slot per SIMD, so two of
+        // them share a CU with the SIMDs evenly loaded (a five-wave group
+        // takes two slots per SIMD and runs alone). Preferred: four compute
+        // waves that share the tile loads themselves (16-byte layouts, when
+        // their staged probability tiles fit in LDS); else three compute
+        // waves plus a loader wave. Two compute waves when that leaves fewer
+        // than two workgroups per CU; float32 at D = 128 takes two (its
+        // tiles are twice as large). Causal calls keep the 96-row blocks:
+        // their work per block grows with the block index, and with 128-row
+        // blocks the grid no longer has enough blocks to balance the CUs
+        // (measured slower).
         const int64_t bh = sh.B * sh.Hq;
-        const int wide = (sh.D < 128 && (sh.dtype != SDPA_F32 || sh.D == 32)) ? 4 : 3;
-        p->waves = (bh * cdiv(sh.Sq, 96) >= 512) ? 3 : 2;
+        const bool nl_ok = vec && (sh.dtype == SDPA_F32    ? sdpa::twopass_nl_ok_f32((int)sh.D, sh.mask_kind)
+                                   : sh.dtype == SDPA_F16 ? sdpa::twopass_nl_ok_f16((int)sh.D, sh.mask_kind)
+                                                          : sdpa::twopass_nl_ok_bf16((int)sh.D, sh.mask_kind));
+        if (nl_ok && !causal && bh * cdiv(sh.Sq, 128) >= 512) p->waves = 4;
+        else p->waves = (bh * cdiv(sh.Sq, 96) >= 512) ? 3 : 2;
         if (const char* e = std::getenv("SDPA_MATH_TP_WAVES")) {
             const int wv = std::atoi(e);
-            if (wv >= 2 && wv <= wide) p->waves = wv;
+            if (wv == 2 || wv == 3 || (wv == 4 && nl_ok)) p->waves = wv;
         }
-        // float32 128-wide tiles only fit LDS with two compute waves; the
-        // element-wise variant is built with two only
-        if ((sh.dtype == SDPA_F32 && sh.D == 128) || !vec) p->waves = 2;
+        if ((sh.dtype == SDPA_F32 && sh.D == 128 && p->waves == 3) || !vec) p->waves = 2;
         p->keys_per_wave = 0;
         p->q_rows = 32 * p->waves;
     }

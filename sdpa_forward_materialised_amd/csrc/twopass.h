@@ -44,8 +44,11 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
 // vmcnt(0) only (expcnt and lgkmcnt left at their maxima)
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-template <typename T, int D, int NW, int MASK, bool VEC, int TN>
+// NL: no loader wave; the compute waves share the tile loads (and defer
+// each tile's probability stores by one tile, see the kernel).
+template <typename T, int D, int NW, int MASK, bool VEC, int TN, bool NL>
 struct TwoPassCfg {
+    static constexpr int NWAVES = NL ? NW : NW + 1;  // waves per workgroup
     static constexpr int SZ = (int)sizeof(T);
     static constexpr int BN = TN;                 // keys per tile: 32 or 64 (one or two MFMA blocks)
     static constexpr int NKB = TN / 32;
@@ -74,7 +77,7 @@ struct TwoPassCfg {
     static constexpr int KVM_BYTES = 2 * (2 * TILEB + MTILEB);
     static constexpr bool PSTAGE = VEC && KVM_BYTES + NW * PSTB <= 80 * 1024;
     static constexpr int LDS_BYTES = KVM_BYTES + (PSTAGE ? NW * PSTB : 0);
-    static_assert(LDS_BYTES <= 160 * 1024, "tile buffers exceed the 160 KB LDS of a compute unit");
+
     // LDS tile layouts, in 16-byte chunk positions: row-major, with the
     // chunks of each row permuted by an XOR (chunk c of row r at position
     // r * CPR + (c ^ f(r))). Each buffer-to-LDS instruction then fetches whole
@@ -101,11 +104,13 @@ struct TwoPassCfg {
 #define SDPA_TP_WPE(NW) ((NW) >= 4 ? 3 : 2)
 #endif
 
-template <typename T, int D, int NW, int MASK, bool VEC, int TN>
-__global__ __attribute__((amdgpu_flat_work_group_size((NW + 1) * 64, (NW + 1) * 64),
-                          amdgpu_waves_per_eu(SDPA_TP_WPE(NW))))
+template <typename T, int D, int NW, int MASK, bool VEC, int TN, bool NL>
+__global__ __attribute__((amdgpu_flat_work_group_size((NL ? NW : NW + 1) * 64, (NL ? NW : NW + 1) * 64),
+                          amdgpu_waves_per_eu(NL ? 2 : SDPA_TP_WPE(NW))))
 void sdpa_twopass_kernel(const FwdArgs a) {
-    using C = TwoPassCfg<T, D, NW, MASK, VEC, TN>;
+    using C = TwoPassCfg<T, D, NW, MASK, VEC, TN, NL>;
+    static_assert(!NL || C::PSTAGE, "without a loader wave the probability stores must be staged");
+    static_assert(C::LDS_BYTES <= 160 * 1024, "tile buffers exceed the 160 KB LDS of a compute unit");
     constexpr int BN = C::BN;
     constexpr int NKB = C::NKB;
     using TR = Tr<T>;
@@ -143,36 +148,39 @@ void sdpa_twopass_kernel(const FwdArgs a) {
     const uint32_t krow_bytes = (uint32_t)(a.k_s[2] * SZ);
     const uint32_t vrow_bytes = (uint32_t)(a.v_s[2] * SZ);
 
-    // ======================================================== loader wave
-    if (wave == NW) {
+    // ------------------------------------------------ tile loads (buffer to LDS)
         // instruction j of a tile fills chunk positions [64 j, 64 j + 64), i.e.
         // rows j * RPI .. +RPI: lane l fetches the chunk the layout puts at
         // position 64 j + l
-        auto dma_k = [&](uint8_t* dst, int t) {
+        // (j0, js): issue instructions j0, j0 + js, ... of the tile
+        auto dma_k = [&](uint8_t* dst, int t, int j0, int js) {
             const uint32_t so = (uint32_t)(t * BN) * krow_bytes;
 #pragma unroll
             for (int j = 0; j < C::CPR * BN / 64; ++j) {
+                if ((j - j0) % js != 0) continue;
                 const int row = j * C::RPI + lane / C::CPR;
                 const int chunk = (lane % C::CPR) ^ C::fk(row);
                 const uint32_t vo = pred(t * BN + row < a.Skv, row * krow_bytes + (uint32_t)(chunk * 16));
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(dst + j * 1024), 16, vo, so, 0, 0);
             }
         };
-        auto dma_v = [&](uint8_t* dst, int t) {
+        auto dma_v = [&](uint8_t* dst, int t, int j0, int js) {
             const uint32_t so = (uint32_t)(t * BN) * vrow_bytes;
 #pragma unroll
             for (int j = 0; j < C::CPR * BN / 64; ++j) {
+                if ((j - j0) % js != 0) continue;
                 const int row = j * C::RPI + lane / C::CPR;
                 const int chunk = (lane % C::CPR) ^ C::fv(row);
                 const uint32_t vo = pred(t * BN + row < a.Skv, row * vrow_bytes + (uint32_t)(chunk * 16));
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(dst + j * 1024), 16, vo, so, 0, 0);
             }
         };
-        auto dma_m = [&](int t, int b) {
+        auto dma_m = [&](int t, int b, int j0, int js) {
             if constexpr (C::MLDS) {
                 const int mrow = lane / C::MCPR, mch = lane % C::MCPR;
 #pragma unroll
                 for (int j = 0; j < C::MNI; ++j) {
+                    if ((j - j0) % js != 0) continue;
                     const int row = j * C::MRPI + mrow;  // query row q0 + row
                     // whole 16-byte chunks only: Skv is a multiple of the keys per chunk here
                     const uint32_t vo = pred(q0 + row < a.Sq && t * BN + mch * (16 / ME) < a.Skv,
@@ -182,34 +190,36 @@ void sdpa_twopass_kernel(const FwdArgs a) {
                 }
             }
         };
+    // ======================================================== loader wave
+    if (!NL && wave == NW) {
         // sweep 1: K (+ mask)
         if (ntiles > 0) {
-            dma_k(kbuf(0), 0);
-            dma_m(0, 0);
+            dma_k(kbuf(0), 0, 0, 1);
+            dma_m(0, 0, 0, 1);
             wait_vmem();
         }
         __syncthreads();
         for (int t = 0; t < ntiles; ++t) {
             if (t + 1 < ntiles) {
-                dma_k(kbuf((t + 1) & 1), t + 1);
-                dma_m(t + 1, (t + 1) & 1);
+                dma_k(kbuf((t + 1) & 1), t + 1, 0, 1);
+                dma_m(t + 1, (t + 1) & 1, 0, 1);
                 wait_vmem();
             }
             __syncthreads();
         }
         // sweep 2: K, V (+ mask)
         if (ntiles > 0) {
-            dma_k(kbuf(0), 0);
-            dma_v(vbuf(0), 0);
-            dma_m(0, 0);
+            dma_k(kbuf(0), 0, 0, 1);
+            dma_v(vbuf(0), 0, 0, 1);
+            dma_m(0, 0, 0, 1);
             wait_vmem();
         }
         __syncthreads();
         for (int t = 0; t < ntiles; ++t) {
             if (t + 1 < ntiles) {
-                dma_k(kbuf((t + 1) & 1), t + 1);
-                dma_v(vbuf((t + 1) & 1), t + 1);
-                dma_m(t + 1, (t + 1) & 1);
+                dma_k(kbuf((t + 1) & 1), t + 1, 0, 1);
+                dma_v(vbuf((t + 1) & 1), t + 1, 0, 1);
+                dma_m(t + 1, (t + 1) & 1, 0, 1);
                 wait_vmem();
             }
             __syncthreads();
@@ -371,18 +381,39 @@ void sdpa_twopass_kernel(const FwdArgs a) {
             }
         }
     };
-    __syncthreads();  // tile 0 staged
+    // Without a loader wave each compute wave issues its share of the next
+    // tile's loads before working on the current one, and waits for them
+    // (its only outstanding memory operations here) before the barrier.
+    auto load1 = [&](int t) {
+        if constexpr (NL) {
+            if (t < ntiles) {
+                dma_k(kbuf(t & 1), t, wave, NW);
+                dma_m(t, t & 1, wave, NW);
+            }
+        }
+    };
+    auto end_tile = [&]() {
+        if constexpr (NL) wait_vmem();
+        __syncthreads();  // tile t consumed, tile t+1 staged
+    };
+    load1(0);
+    end_tile();  // tile 0 staged
     {
         int t = 0;
         for (; t < t_fast; ++t) {
+            load1(t + 1);
             sweep1_tile(t, std::false_type{});
-            __syncthreads();  // tile t consumed, tile t+1 staged
+            end_tile();
         }
         for (; t < t_comp; ++t) {
+            load1(t + 1);
             sweep1_tile(t, std::true_type{});
-            __syncthreads();
+            end_tile();
         }
-        for (; t < ntiles; ++t) __syncthreads();
+        for (; t < ntiles; ++t) {
+            load1(t + 1);
+            end_tile();
+        }
     }
     {  // the two half-waves holding the same query row
         const float m_o = __shfl_xor(m_run, 32);
@@ -396,9 +427,6 @@ void sdpa_twopass_kernel(const FwdArgs a) {
     const bool dead = (m_run == -INFINITY);
     // dead rows: lse2 = +inf makes every probability exp2(-inf) = +0
     const float lse2 = dead ? INFINITY : m_run + __log2f(l_run);
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, dead ? -INFINITY : lse2 * LN2), lr,
-                                          pred(row_ok && hf == 0, (uint32_t)((int64_t)(row_ok ? qi : 0) * a.l_s[2] * 4)),
-                                          0, 0);
 
     // ---------------- sweep 2: P = exp2(t - lse2), store, O^T += V^T P^T
     f32x16 oacc[ND];
@@ -452,6 +480,41 @@ void sdpa_twopass_kernel(const FwdArgs a) {
     };
 
     uint8_t* pst = smem + C::KVM_BYTES + (C::PSTAGE ? wave * C::PSTB : 0);  // this wave's staged P tile
+    // whole-row stores of the staged P tile with first key k0
+    auto store_staged = [&](int k0, bool edge) {
+#pragma unroll
+        for (int i = 0; i < 32 * C::ZC / 64; ++i) {
+            const int row = i * (64 / C::ZC) + lane / C::ZC;
+            const int chunk = lane % C::ZC;
+            const u32x4 bits = *reinterpret_cast<const u32x4*>(pst + C::pos_p(row, chunk) * 16);
+            const int grow = qw + row, key = k0 + chunk * (16 / SZ);
+            const bool ok = grow < a.Sq && (!edge || key < a.Skv);
+            st128(pr, pred(ok, (uint32_t)((int64_t)(grow < a.Sq ? grow : 0) * a.p_s[2] * SZ) + (uint32_t)(key * SZ)),
+                  bits);
+        }
+    };
+    // a tile wholly above this wave's diagonal: P is zero
+    auto zero_tile = [&](int t) {
+        if (!live) {
+            // nothing to store
+        } else if constexpr (VEC) {
+            // whole-row 16-byte stores: instruction i covers rows 64 i / ZC ..
+            constexpr int ZC = BN * SZ / 16;  // 16-byte chunks per row of the tile
+#pragma unroll
+            for (int i = 0; i < 32 * ZC / 64; ++i) {
+                const int row = qw + i * (64 / ZC) + lane / ZC;
+                const int key = t * BN + (lane % ZC) * (16 / SZ);
+                st128(pr, pred(row < a.Sq && key < a.Skv,
+                               (uint32_t)((int64_t)(row < a.Sq ? row : 0) * a.p_s[2] * SZ) + (uint32_t)(key * SZ)),
+                      u32x4{0u, 0u, 0u, 0u});
+            }
+        } else {
+            const float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            const bool edge = (t + 1) * BN > a.Skv;
+#pragma unroll
+            for (int q = 0; q < 2 * NKB; ++q) store_run(t * BN, q >> 1, q & 1, edge, z);
+        }
+    };
     auto sweep2_tile = [&](int t, auto edge_c) {
         constexpr bool edge = decltype(edge_c)::value;
         const int k0 = t * BN;
@@ -518,54 +581,59 @@ void sdpa_twopass_kernel(const FwdArgs a) {
                 }
             }
         }
-        if constexpr (C::PSTAGE) {
-            // whole-row stores: instruction i covers rows i * 64 / ZC ..
-#pragma unroll
-            for (int i = 0; i < 32 * C::ZC / 64; ++i) {
-                const int row = i * (64 / C::ZC) + lane / C::ZC;
-                const int chunk = lane % C::ZC;
-                const u32x4 bits = *reinterpret_cast<const u32x4*>(pst + C::pos_p(row, chunk) * 16);
-                const int grow = qw + row, key = k0 + chunk * (16 / SZ);
-                const bool ok = grow < a.Sq && (!edge || key < a.Skv);
-                st128(pr, pred(ok, (uint32_t)((int64_t)(grow < a.Sq ? grow : 0) * a.p_s[2] * SZ) + (uint32_t)(key * SZ)),
-                      bits);
+        if constexpr (C::PSTAGE && !NL) store_staged(k0, edge);
+    };
+    // Without a loader wave a tile's probability stores are issued at the
+    // start of the next tile (from the staged copy), so the wait before the
+    // next barrier finds them a whole tile old rather than just issued.
+    auto load2 = [&](int t) {
+        if constexpr (NL) {
+            if (t < ntiles) {
+                dma_k(kbuf(t & 1), t, wave, NW);
+                dma_v(vbuf(t & 1), t, wave, NW);
+                dma_m(t, t & 1, wave, NW);
             }
         }
     };
-    __syncthreads();  // tile 0 staged
+    int pend_k0 = -1;          // key of the staged tile not yet stored (NL)
+    bool pend_edge = false;
+    auto flush = [&]() {
+        if constexpr (NL) {
+            if (pend_k0 >= 0) store_staged(pend_k0, pend_edge);
+            pend_k0 = -1;
+        }
+    };
+    load2(0);
+    end_tile();  // tile 0 staged
     {
         int t = 0;
         for (; t < t_fast; ++t) {
+            flush();
+            load2(t + 1);
             sweep2_tile(t, std::false_type{});
-            __syncthreads();  // tile t consumed, tile t+1 staged
+            pend_k0 = t * BN;
+            pend_edge = false;
+            end_tile();
         }
         for (; t < t_comp; ++t) {
+            flush();
+            load2(t + 1);
             sweep2_tile(t, std::true_type{});
-            __syncthreads();
+            pend_k0 = t * BN;
+            pend_edge = true;
+            end_tile();
         }
+        flush();
         // whole tiles above this wave's diagonal: P is zero, O unchanged
+        // (without a loader wave the zeros are written after the last tile)
+        const int t_zero = t;
         for (; t < ntiles; ++t) {
-            if (!live) {
-                // nothing to store
-            } else if constexpr (VEC) {
-                // whole-row 16-byte stores: instruction i covers rows 64 i / ZC ..
-                constexpr int ZC = BN * SZ / 16;  // 16-byte chunks per row of the tile
-#pragma unroll
-                for (int i = 0; i < 32 * ZC / 64; ++i) {
-                    const int row = qw + i * (64 / ZC) + lane / ZC;
-                    const int key = t * BN + (lane % ZC) * (16 / SZ);
-                    st128(pr, pred(row < a.Sq && key < a.Skv,
-                                   (uint32_t)((int64_t)(row < a.Sq ? row : 0) * a.p_s[2] * SZ) + (uint32_t)(key * SZ)),
-                          u32x4{0u, 0u, 0u, 0u});
-                }
-            } else {
-                const float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-                const bool edge = (t + 1) * BN > a.Skv;
-#pragma unroll
-                for (int q = 0; q < 2 * NKB; ++q) store_run(t * BN, q >> 1, q & 1, edge, z);
-            }
-            __syncthreads();
+            load2(t + 1);
+            if constexpr (!NL) zero_tile(t);
+            end_tile();
         }
+        if constexpr (NL)
+            for (int tz = t_zero; tz < ntiles; ++tz) zero_tile(tz);
     }
 
     // ---------------- O: lane (n, h) holds O[qi][32d + 8h ..+8) and [32d + 16 + 8h ..+8)
@@ -583,41 +651,74 @@ void sdpa_twopass_kernel(const FwdArgs a) {
 
     // ---------------- causal: keys past this workgroup's last row are zero
     zero_rows<T, VEC>(pr, a.p_s[2], qw, a.Sq, ntiles * BN, a.Skv, lane);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, dead ? -INFINITY : lse2 * LN2), lr,
+                                          pred(row_ok && hf == 0, (uint32_t)((int64_t)(row_ok ? qi : 0) * a.l_s[2] * 4)),
+                                          0, 0);
 }
 
 #ifndef SDPA_TP_TN
 #define SDPA_TP_TN 64
 #endif
 
-template <typename T, int D, int NW, bool VEC>
+template <typename T, int D, int NW, bool VEC, bool NL>
 static int launch_twopass_mask(int mask_kind, const FwdArgs& a, hipStream_t s) {
     constexpr int TN = SDPA_TP_TN;
-    dim3 grid(a.n_blocks), block((NW + 1) * 64);
+    dim3 grid(a.n_blocks), block((NL ? NW : NW + 1) * 64);
     switch (mask_kind) {
-        case MASK_NONE: hipLaunchKernelGGL((sdpa_twopass_kernel<T, D, NW, MASK_NONE, VEC, TN>), grid, block, 0, s, a); break;
-        case MASK_BOOL: hipLaunchKernelGGL((sdpa_twopass_kernel<T, D, NW, MASK_BOOL, VEC, TN>), grid, block, 0, s, a); break;
-        case MASK_ADD: hipLaunchKernelGGL((sdpa_twopass_kernel<T, D, NW, MASK_ADD, VEC, TN>), grid, block, 0, s, a); break;
+#define SDPA_TP_CASE(MK)                                                                              \
+    case MK:                                                                                          \
+        if constexpr (!NL || TwoPassCfg<T, D, NW, MK, VEC, TN, true>::PSTAGE) {                       \
+            hipLaunchKernelGGL((sdpa_twopass_kernel<T, D, NW, MK, VEC, TN, NL>), grid, block, 0, s, a); \
+            break;                                                                                    \
+        } else {                                                                                      \
+            return (int)hipErrorInvalidValue;                                                         \
+        }
+        SDPA_TP_CASE(MASK_NONE)
+        SDPA_TP_CASE(MASK_BOOL)
+        SDPA_TP_CASE(MASK_ADD)
+#undef SDPA_TP_CASE
         default: return (int)hipErrorInvalidValue;
     }
     return (int)hipGetLastError();
 }
 
+// Whether four compute waves without a loader wave can run for this shape:
+// the staged probability tiles of four waves must fit next to the K/V (and
+// mask) tiles within the LDS of half a CU.
+template <typename T>
+static bool twopass_nl_ok_t(int D, int mask_kind) {
+    constexpr int TN = SDPA_TP_TN;
+#define SDPA_NL(DD, MK) TwoPassCfg<T, DD, 4, MK, true, TN, true>::PSTAGE
+#define SDPA_NL_D(DD)                                                                 \
+    case DD:                                                                          \
+        return mask_kind == MASK_NONE ? SDPA_NL(DD, MASK_NONE)                        \
+             : mask_kind == MASK_BOOL ? SDPA_NL(DD, MASK_BOOL) : SDPA_NL(DD, MASK_ADD);
+    switch (D) {
+        SDPA_NL_D(32)
+        SDPA_NL_D(64)
+        SDPA_NL_D(128)
+        default: return false;
+    }
+#undef SDPA_NL_D
+#undef SDPA_NL
+}
+
+// waves: 4 = four compute waves without a loader wave (16-byte layouts only,
+// when twopass_nl_ok); 3 or 2 = that many compute waves plus a loader wave.
 // Element-wise layouts only need correctness: they get one two-wave shape.
-// float32 takes at most three compute waves at D = 64 (register budget) and
-// two at D = 128 (its tiles are twice as large: two waves keep them in LDS).
+// float32 takes at most two compute waves at D = 128 (its tiles are twice
+// as large: two waves keep them within LDS).
 template <typename T>
 static int launch_twopass_t(int D, int mask_kind, int waves, bool vec, const FwdArgs& a, void* stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-#define SDPA_TP_DIM(DD)                                                                     \
-    case DD:                                                                                \
-        if (!vec) return launch_twopass_mask<T, DD, 2, false>(mask_kind, a, s);             \
-        if constexpr (DD < 128 && (sizeof(T) == 2 || DD == 32)) {                            \
-            if (waves == 4) return launch_twopass_mask<T, DD, 4, true>(mask_kind, a, s);    \
-        }                                                                                   \
-        if constexpr (sizeof(T) == 2 || DD < 128) {                                          \
-            if (waves == 3) return launch_twopass_mask<T, DD, 3, true>(mask_kind, a, s);    \
-        }                                                                                   \
-        if (waves == 2 || waves == 4) return launch_twopass_mask<T, DD, 2, true>(mask_kind, a, s); \
+#define SDPA_TP_DIM(DD)                                                                      \
+    case DD:                                                                                 \
+        if (!vec) return launch_twopass_mask<T, DD, 2, false, false>(mask_kind, a, s);       \
+        if (waves == 4) return launch_twopass_mask<T, DD, 4, true, true>(mask_kind, a, s);   \
+        if constexpr (sizeof(T) == 2 || DD < 128) {                                           \
+            if (waves == 3) return launch_twopass_mask<T, DD, 3, true, false>(mask_kind, a, s); \
+        }                                                                                    \
+        if (waves == 2) return launch_twopass_mask<T, DD, 2, true, false>(mask_kind, a, s);  \
         return (int)hipErrorInvalidValue;
     switch (D) {
         SDPA_TP_DIM(32)

@@ -7,4 +7,6 @@ int launch_twopass_bf16(int D, int mask_kind, int waves, bool vec, const FwdArgs
     return launch_twopass_t<__bf16>(D, mask_kind, waves, vec, a, stream);
 }
 
+bool twopass_nl_ok_bf16(int D, int mask_kind) { return twopass_nl_ok_t<__bf16>(D, mask_kind); }
+
 }  // namespace sdpa

@@ -7,4 +7,6 @@ int launch_twopass_f32(int D, int mask_kind, int waves, bool vec, const FwdArgs&
     return launch_twopass_t<float>(D, mask_kind, waves, vec, a, stream);
 }
 
+bool twopass_nl_ok_f32(int D, int mask_kind) { return twopass_nl_ok_t<float>(D, mask_kind); }
+
 }  // namespace sdpa
