@@ -241,8 +241,11 @@ def cpu_baseline(w, budget_s=12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # The GPU raises its clock only after some tens of ms of sustained work:
+    # the default warm-up runs a few hundred steps (~50 ms) so that the timed
+    # steps see the steady state.
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--path", default="auto", choices=["auto", "fused", "twopass"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp16", action="store_true", help="skip the same-shape fp16 line")
@@ -287,7 +290,7 @@ def main():
         log(f"[bench] fp16: {r16['ms']:.4f} ms/step")
 
     if not args.no_configs:
-        extra["configs"] = all_configs(min(args.steps, 20), min(args.warmup, 3), args.path)
+        extra["configs"] = all_configs(min(args.steps, 50), min(args.warmup, 100), args.path)
 
     cpu = None
     if not args.no_cpu_baseline:
