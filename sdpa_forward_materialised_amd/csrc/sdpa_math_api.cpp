@@ -287,17 +287,18 @@ sdpa_status_t make_plan(const Shape& sh, bool causal, int forced, bool vec, sdpa
         // waves that share the tile loads themselves (16-byte layouts, when
         // their staged probability tiles fit in LDS); else three compute
         // waves plus a loader wave. Two compute waves when that leaves fewer
-        // than two workgroups per CU; float32 at D = 128 takes two (its
-        // tiles are twice as large). Causal calls keep the 96-row blocks:
-        // their work per block grows with the block index, and with 128-row
-        // blocks the grid no longer has enough blocks to balance the CUs
-        // (measured slower).
+        // than one workgroup per CU (a 1024-row causal prefill at D = 64,
+        // 352 blocks, runs 7 % faster on three: measured); float32 at D = 128
+        // takes two (its tiles are twice as large). Causal calls keep the
+        // 96-row blocks: their work per block grows with the block index,
+        // and with 128-row blocks the grid no longer has enough blocks to
+        // balance the CUs (measured slower).
         const int64_t bh = sh.B * sh.Hq;
         const bool nl_ok = vec && (sh.dtype == SDPA_F32    ? sdpa::twopass_nl_ok_f32((int)sh.D, sh.mask_kind)
                                    : sh.dtype == SDPA_F16 ? sdpa::twopass_nl_ok_f16((int)sh.D, sh.mask_kind)
                                                           : sdpa::twopass_nl_ok_bf16((int)sh.D, sh.mask_kind));
         if (nl_ok && !causal && bh * cdiv(sh.Sq, 128) >= 512) p->waves = 4;
-        else p->waves = (bh * cdiv(sh.Sq, 96) >= 512) ? 3 : 2;
+        else p->waves = (bh * cdiv(sh.Sq, 96) >= 256) ? 3 : 2;
         if (const char* e = std::getenv("SDPA_MATH_TP_WAVES")) {
             const int wv = std::atoi(e);
             if (wv == 2 || wv == 3 || (wv == 4 && nl_ok)) p->waves = wv;

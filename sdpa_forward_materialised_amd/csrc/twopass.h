@@ -396,10 +396,73 @@ void sdpa_twopass_kernel(const FwdArgs a) {
         if constexpr (NL) wait_vmem();
         __syncthreads();  // tile t consumed, tile t+1 staged
     };
+    // Fast tiles without a mask, software-pipelined: the MFMA chain of the
+    // next score block is interleaved with the max / exp2 / sum fold of the
+    // previous one, so a single wave keeps the matrix unit and the vector
+    // unit busy together. The fold of a tile's last block runs after the
+    // tile barrier (its scores are in registers). Same arithmetic, in the
+    // same order, as sweep1_tile's fast branch.
+    auto fold_fast = [&](const f32x16& acc) {
+        float mx = acc[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, acc[r]);
+        const float mn = fmaxf(m_run, mx * a.scale_log2);
+        float sum = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sum += fast_exp2(__builtin_fmaf(acc[r], a.scale_log2, -mn));
+        l_run = l_run * fast_exp2(m_run - mn) + sum;
+        m_run = mn;
+    };
+    // S^T of block kb of tile buffer kt, with the fold of `prev` interleaved
+    // by hand (scheduling fences keep the order): the DS reads, the fold's
+    // max while they land, then per MFMA step the exp2 / sum of a few
+    // scores. The sum runs over r in order, as in fold_fast.
+    auto qk_fold = [&](const uint8_t* kt, int kb, const f32x16& prev) -> f32x16 {
+        f32x16 acc = {};
+        vec ka[NKS];
+#pragma unroll
+        for (int c = 0; c < NKS; ++c) ka[c] = k_operand(kt, kb, c);
+        __builtin_amdgcn_sched_barrier(0);
+        float mx = prev[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, prev[r]);
+        const float mn = fmaxf(m_run, mx * a.scale_log2);
+        const float resc = fast_exp2(m_run - mn);
+        float sum = 0.0f;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = 0; c < NKS; ++c) {
+            acc = TR::mfma(ka[c], qf[c], acc);
+#pragma unroll
+            for (int e = c * 16 / NKS; e < (c + 1) * 16 / NKS; ++e)
+                sum += fast_exp2(__builtin_fmaf(prev[e], a.scale_log2, -mn));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        l_run = l_run * resc + sum;
+        m_run = mn;
+        return acc;
+    };
+    const bool pipe1 = MASK == MASK_NONE && a.scale_log2 > 0.0f;
+
     load1(0);
     end_tile();  // tile 0 staged
     {
         int t = 0;
+        if (pipe1 && t_fast > 0) {
+            load1(1);
+            f32x16 pend = qk_block(kbuf(0), 0);
+#pragma unroll
+            for (int kb = 1; kb < NKB; ++kb) pend = qk_fold(kbuf(0), kb, pend);
+            end_tile();
+            for (t = 1; t < t_fast; ++t) {
+                load1(t + 1);
+                const uint8_t* kt = kbuf(t & 1);
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) pend = qk_fold(kt, kb, pend);
+                end_tile();
+            }
+            fold_fast(pend);
+        }
         for (; t < t_fast; ++t) {
             load1(t + 1);
             sweep1_tile(t, std::false_type{});
