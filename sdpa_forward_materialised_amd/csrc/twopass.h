@@ -552,7 +552,7 @@ void sdpa_twopass_kernel(const FwdArgs a) {
             const u32x4 bits = *reinterpret_cast<const u32x4*>(pst + C::pos_p(row, chunk) * 16);
             const int grow = qw + row, key = k0 + chunk * (16 / SZ);
             const bool ok = grow < a.Sq && (!edge || key < a.Skv);
-            st128(pr, pred(ok, (uint32_t)((int64_t)(grow < a.Sq ? grow : 0) * a.p_s[2] * SZ) + (uint32_t)(key * SZ)),
+            st128_nt(pr, pred(ok, (uint32_t)((int64_t)(grow < a.Sq ? grow : 0) * a.p_s[2] * SZ) + (uint32_t)(key * SZ)),
                   bits);
         }
     };
@@ -567,7 +567,7 @@ void sdpa_twopass_kernel(const FwdArgs a) {
             for (int i = 0; i < 32 * ZC / 64; ++i) {
                 const int row = qw + i * (64 / ZC) + lane / ZC;
                 const int key = t * BN + (lane % ZC) * (16 / SZ);
-                st128(pr, pred(row < a.Sq && key < a.Skv,
+                st128_nt(pr, pred(row < a.Sq && key < a.Skv,
                                (uint32_t)((int64_t)(row < a.Sq ? row : 0) * a.p_s[2] * SZ) + (uint32_t)(key * SZ)),
                       u32x4{0u, 0u, 0u, 0u});
             }
