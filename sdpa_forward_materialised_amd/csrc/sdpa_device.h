@@ -133,10 +133,14 @@ struct Work {
 // Workgroup ids are handed to the 8 XCDs in turn (id % 8), each XCD with its
 // own L2. Remap so that an XCD receives a contiguous range of logical ids:
 // the query blocks of a (batch, head), and the heads that share a KV head,
-// then read K and V through the same L2. For causal calls the XCD's first
-// half of dispatches takes the heavy (late) query blocks in decreasing
-// order and its second half the light ones in increasing order, so the two
-// workgroups that share a compute unit carry about the same total work.
+// then read K and V through the same L2. Orders (a.sched):
+//  0  head-major; causal blocks of a head heaviest (latest) first;
+//  1  causal: the XCD's first half of dispatches takes the heavy blocks in
+//     decreasing order, its second half the light ones increasing;
+//  2  causal: heaviest first over the whole grid (every head at once);
+//  3  causal: each XCD takes its heads two at a time, the pair's blocks
+//     interleaved heaviest first: the balance of heaviest-first order with
+//     the K/V working set of two heads per L2 (measured fastest).
 __device__ __forceinline__ Work decode_block(int L, const FwdArgs& a) {
     const int nb = a.n_blocks;
     const int nfull = nb & ~7;
@@ -154,6 +158,14 @@ __device__ __forceinline__ Work decode_block(int L, const FwdArgs& a) {
             w.b = head / a.Hq;
             w.hq = head - w.b * a.Hq;
             w.qblk = r;
+            return w;
+        }
+        if (a.sched == 3 && per % (2 * nq) == 0) {
+            const int g = i / (2 * nq), j = i - g * 2 * nq;
+            const int head = x * (per / nq) + 2 * g + (j & 1);
+            w.b = head / a.Hq;
+            w.hq = head - w.b * a.Hq;
+            w.qblk = nq - 1 - (j >> 1);
             return w;
         }
         L = x * per + i;

@@ -31,7 +31,7 @@ struct FwdArgs {
     int n_qblk;      // query blocks per (batch, head)
     int n_blocks;    // workgroups in the grid
     int keys_per_wave;  // fused path: key range of one wave
-    int sched;       // workgroup order: 0 head-major, 1 heavy/light interleaved per XCD, 2 heaviest first (causal)
+    int sched;       // workgroup order (causal: 1, 2, 3), see decode_block
     // Byte extent of one (batch, head) slice of each tensor (< 2^31); the
     // kernels address every tensor through a buffer descriptor of this size.
     uint32_t q_ext, k_ext, v_ext, o_ext, p_ext, m_ext, l_ext;

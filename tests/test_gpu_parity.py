@@ -109,6 +109,22 @@ def test_compute_wave_counts(label, spec, waves, monkeypatch):
     _check(c, "twopass", label=f"{label} waves={waves}")
 
 
+def test_dispatch_orders_identical(monkeypatch):
+    """Every causal workgroup order (a permutation of the query blocks) gives the same bits, and
+    the default one matches the oracle. 16 heads: whole head pairs per XCD, so order 3 applies."""
+    c = W.make_case(124, "bf16", 2, 8, 8, 384, 384, 64, causal=True)
+    outs = {}
+    for sched in ("0", "1", "2", "3"):
+        monkeypatch.setenv("SDPA_MATH_SCHED", sched)
+        outs[sched] = _run(c, "twopass", label=f"order {sched}")
+    monkeypatch.delenv("SDPA_MATH_SCHED")
+    ref = run_oracle(c["q"], c["k"], c["v"], None, True, None, False)
+    compare(*outs["3"], ref, torch.bfloat16, "order 3")
+    for sched in ("0", "1", "2"):
+        for x, y in zip(outs["3"], outs[sched]):
+            assert torch.equal(x, y), sched
+
+
 @pytest.mark.parametrize("path", PATHS)
 def test_fully_masked_rows(path):
     c = W.make_case(120, "f16", 2, 4, 2, 96, 160, 64, mask="bool", mask_shape=(2, 4, 96, 160), p=0.2)
