@@ -77,6 +77,8 @@ SMALL = [
     ("bf16-d32-single", dict(seed=112, dtype="bf16", B=1, Hq=1, Hkv=1, Sq=1, Skv=1, D=32)),
     ("f16-d128-decode-row", dict(seed=113, dtype="f16", B=3, Hq=8, Hkv=8, Sq=1, Skv=1025, D=128)),
     ("f16-d64-odd-skv", dict(seed=114, dtype="f16", B=1, Hq=2, Hkv=2, Sq=50, Skv=37, D=64, mask="bool")),
+    ("bf16-d64-add-rows-shared", dict(seed=115, dtype="bf16", B=2, Hq=4, Hkv=2, Sq=150, Skv=264, D=64, mask="add",
+                                      mask_shape=(2, 1, 1, 264), p=0.2)),
 ]
 
 
@@ -107,6 +109,25 @@ def test_compute_wave_counts(label, spec, waves, monkeypatch):
     monkeypatch.setenv("SDPA_MATH_TP_WAVES", str(waves))
     c = W.make_case(**spec)
     _check(c, "twopass", label=f"{label} waves={waves}")
+
+
+# A mask whose rows are all equal, passed as a full-size expanded view (sizes
+# [B, Hq, Sq, Skv], row stride 0): every query row's mask tile reads the same
+# bytes; every compute-wave count.
+@pytest.mark.parametrize("waves", [2, 3, 4])
+@pytest.mark.parametrize("kind,D", [("bool", 128), ("add", 64), ("neginf", 32)])
+def test_shared_mask_rows_expanded(kind, D, waves, monkeypatch):
+    monkeypatch.setenv("SDPA_MATH_TP_WAVES", str(waves))
+    c = W.make_case(125, "f16", 2, 4, 4, 200, 136, D, mask=kind, mask_shape=(2, 4, 1, 136), p=0.25)
+    S = _lib()
+    gm = c["mask"].to(DEV).expand(2, 4, 200, 136)  # expanded on the device: row stride 0
+    assert gm.stride(2) == 0
+    out = poisoned_outputs(2, 4, 200, 136, D, torch.float16, DEV)
+    print(f"[case] shared rows {kind} D={D} waves={waves}", flush=True)
+    O, P, L = S.fwd(c["q"].to(DEV), c["k"].to(DEV), c["v"].to(DEV), gm, False, None, False, path="twopass", out=out)
+    torch.cuda.synchronize()
+    ref = run_oracle(c["q"], c["k"], c["v"], c["mask"], False, None, False)
+    compare(O, P, L, ref, torch.float16, f"shared rows {kind} D={D} waves={waves}")
 
 
 def test_dispatch_orders_identical(monkeypatch):
