@@ -29,6 +29,10 @@
 
 #include "sdpa_device.h"
 
+// lambdas of the kernels below are always inlined: one that became a call
+// would put the arrays it captures by reference (accumulators) in scratch
+#define SDPA_INLINE __attribute__((always_inline))
+
 namespace sdpa {
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -153,7 +157,7 @@ void sdpa_twopass_kernel(const FwdArgs a) {
         // rows j * RPI .. +RPI: lane l fetches the chunk the layout puts at
         // position 64 j + l
         // (j0, js): issue instructions j0, j0 + js, ... of the tile
-        auto dma_k = [&](uint8_t* dst, int t, int j0, int js) {
+        auto dma_k = [&](uint8_t* dst, int t, int j0, int js) SDPA_INLINE {
             const uint32_t so = (uint32_t)(t * BN) * krow_bytes;
 #pragma unroll
             for (int j = 0; j < C::CPR * BN / 64; ++j) {
@@ -164,7 +168,7 @@ void sdpa_twopass_kernel(const FwdArgs a) {
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(dst + j * 1024), 16, vo, so, 0, 0);
             }
         };
-        auto dma_v = [&](uint8_t* dst, int t, int j0, int js) {
+        auto dma_v = [&](uint8_t* dst, int t, int j0, int js) SDPA_INLINE {
             const uint32_t so = (uint32_t)(t * BN) * vrow_bytes;
 #pragma unroll
             for (int j = 0; j < C::CPR * BN / 64; ++j) {
@@ -175,7 +179,7 @@ void sdpa_twopass_kernel(const FwdArgs a) {
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(dst + j * 1024), 16, vo, so, 0, 0);
             }
         };
-        auto dma_m = [&](int t, int b, int j0, int js) {
+        auto dma_m = [&](int t, int b, int j0, int js) SDPA_INLINE {
             if constexpr (C::MLDS) {
                 const int mrow = lane / C::MCPR, mch = lane % C::MCPR;
 #pragma unroll
@@ -254,7 +258,7 @@ void sdpa_twopass_kernel(const FwdArgs a) {
     // K operand (A) of S^T block kb, k-step c: lane (m, h) reads row 32kb +
     // swap23(m), elements c*KSTEP + h*KH .. +KH
     const int kr0 = swap23(n);
-    auto k_operand = [&](const uint8_t* kt, int kb, int c) -> vec {
+    auto k_operand = [&](const uint8_t* kt, int kb, int c) SDPA_INLINE -> vec {
         const int row = 32 * kb + kr0;
         const int elem = c * KSTEP + hf * KH;
         const uint8_t* p = kt + C::pos_k(row, elem * SZ / 16) * 16 + ((elem * SZ) & 15);
@@ -264,7 +268,7 @@ void sdpa_twopass_kernel(const FwdArgs a) {
     // S^T of 32-key block kb (one MFMA chain over the head dim)
     // All K operand reads of the block are issued before its MFMA chain, so
     // the chain does not wait on LDS latency between steps.
-    auto qk_block = [&](const uint8_t* kt, int kb) -> f32x16 {
+    auto qk_block = [&](const uint8_t* kt, int kb) SDPA_INLINE -> f32x16 {
         f32x16 acc = {};
         vec ka[NKS];
 #pragma unroll
@@ -277,7 +281,7 @@ void sdpa_twopass_kernel(const FwdArgs a) {
     };
 
     // mask terms of register r of block kb: keep flag (bool) or base-2 additive term
-    auto mask_terms = [&](const uint8_t* mt, int k0, int kb, float* mv) {
+    auto mask_terms = [&](const uint8_t* mt, int k0, int kb, float* mv) SDPA_INLINE {
         if constexpr (MASK == MASK_NONE) {
             return;
         } else if constexpr (C::MLDS) {
@@ -312,7 +316,7 @@ void sdpa_twopass_kernel(const FwdArgs a) {
 
     // Base-2 scaled, masked scores t[r] of one block. `edge`: the block may
     // hold keys past Skv or past this wave's causal diagonal.
-    auto scores = [&](const f32x16& acc, const float* mv, int kb, int k0, bool edge, float* t) {
+    auto scores = [&](const f32x16& acc, const float* mv, int kb, int k0, bool edge, float* t) SDPA_INLINE {
         const int jb = k0 + 32 * kb;
         // register r holds key jb + kk(hf, r) = jb + 8 hf + kk(0, r); it is
         // dropped when kk(0, r) > lim (a compile-time constant per register)
@@ -345,7 +349,7 @@ void sdpa_twopass_kernel(const FwdArgs a) {
 
     // ---------------- sweep 1: row maximum and sum (base 2)
     float m_run = -INFINITY, l_run = 0.0f;
-    auto sweep1_tile = [&](int t, auto edge_c) {
+    auto sweep1_tile = [&](int t, auto edge_c) SDPA_INLINE {
         constexpr bool edge = decltype(edge_c)::value;
         const int k0 = t * BN;
         const int buf = t & 1;
@@ -384,7 +388,7 @@ void sdpa_twopass_kernel(const FwdArgs a) {
     // Without a loader wave each compute wave issues its share of the next
     // tile's loads before working on the current one, and waits for them
     // (its only outstanding memory operations here) before the barrier.
-    auto load1 = [&](int t) {
+    auto load1 = [&](int t) SDPA_INLINE {
         if constexpr (NL) {
             if (t < ntiles) {
                 dma_k(kbuf(t & 1), t, wave, NW);
@@ -392,7 +396,7 @@ void sdpa_twopass_kernel(const FwdArgs a) {
             }
         }
     };
-    auto end_tile = [&]() {
+    auto end_tile = [&]() SDPA_INLINE {
         if constexpr (NL) wait_vmem();
         __syncthreads();  // tile t consumed, tile t+1 staged
     };
@@ -402,7 +406,7 @@ void sdpa_twopass_kernel(const FwdArgs a) {
     // unit busy together. The fold of a tile's last block runs after the
     // tile barrier (its scores are in registers). Same arithmetic, in the
     // same order, as sweep1_tile's fast branch.
-    auto fold_fast = [&](const f32x16& acc) {
+    auto fold_fast = [&](const f32x16& acc) SDPA_INLINE {
         float mx = acc[0];
 #pragma unroll
         for (int r = 1; r < 16; ++r) mx = fmaxf(mx, acc[r]);
@@ -417,7 +421,7 @@ void sdpa_twopass_kernel(const FwdArgs a) {
     // by hand (scheduling fences keep the order): the DS reads, the fold's
     // max while they land, then per MFMA step the exp2 / sum of a few
     // scores. The sum runs over r in order, as in fold_fast.
-    auto qk_fold = [&](const uint8_t* kt, int kb, const f32x16& prev) -> f32x16 {
+    auto qk_fold = [&](const uint8_t* kt, int kb, const f32x16& prev) SDPA_INLINE -> f32x16 {
         f32x16 acc = {};
         vec ka[NKS];
 #pragma unroll
@@ -454,13 +458,20 @@ void sdpa_twopass_kernel(const FwdArgs a) {
 #pragma unroll
             for (int kb = 1; kb < NKB; ++kb) pend = qk_fold(kbuf(0), kb, pend);
             end_tile();
-            for (t = 1; t < t_fast; ++t) {
-                load1(t + 1);
-                const uint8_t* kt = kbuf(t & 1);
+            // tiles in pairs, so that each one's buffer is a compile-time
+            // constant (its offset folds into the LDS instructions)
+            auto fast1 = [&](int tt, auto par) SDPA_INLINE {
+                load1(tt + 1);
+                const uint8_t* kt = kbuf(decltype(par)::value);
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) pend = qk_fold(kt, kb, pend);
                 end_tile();
+            };
+            for (t = 1; t + 1 < t_fast; t += 2) {
+                fast1(t, std::integral_constant<int, 1>{});
+                fast1(t + 1, std::integral_constant<int, 0>{});
             }
+            if (t < t_fast) fast1(t++, std::integral_constant<int, 1>{});
             fold_fast(pend);
         }
         for (; t < t_fast; ++t) {
@@ -505,7 +516,7 @@ void sdpa_twopass_kernel(const FwdArgs a) {
     const int tr_sig = ((trs & 1) << 1) | ((trs >> 1) & 1);
     const int tr_row = 8 * (trg >> 1) + (trs >> 2);
     const int tr_col = 16 * (trg & 1) + 4 * tr_sig;
-    auto v_operand = [&](const uint8_t* vt, int key0, int d) -> vec {
+    auto v_operand = [&](const uint8_t* vt, int key0, int d) SDPA_INLINE -> vec {
         if constexpr (sizeof(T) == 2) {
             // rows key0 + tr_row and key0 + tr_row + 4, columns 32d + tr_col .. +3
             u32x2 half[2];
@@ -522,7 +533,7 @@ void sdpa_twopass_kernel(const FwdArgs a) {
     };
 
     // store of 8 probabilities (one run) of block kb, run c
-    auto store_run = [&](int k0, int kb, int c, bool edge, const float* x) {
+    auto store_run = [&](int k0, int kb, int c, bool edge, const float* x) SDPA_INLINE {
         const int jrel = 32 * kb + 16 * c + 8 * hf;
         if constexpr (VEC) {
             uint32_t vo = prow + (uint32_t)(jrel * SZ);
@@ -544,7 +555,7 @@ void sdpa_twopass_kernel(const FwdArgs a) {
 
     uint8_t* pst = smem + C::KVM_BYTES + (C::PSTAGE ? wave * C::PSTB : 0);  // this wave's staged P tile
     // whole-row stores of the staged P tile with first key k0
-    auto store_staged = [&](int k0, bool edge) {
+    auto store_staged = [&](int k0, bool edge) SDPA_INLINE {
 #pragma unroll
         for (int i = 0; i < 32 * C::ZC / 64; ++i) {
             const int row = i * (64 / C::ZC) + lane / C::ZC;
@@ -557,7 +568,7 @@ void sdpa_twopass_kernel(const FwdArgs a) {
         }
     };
     // a tile wholly above this wave's diagonal: P is zero
-    auto zero_tile = [&](int t) {
+    auto zero_tile = [&](int t) SDPA_INLINE {
         if (!live) {
             // nothing to store
         } else if constexpr (VEC) {
@@ -578,10 +589,10 @@ void sdpa_twopass_kernel(const FwdArgs a) {
             for (int q = 0; q < 2 * NKB; ++q) store_run(t * BN, q >> 1, q & 1, edge, z);
         }
     };
-    auto sweep2_tile = [&](int t, auto edge_c) {
+    // buf: t & 1, passed as a constant by the paired fast loop
+    auto sweep2_tile = [&](int t, auto edge_c, int buf) SDPA_INLINE {
         constexpr bool edge = decltype(edge_c)::value;
         const int k0 = t * BN;
-        const int buf = t & 1;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
             const f32x16 acc = qk_block(kbuf(buf), kb);
@@ -649,7 +660,7 @@ void sdpa_twopass_kernel(const FwdArgs a) {
     // Without a loader wave a tile's probability stores are issued at the
     // start of the next tile (from the staged copy), so the wait before the
     // next barrier finds them a whole tile old rather than just issued.
-    auto load2 = [&](int t) {
+    auto load2 = [&](int t) SDPA_INLINE {
         if constexpr (NL) {
             if (t < ntiles) {
                 dma_k(kbuf(t & 1), t, wave, NW);
@@ -660,7 +671,7 @@ void sdpa_twopass_kernel(const FwdArgs a) {
     };
     int pend_k0 = -1;          // key of the staged tile not yet stored (NL)
     bool pend_edge = false;
-    auto flush = [&]() {
+    auto flush = [&]() SDPA_INLINE {
         if constexpr (NL) {
             if (pend_k0 >= 0) store_staged(pend_k0, pend_edge);
             pend_k0 = -1;
@@ -670,18 +681,23 @@ void sdpa_twopass_kernel(const FwdArgs a) {
     end_tile();  // tile 0 staged
     {
         int t = 0;
-        for (; t < t_fast; ++t) {
+        auto fast2 = [&](int tt, int buf) SDPA_INLINE {
             flush();
-            load2(t + 1);
-            sweep2_tile(t, std::false_type{});
-            pend_k0 = t * BN;
+            load2(tt + 1);
+            sweep2_tile(tt, std::false_type{}, buf);
+            pend_k0 = tt * BN;
             pend_edge = false;
             end_tile();
+        };
+        for (; t + 1 < t_fast; t += 2) {  // in pairs: constant buffers, as in sweep 1
+            fast2(t, 0);
+            fast2(t + 1, 1);
         }
+        if (t < t_fast) fast2(t++, 0);
         for (; t < t_comp; ++t) {
             flush();
             load2(t + 1);
-            sweep2_tile(t, std::true_type{});
+            sweep2_tile(t, std::true_type{}, t & 1);
             pend_k0 = t * BN;
             pend_edge = true;
             end_tile();
