@@ -657,6 +657,72 @@ void sdpa_twopass_kernel(const FwdArgs a) {
         }
         if constexpr (C::PSTAGE && !NL) store_staged(k0, edge);
     };
+    // Fast tile (no mask, no edge, 16-bit, two 32-key blocks, staged P) with
+    // the two blocks software-pipelined by hand (scheduling fences keep the
+    // order): block 1's S^T chain runs under block 0's exp2, block 0's
+    // O^T += V^T P^T chain under block 1's exp2, and the operand reads go out
+    // under the MFMAs. Same arithmetic, and the same accumulation order into
+    // O^T, as sweep2_tile.
+    auto sweep2_pipe = [&](int t, int buf) SDPA_INLINE {
+      if constexpr (sizeof(T) == 2 && NKB == 2) {
+        const uint8_t* kt = kbuf(buf);
+        const uint8_t* vt = vbuf(buf);
+        vec ka[NKS], kn[NKS];
+        vec va0[2][ND], va1[2][ND];
+#pragma unroll
+        for (int c = 0; c < NKS; ++c) ka[c] = k_operand(kt, 0, c);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16 acc0 = {};
+#pragma unroll
+        for (int c = 0; c < NKS; ++c) {  // S^T of block 0; reads of block 1's K and block 0's V
+            acc0 = TR::mfma(ka[c], qf[c], acc0);
+            kn[c] = k_operand(kt, 1, c);
+            va0[c / ND][c % ND] = v_operand(vt, 16 * (c / ND), c % ND);  // 2 ND = NKS operands
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        f32x16 acc1 = {};
+        float p0[16], p1[16];
+#pragma unroll
+        for (int c = 0; c < NKS; ++c) {  // S^T of block 1 under block 0's exp2
+            acc1 = TR::mfma(kn[c], qf[c], acc1);
+#pragma unroll
+            for (int e = c * 16 / NKS; e < (c + 1) * 16 / NKS; ++e)
+                p0[e] = fast_exp2(__builtin_fmaf(acc0[e], a.scale_log2, -lse2));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        vec pv0[2], pv1[2];
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+            pv0[c2] = TR::cvt8(p0 + 8 * c2);
+            *reinterpret_cast<u32x4*>(pst + C::pos_p(n, (16 * c2 + 8 * hf) * SZ / 16) * 16) =
+                __builtin_bit_cast(u32x4, pv0[c2]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 2 * ND; ++i) {  // O^T += V^T P^T of block 0 under block 1's exp2
+            const int c2 = i / ND, d = i % ND;
+            oacc[d] = TR::mfma(va0[c2][d], pv0[c2], oacc[d]);
+            va1[c2][d] = v_operand(vt, 32 + 16 * c2, d);
+#pragma unroll
+            for (int e = i * 16 / (2 * ND); e < (i + 1) * 16 / (2 * ND); ++e)
+                p1[e] = fast_exp2(__builtin_fmaf(acc1[e], a.scale_log2, -lse2));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+            pv1[c2] = TR::cvt8(p1 + 8 * c2);
+            *reinterpret_cast<u32x4*>(pst + C::pos_p(n, (32 + 16 * c2 + 8 * hf) * SZ / 16) * 16) =
+                __builtin_bit_cast(u32x4, pv1[c2]);
+        }
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+            for (int d = 0; d < ND; ++d) oacc[d] = TR::mfma(va1[c2][d], pv1[c2], oacc[d]);
+        if constexpr (!NL) store_staged(t * BN, false);
+      }
+    };
+    // (not without a loader wave: its deferred stores leave too few registers)
+    constexpr bool PIPE2 = sizeof(T) == 2 && NKB == 2 && MASK == MASK_NONE && C::PSTAGE && !NL;
     // Without a loader wave a tile's probability stores are issued at the
     // start of the next tile (from the staged copy), so the wait before the
     // next barrier finds them a whole tile old rather than just issued.
@@ -684,7 +750,8 @@ void sdpa_twopass_kernel(const FwdArgs a) {
         auto fast2 = [&](int tt, int buf) SDPA_INLINE {
             flush();
             load2(tt + 1);
-            sweep2_tile(tt, std::false_type{}, buf);
+            if constexpr (PIPE2) sweep2_pipe(tt, buf);
+            else sweep2_tile(tt, std::false_type{}, buf);
             pend_k0 = tt * BN;
             pend_edge = false;
             end_tile();
