@@ -135,10 +135,11 @@ sdpa_status_t sdpa_math_fwd_path(const sdpa_tensor_t* q, const sdpa_tensor_t* k,
  *                 page's fused-vs-two-stage rule, single-kernel fusion update)
  * out/probs/lse may be NULL here. Any output pointer may be NULL.
  * SDPA_PATH_AUTO takes the fused path when that path can hold the keys,
- * Sq <= 256 and tiles_64 <= 128 (thresholds measured on MI355X), else the
- * two-pass path. The environment variable SDPA_MATH_PATH=auto|fused|twopass
- * forces the choice; SDPA_MATH_FUSED_MAX_ROWS=<n> and
- * SDPA_MATH_FUSED_MAX_TILES=<n> move the two thresholds.
+ * Sq <= 128, tiles_64 <= 64 and (is_causal or Skv >= 512) (thresholds
+ * measured on MI355X), else the two-pass path. The environment variable
+ * SDPA_MATH_PATH=auto|fused|twopass forces the choice;
+ * SDPA_MATH_FUSED_MAX_ROWS=<n>, SDPA_MATH_FUSED_MAX_TILES=<n> and
+ * SDPA_MATH_FUSED_MIN_KEYS=<n> move the three thresholds.
  */
 sdpa_status_t sdpa_math_plan(const sdpa_tensor_t* q, const sdpa_tensor_t* k,
                              const sdpa_tensor_t* v, const sdpa_tensor_t* mask,

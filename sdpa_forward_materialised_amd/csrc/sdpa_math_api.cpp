@@ -198,12 +198,15 @@ int64_t count_tiles(int64_t Sq, int64_t Skv, bool causal, int64_t rows) {
 // causal and not, Sq 32..1024, Skv 128..2048), the tile count alone picks
 // the fused kernel where it loses: it re-reads K and V for every 32-row
 // block, while the two-pass kernel shares them over 96-128 rows and only
-// runs out of parallelism when the query range is short. The switch is
-// therefore: fused iff Sq <= 256 rows and at most 128 tiles per (batch,
-// head) (within 1% of the per-shape best on the sweep; tile count alone at
-// its best threshold, 32, is 2% off and up to 1.96x off on single shapes).
-constexpr int64_t kFusedMaxTiles64 = 128;
-constexpr int64_t kFusedMaxRows = 256;
+// runs out of parallelism when the query range is short; a non-causal call
+// with few keys per row gives the fused kernel too little to hide its
+// latencies. The switch is therefore: fused iff Sq <= 128 rows, at most 64
+// tiles per (batch, head), and (causal or Skv >= 512) -- 0.5 % above the
+// per-shape best on the sweep (worst shape 1.11x); tile count alone at its
+// best threshold is 6 % off and up to 1.4x.
+constexpr int64_t kFusedMaxTiles64 = 64;
+constexpr int64_t kFusedMaxRows = 128;
+constexpr int64_t kFusedMinKeysNonCausal = 512;
 
 int env_path() {
     const char* e = std::getenv("SDPA_MATH_PATH");
@@ -216,6 +219,12 @@ int env_path() {
 int64_t env_max_tiles() {
     const char* e = std::getenv("SDPA_MATH_FUSED_MAX_TILES");
     if (!e || !*e) return kFusedMaxTiles64;
+    return std::strtoll(e, nullptr, 10);
+}
+
+int64_t env_min_keys() {
+    const char* e = std::getenv("SDPA_MATH_FUSED_MIN_KEYS");
+    if (!e || !*e) return kFusedMinKeysNonCausal;
     return std::strtoll(e, nullptr, 10);
 }
 
@@ -269,7 +278,8 @@ sdpa_status_t make_plan(const Shape& sh, bool causal, int forced, bool vec, sdpa
     int path = forced;
     if (path == SDPA_PATH_AUTO) path = env_path();
     if (path == SDPA_PATH_AUTO)
-        path = (fused_ok && p->tiles_64 <= env_max_tiles() && sh.Sq <= env_max_rows()) ? SDPA_PATH_FUSED
+        path = (fused_ok && p->tiles_64 <= env_max_tiles() && sh.Sq <= env_max_rows() &&
+                (causal || sh.Skv >= env_min_keys())) ? SDPA_PATH_FUSED
                                                                                       : SDPA_PATH_TWOPASS;
     if (path == SDPA_PATH_FUSED && !fused_ok)
         return fail(SDPA_ERR_UNSUPPORTED, "the fused path cannot take this shape (more than %d keys per wave x %d waves)",
