@@ -217,8 +217,11 @@ __device__ __forceinline__ void load_mask16(const FwdArgs& a, rsrc_t mr, uint32_
                 const u32x4 w1 = ld128(mr, off + 16);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    out[8 * c + e] = __builtin_bit_cast(float, w0[e]) * LOG2E;
-                    out[8 * c + 4 + e] = __builtin_bit_cast(float, w1[e]) * LOG2E;
+                    // element to a scalar first: bit_cast of a vector element
+                    // reads element 0 whatever the index (seen with this clang)
+                    const uint32_t b0 = w0[e], b1 = w1[e];
+                    out[8 * c + e] = __builtin_bit_cast(float, b0) * LOG2E;
+                    out[8 * c + 4 + e] = __builtin_bit_cast(float, b1) * LOG2E;
                 }
             }
         } else {

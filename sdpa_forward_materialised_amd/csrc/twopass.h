@@ -302,8 +302,10 @@ void sdpa_twopass_kernel(const FwdArgs a) {
                     const u32x4 w1 = *reinterpret_cast<const u32x4*>(base + jrel * 4 + 16);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        mv[8 * c + e] = __builtin_bit_cast(float, w0[e]) * LOG2E;
-                        mv[8 * c + 4 + e] = __builtin_bit_cast(float, w1[e]) * LOG2E;
+                        // element to a scalar first (bit_cast of a vector element reads element 0)
+                        const uint32_t b0 = w0[e], b1 = w1[e];
+                        mv[8 * c + e] = __builtin_bit_cast(float, b0) * LOG2E;
+                        mv[8 * c + 4 + e] = __builtin_bit_cast(float, b1) * LOG2E;
                     }
                 }
             }

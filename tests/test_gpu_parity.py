@@ -77,6 +77,8 @@ SMALL = [
     ("bf16-d32-single", dict(seed=112, dtype="bf16", B=1, Hq=1, Hkv=1, Sq=1, Skv=1, D=32)),
     ("f16-d128-decode-row", dict(seed=113, dtype="f16", B=3, Hq=8, Hkv=8, Sq=1, Skv=1025, D=128)),
     ("f16-d64-odd-skv", dict(seed=114, dtype="f16", B=1, Hq=2, Hkv=2, Sq=50, Skv=37, D=64, mask="bool")),
+    ("f32-d64-add-staged", dict(seed=116, dtype="f32", B=1, Hq=2, Hkv=2, Sq=100, Skv=136, D=64, mask="add", p=0.1)),
+    ("f32-d32-add-full-staged", dict(seed=117, dtype="f32", B=2, Hq=2, Hkv=1, Sq=70, Skv=200, D=32, mask="add", p=0.2)),
     ("bf16-d64-add-rows-shared", dict(seed=115, dtype="bf16", B=2, Hq=4, Hkv=2, Sq=150, Skv=264, D=64, mask="add",
                                       mask_shape=(2, 1, 1, 264), p=0.2)),
 ]
