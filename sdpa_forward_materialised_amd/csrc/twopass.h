@@ -316,6 +316,24 @@ void sdpa_twopass_kernel(const FwdArgs a) {
         }
     };
 
+    // Whether the staged bool mask tile removes every key of this wave's 32
+    // rows (a key-padding tail, for instance): such a tile adds nothing to
+    // the row sums and its probabilities are all zero, so its products and
+    // exponentials are skipped (the results are the same bits).
+    auto tile_dead = [&](const uint8_t* mt) SDPA_INLINE -> bool {
+        if constexpr (MASK == MASK_BOOL && C::MLDS) {
+            constexpr int NCH = 32 * C::MROWB / 16 / 64;  // 16-byte chunks per lane
+            static_assert(NCH >= 1 && 32 * C::MROWB % 1024 == 0, "mask tile rows of a wave must split into lane chunks");
+            const u32x4* c = reinterpret_cast<const u32x4*>(mt + 32 * wave * C::MROWB) + lane * NCH;
+            u32x4 x = c[0];
+#pragma unroll
+            for (int i = 1; i < NCH; ++i) x |= c[i];
+            return __builtin_amdgcn_ballot_w64((x[0] | x[1] | x[2] | x[3]) != 0u) == 0;
+        } else {
+            return false;
+        }
+    };
+
     // Base-2 scaled, masked scores t[r] of one block. `edge`: the block may
     // hold keys past Skv or past this wave's causal diagonal.
     auto scores = [&](const f32x16& acc, const float* mv, int kb, int k0, bool edge, float* t) SDPA_INLINE {
@@ -355,6 +373,7 @@ void sdpa_twopass_kernel(const FwdArgs a) {
         constexpr bool edge = decltype(edge_c)::value;
         const int k0 = t * BN;
         const int buf = t & 1;
+        if (tile_dead(mbuf(buf))) return;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
             const f32x16 acc = qk_block(kbuf(buf), kb);
@@ -595,6 +614,17 @@ void sdpa_twopass_kernel(const FwdArgs a) {
     auto sweep2_tile = [&](int t, auto edge_c, int buf) SDPA_INLINE {
         constexpr bool edge = decltype(edge_c)::value;
         const int k0 = t * BN;
+        if (tile_dead(mbuf(buf))) {  // P = 0, O unchanged
+            if constexpr (C::PSTAGE) {
+#pragma unroll
+                for (int i = 0; i < C::PSTB / 1024; ++i)
+                    *reinterpret_cast<u32x4*>(pst + (i * 64 + lane) * 16) = u32x4{0u, 0u, 0u, 0u};
+                if constexpr (!NL) store_staged(k0, edge);
+            } else {
+                zero_tile(t);
+            }
+            return;
+        }
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
             const f32x16 acc = qk_block(kbuf(buf), kb);

@@ -91,6 +91,22 @@ def test_small_cases(label, spec, path):
     _check(c, path, label=label)
 
 
+# Bool key-padding masks whose tails remove whole 64-key tiles for every row a
+# wave holds (those tiles are skipped), with some rows removed entirely, at
+# each head dim and compute-wave count.
+@pytest.mark.parametrize("waves", [2, 3, 4])
+@pytest.mark.parametrize("D,dtype", [(32, "f16"), (64, "bf16"), (128, "f16")])
+def test_key_padding_dead_tiles(D, dtype, waves, monkeypatch):
+    monkeypatch.setenv("SDPA_MATH_TP_WAVES", str(waves))
+    c = W.make_case(seed=150 + D, dtype=dtype, B=3, Hq=4, Hkv=2, Sq=200, Skv=512, D=D)
+    keep = torch.zeros(3, 1, 200, 512, dtype=torch.bool)
+    for b, n in enumerate((130, 300, 512)):
+        keep[b, :, :, :n] = True
+    keep[0, :, 40:75, :] = False   # rows with every key removed
+    c["mask"] = keep
+    _check(c, "twopass", label=f"keypad D={D} {dtype} waves={waves}")
+
+
 # Every compute-wave count the kernel is built for (a tuning knob read at each
 # call): 2 or 3 compute waves plus a loader wave, or 4 compute waves sharing
 # the tile loads (where their staged tiles fit in LDS; otherwise the request
