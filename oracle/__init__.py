@@ -18,7 +18,10 @@ plan-time compile, sym_int THD extents", merge-log notes on dead rows and the
 LSE layout):
   * bool mask: True keeps a key, False removes it (score -inf);
   * additive mask: added to the scaled score;
-  * causal: top-left, key j is removed for query i when j > i;
+  * causal: top-left, key j is removed for query i when j > i; with
+    ``causal_alignment="bottom_right"`` when j > i + Skv - Sq (the chunked-
+    prefill alignment named in the cudnn-frontend merge-log notes: the last
+    query row keeps every key; rows i < Sq - Skv keep none and are dead);
   * causal together with a mask is an error; Hq not a multiple of Hkv is an
     error; Hq != Hkv without ``enable_gqa`` is an error;
   * a row with every key removed has P = 0, O = 0 and LSE = -inf.
@@ -59,8 +62,8 @@ _lib_cache = {}
 def load(path: str = _LIB) -> ctypes.CDLL:
     if path in _lib_cache:
         return _lib_cache[path]
-    if not os.path.exists(path):
-        build(force=False, out=path)
+    if not os.path.exists(path) or (path == _LIB and os.path.getmtime(_SRC) > os.path.getmtime(path)):
+        build(force=True, out=path)  # missing, or older than its source
     lib = ctypes.CDLL(path)
     dp = ctypes.POINTER(ctypes.c_double)
     i64 = ctypes.c_int64
@@ -113,10 +116,21 @@ def _mask_array(mask, full_shape):
     return kind, arr, strides
 
 
+def causal_code(is_causal, causal_alignment: str = "top_left") -> int:
+    """0 no causal mask, 1 top-left, 2 bottom-right."""
+    if causal_alignment not in ("top_left", "bottom_right"):
+        raise ValueError(f"unknown causal alignment {causal_alignment!r}")
+    if not is_causal:
+        return 0
+    return 2 if causal_alignment == "bottom_right" else 1
+
+
 def sdpa_reference(q, k, v, attn_mask=None, is_causal: bool = False,
                    scale: Optional[float] = None, enable_gqa: bool = False,
-                   lib_path: str = _LIB) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+                   lib_path: str = _LIB, causal_alignment: str = "top_left"
+                   ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Return (O [B,Hq,Sq,Dv], P [B,Hq,Sq,Skv], LSE [B,Hq,Sq]) in float64."""
+    causal = causal_code(is_causal, causal_alignment)
     q, k, v = _f64(q), _f64(k), _f64(v)
     if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
         raise ValueError("q, k, v must be 4-D [B, H, S, D]")
@@ -145,7 +159,7 @@ def sdpa_reference(q, k, v, attn_mask=None, is_causal: bool = False,
     rc = lib.oracle_sdpa_fwd(q.ctypes.data_as(dp), k.ctypes.data_as(dp), v.ctypes.data_as(dp),
                              B, Hq, Hkv, Sq, Skv, D, Dv, kind,
                              None if marr is None else marr.ctypes.data_as(ctypes.c_void_p),
-                             st, int(bool(is_causal)), float(scale),
+                             st, causal, float(scale),
                              out.ctypes.data_as(dp), probs.ctypes.data_as(dp), lse.ctypes.data_as(dp))
     if rc != 0:
         raise ValueError(f"oracle rejected the call (code {rc})")

@@ -32,7 +32,8 @@ def _array(x):
 
 
 def sdpa_brute(q, k, v, attn_mask=None, is_causal: bool = False,
-               scale: Optional[float] = None, enable_gqa: bool = False):
+               scale: Optional[float] = None, enable_gqa: bool = False,
+               causal_alignment: str = "top_left"):
     q = _array(q).astype(np.float64)
     k = _array(k).astype(np.float64)
     v = _array(v).astype(np.float64)
@@ -44,6 +45,10 @@ def sdpa_brute(q, k, v, attn_mask=None, is_causal: bool = False,
         raise ValueError("Hq != Hkv requires enable_gqa")
     if is_causal and attn_mask is not None:
         raise ValueError("is_causal and attn_mask are mutually exclusive")
+    if causal_alignment not in ("top_left", "bottom_right"):
+        raise ValueError(f"unknown causal alignment {causal_alignment!r}")
+    # the last key query i may see: i (top-left) or i + Skv - Sq (bottom-right)
+    shift = Skv - Sq if causal_alignment == "bottom_right" else 0
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     mask = None if attn_mask is None else _array(attn_mask)
@@ -61,7 +66,7 @@ def sdpa_brute(q, k, v, attn_mask=None, is_causal: bool = False,
                 for j in range(Skv):
                     x = scale * math.fsum(float(q[b, h, i, d]) * float(k[b, hk, j, d])
                                           for d in range(D))
-                    if is_causal and j > i:
+                    if is_causal and j > i + shift:
                         x = -math.inf
                     elif mask is not None:
                         mv = _lookup(mask, b, h, i, j)

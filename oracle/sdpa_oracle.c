@@ -11,8 +11,11 @@
  * blocking, no fusion, no online rescaling):
  *
  *   s_j   = scale * sum_d q[d] * k_{h'}[j][d]        j = 0 .. Skv-1
- *   s_j   = -inf  where a causal (top-left, j > i) or boolean (False) mask
- *                 removes key j; s_j += mask[i][j] for an additive mask
+ *   s_j   = -inf  where a causal or boolean (False) mask removes key j;
+ *                 s_j += mask[i][j] for an additive mask. Causal removes
+ *                 j > i + c: c = 0 top-left (is_causal 1), c = Skv - Sq
+ *                 bottom-right (is_causal 2: the last query row keeps every
+ *                 key, rows i < Sq - Skv keep none)
  *   m     = max_j s_j
  *   dead row (m == -inf):  P[i][:] = 0, O[i][:] = 0, LSE[i] = -inf
  *   else:  LSE = m + log(sum_j exp(s_j - m)),  P_j = exp(s_j - LSE),
@@ -29,7 +32,9 @@
  *    row-wise LSE.
  *  - cudnn-frontend pull request "[SDPA] SM80 fwd: TemplateParams kernels,
  *    plan-time compile, sym_int THD extents", merge-log notes: a dead row
- *    reports LSE = -inf and O = 0; LSE is float32 laid out (B, H, S).
+ *    reports LSE = -inf and O = 0; LSE is float32 laid out (B, H, S);
+ *    bottom-right causal is the alignment of chunked prefill (a chunk of
+ *    queries against a longer key cache).
  *
  * Inputs are contiguous float64 arrays (the caller upcasts the exact
  * dtype-rounded values the GPU receives):
@@ -40,7 +45,7 @@
  * Outputs (contiguous float64): out [B,Hq,Sq,Dv], probs [B,Hq,Sq,Skv],
  *   lse [B,Hq,Sq].
  * Returns 0 on success, 1 when Hq is not a multiple of Hkv, 2 when causal is
- * combined with a mask, 3 for a bad mask kind.
+ * combined with a mask, 3 for a bad mask kind, 4 for a bad is_causal.
  */
 #include <math.h>
 #include <stddef.h>
@@ -71,6 +76,9 @@ int oracle_sdpa_fwd(const double* q, const double* k, const double* v,
 {
     if (Hkv <= 0 || Hq % Hkv != 0)
         return 1;
+    if (is_causal < 0 || is_causal > 2)
+        return 4;
+    const int64_t coff = is_causal == 2 ? Skv - Sq : 0;
     if (is_causal && mask_kind != ORACLE_MASK_NONE)
         return 2;
     if (mask_kind != ORACLE_MASK_NONE && mask_kind != ORACLE_MASK_BOOL &&
@@ -100,7 +108,7 @@ int oracle_sdpa_fwd(const double* q, const double* k, const double* v,
             for (int64_t d = 0; d < D; ++d)
                 dot += qi[d] * kh[j * D + d];
             double s = scale * dot;
-            if (is_causal && j > i) {
+            if (is_causal && j > i + coff) {
                 s = -INFINITY;
             } else if (mask_kind != ORACLE_MASK_NONE) {
                 const int64_t off = b * mask_strides[0] + h * mask_strides[1] +

@@ -256,6 +256,63 @@ def test_bool_mask_equals_neginf_float_mask():
         np.testing.assert_array_equal(x, y)
 
 
+# ---------------------------------------------------------------- bottom-right causal
+# (query i keeps keys j <= i + Skv - Sq: the alignment of a query chunk against
+# a longer key cache, cudnn-frontend merge-log notes)
+
+@pytest.mark.parametrize("spec", [
+    dict(seed=71, Sq=5, Skv=7), dict(seed=72, Sq=9, Skv=4), dict(seed=73, Sq=3, Skv=9),
+    dict(seed=74, Sq=6, Skv=6), dict(seed=75, Hq=4, Hkv=2, Sq=4, Skv=10, D=5, Dv=3),
+], ids=lambda s: "-".join(f"{k}{v}" for k, v in s.items()))
+def test_bottom_right_matches_brute_force(spec):
+    c = _case(causal=True, **spec)
+    gqa = c["q"].shape[1] != c["k"].shape[1]
+    a = oracle.sdpa_reference(c["q"], c["k"], c["v"], None, True, 0.41, gqa, causal_alignment="bottom_right")
+    b = sdpa_brute(c["q"], c["k"], c["v"], None, True, 0.41, gqa, causal_alignment="bottom_right")
+    np.testing.assert_allclose(a[1], b[1], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(a[0], b[0], rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(np.isneginf(a[2]), np.isneginf(b[2]))
+    fin = np.isfinite(b[2])
+    np.testing.assert_allclose(a[2][fin], b[2][fin], rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(a[1] == 0, b[1] == 0)
+
+
+@pytest.mark.parametrize("sq,skv", [(6, 6), (9, 4), (3, 9), (1, 8)])
+def test_bottom_right_equals_shifted_tril_bool_mask(sq, skv):
+    c = _case(34, Sq=sq, Skv=skv, causal=True)
+    a = oracle.sdpa_reference(c["q"], c["k"], c["v"], None, True, causal_alignment="bottom_right")
+    keep = torch.ones(sq, skv, dtype=torch.bool).tril(diagonal=skv - sq)
+    b = oracle.sdpa_reference(c["q"], c["k"], c["v"], keep, False)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
+def test_bottom_right_closed_forms():
+    # square: the same as top-left
+    c = _case(35, Sq=7, Skv=7, causal=True)
+    a = oracle.sdpa_reference(c["q"], c["k"], c["v"], None, True, causal_alignment="bottom_right")
+    b = oracle.sdpa_reference(c["q"], c["k"], c["v"], None, True)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+    # a chunk against a longer cache: the last row keeps every key (the
+    # non-causal row); row i keeps exactly i + Skv - Sq + 1 keys
+    c = _case(36, Sq=3, Skv=8, causal=True)
+    o, p, lse = oracle.sdpa_reference(c["q"], c["k"], c["v"], None, True, causal_alignment="bottom_right")
+    on, pn, ln = oracle.sdpa_reference(c["q"], c["k"], c["v"], None, False)
+    np.testing.assert_array_equal(p[:, :, -1], pn[:, :, -1])
+    np.testing.assert_array_equal(o[:, :, -1], on[:, :, -1])
+    for i in range(3):
+        assert ((p[:, :, i] > 0).sum(axis=-1) == i + 5 + 1).all()
+        assert (p[:, :, i, i + 6:] == 0).all()
+    # more queries than keys: rows i < Sq - Skv keep no key (dead rows)
+    c = _case(37, Sq=9, Skv=4, causal=True)
+    o, p, lse = oracle.sdpa_reference(c["q"], c["k"], c["v"], None, True, causal_alignment="bottom_right")
+    assert (p[:, :, :5] == 0).all() and (o[:, :, :5] == 0).all() and np.isneginf(lse[:, :, :5]).all()
+    np.testing.assert_allclose(p[:, :, 5:].sum(-1), 1.0, rtol=0, atol=1e-12)
+    with pytest.raises(ValueError):
+        oracle.sdpa_reference(c["q"], c["k"], c["v"], None, True, causal_alignment="middle")
+
+
 @pytest.mark.parametrize("sq,skv", [(6, 6), (9, 4), (3, 9)])
 def test_causal_equals_tril_bool_mask(sq, skv):
     c = _case(33, Sq=sq, Skv=skv, causal=True)
@@ -327,14 +384,16 @@ def _pins_pass(lib_path):
     for spec in (dict(seed=61, Hq=4, Hkv=2, Sq=6, Skv=6, causal=True),
                  dict(seed=62, Hq=4, Hkv=2, mask="bool", p=0.5, Sq=8),
                  dict(seed=63, mask="add"), dict(seed=64, Sq=4, Skv=9, D=6, Dv=3),
-                 dict(seed=65, mask="bool", p=0.2)):
-        c = _case(**spec)
+                 dict(seed=65, mask="bool", p=0.2),
+                 dict(seed=66, Sq=4, Skv=9, causal=True, align="bottom_right")):
+        c = _case(**{k: x for k, x in spec.items() if k != "align"})
         if spec["seed"] == 65:
             c["mask"][0, 1, 3, :] = False  # one dead row
         gqa = c["q"].shape[1] != c["k"].shape[1]
+        al = spec.get("align", "top_left")
         a = oracle.sdpa_reference(c["q"], c["k"], c["v"], c["mask"], c["causal"], None, gqa,
-                                  lib_path=lib_path)
-        b = sdpa_brute(c["q"], c["k"], c["v"], c["mask"], c["causal"], None, gqa)
+                                  lib_path=lib_path, causal_alignment=al)
+        b = sdpa_brute(c["q"], c["k"], c["v"], c["mask"], c["causal"], None, gqa, causal_alignment=al)
         for x, y in zip(a, b):
             same_inf = np.array_equal(np.isneginf(x), np.isneginf(y))
             fin = np.isfinite(y)
@@ -346,7 +405,8 @@ def _pins_pass(lib_path):
 MUTANTS = [
     ("dropped scale", "double s = scale * dot;", "double s = dot;"),
     ("GQA head index", "const int64_t hk = h / group;", "const int64_t hk = h % Hkv;"),
-    ("causal diagonal", "if (is_causal && j > i)", "if (is_causal && j >= i)"),
+    ("causal diagonal", "if (is_causal && j > i + coff)", "if (is_causal && j >= i + coff)"),
+    ("bottom-right offset sign", "is_causal == 2 ? Skv - Sq : 0;", "is_causal == 2 ? Sq - Skv : 0;"),
     ("bool polarity", "[off] == 0)", "[off] != 0)"),
     ("additive sign", "s += ((const double*)mask)[off];", "s -= ((const double*)mask)[off];"),
     ("LSE missing log-sum", "const double L = m + log(l);", "const double L = m;"),
