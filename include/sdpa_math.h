@@ -12,7 +12,9 @@
  * For every batch b, query head h, query row i and key j, with
  * g = Hq / Hkv and kv head h' = h / g:
  *   s_ij = scale * sum_d Q[b,h,i,d] * K[b,h',j,d]
- *   s_ij = -inf  if causal and j > i (top-left alignment), or if a boolean
+ *   s_ij = -inf  if causal and j > i + c (c = 0: top-left alignment;
+ *                c = Skv - Sq: bottom-right, the last query row keeps every
+ *                key), or if a boolean
  *                mask holds False at (b,h,i,j); s_ij += mask[b,h,i,j] for an
  *                additive mask (masks broadcast over size-1 dimensions)
  *   LSE_i  = log sum_j exp(s_ij)            (-inf when every key is removed)
@@ -85,7 +87,11 @@ typedef enum {
  * v      [B, Hkv, Skv, Dv] same dtype as q; Dv == D in this version
  * mask   NULL, or a bool or q-dtype tensor broadcastable to [B, Hq, Sq, Skv]
  *        (bool: True keeps the key; float: added to the scaled score)
- * is_causal  nonzero for the top-left causal mask (exclusive with `mask`)
+ * is_causal  0: no causal mask; 1: top-left causal; 2: bottom-right causal
+ *        (query i keeps keys j <= i + Skv - Sq: the alignment of a query chunk
+ *        against a longer key cache, named by the cudnn-frontend merge-log
+ *        notes; when Sq > Skv the first Sq - Skv rows keep no key and are dead
+ *        rows). Exclusive with `mask`; other values are INVALID_ARG.
  * scale  multiplier of Q K^T (the Python layer passes 1/sqrt(D) by default,
  *        as the cudnn-frontend merge-log notes resolve a missing scale)
  * enable_gqa nonzero lets Hq be a multiple of Hkv; query head h then reads

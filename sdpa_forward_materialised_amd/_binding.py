@@ -22,6 +22,7 @@ SDPA_F32, SDPA_F16, SDPA_BF16, SDPA_BOOL = 0, 1, 2, 3
 PATH_AUTO, PATH_FUSED, PATH_TWOPASS = 0, 1, 2
 PATHS = {"auto": PATH_AUTO, "fused": PATH_FUSED, "twopass": PATH_TWOPASS}
 PATH_NAMES = {v: k for k, v in PATHS.items()}
+CAUSAL_ALIGNMENTS = {"top_left": 1, "bottom_right": 2}  # the C ABI's is_causal codes
 
 _DTYPES = {torch.float32: SDPA_F32, torch.float16: SDPA_F16, torch.bfloat16: SDPA_BF16,
            torch.bool: SDPA_BOOL}
@@ -113,18 +114,28 @@ def _check_devices(*ts):
     return dev
 
 
+def _causal_code(is_causal, causal_alignment: str) -> int:
+    if causal_alignment not in CAUSAL_ALIGNMENTS:
+        raise ValueError(f"causal_alignment must be one of {sorted(CAUSAL_ALIGNMENTS)}")
+    return CAUSAL_ALIGNMENTS[causal_alignment] if is_causal else 0
+
+
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, attn_mask: Optional[torch.Tensor] = None,
         is_causal: bool = False, scale: Optional[float] = None, enable_gqa: bool = False,
-        path: str = "auto", out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None
-        ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+        path: str = "auto", out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
+        causal_alignment: str = "top_left") -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """Return (O [B,Hq,Sq,Dv], P [B,Hq,Sq,Skv], LSE [B,Hq,Sq] float32).
 
     ``scale=None`` means 1/sqrt(D). ``path`` is "auto", "fused" or "twopass".
+    ``causal_alignment`` ("top_left" or "bottom_right") places the causal
+    diagonal when ``is_causal``: key j is removed for query i when j > i, or
+    when j > i + Skv - Sq.
     ``out`` may pass preallocated (O, P, LSE) buffers (any strides with a
     contiguous last dim); by default P and O share one allocation.
     """
     lib = load_library()
     dev = _check_devices(q, k, v, attn_mask)
+    causal = _causal_code(is_causal, causal_alignment)
     if path not in PATHS:
         raise ValueError(f"path must be one of {sorted(PATHS)}")
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
@@ -149,7 +160,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, attn_mask: Optional[t
     do, dp, dl = _desc(O, 4), _desc(P, 4), _desc(L, 3)
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
-        rc = lib.sdpa_math_fwd_path(_ref(dq), _ref(dk), _ref(dv), _ref(dm), int(bool(is_causal)),
+        rc = lib.sdpa_math_fwd_path(_ref(dq), _ref(dk), _ref(dv), _ref(dm), causal,
                                     float(scale), int(bool(enable_gqa)), _ref(do), _ref(dp), _ref(dl),
                                     ctypes.c_void_p(stream), PATHS[path])
     if rc != 0:
@@ -158,7 +169,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, attn_mask: Optional[t
 
 
 def plan(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, attn_mask: Optional[torch.Tensor] = None,
-         is_causal: bool = False, enable_gqa: bool = False):
+         is_causal: bool = False, enable_gqa: bool = False, causal_alignment: str = "top_left"):
     """Validate like ``fwd`` and return (path name, tiles per (b,h), 64x64 tiles per (b,h)).
 
     Reads only shapes, strides, dtypes and pointers; works on CPU tensors too.
@@ -168,7 +179,8 @@ def plan(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, attn_mask: Optional[
     tiles = ctypes.c_int64(-1)
     tiles64 = ctypes.c_int64(-1)
     rc = lib.sdpa_math_plan(_ref(_desc(q, 4)), _ref(_desc(k, 4)), _ref(_desc(v, 4)),
-                            _ref(_desc(attn_mask, 4)), int(bool(is_causal)), int(bool(enable_gqa)),
+                            _ref(_desc(attn_mask, 4)), _causal_code(is_causal, causal_alignment),
+                            int(bool(enable_gqa)),
                             ctypes.byref(path), ctypes.byref(tiles), ctypes.byref(tiles64))
     if rc != 0:
         _raise(rc, lib)

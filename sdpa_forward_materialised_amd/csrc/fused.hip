@@ -81,7 +81,7 @@ void sdpa_fused_kernel(const FwdArgs a) {
     const int qi = q0 + n;
     const bool row_ok = qi < a.Sq;
     // keys any row of this block may keep
-    const int kend = a.causal ? min(a.Skv, q0 + 32) : a.Skv;
+    const int kend = a.causal ? min(a.Skv, max(0, q0 + 32 + a.coff)) : a.Skv;
     const int kpw = a.keys_per_wave;
     const int kbase = wave * kpw;
     const int nb = max(0, min((kend - kbase + 31) / 32, kpw / 32));
@@ -135,7 +135,7 @@ void sdpa_fused_kernel(const FwdArgs a) {
             float mv[16];
             if constexpr (MASK != MASK_NONE)
                 load_mask16<T, MASK, VEC>(a, mr, (uint32_t)((int64_t)(row_ok ? qi : 0) * a.m_s[2] * ME), jb, hf, mv);
-            const bool edge = (jb + 32 > a.Skv) || (a.causal && jb + 31 > q0);
+            const bool edge = (jb + 32 > a.Skv) || (a.causal && jb + 31 > q0 + a.coff);
             float t[16];
             scores16<MASK>(a, acc, mv, jb, hf, qi, edge, t);
 #pragma unroll

@@ -254,7 +254,7 @@ __device__ __forceinline__ void scores16(const FwdArgs& a, const f32x16& acc, co
         if constexpr (MASK == MASK_BOOL) drop = mv[r] == 0.0f;
         if (edge) {
             const int j = jblk + kk(hf, r);
-            drop = drop || j >= a.Skv || (a.causal && j > qi);
+            drop = drop || j >= a.Skv || (a.causal && j > qi + a.coff);
         }
         t[r] = drop ? -INFINITY : x;
     }

@@ -24,6 +24,8 @@ struct FwdArgs {
     int64_t m_s[4];
     int B, Hq, Hkv, Sq, Skv, group;
     int causal;
+    int coff;        // causal: key j is removed for query i when j > i + coff
+                     // (0 top-left; Skv - Sq bottom-right)
     int mask_vec;    // mask rows can be read with aligned vector loads
     int p_vec;       // P rows can be written with aligned 16-byte stores
     int o_vec;       // O rows likewise

@@ -126,6 +126,9 @@ sdpa_status_t validate_inputs(const sdpa_tensor_t* q, const sdpa_tensor_t* k, co
     if (sh->Hq != sh->Hkv && !enable_gqa)
         return fail(SDPA_ERR_INVALID_ARG, "Hq (%lld) != Hkv (%lld) needs enable_gqa", (long long)sh->Hq,
                     (long long)sh->Hkv);
+    if (is_causal < 0 || is_causal > 2)
+        return fail(SDPA_ERR_INVALID_ARG, "is_causal must be 0 (none), 1 (top-left) or 2 (bottom-right), got %d",
+                    is_causal);
     sh->mask_kind = sdpa::MASK_NONE;
     if (mask) {
         if (is_causal) return fail(SDPA_ERR_INVALID_ARG, "is_causal and an explicit mask are mutually exclusive");
@@ -179,15 +182,21 @@ sdpa_status_t validate_outputs(const Shape& sh, const sdpa_tensor_t* out, const 
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Causal diagonal offset: key j is removed for query i when j > i + offset
+// (is_causal 1: top-left, offset 0; 2: bottom-right, the alignment of a query
+// chunk against a longer key cache, offset Skv - Sq).
+int64_t causal_offset(const Shape& sh, int is_causal) { return is_causal == 2 ? sh.Skv - sh.Sq : 0; }
+
 // Score tiles one (batch, head) processes with `rows` query rows per block
-// and 64 keys per tile, after top-left causal truncation.
-int64_t count_tiles(int64_t Sq, int64_t Skv, bool causal, int64_t rows) {
+// and 64 keys per tile, after causal truncation (key j removed for query i
+// when j > i + coff: coff 0 top-left, Skv - Sq bottom-right).
+int64_t count_tiles(int64_t Sq, int64_t Skv, bool causal, int64_t rows, int64_t coff = 0) {
     const int64_t ktiles = cdiv(Skv, sdpa::TILE_N);
     if (!causal) return cdiv(Sq, rows) * ktiles;
     int64_t total = 0;
     for (int64_t r0 = 0; r0 < Sq; r0 += rows) {
-        const int64_t last = std::min(Sq, r0 + rows);  // keys j < last are reachable
-        total += cdiv(std::min(Skv, last), sdpa::TILE_N);
+        const int64_t last = std::min(Sq, r0 + rows) + coff;  // keys j < last are reachable
+        total += cdiv(std::max<int64_t>(0, std::min(Skv, last)), sdpa::TILE_N);
     }
     return total;
 }
@@ -238,8 +247,8 @@ int64_t env_max_rows() {
 // each keeping at most the per-head-dim limit of scores in registers. Waves
 // are added until a wave holds at most 128 keys (fewer registers, more waves
 // in flight) or the wave count is at its maximum.
-bool fused_config(const Shape& sh, bool causal, int* waves, int* keys_per_wave) {
-    const int64_t keys = causal ? std::min(sh.Skv, sh.Sq) : sh.Skv;
+bool fused_config(const Shape& sh, bool causal, int64_t coff, int* waves, int* keys_per_wave) {
+    const int64_t keys = causal ? std::min(sh.Skv, sh.Sq + coff) : sh.Skv;  // the last row's keys
     if (keys <= 0) return false;
     const int64_t limit = sh.D == 128 ? sdpa::FUSED_MAX_KEYS_PER_WAVE_D128 : sdpa::FUSED_MAX_KEYS_PER_WAVE;
     for (int w = 1; w <= sdpa::FUSED_MAX_WAVES; w *= 2) {
@@ -271,10 +280,10 @@ bool staged_layout(const Shape& sh, const sdpa_tensor_t* mask, const sdpa_tensor
     return true;
 }
 
-sdpa_status_t make_plan(const Shape& sh, bool causal, int forced, bool vec, sdpa::Plan* p) {
-    p->tiles_64 = count_tiles(sh.Sq, sh.Skv, causal, 64);
+sdpa_status_t make_plan(const Shape& sh, bool causal, int64_t coff, int forced, bool vec, sdpa::Plan* p) {
+    p->tiles_64 = count_tiles(sh.Sq, sh.Skv, causal, 64, coff);
     int fw = 0, fk = 0;
-    const bool fused_ok = fused_available() && fused_config(sh, causal, &fw, &fk);
+    const bool fused_ok = fused_available() && fused_config(sh, causal, coff, &fw, &fk);
     int path = forced;
     if (path == SDPA_PATH_AUTO) path = env_path();
     if (path == SDPA_PATH_AUTO)
@@ -319,7 +328,7 @@ sdpa_status_t make_plan(const Shape& sh, bool causal, int forced, bool vec, sdpa
     }
     p->n_qblk = (int)cdiv(sh.Sq, p->q_rows);
     p->grid = sh.B * sh.Hq * p->n_qblk;
-    p->tiles_per_bh = count_tiles(sh.Sq, sh.Skv, causal, p->q_rows);
+    p->tiles_per_bh = count_tiles(sh.Sq, sh.Skv, causal, p->q_rows, coff);
     if (p->grid > INT32_MAX) return fail(SDPA_ERR_UNSUPPORTED, "grid too large");
     return SDPA_OK;
 }
@@ -345,7 +354,7 @@ sdpa_status_t run(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_ten
     if (sh.B * sh.Hq * sh.Sq == 0) return SDPA_OK;
     const bool vec = staged_layout(sh, mask, out, probs);
     sdpa::Plan plan;
-    if ((st = make_plan(sh, is_causal != 0, path, vec, &plan))) return st;
+    if ((st = make_plan(sh, is_causal != 0, causal_offset(sh, is_causal), path, vec, &plan))) return st;
 
     sdpa::FwdArgs a;
     std::memset(&a, 0, sizeof a);
@@ -371,6 +380,7 @@ sdpa_status_t run(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_ten
     a.Skv = (int)sh.Skv;
     a.group = (int)(sh.Hq / sh.Hkv);
     a.causal = is_causal ? 1 : 0;
+    a.coff = (int)causal_offset(sh, is_causal);
     const int64_t es = elt_size(sh.dtype);
     const int64_t me = sh.mask_kind == sdpa::MASK_BOOL ? 1 : es;
     a.mask_vec = vec && mask;
@@ -467,7 +477,8 @@ sdpa_status_t sdpa_math_plan(const sdpa_tensor_t* q, const sdpa_tensor_t* k, con
     sdpa_status_t st = validate_inputs(q, k, v, mask, is_causal, enable_gqa, &sh);
     if (st) return st;
     sdpa::Plan plan;
-    if ((st = make_plan(sh, is_causal != 0, SDPA_PATH_AUTO, staged_layout(sh, mask, nullptr, nullptr), &plan)))
+    if ((st = make_plan(sh, is_causal != 0, causal_offset(sh, is_causal), SDPA_PATH_AUTO,
+                        staged_layout(sh, mask, nullptr, nullptr), &plan)))
         return st;
     if (path) *path = plan.path;
     if (tiles_per_bh) *tiles_per_bh = plan.tiles_per_bh;

@@ -141,7 +141,7 @@ void sdpa_twopass_kernel(const FwdArgs a) {
     const Work w = decode_block(blockIdx.x, a);
     const int hk = w.hq / a.group;
     const int q0 = w.qblk * QB;
-    const int kend = a.causal ? min(a.Skv, q0 + QB) : a.Skv;
+    const int kend = a.causal ? min(a.Skv, max(0, q0 + QB + a.coff)) : a.Skv;
     const int ntiles = (kend + BN - 1) / BN;
 
     const rsrc_t kr = make_rsrc(static_cast<const T*>(a.k) + w.b * a.k_s[0] + hk * a.k_s[1], a.k_ext);
@@ -340,7 +340,7 @@ void sdpa_twopass_kernel(const FwdArgs a) {
         const int jb = k0 + 32 * kb;
         // register r holds key jb + kk(hf, r) = jb + 8 hf + kk(0, r); it is
         // dropped when kk(0, r) > lim (a compile-time constant per register)
-        const int lim = edge ? min(a.Skv - 1 - jb, a.causal ? qi - jb : 0x7fffffff) - 8 * hf : 0x7fffffff;
+        const int lim = edge ? min(a.Skv - 1 - jb, a.causal ? qi + a.coff - jb : 0x7fffffff) - 8 * hf : 0x7fffffff;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             float x;
@@ -364,8 +364,9 @@ void sdpa_twopass_kernel(const FwdArgs a) {
     // a wave whose rows all lie past Sq (the last block of a ragged Sq) only
     // keeps the barrier count
     const bool live = qw < a.Sq;
-    const int t_comp = !live ? 0 : a.causal ? min(ntiles, (qw + 31) / BN + 1) : ntiles;
-    const int t_fast = min(t_comp, a.causal ? min(a.Skv / BN, (qw + 1) / BN) : a.Skv / BN);
+    const int dlast = qw + 31 + a.coff;  // causal: last key the wave's last row keeps
+    const int t_comp = !live ? 0 : a.causal ? (dlast < 0 ? 0 : min(ntiles, dlast / BN + 1)) : ntiles;
+    const int t_fast = min(t_comp, a.causal ? min(a.Skv / BN, max(0, qw + a.coff + 1) / BN) : a.Skv / BN);
 
     // ---------------- sweep 1: row maximum and sum (base 2)
     float m_run = -INFINITY, l_run = 0.0f;

@@ -85,8 +85,8 @@ def compare(O, P, L, ref, dtype, label=""):
             "max_abs_o_ref": float(np.abs(ro).max()) if ro.size else 0.0}
 
 
-def run_oracle(q, k, v, mask, causal, scale, gqa):
-    return oracle.sdpa_reference(q, k, v, mask, causal, scale, gqa)
+def run_oracle(q, k, v, mask, causal, scale, gqa, causal_alignment="top_left"):
+    return oracle.sdpa_reference(q, k, v, mask, causal, scale, gqa, causal_alignment=causal_alignment)
 
 
 def head_slice(q, k, v, mask, b, h):

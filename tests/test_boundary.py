@@ -129,3 +129,38 @@ def test_plan_picks_fused_for_few_tiles():
     # few tiles, but more keys than the fused waves hold at D=128: two-pass
     q, k = _z(1, 2, 1, 128), _z(1, 2, 1100, 128)
     assert S.plan(q, k, k) == ("twopass", 18, 18)
+
+
+def _tiles64_brute(Sq, Skv, coff):
+    """64x64 score tiles holding at least one key kept under causal offset coff."""
+    n = 0
+    for r0 in range(0, Sq, 64):
+        for c0 in range(0, Skv, 64):
+            last_row = min(Sq, r0 + 64) - 1
+            if c0 <= last_row + coff:
+                n += 1
+    return n
+
+
+@pytest.mark.parametrize("Sq,Skv", [(512, 2048), (100, 1152), (64, 64), (200, 100), (1, 300), (700, 700)])
+def test_plan_bottom_right_tile_counts(Sq, Skv):
+    q, k = _z(1, 2, Sq, 64), _z(1, 2, Skv, 64)
+    _, _, t64 = S.plan(q, k, k, is_causal=True, causal_alignment="bottom_right")
+    assert t64 == _tiles64_brute(Sq, Skv, Skv - Sq)
+    _, _, t64_tl = S.plan(q, k, k, is_causal=True)
+    assert t64_tl == _tiles64_brute(Sq, Skv, 0)
+    if Sq == Skv:
+        assert S.plan(q, k, k, is_causal=True, causal_alignment="bottom_right") == S.plan(q, k, k, is_causal=True)
+
+
+def test_causal_codes_validated():
+    q = _z(1, 2, 8, 64)
+    with pytest.raises(ValueError, match="causal_alignment"):
+        S.plan(q, q, q, is_causal=True, causal_alignment="middle")
+    lib = S.load_library()
+    d = B._desc(q, 4)
+    out = (ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int64())
+    for code, want in ((0, 0), (1, 0), (2, 0), (3, 1), (-1, 1)):
+        rc = lib.sdpa_math_plan(B._ref(d), B._ref(d), B._ref(d), None, code, 0, *(ctypes.byref(x) for x in out))
+        assert rc == want, (code, S.last_error())
+    assert "is_causal" in (S.last_error() or "")

@@ -39,7 +39,8 @@ def _run(c, path, scale=None, gqa=None, label=""):
           f"{None if m is None else (tuple(m.shape), m.dtype)} causal={c['causal']}", flush=True)
     gm = None if m is None else m.to(DEV)
     try:
-        O, P, L = S.fwd(q.to(DEV), k.to(DEV), v.to(DEV), gm, c["causal"], scale, gqa, path=path, out=out)
+        O, P, L = S.fwd(q.to(DEV), k.to(DEV), v.to(DEV), gm, c["causal"], scale, gqa, path=path, out=out,
+                        causal_alignment=c.get("align", "top_left"))
     except NotImplementedError as e:
         if path == "fused":
             pytest.skip(f"the fused path cannot take this shape: {e}")
@@ -51,7 +52,7 @@ def _run(c, path, scale=None, gqa=None, label=""):
 def _check(c, path, scale=None, label=""):
     O, P, L = _run(c, path, scale, label=label)
     gqa = c["q"].shape[1] != c["k"].shape[1]
-    ref = run_oracle(c["q"], c["k"], c["v"], c["mask"], c["causal"], scale, gqa)
+    ref = run_oracle(c["q"], c["k"], c["v"], c["mask"], c["causal"], scale, gqa, c.get("align", "top_left"))
     return compare(O, P, L, ref, c["q"].dtype, label)
 
 
@@ -105,6 +106,37 @@ def test_key_padding_dead_tiles(D, dtype, waves, monkeypatch):
     keep[0, :, 40:75, :] = False   # rows with every key removed
     c["mask"] = keep
     _check(c, "twopass", label=f"keypad D={D} {dtype} waves={waves}")
+
+
+# Bottom-right causal (query i keeps keys j <= i + Skv - Sq): a query chunk
+# against a longer key cache, grouped heads, more queries than keys (leading
+# dead rows), ragged float32, square, a few rows against a long cache, and a
+# 512-row chunk against a 2048-key cache.
+BOTTOM_RIGHT = [
+    ("bf16-d128-chunk-vs-cache", dict(seed=160, dtype="bf16", B=1, Hq=2, Hkv=2, Sq=130, Skv=520, D=128)),
+    ("f16-d64-chunk-gqa", dict(seed=161, dtype="f16", B=2, Hq=4, Hkv=2, Sq=64, Skv=1000, D=64)),
+    ("f16-d32-more-queries", dict(seed=162, dtype="f16", B=1, Hq=2, Hkv=2, Sq=150, Skv=90, D=32)),
+    ("f32-d64-ragged", dict(seed=163, dtype="f32", B=1, Hq=2, Hkv=2, Sq=37, Skv=101, D=64)),
+    ("bf16-d128-square", dict(seed=164, dtype="bf16", B=1, Hq=2, Hkv=2, Sq=100, Skv=100, D=128)),
+    ("f16-d128-few-rows", dict(seed=165, dtype="f16", B=2, Hq=4, Hkv=4, Sq=3, Skv=776, D=128)),
+    ("bf16-d128-chunk512-cache2048", dict(seed=166, dtype="bf16", B=1, Hq=4, Hkv=4, Sq=512, Skv=2048, D=128)),
+]
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("label,spec", BOTTOM_RIGHT, ids=[s[0] for s in BOTTOM_RIGHT])
+def test_bottom_right_causal(label, spec, path):
+    c = W.make_case(causal=True, **spec)
+    c["align"] = "bottom_right"
+    _check(c, path, label=f"{label} bottom-right")
+
+
+@pytest.mark.parametrize("waves", [2, 3, 4])
+def test_bottom_right_causal_wave_counts(waves, monkeypatch):
+    monkeypatch.setenv("SDPA_MATH_TP_WAVES", str(waves))
+    c = W.make_case(seed=167, dtype="bf16", B=1, Hq=2, Hkv=2, Sq=300, Skv=712, D=64, causal=True)
+    c["align"] = "bottom_right"
+    _check(c, "twopass", label=f"bottom-right waves={waves}")
 
 
 # Every compute-wave count the kernel is built for (a tuning knob read at each
