@@ -70,15 +70,15 @@ def time_gpu(w, steps, warmup, path="auto", warm_ms=0.0):
     P = torch.empty(B, Hq, Sq, Skv, dtype=q.dtype, device=dev)
     L = torch.empty(B, Hq, Sq, dtype=torch.float32, device=dev)
     out = (O, P, L)
-    chosen, tiles, tiles64 = S.plan(q, k, v, m, w.causal, w.gqa)
+    chosen, tiles, tiles64 = S.plan(q, k, v, m, w.causal, w.gqa, causal_alignment=w.align)
     for _ in range(warmup):
-        S.fwd(q, k, v, m, w.causal, w.scale, w.gqa, path=path, out=out)
+        S.fwd(q, k, v, m, w.causal, w.scale, w.gqa, path=path, out=out, causal_alignment=w.align)
     torch.cuda.synchronize()
     # and at least warm_ms of sustained work: the clock ramps up over tens of ms
     t_w = time.perf_counter()
     while (time.perf_counter() - t_w) * 1e3 < warm_ms:
         for _ in range(20):
-            S.fwd(q, k, v, m, w.causal, w.scale, w.gqa, path=path, out=out)
+            S.fwd(q, k, v, m, w.causal, w.scale, w.gqa, path=path, out=out, causal_alignment=w.align)
         torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     ev0 = torch.cuda.Event(enable_timing=True)
@@ -86,7 +86,7 @@ def time_gpu(w, steps, warmup, path="auto", warm_ms=0.0):
     t0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(steps):
-        S.fwd(q, k, v, m, w.causal, w.scale, w.gqa, path=path, out=out)
+        S.fwd(q, k, v, m, w.causal, w.scale, w.gqa, path=path, out=out, causal_alignment=w.align)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -194,17 +194,29 @@ def threshold_sweep(reps=15, warmup=3):
                     print(json.dumps(res), flush=True)
 
 
-def all_configs(steps, warmup, path):
+def kept_pairs(Sq, Skv, align):
+    """(query, key) pairs a causal mask keeps: query i keeps keys j <= i + c
+    (c = 0 top-left, Skv - Sq bottom-right)."""
+    c = Skv - Sq if align == "bottom_right" else 0
+    return sum(max(0, min(Skv, i + c + 1)) for i in range(Sq))
+
+
+def all_configs(steps, warmup, path, workloads=None):
     """Every seeded workload: time, effective TFLOPS, P-write GB/s and the
-    fraction of the HBM roofline each reaches."""
+    fraction of the HBM roofline each reaches. FLOPs follow the perf-gate
+    convention (causal halves the square); a causal shape with Sq != Skv
+    counts the (query, key) pairs its mask keeps."""
     import sdpa_workloads as W
 
     rows = []
-    for w in W.WORKLOADS:
+    for w in (W.WORKLOADS if workloads is None else workloads):
         r = time_gpu(w, steps, warmup, path, warm_ms=50.0)
         by = algorithmic_bytes(w, r["mask_bytes"])
         sec = r["ms"] * 1e-3
-        fl = algorithmic_flops(w.B, w.Hq, w.Sq, w.Skv, w.D, w.dv, w.causal)
+        if w.causal and w.Sq != w.Skv:
+            fl = 2.0 * w.B * w.Hq * kept_pairs(w.Sq, w.Skv, w.align) * (w.D + w.dv)
+        else:
+            fl = algorithmic_flops(w.B, w.Hq, w.Sq, w.Skv, w.D, w.dv, w.causal)
         rows.append({"workload": w.name, "dtype": w.dtype, "path": r["path"], "ms": round(r["ms"], 5),
                      "tflops": round(fl / sec / 1e12, 2), "p_write_gbps": round(by["p"] / sec / 1e9, 1),
                      "hbm_gbps": round(by["total"] / sec / 1e9, 1),
@@ -297,6 +309,8 @@ def main():
 
     if not args.no_configs:
         extra["configs"] = all_configs(min(args.steps, 50), min(args.warmup, 100), args.path)
+        extra["extra_configs"] = all_configs(min(args.steps, 50), min(args.warmup, 100), args.path,
+                                             W.EXTRA_WORKLOADS)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -45,6 +45,7 @@ class Workload:
     mask: str           # "none" | "keypad_bool" | "random_neginf_add"
     seed: int
     Dv: Optional[int] = None
+    align: str = "top_left"  # causal alignment: "top_left" | "bottom_right"
 
     @property
     def dv(self) -> int:
@@ -73,7 +74,15 @@ WORKLOADS: Sequence[Workload] = (
              "random_neginf_add", 5),
 )
 
-BY_NAME: Dict[str, Workload] = {w.name: w for w in WORKLOADS}
+# Measured beside them, not one of the five: a 512-query chunk of a prefill
+# against a 2048-key cache with bottom-right causal alignment (the chunked-
+# prefill shape the cudnn-frontend merge-log notes time), bf16, head dim 128.
+EXTRA_WORKLOADS: Sequence[Workload] = (
+    Workload("chunk_512x2048_d128_bf16_bottom_right", "bf16", 2, 16, 16, 512, 2048, 128, True, "none", 6,
+             align="bottom_right"),
+)
+
+BY_NAME: Dict[str, Workload] = {w.name: w for w in (*WORKLOADS, *EXTRA_WORKLOADS)}
 
 
 def to_dtype(x: np.ndarray, dtype: str) -> torch.Tensor:
