@@ -316,21 +316,34 @@ void sdpa_twopass_kernel(const FwdArgs a) {
         }
     };
 
-    // Whether the staged bool mask tile removes every key of this wave's 32
-    // rows (a key-padding tail, for instance): such a tile adds nothing to
-    // the row sums and its probabilities are all zero, so its products and
-    // exponentials are skipped (the results are the same bits).
-    auto tile_dead = [&](const uint8_t* mt) SDPA_INLINE -> bool {
+    // What the staged bool mask tile does to this wave's 32 rows: DEAD, it
+    // removes every key (a key-padding tail, for instance): the tile adds
+    // nothing to the row sums and its probabilities are all zero, so its
+    // products and exponentials are skipped (the same bits as computing
+    // them); FULL, it keeps every key: the tile takes the unmasked code (the
+    // scale folded into one fma per exponent, one rounding fewer).
+    constexpr int TILE_DEAD = 1, TILE_FULL = 2;
+    auto tile_flags = [&](const uint8_t* mt) SDPA_INLINE -> int {
         if constexpr (MASK == MASK_BOOL && C::MLDS) {
             constexpr int NCH = 32 * C::MROWB / 16 / 64;  // 16-byte chunks per lane
             static_assert(NCH >= 1 && 32 * C::MROWB % 1024 == 0, "mask tile rows of a wave must split into lane chunks");
             const u32x4* c = reinterpret_cast<const u32x4*>(mt + 32 * wave * C::MROWB) + lane * NCH;
-            u32x4 x = c[0];
+            uint32_t any = 0u, zero_byte = 0u;
 #pragma unroll
-            for (int i = 1; i < NCH; ++i) x |= c[i];
-            return __builtin_amdgcn_ballot_w64((x[0] | x[1] | x[2] | x[3]) != 0u) == 0;
+            for (int i = 0; i < NCH; ++i) {
+                const u32x4 x = c[i];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t w = x[e];
+                    any |= w;
+                    zero_byte |= (w - 0x01010101u) & ~w & 0x80808080u;  // nonzero iff w has a zero byte
+                }
+            }
+            const bool dead = __builtin_amdgcn_ballot_w64(any != 0u) == 0;
+            const bool full = __builtin_amdgcn_ballot_w64(zero_byte != 0u) == 0;
+            return (dead ? TILE_DEAD : 0) | (full ? TILE_FULL : 0);
         } else {
-            return false;
+            return 0;
         }
     };
 
@@ -374,12 +387,14 @@ void sdpa_twopass_kernel(const FwdArgs a) {
         constexpr bool edge = decltype(edge_c)::value;
         const int k0 = t * BN;
         const int buf = t & 1;
-        if (tile_dead(mbuf(buf))) return;
+        const int flags = tile_flags(mbuf(buf));
+        if (flags & TILE_DEAD) return;
+        const bool plain = MASK == MASK_NONE || (flags & TILE_FULL);  // no key of the tile is masked
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
             const f32x16 acc = qk_block(kbuf(buf), kb);
             float sum = 0.0f;
-            if (MASK == MASK_NONE && !edge && a.scale_log2 > 0.0f) {
+            if (plain && !edge && a.scale_log2 > 0.0f) {
                 // max on the raw scores (the scale is positive), then one fma per exponent
                 float mx = acc[0];
 #pragma unroll
@@ -615,7 +630,9 @@ void sdpa_twopass_kernel(const FwdArgs a) {
     auto sweep2_tile = [&](int t, auto edge_c, int buf) SDPA_INLINE {
         constexpr bool edge = decltype(edge_c)::value;
         const int k0 = t * BN;
-        if (tile_dead(mbuf(buf))) {  // P = 0, O unchanged
+        const int flags = tile_flags(mbuf(buf));
+        const bool plain = MASK == MASK_NONE || (flags & TILE_FULL);  // no key of the tile is masked
+        if (flags & TILE_DEAD) {  // P = 0, O unchanged
             if constexpr (C::PSTAGE) {
 #pragma unroll
                 for (int i = 0; i < C::PSTB / 1024; ++i)
@@ -630,7 +647,7 @@ void sdpa_twopass_kernel(const FwdArgs a) {
         for (int kb = 0; kb < NKB; ++kb) {
             const f32x16 acc = qk_block(kbuf(buf), kb);
             float p[16];
-            if (MASK == MASK_NONE && !edge) {
+            if (plain && !edge) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) p[r] = fast_exp2(__builtin_fmaf(acc[r], a.scale_log2, -lse2));
             } else {
