@@ -117,10 +117,17 @@ def test_plan_reports_paths_and_tiles():
 
 
 def test_plan_picks_fused_for_few_tiles():
-    # decode-like: 100 queries x 1152 keys is 36 tiles of 64x64 per (b, h)
+    # decode-like: 100 queries x 1152 keys is 36 tiles of 64x64 per (b, h);
+    # a bool mask takes the fused path (32-row blocks x 64-key tiles), an
+    # additive one over more than 64 rows the two-pass path with 64-row
+    # blocks (96-row blocks would leave 92 of 192 rows empty)
     q, k = _z(16, 8, 100, 64), _z(16, 8, 1152, 64)
+    mb = torch.ones(16, 8, 100, 1152, dtype=torch.bool)
+    assert S.plan(q, k, k, mb) == ("fused", 4 * 18, 36)
     m = torch.zeros(16, 8, 100, 1152, dtype=torch.float16)
-    assert S.plan(q, k, k, m) == ("fused", 4 * 18, 36)  # 32-row blocks x 64-key tiles
+    assert S.plan(q, k, k, m) == ("twopass", 2 * 18, 36)
+    q64 = _z(16, 8, 64, 64)
+    assert S.plan(q64, k, k, m[:, :, :64]) == ("fused", 2 * 18, 18)
     q = _z(1, 2, 64, 32, dtype=torch.float32)
     assert S.plan(q, q, q, is_causal=True)[0] == "fused"
     # many tiles: two-pass
