@@ -192,7 +192,8 @@ __device__ __forceinline__ Work decode_block(int L, const FwdArgs& a) {
 // ---------------------------------------------------------------- masks and scores
 
 // Mask terms for the 16 keys lane (n, h) holds in one 32-key block starting
-// at key jblk: base-2 additive terms, or 0/1 keep flags for a bool mask.
+// at key jblk: base-2 additive terms (a bool mask gives 0 where it keeps the
+// key, -inf where it removes it).
 // VEC: the mask row is contiguous and 8-byte (bool) / 16-byte aligned, and
 // Skv is a multiple of 8, so each run of 8 keys is one load.
 template <typename T, int MASK, bool VEC>
@@ -207,7 +208,7 @@ __device__ __forceinline__ void load_mask16(const FwdArgs& a, rsrc_t mr, uint32_
             if constexpr (MASK == MASK_BOOL) {
                 const u32x2 w = ld64(mr, off);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) out[8 * c + e] = ((w[e >> 2] >> (8 * (e & 3))) & 0xffu) ? 1.0f : 0.0f;
+                for (int e = 0; e < 8; ++e) out[8 * c + e] = ((w[e >> 2] >> (8 * (e & 3))) & 0xffu) ? 0.0f : -INFINITY;
             } else if constexpr (sizeof(T) == 2) {
                 const u32x4 w = ld128(mr, off);
 #pragma unroll
@@ -229,7 +230,7 @@ __device__ __forceinline__ void load_mask16(const FwdArgs& a, rsrc_t mr, uint32_
             for (int e = 0; e < 8; ++e) {
                 const uint32_t off = pred(j + e < a.Skv, row_off + (uint32_t)((int64_t)(j + e) * a.m_s[3] * ME));
                 if constexpr (MASK == MASK_BOOL) {
-                    out[8 * c + e] = __builtin_amdgcn_raw_buffer_load_b8(mr, off, 0, 0) ? 1.0f : 0.0f;
+                    out[8 * c + e] = __builtin_amdgcn_raw_buffer_load_b8(mr, off, 0, 0) ? 0.0f : -INFINITY;
                 } else if constexpr (sizeof(T) == 2) {
                     out[8 * c + e] = Tr<T>::to_f(__builtin_amdgcn_raw_buffer_load_b16(mr, off, 0, 0)) * LOG2E;
                 } else {
@@ -249,9 +250,8 @@ __device__ __forceinline__ void scores16(const FwdArgs& a, const f32x16& acc, co
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         float x = acc[r] * a.scale_log2;
-        if constexpr (MASK == MASK_ADD) x = x + mv[r];
+        if constexpr (MASK != MASK_NONE) x = x + mv[r];  // + 0 keeps x, + -inf removes the key
         bool drop = false;
-        if constexpr (MASK == MASK_BOOL) drop = mv[r] == 0.0f;
         if (edge) {
             const int j = jblk + kk(hf, r);
             drop = drop || j >= a.Skv || (a.causal && j > qi + a.coff);

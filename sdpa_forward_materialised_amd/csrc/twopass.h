@@ -280,7 +280,8 @@ void sdpa_twopass_kernel(const FwdArgs a) {
         return acc;
     };
 
-    // mask terms of register r of block kb: keep flag (bool) or base-2 additive term
+    // base-2 additive mask term of register r of block kb (a bool mask gives
+    // 0 where it keeps the key, -inf where it removes it)
     auto mask_terms = [&](const uint8_t* mt, int k0, int kb, float* mv) SDPA_INLINE {
         if constexpr (MASK == MASK_NONE) {
             return;
@@ -292,7 +293,7 @@ void sdpa_twopass_kernel(const FwdArgs a) {
                 if constexpr (ME == 1) {
                     const u32x2 wv = *reinterpret_cast<const u32x2*>(base + jrel);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) mv[8 * c + e] = ((wv[e >> 2] >> (8 * (e & 3))) & 0xffu) ? 1.0f : 0.0f;
+                    for (int e = 0; e < 8; ++e) mv[8 * c + e] = ((wv[e >> 2] >> (8 * (e & 3))) & 0xffu) ? 0.0f : -INFINITY;
                 } else if constexpr (ME == 2) {
                     const u32x4 wv = *reinterpret_cast<const u32x4*>(base + jrel * 2);
 #pragma unroll
@@ -356,15 +357,10 @@ void sdpa_twopass_kernel(const FwdArgs a) {
         const int lim = edge ? min(a.Skv - 1 - jb, a.causal ? qi + a.coff - jb : 0x7fffffff) - 8 * hf : 0x7fffffff;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            float x;
+            // fma with a 0 term rounds like the plain product
+            const float x = MASK != MASK_NONE ? __builtin_fmaf(acc[r], a.scale_log2, mv[r]) : acc[r] * a.scale_log2;
             bool drop = false;
-            if constexpr (MASK == MASK_ADD) {
-                x = __builtin_fmaf(acc[r], a.scale_log2, mv[r]);
-            } else {
-                x = acc[r] * a.scale_log2;
-                if constexpr (MASK == MASK_BOOL) drop = mv[r] == 0.0f;
-            }
-            if (edge) drop = drop || kk(0, r) > lim;
+            if (edge) drop = kk(0, r) > lim;
             t[r] = drop ? -INFINITY : x;
         }
     };
