@@ -68,7 +68,7 @@ typedef struct {
 typedef enum {
     SDPA_OK = 0,
     SDPA_ERR_INVALID_ARG = 1, /* shapes, dtypes, null pointers, semantic rule broken */
-    SDPA_ERR_UNSUPPORTED = 2, /* valid call this build does not implement (layout, head dim) */
+    SDPA_ERR_UNSUPPORTED = 2, /* valid call the library does not implement (layout, head dim) */
     SDPA_ERR_HIP = 3          /* the HIP runtime reported an error at launch */
 } sdpa_status_t;
 
