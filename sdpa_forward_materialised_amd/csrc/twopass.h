@@ -848,20 +848,24 @@ void sdpa_twopass_kernel(const FwdArgs a) {
                                           0, 0);
 }
 
-#ifndef SDPA_TP_TN
-#define SDPA_TP_TN 64
-#endif
+// Keys per tile by mask kind: 32 with a bool mask, 64 otherwise. A bool mask
+// tile of 32 keys is more often wholly kept or wholly removed for a wave's
+// rows (key padding), which skips its decode or its arithmetic: the GQA
+// key-padding workload runs 166 -> 153 us (MI355X); without a mask or with an
+// additive one, 32-key tiles are slower (2k causal prefill 90 -> 119 us,
+// decode with an additive mask 32 -> 40 us).
+template <int MK>
+constexpr int tile_keys() { return MK == MASK_BOOL ? 32 : 64; }
 
 template <typename T, int D, int NW, bool VEC, bool NL>
 static int launch_twopass_mask(int mask_kind, const FwdArgs& a, hipStream_t s) {
-    constexpr int TN = SDPA_TP_TN;
     dim3 grid(a.n_blocks), block((NL ? NW : NW + 1) * 64);
     switch (mask_kind) {
-#define SDPA_TP_CASE(MK)                                                                              \
-    case MK:                                                                                          \
-        if constexpr (!NL || TwoPassCfg<T, D, NW, MK, VEC, TN, true>::PSTAGE) {                       \
-            hipLaunchKernelGGL((sdpa_twopass_kernel<T, D, NW, MK, VEC, TN, NL>), grid, block, 0, s, a); \
-            break;                                                                                    \
+#define SDPA_TP_CASE(MK)                                                                                          \
+    case MK:                                                                                                      \
+        if constexpr (!NL || TwoPassCfg<T, D, NW, MK, VEC, tile_keys<MK>(), true>::PSTAGE) {                       \
+            hipLaunchKernelGGL((sdpa_twopass_kernel<T, D, NW, MK, VEC, tile_keys<MK>(), NL>), grid, block, 0, s, a); \
+            break;                                                                                                \
         } else {                                                                                      \
             return (int)hipErrorInvalidValue;                                                         \
         }
@@ -879,8 +883,7 @@ static int launch_twopass_mask(int mask_kind, const FwdArgs& a, hipStream_t s) {
 // mask) tiles within the LDS of half a CU.
 template <typename T>
 static bool twopass_nl_ok_t(int D, int mask_kind) {
-    constexpr int TN = SDPA_TP_TN;
-#define SDPA_NL(DD, MK) TwoPassCfg<T, DD, 4, MK, true, TN, true>::PSTAGE
+#define SDPA_NL(DD, MK) TwoPassCfg<T, DD, 4, MK, true, tile_keys<MK>(), true>::PSTAGE
 #define SDPA_NL_D(DD)                                                                 \
     case DD:                                                                          \
         return mask_kind == MASK_NONE ? SDPA_NL(DD, MASK_NONE)                        \
