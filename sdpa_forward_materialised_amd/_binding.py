@@ -31,6 +31,9 @@ EXPORTS = ("sdpa_math_fwd", "sdpa_math_fwd_path", "sdpa_math_plan", "sdpa_math_l
            "sdpa_math_version", "sdpa_probe_fill", "sdpa_probe_copy")
 
 
+_I64x4 = ctypes.c_int64 * 4
+
+
 class SdpaTensor(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
                 ("sizes", ctypes.c_int64 * 4), ("strides", ctypes.c_int64 * 4)]
@@ -75,16 +78,11 @@ def _desc(t: Optional[torch.Tensor], ndim: int) -> Optional[SdpaTensor]:
         raise ValueError(f"expected at most {ndim} dims, got {t.dim()}")
     while t.dim() < ndim:  # right-align (a mask may have fewer dims)
         t = t.unsqueeze(0)
-    if t.dtype not in _DTYPES:
+    dt = _DTYPES.get(t.dtype)
+    if dt is None:
         raise ValueError(f"unsupported dtype {t.dtype}")
-    d = SdpaTensor()
-    d.data = t.data_ptr() if t.numel() > 0 else None
-    d.dtype = _DTYPES[t.dtype]
-    d.ndim = ndim
-    for i in range(ndim):
-        d.sizes[i] = t.shape[i]
-        d.strides[i] = t.stride(i)
-    return d
+    # one constructor call (field-by-field assignment costs several us per call)
+    return SdpaTensor(t.data_ptr() if t.numel() > 0 else None, dt, ndim, _I64x4(*t.shape), _I64x4(*t.stride()))
 
 
 def _ref(d: Optional[SdpaTensor]):
@@ -158,11 +156,18 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, attn_mask: Optional[t
     dq, dk, dv = _desc(q, 4), _desc(k, 4), _desc(v, 4)
     dm = _desc(attn_mask, 4)
     do, dp, dl = _desc(O, 4), _desc(P, 4), _desc(L, 3)
-    with torch.cuda.device(dev):
+    def launch():
         stream = torch.cuda.current_stream(dev).cuda_stream
-        rc = lib.sdpa_math_fwd_path(_ref(dq), _ref(dk), _ref(dv), _ref(dm), causal,
-                                    float(scale), int(bool(enable_gqa)), _ref(do), _ref(dp), _ref(dl),
-                                    ctypes.c_void_p(stream), PATHS[path])
+        return lib.sdpa_math_fwd_path(_ref(dq), _ref(dk), _ref(dv), _ref(dm), causal,
+                                      float(scale), int(bool(enable_gqa)), _ref(do), _ref(dp), _ref(dl),
+                                      ctypes.c_void_p(stream), PATHS[path])
+
+    # the launch goes to the tensors' device (made current only when it is not)
+    if dev.index == torch.cuda.current_device():
+        rc = launch()
+    else:
+        with torch.cuda.device(dev):
+            rc = launch()
     if rc != 0:
         _raise(rc, lib)
     return O, P, L
