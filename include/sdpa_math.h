@@ -132,6 +132,35 @@ sdpa_status_t sdpa_math_fwd_path(const sdpa_tensor_t* q, const sdpa_tensor_t* k,
                                  void* hip_stream, int path);
 
 /*
+ * sdpa_math_workspace_bytes — bytes of device workspace with which
+ * sdpa_math_fwd_ws splits the keys of this call over more workgroups (0: it
+ * would not split). Splitting pays when there are few query rows per key
+ * (decode, a short query chunk against a long key cache): each query block's
+ * keys are cut into ranges whose row statistics and float32 partial outputs
+ * go to the workspace, combined into the same O, P and LSE (the FlagOS-OP
+ * "P800 exact-P fast path" update: P = exp(S - LSE) with the row LSE folded
+ * from the ranges' statistics). Validates like sdpa_math_plan; *bytes is set
+ * to 0 on error.
+ */
+sdpa_status_t sdpa_math_workspace_bytes(const sdpa_tensor_t* q, const sdpa_tensor_t* k,
+                                        const sdpa_tensor_t* v, const sdpa_tensor_t* mask,
+                                        int is_causal, int enable_gqa, size_t* bytes);
+
+/*
+ * sdpa_math_fwd_ws — sdpa_math_fwd_path with a caller-owned device workspace
+ * (256-byte aligned, at least sdpa_math_workspace_bytes, or NULL). The
+ * library still allocates nothing; with a NULL or too small workspace the
+ * call runs unsplit. The workspace is scratch for this call only (its
+ * contents afterwards are unspecified); calls that share a workspace must be
+ * ordered on one stream.
+ */
+sdpa_status_t sdpa_math_fwd_ws(const sdpa_tensor_t* q, const sdpa_tensor_t* k,
+                               const sdpa_tensor_t* v, const sdpa_tensor_t* mask,
+                               int is_causal, float scale, int enable_gqa,
+                               sdpa_tensor_t* out, sdpa_tensor_t* probs, sdpa_tensor_t* lse,
+                               void* workspace, size_t workspace_bytes, void* hip_stream, int path);
+
+/*
  * sdpa_math_plan — validate the shapes exactly as sdpa_math_fwd would and
  * report, without launching anything:
  *   *path         the path SDPA_PATH_AUTO resolves to

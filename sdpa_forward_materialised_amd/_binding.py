@@ -27,7 +27,8 @@ CAUSAL_ALIGNMENTS = {"top_left": 1, "bottom_right": 2}  # the C ABI's is_causal 
 _DTYPES = {torch.float32: SDPA_F32, torch.float16: SDPA_F16, torch.bfloat16: SDPA_BF16,
            torch.bool: SDPA_BOOL}
 
-EXPORTS = ("sdpa_math_fwd", "sdpa_math_fwd_path", "sdpa_math_plan", "sdpa_math_last_error",
+EXPORTS = ("sdpa_math_fwd", "sdpa_math_fwd_path", "sdpa_math_fwd_ws", "sdpa_math_workspace_bytes",
+           "sdpa_math_plan", "sdpa_math_last_error",
            "sdpa_math_version", "sdpa_probe_fill", "sdpa_probe_copy")
 
 
@@ -40,6 +41,7 @@ class SdpaTensor(ctypes.Structure):
 
 
 _lib = None
+_WS_BYTES = {}  # workspace bytes per call signature (shapes, dtypes, mask layout, flags)
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -56,6 +58,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sdpa_math_fwd.argtypes = [T, T, T, T, ctypes.c_int, ctypes.c_float, ctypes.c_int, T, T, T, ctypes.c_void_p]
     lib.sdpa_math_fwd_path.restype = ctypes.c_int
     lib.sdpa_math_fwd_path.argtypes = lib.sdpa_math_fwd.argtypes + [ctypes.c_int]
+    lib.sdpa_math_fwd_ws.restype = ctypes.c_int
+    lib.sdpa_math_fwd_ws.argtypes = [T, T, T, T, ctypes.c_int, ctypes.c_float, ctypes.c_int, T, T, T,
+                                     ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int]
+    lib.sdpa_math_workspace_bytes.restype = ctypes.c_int
+    lib.sdpa_math_workspace_bytes.argtypes = [T, T, T, T, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
     lib.sdpa_math_plan.restype = ctypes.c_int
     lib.sdpa_math_plan.argtypes = [T, T, T, T, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int32),
                                    ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
@@ -156,11 +163,27 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, attn_mask: Optional[t
     dq, dk, dv = _desc(q, 4), _desc(k, 4), _desc(v, 4)
     dm = _desc(attn_mask, 4)
     do, dp, dl = _desc(O, 4), _desc(P, 4), _desc(L, 3)
+    # workspace for key ranges, when the library would split this call
+    # (the byte count depends on shapes and flags only: remembered per signature)
+    sig = (tuple(q.shape), tuple(k.shape), q.dtype, None if attn_mask is None else (tuple(attn_mask.shape),
+           attn_mask.dtype, tuple(attn_mask.stride())), causal, bool(enable_gqa),
+           os.environ.get("SDPA_MATH_SPLITS"), os.environ.get("SDPA_MATH_TP_WAVES"))
+    nbytes = _WS_BYTES.get(sig)
+    if nbytes is None:
+        n = ctypes.c_size_t(0)
+        rc = lib.sdpa_math_workspace_bytes(_ref(dq), _ref(dk), _ref(dv), _ref(dm), causal, int(bool(enable_gqa)),
+                                           ctypes.byref(n))
+        if rc != 0:
+            _raise(rc, lib)
+        nbytes = _WS_BYTES[sig] = n.value
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes > 0 else None
+
     def launch():
         stream = torch.cuda.current_stream(dev).cuda_stream
-        return lib.sdpa_math_fwd_path(_ref(dq), _ref(dk), _ref(dv), _ref(dm), causal,
-                                      float(scale), int(bool(enable_gqa)), _ref(do), _ref(dp), _ref(dl),
-                                      ctypes.c_void_p(stream), PATHS[path])
+        return lib.sdpa_math_fwd_ws(_ref(dq), _ref(dk), _ref(dv), _ref(dm), causal,
+                                    float(scale), int(bool(enable_gqa)), _ref(do), _ref(dp), _ref(dl),
+                                    None if ws is None else ctypes.c_void_p(ws.data_ptr()), nbytes,
+                                    ctypes.c_void_p(stream), PATHS[path])
 
     # the launch goes to the tensors' device (made current only when it is not)
     if dev.index == torch.cuda.current_device():

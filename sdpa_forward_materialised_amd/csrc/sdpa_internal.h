@@ -34,6 +34,15 @@ struct FwdArgs {
     int n_blocks;    // workgroups in the grid
     int keys_per_wave;  // fused path: key range of one wave
     int sched;       // workgroup order (causal: 1, 2, 3), see decode_block
+    // Key ranges (split over workgroups): n_splits ranges of split_tiles
+    // tiles (an even count) per query block; the two-pass kernels then run as
+    // a statistics launch, a probability launch and an output combine, with
+    // per-range row statistics (max, sum) and float32 partial O in the
+    // caller's workspace: ws_ml [n_splits][B*Hq][Sq], ws_o [n_splits][B*Hq][Sq][Dv].
+    int n_splits;
+    int split_tiles;
+    float2* ws_ml;
+    float* ws_o;
     // Byte extent of one (batch, head) slice of each tensor (< 2^31); the
     // kernels address every tensor through a buffer descriptor of this size.
     uint32_t q_ext, k_ext, v_ext, o_ext, p_ext, m_ext, l_ext;
@@ -49,6 +58,8 @@ struct Plan {
     int keys_per_wave;  // fused only
     int64_t tiles_per_bh;
     int64_t tiles_64;
+    int n_splits = 1;     // key ranges per query block (two-pass, with a workspace)
+    int split_tiles = 0;  // kernel tiles per key range (even)
 };
 
 // Kernel launchers, one translation unit per dtype. `vec` selects the

@@ -280,7 +280,47 @@ bool staged_layout(const Shape& sh, const sdpa_tensor_t* mask, const sdpa_tensor
     return true;
 }
 
-sdpa_status_t make_plan(const Shape& sh, bool causal, int64_t coff, int forced, bool vec, sdpa::Plan* p) {
+// Key ranges for short grids over long keys (two-pass, loader-wave kernels,
+// 16-byte layouts): with fewer than 256 blocks of 64 query rows and at least
+// 32 key tiles in the heaviest block, its keys are split into ranges of an
+// even number (at least 16) of tiles, towards 1024 workgroups. Each workgroup
+// pays a fixed start-up in each of the two launches, so shorter ranges or
+// fuller grids lose (measured on MI355X, bf16: 4x8 heads, 1 query, 32768 keys
+// 1003 -> 186 us; 1x32 heads, 16 queries, 16384 keys 375 -> 78 us; 2x16
+// heads, 64 queries, 8192 keys at D = 64 136 -> 36 us; 8x8 heads, 32
+// queries, 4096 keys 101 -> 43 us; but 100 queries x 1152 keys with 16x8
+// heads 32 -> 43 us and a 512-query chunk against 2048 keys 48 -> 50 us).
+// SDPA_MATH_SPLITS=n forces n ranges (1: none).
+void split_plan(const Shape& sh, bool causal, int64_t coff, int* n_splits, int* split_tiles) {
+    *n_splits = 1;
+    *split_tiles = 0;
+    const int64_t tn = sh.mask_kind == sdpa::MASK_BOOL ? 32 : 64;  // the kernels' keys per tile
+    const int64_t keys = causal ? std::max<int64_t>(0, std::min(sh.Skv, sh.Sq + coff)) : sh.Skv;
+    const int64_t max_tiles = cdiv(keys, tn);
+    const int64_t blocks = sh.B * sh.Hq * cdiv(sh.Sq, 64);
+    int64_t want = 1;
+    if (blocks < 256 && max_tiles >= 32) want = std::min(cdiv(1024, blocks), max_tiles / 16);
+    if (const char* e = std::getenv("SDPA_MATH_SPLITS")) want = std::max<int64_t>(1, std::atoll(e));
+    if (want < 2 || max_tiles < 2) return;
+    int64_t per = cdiv(max_tiles, want);
+    per += per & 1;
+    const int64_t n = cdiv(max_tiles, per);
+    if (n < 2) return;
+    *n_splits = (int)n;
+    *split_tiles = (int)per;
+}
+
+// Workspace bytes of a split plan: per range and row the (max, sum) pair,
+// then (256-byte aligned) the float32 partial O.
+size_t split_ws_ml_bytes(const Shape& sh, int n_splits) { return (size_t)n_splits * sh.B * sh.Hq * sh.Sq * 8; }
+size_t split_ws_bytes(const Shape& sh, int n_splits) {
+    if (n_splits <= 1) return 0;
+    const size_t ml = (split_ws_ml_bytes(sh, n_splits) + 255) / 256 * 256;
+    return ml + (size_t)n_splits * sh.B * sh.Hq * sh.Sq * sh.Dv * 4;
+}
+
+sdpa_status_t make_plan(const Shape& sh, bool causal, int64_t coff, int forced, bool vec, sdpa::Plan* p,
+                        bool allow_split = false) {
     p->tiles_64 = count_tiles(sh.Sq, sh.Skv, causal, 64, coff);
     int fw = 0, fk = 0;
     const bool fused_ok = fused_available() && fused_config(sh, causal, coff, &fw, &fk);
@@ -334,6 +374,10 @@ sdpa_status_t make_plan(const Shape& sh, bool causal, int64_t coff, int forced, 
         }
         if ((sh.dtype == SDPA_F32 && sh.D == 128 && p->waves == 3) || !vec) p->waves = 2;
         p->keys_per_wave = 0;
+        if (allow_split && vec && p->waves != 4) {
+            split_plan(sh, causal, coff, &p->n_splits, &p->split_tiles);
+            if (p->n_splits > 1) p->waves = 2;  // key ranges run on the two-wave loader kernel
+        }
         p->q_rows = 32 * p->waves;
     }
     p->n_qblk = (int)cdiv(sh.Sq, p->q_rows);
@@ -353,7 +397,7 @@ void fill_strides3(const sdpa_tensor_t* t, int64_t* s) {
 
 sdpa_status_t run(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_tensor_t* v, const sdpa_tensor_t* mask,
                   int is_causal, float scale, int enable_gqa, sdpa_tensor_t* out, sdpa_tensor_t* probs,
-                  sdpa_tensor_t* lse, void* stream, int path) {
+                  sdpa_tensor_t* lse, void* stream, int path, void* ws = nullptr, size_t ws_bytes = 0) {
     g_last_error.clear();
     if (path < SDPA_PATH_AUTO || path > SDPA_PATH_TWOPASS) return fail(SDPA_ERR_INVALID_ARG, "unknown path %d", path);
     Shape sh;
@@ -364,7 +408,9 @@ sdpa_status_t run(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_ten
     if (sh.B * sh.Hq * sh.Sq == 0) return SDPA_OK;
     const bool vec = staged_layout(sh, mask, out, probs);
     sdpa::Plan plan;
-    if ((st = make_plan(sh, is_causal != 0, causal_offset(sh, is_causal), path, vec, &plan))) return st;
+    if ((st = make_plan(sh, is_causal != 0, causal_offset(sh, is_causal), path, vec, &plan, ws != nullptr))) return st;
+    if (plan.n_splits > 1 && (reinterpret_cast<uintptr_t>(ws) % 256 != 0 || ws_bytes < split_ws_bytes(sh, plan.n_splits)))
+        if ((st = make_plan(sh, is_causal != 0, causal_offset(sh, is_causal), path, vec, &plan))) return st;  // no room: unsplit
 
     sdpa::FwdArgs a;
     std::memset(&a, 0, sizeof a);
@@ -399,6 +445,12 @@ sdpa_status_t run(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_ten
     a.scale_log2 = scale * 1.4426950408889634f;
     a.n_qblk = plan.n_qblk;
     a.n_blocks = (int)plan.grid;
+    a.n_splits = plan.n_splits;
+    a.split_tiles = plan.split_tiles;
+    if (plan.n_splits > 1) {
+        a.ws_ml = static_cast<float2*>(ws);
+        a.ws_o = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + (split_ws_ml_bytes(sh, plan.n_splits) + 255) / 256 * 256);
+    }
     a.keys_per_wave = plan.keys_per_wave;
     // Workgroup order (decode_block). Non-causal: head-major, each XCD taking
     // consecutive blocks (shared K/V in its L2). Causal: when the grid is
@@ -455,9 +507,9 @@ sdpa_status_t run(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_ten
     if (err != 0)
         return fail(SDPA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(static_cast<hipError_t>(err)));
     if (std::getenv("SDPA_MATH_DEBUG"))
-        std::fprintf(stderr, "sdpa_math: path=%s waves=%d vec=%d sched=%d grid=%lld tiles/bh=%lld tiles64/bh=%lld\n",
+        std::fprintf(stderr, "sdpa_math: path=%s waves=%d vec=%d sched=%d splits=%d grid=%lld tiles/bh=%lld tiles64/bh=%lld\n",
                      plan.path == SDPA_PATH_FUSED ? "fused" : "twopass", plan.waves, vec ? 1 : 0, a.sched,
-                     (long long)plan.grid,
+                     plan.n_splits, (long long)plan.grid,
                      (long long)plan.tiles_per_bh, (long long)plan.tiles_64);
     return SDPA_OK;
 }
@@ -493,6 +545,31 @@ sdpa_status_t sdpa_math_plan(const sdpa_tensor_t* q, const sdpa_tensor_t* k, con
     if (path) *path = plan.path;
     if (tiles_per_bh) *tiles_per_bh = plan.tiles_per_bh;
     if (tiles_64) *tiles_64 = plan.tiles_64;
+    return SDPA_OK;
+}
+
+sdpa_status_t sdpa_math_fwd_ws(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_tensor_t* v,
+                               const sdpa_tensor_t* mask, int is_causal, float scale, int enable_gqa,
+                               sdpa_tensor_t* out, sdpa_tensor_t* probs, sdpa_tensor_t* lse, void* workspace,
+                               size_t workspace_bytes, void* hip_stream, int path) {
+    return run(q, k, v, mask, is_causal, scale, enable_gqa, out, probs, lse, hip_stream, path, workspace,
+               workspace_bytes);
+}
+
+sdpa_status_t sdpa_math_workspace_bytes(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_tensor_t* v,
+                                        const sdpa_tensor_t* mask, int is_causal, int enable_gqa, size_t* bytes) {
+    g_last_error.clear();
+    if (!bytes) return fail(SDPA_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = 0;
+    Shape sh;
+    sdpa_status_t st = validate_inputs(q, k, v, mask, is_causal, enable_gqa, &sh);
+    if (st) return st;
+    if (sh.B * sh.Hq * sh.Sq == 0) return SDPA_OK;
+    sdpa::Plan plan;
+    if ((st = make_plan(sh, is_causal != 0, causal_offset(sh, is_causal), SDPA_PATH_AUTO,
+                        staged_layout(sh, mask, nullptr, nullptr), &plan, true)))
+        return st;
+    *bytes = split_ws_bytes(sh, plan.n_splits);
     return SDPA_OK;
 }
 

@@ -108,10 +108,15 @@ struct TwoPassCfg {
 #define SDPA_TP_WPE(NW) ((NW) >= 4 ? 3 : 2)
 #endif
 
-template <typename T, int D, int NW, int MASK, bool VEC, int TN, bool NL>
+// SPL: 0 the whole call; with key ranges (loader-wave kernels only) 1 runs
+// sweep 1 over this workgroup's range and writes its rows' (max, sum), 2
+// folds every range's statistics into the LSE, runs sweep 2 over its range
+// (final P) and writes a float32 partial O.
+template <typename T, int D, int NW, int MASK, bool VEC, int TN, bool NL, int SPL = 0>
 __global__ __attribute__((amdgpu_flat_work_group_size((NL ? NW : NW + 1) * 64, (NL ? NW : NW + 1) * 64),
                           amdgpu_waves_per_eu(NL ? 2 : SDPA_TP_WPE(NW))))
 void sdpa_twopass_kernel(const FwdArgs a) {
+    static_assert(SPL == 0 || !NL, "key ranges run on the loader-wave kernels");
     using C = TwoPassCfg<T, D, NW, MASK, VEC, TN, NL>;
     static_assert(!NL || C::PSTAGE, "without a loader wave the probability stores must be staged");
     static_assert(C::LDS_BYTES <= 160 * 1024, "tile buffers exceed the 160 KB LDS of a compute unit");
@@ -138,11 +143,15 @@ void sdpa_twopass_kernel(const FwdArgs a) {
     const int n = lane & 31;
     const int hf = lane >> 5;
 
-    const Work w = decode_block(blockIdx.x, a);
+    const Work w = decode_block(SPL ? (int)blockIdx.x / a.n_splits : (int)blockIdx.x, a);
     const int hk = w.hq / a.group;
     const int q0 = w.qblk * QB;
     const int kend = a.causal ? min(a.Skv, max(0, q0 + QB + a.coff)) : a.Skv;
     const int ntiles = (kend + BN - 1) / BN;
+    // this workgroup's tiles [t_lo, t_hi) (t_lo even: tile t stays in buffer t & 1)
+    const int split = SPL ? (int)blockIdx.x % a.n_splits : 0;
+    const int t_lo = SPL ? min(ntiles, split * a.split_tiles) : 0;
+    const int t_hi = SPL ? min(ntiles, t_lo + a.split_tiles) : ntiles;
 
     const rsrc_t kr = make_rsrc(static_cast<const T*>(a.k) + w.b * a.k_s[0] + hk * a.k_s[1], a.k_ext);
     const rsrc_t vr = make_rsrc(static_cast<const T*>(a.v) + w.b * a.v_s[0] + hk * a.v_s[1], a.v_ext);
@@ -196,37 +205,41 @@ void sdpa_twopass_kernel(const FwdArgs a) {
         };
     // ======================================================== loader wave
     if (!NL && wave == NW) {
-        // sweep 1: K (+ mask)
-        if (ntiles > 0) {
-            dma_k(kbuf(0), 0, 0, 1);
-            dma_m(0, 0, 0, 1);
-            wait_vmem();
-        }
-        __syncthreads();
-        for (int t = 0; t < ntiles; ++t) {
-            if (t + 1 < ntiles) {
-                dma_k(kbuf((t + 1) & 1), t + 1, 0, 1);
-                dma_m(t + 1, (t + 1) & 1, 0, 1);
+        if constexpr (SPL != 2) {
+            // sweep 1: K (+ mask)
+            if (t_hi > t_lo) {
+                dma_k(kbuf(0), t_lo, 0, 1);
+                dma_m(t_lo, 0, 0, 1);
                 wait_vmem();
             }
             __syncthreads();
+            for (int t = t_lo; t < t_hi; ++t) {
+                if (t + 1 < t_hi) {
+                    dma_k(kbuf((t + 1) & 1), t + 1, 0, 1);
+                    dma_m(t + 1, (t + 1) & 1, 0, 1);
+                    wait_vmem();
+                }
+                __syncthreads();
+            }
         }
-        // sweep 2: K, V (+ mask)
-        if (ntiles > 0) {
-            dma_k(kbuf(0), 0, 0, 1);
-            dma_v(vbuf(0), 0, 0, 1);
-            dma_m(0, 0, 0, 1);
-            wait_vmem();
-        }
-        __syncthreads();
-        for (int t = 0; t < ntiles; ++t) {
-            if (t + 1 < ntiles) {
-                dma_k(kbuf((t + 1) & 1), t + 1, 0, 1);
-                dma_v(vbuf((t + 1) & 1), t + 1, 0, 1);
-                dma_m(t + 1, (t + 1) & 1, 0, 1);
+        if constexpr (SPL != 1) {
+            // sweep 2: K, V (+ mask)
+            if (t_hi > t_lo) {
+                dma_k(kbuf(0), t_lo, 0, 1);
+                dma_v(vbuf(0), t_lo, 0, 1);
+                dma_m(t_lo, 0, 0, 1);
                 wait_vmem();
             }
             __syncthreads();
+            for (int t = t_lo; t < t_hi; ++t) {
+                if (t + 1 < t_hi) {
+                    dma_k(kbuf((t + 1) & 1), t + 1, 0, 1);
+                    dma_v(vbuf((t + 1) & 1), t + 1, 0, 1);
+                    dma_m(t + 1, (t + 1) & 1, 0, 1);
+                    wait_vmem();
+                }
+                __syncthreads();
+            }
         }
         return;
     }
@@ -376,6 +389,9 @@ void sdpa_twopass_kernel(const FwdArgs a) {
     const int dlast = qw + 31 + a.coff;  // causal: last key the wave's last row keeps
     const int t_comp = !live ? 0 : a.causal ? (dlast < 0 ? 0 : min(ntiles, dlast / BN + 1)) : ntiles;
     const int t_fast = min(t_comp, a.causal ? min(a.Skv / BN, max(0, qw + a.coff + 1) / BN) : a.Skv / BN);
+    // the same split within this workgroup's tiles
+    const int tf = min(max(t_fast, t_lo), t_hi);
+    const int tc = min(max(t_comp, t_lo), t_hi);
 
     // ---------------- sweep 1: row maximum and sum (base 2)
     float m_run = -INFINITY, l_run = 0.0f;
@@ -481,12 +497,13 @@ void sdpa_twopass_kernel(const FwdArgs a) {
     };
     const bool pipe1 = MASK == MASK_NONE && a.scale_log2 > 0.0f;
 
-    load1(0);
-    end_tile();  // tile 0 staged
+    if constexpr (SPL != 2) {
+    load1(t_lo);
+    end_tile();  // tile t_lo staged
     {
-        int t = 0;
-        if (pipe1 && t_fast > 0) {
-            load1(1);
+        int t = t_lo;
+        if (pipe1 && tf > t_lo) {
+            load1(t_lo + 1);
             f32x16 pend = qk_block(kbuf(0), 0);
 #pragma unroll
             for (int kb = 1; kb < NKB; ++kb) pend = qk_fold(kbuf(0), kb, pend);
@@ -500,24 +517,24 @@ void sdpa_twopass_kernel(const FwdArgs a) {
                 for (int kb = 0; kb < NKB; ++kb) pend = qk_fold(kt, kb, pend);
                 end_tile();
             };
-            for (t = 1; t + 1 < t_fast; t += 2) {
+            for (t = t_lo + 1; t + 1 < tf; t += 2) {
                 fast1(t, std::integral_constant<int, 1>{});
                 fast1(t + 1, std::integral_constant<int, 0>{});
             }
-            if (t < t_fast) fast1(t++, std::integral_constant<int, 1>{});
+            if (t < tf) fast1(t++, std::integral_constant<int, 1>{});
             fold_fast(pend);
         }
-        for (; t < t_fast; ++t) {
+        for (; t < tf; ++t) {
             load1(t + 1);
             sweep1_tile(t, std::false_type{});
             end_tile();
         }
-        for (; t < t_comp; ++t) {
+        for (; t < tc; ++t) {
             load1(t + 1);
             sweep1_tile(t, std::true_type{});
             end_tile();
         }
-        for (; t < ntiles; ++t) {
+        for (; t < t_hi; ++t) {
             load1(t + 1);
             end_tile();
         }
@@ -529,6 +546,27 @@ void sdpa_twopass_kernel(const FwdArgs a) {
         if (mn != -INFINITY) {
             l_run = l_run * fast_exp2(m_run - mn) + l_o * fast_exp2(m_o - mn);
             m_run = mn;
+        }
+    }
+    }
+    // row index of this lane in the key-range workspace
+    const int64_t ws_row = ((int64_t)split * a.B * a.Hq + (int64_t)w.b * a.Hq + w.hq) * a.Sq + (row_ok ? qi : 0);
+    if constexpr (SPL == 1) {  // this range's (max, sum) of each row, base 2
+        if (row_ok && hf == 0) a.ws_ml[ws_row] = float2{m_run, l_run};
+        return;
+    }
+    if constexpr (SPL == 2) {  // fold every range's statistics, in range order (the same bits in each range)
+        const int64_t stride = (int64_t)a.B * a.Hq * a.Sq;
+        const int64_t r0 = ws_row - (int64_t)split * stride;
+        m_run = -INFINITY;
+        l_run = 0.0f;
+        for (int s2 = 0; s2 < a.n_splits; ++s2) {
+            const float2 st = row_ok ? a.ws_ml[r0 + s2 * stride] : float2{-INFINITY, 0.0f};
+            const float mn = fmaxf(m_run, st.x);
+            if (mn != -INFINITY) {
+                l_run = l_run * fast_exp2(m_run - mn) + st.y * fast_exp2(st.x - mn);
+                m_run = mn;
+            }
         }
     }
     const bool dead = (m_run == -INFINITY);
@@ -789,10 +827,10 @@ void sdpa_twopass_kernel(const FwdArgs a) {
             pend_k0 = -1;
         }
     };
-    load2(0);
-    end_tile();  // tile 0 staged
+    load2(t_lo);
+    end_tile();  // tile t_lo staged
     {
-        int t = 0;
+        int t = t_lo;
         auto fast2 = [&](int tt, int buf) SDPA_INLINE {
             flush();
             load2(tt + 1);
@@ -802,12 +840,12 @@ void sdpa_twopass_kernel(const FwdArgs a) {
             pend_edge = false;
             end_tile();
         };
-        for (; t + 1 < t_fast; t += 2) {  // in pairs: constant buffers, as in sweep 1
+        for (; t + 1 < tf; t += 2) {  // in pairs: constant buffers, as in sweep 1
             fast2(t, 0);
             fast2(t + 1, 1);
         }
-        if (t < t_fast) fast2(t++, 0);
-        for (; t < t_comp; ++t) {
+        if (t < tf) fast2(t++, 0);
+        for (; t < tc; ++t) {
             flush();
             load2(t + 1);
             sweep2_tile(t, std::true_type{}, t & 1);
@@ -819,17 +857,29 @@ void sdpa_twopass_kernel(const FwdArgs a) {
         // whole tiles above this wave's diagonal: P is zero, O unchanged
         // (without a loader wave the zeros are written after the last tile)
         const int t_zero = t;
-        for (; t < ntiles; ++t) {
+        for (; t < t_hi; ++t) {
             load2(t + 1);
             if constexpr (!NL) zero_tile(t);
             end_tile();
         }
         if constexpr (NL)
-            for (int tz = t_zero; tz < ntiles; ++tz) zero_tile(tz);
+            for (int tz = t_zero; tz < t_hi; ++tz) zero_tile(tz);
     }
 
     // ---------------- O: lane (n, h) holds O[qi][32d + 8h ..+8) and [32d + 16 + 8h ..+8)
-    {
+    if constexpr (SPL == 2) {  // float32 partial O of this key range
+        float* const orow = a.ws_o + ws_row * D;
+#pragma unroll
+        for (int d = 0; d < ND; ++d)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                for (int e4 = 0; e4 < 2; ++e4)
+                    if (row_ok)
+                        *reinterpret_cast<f32x4*>(orow + 32 * d + 16 * h2 + 8 * hf + 4 * e4) =
+                            f32x4{oacc[d][8 * h2 + 4 * e4], oacc[d][8 * h2 + 4 * e4 + 1], oacc[d][8 * h2 + 4 * e4 + 2],
+                                  oacc[d][8 * h2 + 4 * e4 + 3]};
+    } else {
         const uint32_t orow_off = (uint32_t)((int64_t)(row_ok ? qi : 0) * a.o_s[2] * SZ);
 #pragma unroll
         for (int d = 0; d < ND; ++d) {
@@ -842,7 +892,9 @@ void sdpa_twopass_kernel(const FwdArgs a) {
     }
 
     // ---------------- causal: keys past this workgroup's last row are zero
-    zero_rows<T, VEC>(pr, a.p_s[2], qw, a.Sq, ntiles * BN, a.Skv, lane);
+    // (with key ranges: written by the last range; LSE by the first)
+    if (SPL == 0 || split == a.n_splits - 1) zero_rows<T, VEC>(pr, a.p_s[2], qw, a.Sq, ntiles * BN, a.Skv, lane);
+    if (SPL == 0 || split == 0)
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, dead ? -INFINITY : lse2 * LN2), lr,
                                           pred(row_ok && hf == 0, (uint32_t)((int64_t)(row_ok ? qi : 0) * a.l_s[2] * 4)),
                                           0, 0);
@@ -878,6 +930,63 @@ static int launch_twopass_mask(int mask_kind, const FwdArgs& a, hipStream_t s) {
     return (int)hipGetLastError();
 }
 
+// Output of a call split into key ranges: the ranges' float32 partial O of
+// each row summed in range order and rounded once to the output dtype. One
+// thread per 8 consecutive columns of a row (16-byte aligned output rows).
+template <typename T>
+__global__ __launch_bounds__(256) void sdpa_split_combine_kernel(const FwdArgs a, int D) {
+    const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
+    const int cpr = D / 8;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= rows * cpr) return;
+    const int64_t row = i / cpr;
+    const int c = (int)(i - row * cpr) * 8;
+    float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int s2 = 0; s2 < a.n_splits; ++s2) {
+        const float* src = a.ws_o + ((int64_t)s2 * rows + row) * D + c;
+        const f32x4 u0 = *reinterpret_cast<const f32x4*>(src);
+        const f32x4 u1 = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[e] += u0[e];
+            x[4 + e] += u1[e];
+        }
+    }
+    const int q = (int)(row % a.Sq);
+    const int64_t bh = row / a.Sq;
+    const int h = (int)(bh % a.Hq);
+    const int b = (int)(bh / a.Hq);
+    T* o = static_cast<T*>(a.o) + b * a.o_s[0] + h * a.o_s[1] + (int64_t)q * a.o_s[2] + c;
+    if constexpr (sizeof(T) == 2) {
+        *reinterpret_cast<u32x4*>(o) = __builtin_bit_cast(u32x4, Tr<T>::cvt8(x));
+    } else {
+        *reinterpret_cast<f32x4*>(o) = f32x4{x[0], x[1], x[2], x[3]};
+        *reinterpret_cast<f32x4*>(o + 4) = f32x4{x[4], x[5], x[6], x[7]};
+    }
+}
+
+// A call split into key ranges (two compute waves and a loader wave,
+// 16-byte layouts): statistics launch, probability launch, output combine.
+template <typename T, int D>
+static int launch_twopass_split(int mask_kind, const FwdArgs& a, hipStream_t s) {
+    dim3 grid((unsigned)a.n_blocks * (unsigned)a.n_splits), block(3 * 64);
+    switch (mask_kind) {
+#define SDPA_SPLIT_CASE(MK)                                                                                      \
+    case MK:                                                                                                     \
+        hipLaunchKernelGGL((sdpa_twopass_kernel<T, D, 2, MK, true, tile_keys<MK>(), false, 1>), grid, block, 0, s, a); \
+        hipLaunchKernelGGL((sdpa_twopass_kernel<T, D, 2, MK, true, tile_keys<MK>(), false, 2>), grid, block, 0, s, a); \
+        break;
+        SDPA_SPLIT_CASE(MASK_NONE)
+        SDPA_SPLIT_CASE(MASK_BOOL)
+        SDPA_SPLIT_CASE(MASK_ADD)
+#undef SDPA_SPLIT_CASE
+        default: return (int)hipErrorInvalidValue;
+    }
+    const int64_t n = (int64_t)a.B * a.Hq * a.Sq * (D / 8);
+    hipLaunchKernelGGL(sdpa_split_combine_kernel<T>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a, D);
+    return (int)hipGetLastError();
+}
+
 // Whether four compute waves without a loader wave can run for this shape:
 // the staged probability tiles of four waves must fit next to the K/V (and
 // mask) tiles within the LDS of half a CU.
@@ -906,6 +1015,15 @@ static bool twopass_nl_ok_t(int D, int mask_kind) {
 template <typename T>
 static int launch_twopass_t(int D, int mask_kind, int waves, bool vec, const FwdArgs& a, void* stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (a.n_splits > 1) {
+        if (!vec || waves != 2) return (int)hipErrorInvalidValue;
+        switch (D) {
+            case 32: return launch_twopass_split<T, 32>(mask_kind, a, s);
+            case 64: return launch_twopass_split<T, 64>(mask_kind, a, s);
+            case 128: return launch_twopass_split<T, 128>(mask_kind, a, s);
+            default: return (int)hipErrorInvalidValue;
+        }
+    }
 #define SDPA_TP_DIM(DD)                                                                      \
     case DD:                                                                                 \
         if (!vec) return launch_twopass_mask<T, DD, 2, false, false>(mask_kind, a, s);       \

@@ -171,3 +171,31 @@ def test_causal_codes_validated():
         rc = lib.sdpa_math_plan(B._ref(d), B._ref(d), B._ref(d), None, code, 0, *(ctypes.byref(x) for x in out))
         assert rc == want, (code, S.last_error())
     assert "is_causal" in (S.last_error() or "")
+
+
+def _ws_bytes(q, k, mask=None, causal=0, gqa=0):
+    lib = S.load_library()
+    n = ctypes.c_size_t(123)
+    rc = lib.sdpa_math_workspace_bytes(B._ref(B._desc(q, 4)), B._ref(B._desc(k, 4)), B._ref(B._desc(k, 4)),
+                                       B._ref(B._desc(mask, 4)), causal, gqa, ctypes.byref(n))
+    return rc, n.value
+
+
+def test_workspace_query(monkeypatch):
+    monkeypatch.delenv("SDPA_MATH_SPLITS", raising=False)
+    # full grids or short key ranges: no split, no workspace
+    assert _ws_bytes(_z(2, 16, 2048, 128, dtype=torch.bfloat16), _z(2, 16, 2048, 128, dtype=torch.bfloat16),
+                     causal=1) == (0, 0)
+    q, k = _z(16, 8, 100, 64), _z(16, 8, 1152, 64)
+    assert _ws_bytes(q, k, torch.zeros(16, 8, 100, 1152, dtype=torch.float16)) == (0, 0)
+    # one query row against 32768 keys, 32 heads: ranges of 16 tiles, 32 of them
+    q, k = _z(4, 8, 1, 128, dtype=torch.bfloat16), _z(4, 8, 32768, 128, dtype=torch.bfloat16)
+    rc, n = _ws_bytes(q, k)
+    rows = 4 * 8 * 1
+    ml = -(-(32 * rows * 8) // 256) * 256
+    assert rc == 0 and n == ml + 32 * rows * 128 * 4
+    # forced ranges; a semantic error leaves the count at 0
+    monkeypatch.setenv("SDPA_MATH_SPLITS", "3")
+    assert _ws_bytes(_z(1, 2, 256, 64), _z(1, 2, 640, 64))[1] > 0  # two-pass shape (the fused path never splits)
+    rc, n = _ws_bytes(_z(1, 3, 8, 64), _z(1, 2, 8, 64))
+    assert rc == 1 and n == 0

@@ -139,6 +139,40 @@ def test_bottom_right_causal_wave_counts(waves, monkeypatch):
     _check(c, "twopass", label=f"bottom-right waves={waves}")
 
 
+# Keys split into ranges over workgroups (statistics launch, probability
+# launch, output combine; forced range counts): causal with empty ranges in
+# the light blocks, bottom-right chunk, additive-mask decode rows, bool key
+# padding, float32 ragged causal, grouped heads.
+SPLIT_CASES = [
+    ("bf16-d128-causal-296", dict(seed=170, dtype="bf16", B=1, Hq=2, Hkv=2, Sq=296, Skv=296, D=128, causal=True), None),
+    ("bf16-d128-chunk-br", dict(seed=171, dtype="bf16", B=1, Hq=2, Hkv=2, Sq=130, Skv=520, D=128, causal=True),
+     "bottom_right"),
+    ("f16-d64-decode-add", dict(seed=172, dtype="f16", B=2, Hq=4, Hkv=4, Sq=100, Skv=1152, D=64, mask="add", p=0.1),
+     None),
+    ("f16-d32-keypad", dict(seed=173, dtype="f16", B=2, Hq=2, Hkv=1, Sq=70, Skv=640, D=32, mask="bool",
+                            mask_shape=(2, 1, 1, 640), p=0.4), None),
+    ("f32-d64-causal-ragged", dict(seed=174, dtype="f32", B=1, Hq=2, Hkv=2, Sq=77, Skv=136, D=64, causal=True), None),
+    ("bf16-d64-gqa", dict(seed=175, dtype="bf16", B=1, Hq=4, Hkv=2, Sq=64, Skv=1000, D=64), None),
+]
+
+
+@pytest.mark.parametrize("splits", [2, 3])
+@pytest.mark.parametrize("label,spec,align", SPLIT_CASES, ids=[s[0] for s in SPLIT_CASES])
+def test_key_ranges(label, spec, align, splits, monkeypatch):
+    monkeypatch.setenv("SDPA_MATH_SPLITS", str(splits))
+    c = W.make_case(**spec)
+    if align:
+        c["align"] = align
+    _check(c, "twopass", label=f"{label} splits={splits}")
+
+
+def test_key_ranges_chosen_by_default(monkeypatch):
+    # few query rows against many keys: the default plan splits the keys
+    monkeypatch.delenv("SDPA_MATH_SPLITS", raising=False)
+    c = W.make_case(seed=176, dtype="bf16", B=1, Hq=2, Hkv=2, Sq=3, Skv=4096, D=64)
+    _check(c, "auto", label="default key ranges")
+
+
 # Every compute-wave count the kernel is built for (a tuning knob read at each
 # call): 2 or 3 compute waves plus a loader wave, or 4 compute waves sharing
 # the tile loads (where their staged tiles fit in LDS; otherwise the request
