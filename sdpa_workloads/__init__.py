@@ -80,6 +80,8 @@ WORKLOADS: Sequence[Workload] = (
 EXTRA_WORKLOADS: Sequence[Workload] = (
     Workload("chunk_512x2048_d128_bf16_bottom_right", "bf16", 2, 16, 16, 512, 2048, 128, True, "none", 6,
              align="bottom_right"),
+    # one query row per head against a long key cache: the keys are split over workgroups
+    Workload("decode_1x32768_d128_bf16", "bf16", 4, 8, 8, 1, 32768, 128, False, "none", 7),
 )
 
 BY_NAME: Dict[str, Workload] = {w.name: w for w in (*WORKLOADS, *EXTRA_WORKLOADS)}
