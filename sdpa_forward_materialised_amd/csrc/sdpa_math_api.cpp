@@ -283,10 +283,10 @@ bool staged_layout(const Shape& sh, const sdpa_tensor_t* mask, const sdpa_tensor
 // Key ranges for short grids over long keys (two-pass, loader-wave kernels,
 // 16-byte layouts): with fewer than 256 blocks of 64 query rows and at least
 // 32 key tiles in the heaviest block, its keys are split into ranges of an
-// even number (at least 16) of tiles, towards 1024 workgroups. Each workgroup
+// even number (at least 16) of tiles, towards 512 workgroups. Each workgroup
 // pays a fixed start-up in each of the two launches, so shorter ranges or
 // fuller grids lose (measured on MI355X, bf16: 4x8 heads, 1 query, 32768 keys
-// 1003 -> 186 us; 1x32 heads, 16 queries, 16384 keys 375 -> 78 us; 2x16
+// 1003 -> 154 us; 1x32 heads, 16 queries, 16384 keys 375 -> 78 us; 2x16
 // heads, 64 queries, 8192 keys at D = 64 136 -> 36 us; 8x8 heads, 32
 // queries, 4096 keys 101 -> 43 us; but 100 queries x 1152 keys with 16x8
 // heads 32 -> 43 us and a 512-query chunk against 2048 keys 48 -> 50 us).
@@ -299,7 +299,7 @@ void split_plan(const Shape& sh, bool causal, int64_t coff, int* n_splits, int* 
     const int64_t max_tiles = cdiv(keys, tn);
     const int64_t blocks = sh.B * sh.Hq * cdiv(sh.Sq, 64);
     int64_t want = 1;
-    if (blocks < 256 && max_tiles >= 32) want = std::min(cdiv(1024, blocks), max_tiles / 16);
+    if (blocks < 256 && max_tiles >= 32) want = std::min(cdiv(512, blocks), max_tiles / 16);
     if (const char* e = std::getenv("SDPA_MATH_SPLITS")) want = std::max<int64_t>(1, std::atoll(e));
     if (want < 2 || max_tiles < 2) return;
     int64_t per = cdiv(max_tiles, want);
