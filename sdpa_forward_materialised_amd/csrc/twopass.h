@@ -12,8 +12,9 @@
 // P·V is accumulated in the pass that writes it.
 //
 // Workgroup = NW compute waves (32 query rows each, one (batch, query head))
-// plus one loader wave. The loader wave copies each 64-key tile of K (and of
-// V and the mask in sweep 2) from global memory straight into LDS with
+// plus one loader wave (or four compute waves that share the loads, NL). The
+// loader wave copies each tile of K (64 keys; 32 with a bool mask), and of V
+// and the mask in sweep 2, from global memory straight into LDS with
 // buffer-to-LDS loads, double-buffered, one barrier per tile. The compute
 // waves issue no global loads inside the loops, so their probability stores
 // are never waited for: on this hardware a wait for a load also waits for
@@ -21,7 +22,8 @@
 // traffic. The LDS tile layouts make every operand read a per-lane base plus
 // a constant offset, free of bank conflicts; the V^T operand of
 // O^T += V^T P^T is read with the gfx950 transposing LDS read
-// (ds_read_b64_tr_b16).
+// (ds_read_b64_tr_b16). For few query rows against many keys the same kernel
+// runs over key ranges (SPL), with a combine kernel for O.
 
 #pragma once
 
@@ -895,9 +897,9 @@ void sdpa_twopass_kernel(const FwdArgs a) {
     // (with key ranges: written by the last range; LSE by the first)
     if (SPL == 0 || split == a.n_splits - 1) zero_rows<T, VEC>(pr, a.p_s[2], qw, a.Sq, ntiles * BN, a.Skv, lane);
     if (SPL == 0 || split == 0)
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, dead ? -INFINITY : lse2 * LN2), lr,
-                                          pred(row_ok && hf == 0, (uint32_t)((int64_t)(row_ok ? qi : 0) * a.l_s[2] * 4)),
-                                          0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, dead ? -INFINITY : lse2 * LN2), lr,
+                                              pred(row_ok && hf == 0, (uint32_t)((int64_t)(row_ok ? qi : 0) * a.l_s[2] * 4)),
+                                              0, 0);
 }
 
 // Keys per tile by mask kind: 32 with a bool mask, 64 otherwise. A bool mask
