@@ -173,6 +173,34 @@ def test_key_ranges_chosen_by_default(monkeypatch):
     _check(c, "auto", label="default key ranges")
 
 
+def test_workspace_missing_short_or_misaligned_runs_unsplit(monkeypatch):
+    # through the C ABI: with no workspace, too small a one or a misaligned one
+    # the call runs unsplit; every variant matches the split call to the bound
+    import ctypes
+    from sdpa_forward_materialised_amd import _binding as Bd
+    monkeypatch.delenv("SDPA_MATH_SPLITS", raising=False)
+    S = _lib()
+    lib = Bd.load_library()
+    c = W.make_case(seed=177, dtype="f16", B=1, Hq=2, Hkv=2, Sq=5, Skv=4096, D=64)
+    q, k, v = (c[x].to(DEV) for x in ("q", "k", "v"))
+    dq, dk, dv = Bd._desc(q, 4), Bd._desc(k, 4), Bd._desc(v, 4)
+    n = ctypes.c_size_t(0)
+    assert lib.sdpa_math_workspace_bytes(Bd._ref(dq), Bd._ref(dk), Bd._ref(dv), None, 0, 0, ctypes.byref(n)) == 0
+    assert n.value > 0
+    ws = torch.empty(n.value + 512, dtype=torch.uint8, device=DEV)
+    ref = run_oracle(c["q"], c["k"], c["v"], None, False, None, False)
+    for label, ptr, size in (("split", ws.data_ptr(), n.value), ("none", None, 0),
+                             ("short", ws.data_ptr(), n.value - 256), ("misaligned", ws.data_ptr() + 16, n.value)):
+        O, P, L = poisoned_outputs(1, 2, 5, 4096, 64, q.dtype, DEV)
+        do, dp, dl = Bd._desc(O, 4), Bd._desc(P, 4), Bd._desc(L, 3)
+        rc = lib.sdpa_math_fwd_ws(Bd._ref(dq), Bd._ref(dk), Bd._ref(dv), None, 0, 0.125, 0, Bd._ref(do), Bd._ref(dp),
+                                  Bd._ref(dl), None if ptr is None else ctypes.c_void_p(ptr), size,
+                                  ctypes.c_void_p(torch.cuda.current_stream().cuda_stream), 0)
+        assert rc == 0, S.last_error()
+        torch.cuda.synchronize()
+        compare(O, P, L, ref, q.dtype, f"workspace {label}")
+
+
 # Every compute-wave count the kernel is built for (a tuning knob read at each
 # call): 2 or 3 compute waves plus a loader wave, or 4 compute waves sharing
 # the tile loads (where their staged tiles fit in LDS; otherwise the request
