@@ -194,6 +194,60 @@ def threshold_sweep(reps=15, warmup=3):
                     print(json.dumps(res), flush=True)
 
 
+def mask_sweep(reps=50, warmup=20):
+    """Masked short-query shapes (fp16, B=16, H=8, non-causal, full [B,H,Sq,Skv]
+    masks with 10 % of keys removed at random; Sq 32..128, Skv 512..2048, D 64/128,
+    additive or bool): event time per call of the fused path and of the two-pass
+    path with 2 and 3 compute waves (forced), best of 3 x ``reps`` calls; one
+    text line per shape, with the path the planner picks."""
+    import torch
+
+    import sdpa_forward_materialised_amd as S
+
+    dev = "cuda:0"
+    g = torch.Generator(device="cpu").manual_seed(0)
+    variants = (("fused", None), ("twopass", "2"), ("twopass", "3"))
+    print("B H Sq Skv D mask | fused tp2 tp3 (us) | auto-plan", flush=True)
+    for Sq in (32, 64, 100, 128):
+        for Skv in (512, 1152, 2048):
+            for D in (64, 128):
+                for mk in ("add", "bool"):
+                    B, H = 16, 8
+                    q = torch.randn(B, H, Sq, D, generator=g).half().to(dev)
+                    k = torch.randn(B, H, Skv, D, generator=g).half().to(dev)
+                    v = torch.randn(B, H, Skv, D, generator=g).half().to(dev)
+                    drop = torch.rand(B, H, Sq, Skv, generator=g) < 0.1
+                    m = (torch.where(drop, float("-inf"), 0.0).half() if mk == "add" else ~drop).to(dev)
+                    out = (torch.empty(B, H, Sq, D, dtype=q.dtype, device=dev),
+                           torch.empty(B, H, Sq, Skv, dtype=q.dtype, device=dev),
+                           torch.empty(B, H, Sq, dtype=torch.float32, device=dev))
+                    res = []
+                    for path, waves in variants:
+                        os.environ.pop("SDPA_MATH_TP_WAVES", None)
+                        if waves:
+                            os.environ["SDPA_MATH_TP_WAVES"] = waves
+                        try:
+                            for _ in range(warmup):
+                                S.fwd(q, k, v, m, False, None, False, path=path, out=out)
+                        except NotImplementedError:
+                            res.append(float("nan"))
+                            continue
+                        torch.cuda.synchronize()
+                        best = 1e9
+                        for _ in range(3):
+                            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                            e0.record()
+                            for _ in range(reps):
+                                S.fwd(q, k, v, m, False, None, False, path=path, out=out)
+                            e1.record()
+                            torch.cuda.synchronize()
+                            best = min(best, e0.elapsed_time(e1) / reps * 1e3)
+                        res.append(best)
+                    os.environ.pop("SDPA_MATH_TP_WAVES", None)
+                    print(f"{B} {H} {Sq} {Skv} {D} {mk} | " + " ".join(f"{x:7.2f}" for x in res) +
+                          f" | {S.plan(q, k, v, m)[0]}", flush=True)
+
+
 def kept_pairs(Sq, Skv, align):
     """(query, key) pairs a causal mask keeps: query i keeps keys j <= i + c
     (c = 0 top-left, Skv - Sq bottom-right)."""
@@ -268,6 +322,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp16", action="store_true", help="skip the same-shape fp16 line")
     ap.add_argument("--no-configs", action="store_true", help="skip the table over every seeded workload")
+    ap.add_argument("--mask-sweep", action="store_true",
+                    help="fused vs two-pass (2 and 3 compute waves) on masked short-query shapes, then exit")
     ap.add_argument("--threshold-sweep", action="store_true",
                     help="only time both paths over a grid of shapes (fused/two-pass switch)")
     ap.add_argument("--probe-copy-mib", type=int, default=0,
@@ -281,6 +337,9 @@ def main():
 
     import sdpa_workloads as W
 
+    if args.mask_sweep:
+        mask_sweep()
+        return
     if args.threshold_sweep:
         threshold_sweep()
         return
