@@ -377,3 +377,29 @@ def test_workload_full_size(w, path):
         assert torch.all(P[:, :, upper] == 0)
     if w.mask == "keypad_bool":
         assert dead[0, :, :8].all() and (dead.sum().item() == 8 * w.Hq)
+
+
+# ------------------------------------------------------------ bench's extra workloads
+
+@pytest.mark.parametrize("w", list(W.EXTRA_WORKLOADS), ids=lambda w: w.name)
+def test_extra_workload_full_size(w):
+    """Chunked prefill (bottom-right causal) and long-key decode at full size,
+    with the default plan (key ranges where the planner picks them): sampled
+    (batch, head) slices against the oracle, plus whole-output properties."""
+    c = _workload_case(w)
+    c["align"] = w.align
+    O, P, L = _run(c, "auto", scale=w.scale, label=w.name)
+    dt = c["q"].dtype
+    for b, h in [(0, 0), (w.B - 1, w.Hq - 1), (w.B // 2, w.Hq // 2 + 1)]:
+        qs, ks, vs, ms = head_slice(c["q"], c["k"], c["v"], c["mask"], b, h)
+        ref = run_oracle(qs, ks, vs, ms, w.causal, w.scale, False, w.align)
+        r = compare(O[b:b + 1, h:h + 1], P[b:b + 1, h:h + 1], L[b:b + 1, h:h + 1], ref, dt, f"{w.name} b{b} h{h}")
+        print(f"[result] {w.name} b={b} h={h} {r}", flush=True)
+    assert not torch.isnan(O).any() and not torch.isnan(P).any() and not torch.isnan(L).any()
+    rows = P.float().sum(-1)
+    assert torch.allclose(rows, torch.ones_like(rows), atol=1e-2)
+    if w.causal:
+        # bottom-right: query i keeps keys j <= i + Skv - Sq
+        off = w.Skv - w.Sq if w.align == "bottom_right" else 0
+        upper = torch.ones(w.Sq, w.Skv, dtype=torch.bool, device=DEV).triu(1 + off)
+        assert torch.all(P[:, :, upper] == 0)
