@@ -11,6 +11,7 @@ from __future__ import annotations
 import ctypes
 import math
 import os
+import struct
 from typing import Optional, Tuple
 
 import torch
@@ -32,13 +33,15 @@ EXPORTS = ("sdpa_math_fwd", "sdpa_math_fwd_path", "sdpa_math_fwd_ws", "sdpa_math
            "sdpa_math_version", "sdpa_probe_fill", "sdpa_probe_copy")
 
 
-_I64x4 = ctypes.c_int64 * 4
-
-
 class SdpaTensor(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
                 ("sizes", ctypes.c_int64 * 4), ("strides", ctypes.c_int64 * 4)]
 
+
+# sdpa_tensor_t byte layouts: pointer, dtype, ndim, sizes[4], strides[4]
+# (unused trailing entries zero)
+_PACK = {4: struct.Struct("<Qii4q4q"), 3: struct.Struct("<Qii3q8x3q8x")}
+assert all(p.size == ctypes.sizeof(SdpaTensor) for p in _PACK.values())
 
 _lib = None
 _WS_BYTES = {}  # workspace bytes per call signature (shapes, dtypes, mask layout, flags)
@@ -88,8 +91,10 @@ def _desc(t: Optional[torch.Tensor], ndim: int) -> Optional[SdpaTensor]:
     dt = _DTYPES.get(t.dtype)
     if dt is None:
         raise ValueError(f"unsupported dtype {t.dtype}")
-    # one constructor call (field-by-field assignment costs several us per call)
-    return SdpaTensor(t.data_ptr() if t.numel() > 0 else None, dt, ndim, _I64x4(*t.shape), _I64x4(*t.stride()))
+    # packed in one go and copied into the struct (a constructor call with
+    # ctypes arrays costs about a microsecond more per descriptor)
+    return SdpaTensor.from_buffer_copy(_PACK[ndim].pack(t.data_ptr() if t.numel() > 0 else 0, dt, ndim,
+                                                        *t.shape, *t.stride()))
 
 
 def _ref(d: Optional[SdpaTensor]):
