@@ -199,3 +199,37 @@ def test_workspace_query(monkeypatch):
     assert _ws_bytes(_z(1, 2, 256, 64), _z(1, 2, 640, 64))[1] > 0  # two-pass shape (the fused path never splits)
     rc, n = _ws_bytes(_z(1, 3, 8, 64), _z(1, 2, 8, 64))
     assert rc == 1 and n == 0
+
+
+@pytest.mark.parametrize("shape,ndim,view", [
+    ((2, 3, 5, 32), 4, None),                 # contiguous 4-D
+    ((2, 3, 7), 3, None),                     # LSE-like 3-D
+    ((5, 9), 4, None),                        # mask with fewer dims: right-aligned
+    ((9,), 4, None),
+    ((2, 3, 0, 32), 4, None),                 # empty: null data pointer
+    ((2, 6, 5, 32), 4, "transpose"),          # strided view
+    ((2, 3, 5, 64), 4, "slice"),              # last-dim slice (offset pointer)
+])
+def test_descriptor_bytes_match_field_layout(shape, ndim, view):
+    """The packed descriptor is byte-for-byte the sdpa_tensor_t that a
+    field-by-field ctypes construction gives (pointer, dtype, ndim, sizes[4],
+    strides[4], unused trailing entries zero)."""
+    t = torch.randn(*shape, dtype=torch.float16)
+    if view == "transpose":
+        t = t.transpose(1, 2)
+    elif view == "slice":
+        t = t[..., 16:48]
+    d = B._desc(t, ndim)
+    u = t
+    while u.dim() < ndim:
+        u = u.unsqueeze(0)
+    ref = B.SdpaTensor()
+    ref.data = u.data_ptr() if u.numel() > 0 else None
+    ref.dtype = B.SDPA_F16
+    ref.ndim = ndim
+    for i in range(ndim):
+        ref.sizes[i] = u.shape[i]
+        ref.strides[i] = u.stride(i)
+    assert bytes(d) == bytes(ref)
+    assert (d.data or 0) == (u.data_ptr() if u.numel() else 0)
+    assert list(d.sizes)[:ndim] == list(u.shape) and list(d.strides)[:ndim] == list(u.stride())
