@@ -124,6 +124,17 @@ def _check_devices(*ts):
     return dev
 
 
+# torch's current stream on a device, as the raw HIP handle (torch's own
+# pointer query when it has one: no Stream object built per call)
+_RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _current_stream(dev: torch.device) -> int:
+    if _RAW_STREAM is not None:
+        return _RAW_STREAM(dev.index)
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
 def _causal_code(is_causal, causal_alignment: str) -> int:
     if causal_alignment not in CAUSAL_ALIGNMENTS:
         raise ValueError(f"causal_alignment must be one of {sorted(CAUSAL_ALIGNMENTS)}")
@@ -184,7 +195,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, attn_mask: Optional[t
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes > 0 else None
 
     def launch():
-        stream = torch.cuda.current_stream(dev).cuda_stream
+        stream = _current_stream(dev)
         return lib.sdpa_math_fwd_ws(_ref(dq), _ref(dk), _ref(dv), _ref(dm), causal,
                                     float(scale), int(bool(enable_gqa)), _ref(do), _ref(dp), _ref(dl),
                                     None if ws is None else ctypes.c_void_p(ws.data_ptr()), nbytes,

@@ -403,3 +403,25 @@ def test_extra_workload_full_size(w):
         off = w.Skv - w.Sq if w.align == "bottom_right" else 0
         upper = torch.ones(w.Sq, w.Skv, dtype=torch.bool, device=DEV).triu(1 + off)
         assert torch.all(P[:, :, upper] == 0)
+
+
+def test_launch_follows_current_stream():
+    """The binding launches on torch's current stream (a side stream inside
+    ``torch.cuda.stream``), and the results equal a default-stream call."""
+    S = _lib()
+    from sdpa_forward_materialised_amd import _binding as B
+    dev = torch.device(DEV)
+    c = W.make_case(seed=120, dtype="bf16", B=2, Hq=4, Hkv=4, Sq=200, Skv=200, D=64, causal=True)
+    q, k, v = (c[x].to(DEV) for x in ("q", "k", "v"))
+    print("[case] side stream bf16 2x4x200x64 causal", flush=True)
+    ref = S.fwd(q, k, v, None, True)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        assert B._current_stream(dev) == side.cuda_stream
+        got = S.fwd(q, k, v, None, True)
+    assert B._current_stream(dev) == torch.cuda.current_stream(dev).cuda_stream
+    side.synchronize()
+    for x, y in zip(ref, got):
+        assert torch.equal(x, y)
