@@ -56,7 +56,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         raise RuntimeError(f"{path} is missing: build it with `python -m sdpa_forward_materialised_amd.build` "
                            "(there is no CPU fallback)")
     lib = ctypes.CDLL(path)
-    T = ctypes.POINTER(SdpaTensor)
+    # tensor descriptors go in as the bytes of an sdpa_tensor_t (built by
+    # _desc; the library only reads them), or None for NULL
+    T = ctypes.c_char_p
     lib.sdpa_math_fwd.restype = ctypes.c_int
     lib.sdpa_math_fwd.argtypes = [T, T, T, T, ctypes.c_int, ctypes.c_float, ctypes.c_int, T, T, T, ctypes.c_void_p]
     lib.sdpa_math_fwd_path.restype = ctypes.c_int
@@ -81,7 +83,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     return lib
 
 
-def _desc(t: Optional[torch.Tensor], ndim: int) -> Optional[SdpaTensor]:
+def _desc(t: Optional[torch.Tensor], ndim: int) -> Optional[bytes]:
     if t is None:
         return None
     if t.dim() > ndim:
@@ -91,14 +93,9 @@ def _desc(t: Optional[torch.Tensor], ndim: int) -> Optional[SdpaTensor]:
     dt = _DTYPES.get(t.dtype)
     if dt is None:
         raise ValueError(f"unsupported dtype {t.dtype}")
-    # packed in one go and copied into the struct (a constructor call with
-    # ctypes arrays costs about a microsecond more per descriptor)
-    return SdpaTensor.from_buffer_copy(_PACK[ndim].pack(t.data_ptr() if t.numel() > 0 else 0, dt, ndim,
-                                                        *t.shape, *t.stride()))
-
-
-def _ref(d: Optional[SdpaTensor]):
-    return None if d is None else ctypes.byref(d)
+    # the sdpa_tensor_t bytes, packed in one go (building a ctypes struct
+    # costs a few microseconds more per call over the seven descriptors)
+    return _PACK[ndim].pack(t.data_ptr() if t.numel() > 0 else 0, dt, ndim, *t.shape, *t.stride())
 
 
 def _raise(code: int, lib) -> None:
@@ -187,7 +184,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, attn_mask: Optional[t
     nbytes = _WS_BYTES.get(sig)
     if nbytes is None:
         n = ctypes.c_size_t(0)
-        rc = lib.sdpa_math_workspace_bytes(_ref(dq), _ref(dk), _ref(dv), _ref(dm), causal, int(bool(enable_gqa)),
+        rc = lib.sdpa_math_workspace_bytes(dq, dk, dv, dm, causal, int(bool(enable_gqa)),
                                            ctypes.byref(n))
         if rc != 0:
             _raise(rc, lib)
@@ -196,8 +193,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, attn_mask: Optional[t
 
     def launch():
         stream = _current_stream(dev)
-        return lib.sdpa_math_fwd_ws(_ref(dq), _ref(dk), _ref(dv), _ref(dm), causal,
-                                    float(scale), int(bool(enable_gqa)), _ref(do), _ref(dp), _ref(dl),
+        return lib.sdpa_math_fwd_ws(dq, dk, dv, dm, causal,
+                                    float(scale), int(bool(enable_gqa)), do, dp, dl,
                                     None if ws is None else ctypes.c_void_p(ws.data_ptr()), nbytes,
                                     ctypes.c_void_p(stream), PATHS[path])
 
@@ -222,8 +219,8 @@ def plan(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, attn_mask: Optional[
     path = ctypes.c_int32(-1)
     tiles = ctypes.c_int64(-1)
     tiles64 = ctypes.c_int64(-1)
-    rc = lib.sdpa_math_plan(_ref(_desc(q, 4)), _ref(_desc(k, 4)), _ref(_desc(v, 4)),
-                            _ref(_desc(attn_mask, 4)), _causal_code(is_causal, causal_alignment),
+    rc = lib.sdpa_math_plan(_desc(q, 4), _desc(k, 4), _desc(v, 4),
+                            _desc(attn_mask, 4), _causal_code(is_causal, causal_alignment),
                             int(bool(enable_gqa)),
                             ctypes.byref(path), ctypes.byref(tiles), ctypes.byref(tiles64))
     if rc != 0:

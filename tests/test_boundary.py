@@ -84,19 +84,19 @@ def test_fwd_rejects_bad_outputs_before_launch():
     q = _z(1, 2, 8, 64)
     o, p, lse = _z(1, 2, 8, 64), _z(1, 2, 8, 9), torch.zeros(1, 2, 8)
     d = [B._desc(t, 4) for t in (q, q, q, o, p)] + [B._desc(lse, 3)]
-    rc = lib.sdpa_math_fwd(ctypes.byref(d[0]), ctypes.byref(d[1]), ctypes.byref(d[2]), None, 0, 0.125, 0,
-                           ctypes.byref(d[3]), ctypes.byref(d[4]), ctypes.byref(d[5]), None)
+    rc = lib.sdpa_math_fwd(d[0], d[1], d[2], None, 0, 0.125, 0,
+                           d[3], d[4], d[5], None)
     assert rc == 1 and "probs dim 3" in S.last_error()
     lse16 = B._desc(torch.zeros(1, 2, 8, dtype=torch.float16), 3)
     p_ok = B._desc(_z(1, 2, 8, 8), 4)
-    rc = lib.sdpa_math_fwd(ctypes.byref(d[0]), ctypes.byref(d[1]), ctypes.byref(d[2]), None, 0, 0.125, 0,
-                           ctypes.byref(d[3]), ctypes.byref(p_ok), ctypes.byref(lse16), None)
+    rc = lib.sdpa_math_fwd(d[0], d[1], d[2], None, 0, 0.125, 0,
+                           d[3], p_ok, lse16, None)
     assert rc == 1 and "lse must be f32" in S.last_error()
-    rc = lib.sdpa_math_fwd(None, ctypes.byref(d[1]), ctypes.byref(d[2]), None, 0, 0.125, 0,
-                           ctypes.byref(d[3]), ctypes.byref(p_ok), ctypes.byref(d[5]), None)
+    rc = lib.sdpa_math_fwd(None, d[1], d[2], None, 0, 0.125, 0,
+                           d[3], p_ok, d[5], None)
     assert rc == 1 and "q is NULL" in S.last_error()
-    rc = lib.sdpa_math_fwd_path(ctypes.byref(d[0]), ctypes.byref(d[1]), ctypes.byref(d[2]), None, 0, 0.125, 0,
-                                ctypes.byref(d[3]), ctypes.byref(p_ok), ctypes.byref(d[5]), None, 7)
+    rc = lib.sdpa_math_fwd_path(d[0], d[1], d[2], None, 0, 0.125, 0,
+                                d[3], p_ok, d[5], None, 7)
     assert rc == 1 and "unknown path" in S.last_error()
 
 
@@ -168,7 +168,7 @@ def test_causal_codes_validated():
     d = B._desc(q, 4)
     out = (ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int64())
     for code, want in ((0, 0), (1, 0), (2, 0), (3, 1), (-1, 1)):
-        rc = lib.sdpa_math_plan(B._ref(d), B._ref(d), B._ref(d), None, code, 0, *(ctypes.byref(x) for x in out))
+        rc = lib.sdpa_math_plan(d, d, d, None, code, 0, *(ctypes.byref(x) for x in out))
         assert rc == want, (code, S.last_error())
     assert "is_causal" in (S.last_error() or "")
 
@@ -176,8 +176,8 @@ def test_causal_codes_validated():
 def _ws_bytes(q, k, mask=None, causal=0, gqa=0):
     lib = S.load_library()
     n = ctypes.c_size_t(123)
-    rc = lib.sdpa_math_workspace_bytes(B._ref(B._desc(q, 4)), B._ref(B._desc(k, 4)), B._ref(B._desc(k, 4)),
-                                       B._ref(B._desc(mask, 4)), causal, gqa, ctypes.byref(n))
+    rc = lib.sdpa_math_workspace_bytes(B._desc(q, 4), B._desc(k, 4), B._desc(k, 4),
+                                       B._desc(mask, 4), causal, gqa, ctypes.byref(n))
     return rc, n.value
 
 
@@ -230,6 +230,7 @@ def test_descriptor_bytes_match_field_layout(shape, ndim, view):
     for i in range(ndim):
         ref.sizes[i] = u.shape[i]
         ref.strides[i] = u.stride(i)
-    assert bytes(d) == bytes(ref)
-    assert (d.data or 0) == (u.data_ptr() if u.numel() else 0)
-    assert list(d.sizes)[:ndim] == list(u.shape) and list(d.strides)[:ndim] == list(u.stride())
+    assert isinstance(d, bytes) and d == bytes(ref)
+    dd = B.SdpaTensor.from_buffer_copy(d)
+    assert (dd.data or 0) == (u.data_ptr() if u.numel() else 0)
+    assert list(dd.sizes)[:ndim] == list(u.shape) and list(dd.strides)[:ndim] == list(u.stride())

@@ -185,7 +185,7 @@ def test_workspace_missing_short_or_misaligned_runs_unsplit(monkeypatch):
     q, k, v = (c[x].to(DEV) for x in ("q", "k", "v"))
     dq, dk, dv = Bd._desc(q, 4), Bd._desc(k, 4), Bd._desc(v, 4)
     n = ctypes.c_size_t(0)
-    assert lib.sdpa_math_workspace_bytes(Bd._ref(dq), Bd._ref(dk), Bd._ref(dv), None, 0, 0, ctypes.byref(n)) == 0
+    assert lib.sdpa_math_workspace_bytes(dq, dk, dv, None, 0, 0, ctypes.byref(n)) == 0
     assert n.value > 0
     ws = torch.empty(n.value + 512, dtype=torch.uint8, device=DEV)
     ref = run_oracle(c["q"], c["k"], c["v"], None, False, None, False)
@@ -193,8 +193,8 @@ def test_workspace_missing_short_or_misaligned_runs_unsplit(monkeypatch):
                              ("short", ws.data_ptr(), n.value - 256), ("misaligned", ws.data_ptr() + 16, n.value)):
         O, P, L = poisoned_outputs(1, 2, 5, 4096, 64, q.dtype, DEV)
         do, dp, dl = Bd._desc(O, 4), Bd._desc(P, 4), Bd._desc(L, 3)
-        rc = lib.sdpa_math_fwd_ws(Bd._ref(dq), Bd._ref(dk), Bd._ref(dv), None, 0, 0.125, 0, Bd._ref(do), Bd._ref(dp),
-                                  Bd._ref(dl), None if ptr is None else ctypes.c_void_p(ptr), size,
+        rc = lib.sdpa_math_fwd_ws(dq, dk, dv, None, 0, 0.125, 0, do, dp,
+                                  dl, None if ptr is None else ctypes.c_void_p(ptr), size,
                                   ctypes.c_void_p(torch.cuda.current_stream().cuda_stream), 0)
         assert rc == 0, S.last_error()
         torch.cuda.synchronize()
