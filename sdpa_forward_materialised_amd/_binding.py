@@ -177,9 +177,9 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, attn_mask: Optional[t
     dm = _desc(attn_mask, 4)
     do, dp, dl = _desc(O, 4), _desc(P, 4), _desc(L, 3)
     # workspace for key ranges, when the library would split this call
-    # (the byte count depends on shapes and flags only: remembered per signature)
-    sig = (tuple(q.shape), tuple(k.shape), q.dtype, None if attn_mask is None else (tuple(attn_mask.shape),
-           attn_mask.dtype, tuple(attn_mask.stride())), causal, bool(enable_gqa),
+    # (the byte count depends on dtypes, shapes, mask layout and flags only:
+    # remembered per signature, the descriptors' bytes past the data pointer)
+    sig = (dq[8:], dk[8:], None if dm is None else dm[8:], causal, bool(enable_gqa),
            os.environ.get("SDPA_MATH_SPLITS"), os.environ.get("SDPA_MATH_TP_WAVES"))
     nbytes = _WS_BYTES.get(sig)
     if nbytes is None:
@@ -188,6 +188,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, attn_mask: Optional[t
                                            ctypes.byref(n))
         if rc != 0:
             _raise(rc, lib)
+        if len(_WS_BYTES) >= 4096:  # many distinct shapes: start over rather than grow
+            _WS_BYTES.clear()
         nbytes = _WS_BYTES[sig] = n.value
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes > 0 else None
 
