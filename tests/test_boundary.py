@@ -234,3 +234,30 @@ def test_descriptor_bytes_match_field_layout(shape, ndim, view):
     dd = B.SdpaTensor.from_buffer_copy(d)
     assert (dd.data or 0) == (u.data_ptr() if u.numel() else 0)
     assert list(dd.sizes)[:ndim] == list(u.shape) and list(dd.strides)[:ndim] == list(u.stride())
+
+
+def _fake_desc(shape, dtype_code, addr):
+    """A dense sdpa_tensor_t at a made-up (16-byte aligned) address: only for
+    calls that the library rejects before anything touches the device."""
+    strides, s = [], 1
+    for n in reversed(shape):
+        strides.insert(0, s)
+        s *= n
+    nd = len(shape)
+    return B._PACK[nd].pack(addr, dtype_code, nd, *shape, *strides)
+
+
+def test_slice_extent_limit():
+    """A (batch, head) slice of any tensor must span less than 1 GiB (the
+    kernels' buffer descriptors hold 32-bit extents): a bf16 P slice of
+    23171 x 23171 is the first square one past it, and is rejected on the host
+    before any launch (23170 x 23170, just under, runs in the GPU parity tests)."""
+    n = 23171
+    assert (n - 1) * (n - 1) * 2 < (1 << 30) <= n * n * 2
+    lib = S.load_library()
+    q = _fake_desc((1, 1, n, 128), B.SDPA_BF16, 1 << 20)
+    o = _fake_desc((1, 1, n, 128), B.SDPA_BF16, 1 << 21)
+    p = _fake_desc((1, 1, n, n), B.SDPA_BF16, 1 << 22)
+    lse = _fake_desc((1, 1, n), B.SDPA_F32, 1 << 23)
+    rc = lib.sdpa_math_fwd(q, q, q, None, 0, 0.088, 0, o, p, lse, None)
+    assert rc == 2 and "1 GiB" in S.last_error()

@@ -425,3 +425,26 @@ def test_launch_follows_current_stream():
     side.synchronize()
     for x, y in zip(ref, got):
         assert torch.equal(x, y)
+
+
+def test_largest_slice():
+    """The largest square bf16 slice the kernels take (Sq = Skv = 23170, P just
+    under 1 GiB), one head at D = 128, non-causal, default plan: sampled query
+    rows (first, last, ragged tail, random) against the oracle, and every row
+    of P summing to 1."""
+    S = _lib()
+    n = 23170
+    c = W.make_case(seed=130, dtype="bf16", B=1, Hq=1, Hkv=1, Sq=n, Skv=n, D=128)
+    print(f"[case] largest slice bf16 1x1x{n}x128", flush=True)
+    O, P, L = S.fwd(c["q"].to(DEV), c["k"].to(DEV), c["v"].to(DEV))
+    torch.cuda.synchronize()
+    rows = sorted({0, 1, 95, 96, n - 35, n - 2, n - 1} |
+                  set(np.random.default_rng(130).integers(0, n, 25).tolist()))
+    idx = torch.tensor(rows)
+    ref = run_oracle(c["q"][:, :, idx], c["k"], c["v"], None, False, None, False)
+    r = compare(O[:, :, idx.to(DEV)], P[:, :, idx.to(DEV)], L[:, :, idx.to(DEV)], ref, torch.bfloat16,
+                "largest slice")
+    print(f"[result] largest slice {r}", flush=True)
+    sums = torch.cat([P[0, 0, i:i + 4096].float().sum(-1) for i in range(0, n, 4096)])
+    assert sums.numel() == n and torch.allclose(sums, torch.ones_like(sums), atol=1e-2)
+    assert not torch.isnan(O).any() and not torch.isnan(L).any()
