@@ -71,8 +71,13 @@ def compare(O, P, L, ref, dtype, label=""):
     # dead rows: LSE exactly -inf; live rows within tolerance
     dead = np.isneginf(rl)
     assert np.array_equal(np.isneginf(lse), dead), f"{label}: dead-row pattern of LSE differs"
-    err_l = float(np.abs(lse[~dead] - rl[~dead]).max()) if (~dead).any() else 0.0
-    assert err_l <= TOL_LSE[dtype], f"{label}: max|dLSE| = {err_l:.3e}"
+    # LSE is float32 whatever the dtype: the stated bound, or four float32 ulps
+    # at the oracle's |LSE| where that is larger (a large scale gives |LSE| of
+    # tens, where float32 scores and their sum cannot hold 1e-5 absolute)
+    dl = np.abs(lse[~dead] - rl[~dead])
+    err_l = float(dl.max()) if dl.size else 0.0
+    lb = np.maximum(TOL_LSE[dtype], 4 * ulp(rl[~dead], torch.float32))
+    assert not (dl > lb).any(), f"{label}: max|dLSE| = {err_l:.3e} (max|LSE_ref| = {np.abs(rl[~dead]).max():.2f})"
     # masked-position pattern of P: bit-exact +0.0 where the oracle is exactly 0
     if P.numel():
         bits = P.detach().cpu().contiguous().view(torch.int16 if P.element_size() == 2 else torch.int32)

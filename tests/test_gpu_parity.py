@@ -448,3 +448,23 @@ def test_largest_slice():
     sums = torch.cat([P[0, 0, i:i + 4096].float().sum(-1) for i in range(0, n, 4096)])
     assert sums.numel() == n and torch.allclose(sums, torch.ones_like(sums), atol=1e-2)
     assert not torch.isnan(O).any() and not torch.isnan(L).any()
+
+
+SCALE_CASES = [
+    ("bf16-d128-causal", dict(seed=140, dtype="bf16", B=1, Hq=2, Hkv=2, Sq=200, Skv=200, D=128, causal=True)),
+    ("f16-d64-bool", dict(seed=141, dtype="f16", B=2, Hq=2, Hkv=1, Sq=100, Skv=300, D=64, mask="bool")),
+    ("f16-d64-add", dict(seed=142, dtype="f16", B=1, Hq=2, Hkv=2, Sq=130, Skv=260, D=64, mask="add", p=0.1)),
+    ("f32-d32-nomask", dict(seed=143, dtype="f32", B=1, Hq=2, Hkv=2, Sq=70, Skv=150, D=32)),
+]
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("scale", [-0.125, 0.0, 3.0])
+@pytest.mark.parametrize("label,spec", SCALE_CASES, ids=[s[0] for s in SCALE_CASES])
+def test_nonpositive_and_large_scale(label, spec, scale, path):
+    """A negative scale (the row maximum then comes from the smallest raw
+    score), zero (P uniform over the kept keys) and a large one (nearly
+    one-hot rows) against the oracle."""
+    c = W.make_case(**spec)
+    r = _check(c, path, scale=scale, label=f"{label} scale={scale}")
+    print(f"[result] {label} scale={scale} {path} {r}", flush=True)
