@@ -468,3 +468,29 @@ def test_nonpositive_and_large_scale(label, spec, scale, path):
     c = W.make_case(**spec)
     r = _check(c, path, scale=scale, label=f"{label} scale={scale}")
     print(f"[result] {label} scale={scale} {path} {r}", flush=True)
+
+
+def test_concurrent_streams_independent():
+    """Two calls in flight at once on two streams (one split over key ranges,
+    with its own workspace; one unsplit), launched back to back with no
+    synchronisation between them: each equals the same call made alone."""
+    S = _lib()
+    dev = torch.device(DEV)
+    a = W.make_case(seed=150, dtype="bf16", B=2, Hq=4, Hkv=4, Sq=1, Skv=8192, D=128)
+    b = W.make_case(seed=151, dtype="f16", B=1, Hq=8, Hkv=2, Sq=300, Skv=300, D=64, mask="bool",
+                    mask_shape=(1, 1, 300, 300), causal=False)
+    ga = [a[x].to(DEV) for x in ("q", "k", "v")]
+    gb = [b[x].to(DEV) for x in ("q", "k", "v")] + [b["mask"].to(DEV)]
+    print("[case] two streams: bf16 2x4x1x8192x128 (split) + f16 gqa 300x300 bool", flush=True)
+    ref_a = S.fwd(*ga)
+    ref_b = S.fwd(*gb, False, None, True)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            got_a = S.fwd(*ga)
+        with torch.cuda.stream(s2):
+            got_b = S.fwd(*gb, False, None, True)
+        torch.cuda.synchronize()
+        for x, y in zip(ref_a + ref_b, got_a + got_b):
+            assert torch.equal(x, y)
