@@ -1,11 +1,14 @@
 """Benchmark of the materialised-probability SDPA forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
 One step = one ``sdpa_math_fwd`` call (validation, path choice, kernel launch)
 on the 2k-token, head-dim-128, causal bf16 prefill workload (B=2, H=16,
-Sq=Skv=2048), inputs resident in HBM. Prints one JSON line on stdout;
-progress goes to stderr.
+Sq=Skv=2048) by default, inputs resident in HBM. Before each timed call the
+caches are flushed (a 512 MiB write, outside the call's event interval: the
+cudnn-frontend page's merge-log notes on measurement flush L2 per
+iteration); the call's own events give its time. Prints one JSON line on
+stdout; progress goes to stderr.
 
 Accounting (the FlagOS-OP page's perf-gate convention, Validation table):
   flops = 2 * B * Hq * Sq * Skv * (D + Dv), halved when causal
@@ -52,7 +55,36 @@ def algorithmic_bytes(w, mask_bytes=0):
     return {"total": q + k + v + o + p + lse + mask_bytes, "p": p}
 
 
-def time_gpu(w, steps, warmup, path="auto", warm_ms=0.0):
+FLUSH_BYTES = 512 << 20   # written before each timed call: more than L2 (8 x 4 MB) and the 256 MB MALL
+_flush_buf = None
+
+
+def flush_caches():
+    """Stream-write a 512 MiB buffer (the library's fill kernel) so that the
+    next call finds neither its inputs nor its outputs in L2 or the MALL."""
+    import torch
+
+    import sdpa_forward_materialised_amd as S
+
+    global _flush_buf
+    if _flush_buf is None:
+        _flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda:0")
+    S.probe_fill(_flush_buf, 0)
+
+
+def time_gpu(w, steps, warmup, path="auto", warm_ms=50.0, flush=True):
+    """Time ``steps`` calls of workload ``w`` with inputs and preallocated
+    outputs resident in HBM.
+
+    Per call: a cache flush (outside the timed interval), then an event pair
+    on the launch stream around the call alone; reported are the mean and
+    median of those per-call times (device time of the call plus its launch
+    gap). Before that, ``warmup`` calls and at least ``warm_ms`` of sustained
+    work (the clock ramps up over tens of ms). Beside it, the same calls back
+    to back without flushes, as one event interval / steps (labelled
+    secondary: later calls may find data in the caches)."""
+    import statistics
+
     import torch
 
     import sdpa_forward_materialised_amd as S
@@ -65,33 +97,47 @@ def time_gpu(w, steps, warmup, path="auto", warm_ms=0.0):
     mask_bytes = 0 if m is None else m.numel() * m.element_size()
     B, Hq, Sq, D = q.shape
     Skv, Dv = k.shape[2], v.shape[3]
-    # preallocated outputs: the timed region is the forward alone
     O = torch.empty(B, Hq, Sq, Dv, dtype=q.dtype, device=dev)
     P = torch.empty(B, Hq, Sq, Skv, dtype=q.dtype, device=dev)
     L = torch.empty(B, Hq, Sq, dtype=torch.float32, device=dev)
     out = (O, P, L)
     chosen, tiles, tiles64 = S.plan(q, k, v, m, w.causal, w.gqa, causal_alignment=w.align)
-    for _ in range(warmup):
+
+    def call():
         S.fwd(q, k, v, m, w.causal, w.scale, w.gqa, path=path, out=out, causal_alignment=w.align)
+
+    for _ in range(warmup):
+        call()
     torch.cuda.synchronize()
-    # and at least warm_ms of sustained work: the clock ramps up over tens of ms
     t_w = time.perf_counter()
     while (time.perf_counter() - t_w) * 1e3 < warm_ms:
         for _ in range(20):
-            S.fwd(q, k, v, m, w.causal, w.scale, w.gqa, path=path, out=out, causal_alignment=w.align)
+            call()
         torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(steps):
-        S.fwd(q, k, v, m, w.causal, w.scale, w.gqa, path=path, out=out, causal_alignment=w.align)
-    ev1.record(stream)
+    for i in range(steps):
+        if flush:
+            flush_caches()
+        starts[i].record(stream)
+        call()
+        ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = ev0.elapsed_time(ev1) / steps
-    return {"ms": ms, "wall_ms": wall * 1e3 / steps, "mask_bytes": mask_bytes,
+    per_call = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    # secondary: back to back, no flushes
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return {"ms": statistics.fmean(per_call), "ms_median": statistics.median(per_call), "ms_min": min(per_call),
+            "ms_back_to_back": e0.elapsed_time(e1) / steps, "wall_ms": wall * 1e3 / steps,
+            "mask_bytes": mask_bytes, "flushed": flush,
             "path": path if path != "auto" else chosen, "tiles_per_bh": tiles, "tiles64_per_bh": tiles64}
 
 
@@ -255,28 +301,36 @@ def kept_pairs(Sq, Skv, align):
     return sum(max(0, min(Skv, i + c + 1)) for i in range(Sq))
 
 
-def all_configs(steps, warmup, path, workloads=None):
-    """Every seeded workload: time, effective TFLOPS, P-write GB/s and the
-    fraction of the HBM roofline each reaches. FLOPs follow the perf-gate
-    convention (causal halves the square); a causal shape with Sq != Skv
-    counts the (query, key) pairs its mask keeps."""
+def workload_row(w, r):
+    """One table row: median per-call time with flushed caches, effective
+    TFLOPS, P-write GB/s and the fraction of the HBM and MFMA rooflines. FLOPs
+    follow the perf-gate convention (causal halves the square); a causal shape
+    with Sq != Skv counts the (query, key) pairs its mask keeps."""
+    by = algorithmic_bytes(w, r["mask_bytes"])
+    sec = r["ms_median"] * 1e-3
+    if w.causal and w.Sq != w.Skv:
+        fl = 2.0 * w.B * w.Hq * kept_pairs(w.Sq, w.Skv, w.align) * (w.D + w.dv)
+    else:
+        fl = algorithmic_flops(w.B, w.Hq, w.Sq, w.Skv, w.D, w.dv, w.causal)
+    return {"workload": w.name, "dtype": w.dtype, "path": r["path"], "ms": round(r["ms_median"], 5),
+            "ms_mean": round(r["ms"], 5), "ms_back_to_back": round(r["ms_back_to_back"], 5),
+            "tflops": round(fl / sec / 1e12, 2), "p_write_gbps": round(by["p"] / sec / 1e9, 1),
+            "hbm_gbps": round(by["total"] / sec / 1e9, 1),
+            "hbm_frac": round(by["total"] / sec / 1e9 / HBM_PEAK_GBPS, 4),
+            "mfma_frac": round(fl / sec / 1e12 / MFMA_PEAK_TFLOPS[w.dtype], 4),
+            "bytes": by["total"], "flops": fl}
+
+
+def all_configs(path, workloads=None, reps=100, warmup=10):
+    """Every seeded workload, ``reps`` flushed calls each (median reported)."""
     import sdpa_workloads as W
 
     rows = []
     for w in (W.WORKLOADS if workloads is None else workloads):
-        r = time_gpu(w, steps, warmup, path, warm_ms=50.0)
-        by = algorithmic_bytes(w, r["mask_bytes"])
-        sec = r["ms"] * 1e-3
-        if w.causal and w.Sq != w.Skv:
-            fl = 2.0 * w.B * w.Hq * kept_pairs(w.Sq, w.Skv, w.align) * (w.D + w.dv)
-        else:
-            fl = algorithmic_flops(w.B, w.Hq, w.Sq, w.Skv, w.D, w.dv, w.causal)
-        rows.append({"workload": w.name, "dtype": w.dtype, "path": r["path"], "ms": round(r["ms"], 5),
-                     "tflops": round(fl / sec / 1e12, 2), "p_write_gbps": round(by["p"] / sec / 1e9, 1),
-                     "hbm_gbps": round(by["total"] / sec / 1e9, 1),
-                     "hbm_frac": round(by["total"] / sec / 1e9 / HBM_PEAK_GBPS, 4),
-                     "mfma_frac": round(fl / sec / 1e12 / MFMA_PEAK_TFLOPS[w.dtype], 4)})
-        log(f"[bench] {w.name}: {r['ms']:.4f} ms, {rows[-1]['hbm_frac'] * 100:.1f}% of HBM roofline")
+        r = time_gpu(w, reps, warmup, path, warm_ms=50.0)
+        rows.append(workload_row(w, r))
+        log(f"[bench] {w.name}: {r['ms_median']:.4f} ms median (flushed), {rows[-1]['hbm_frac'] * 100:.1f}% "
+            f"of HBM roofline; back to back {r['ms_back_to_back']:.4f} ms")
     return rows
 
 
@@ -306,19 +360,34 @@ def cpu_baseline(w, budget_s=12.0):
         done += 1
     flops = algorithmic_flops(1, done, w.Sq, w.Skv, w.D, w.dv, w.causal)
     return {"value": flops / t_used / 1e12, "unit": "TFLOPS", "cores": oracle.threads(), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{done} (batch, head) slices of {w.name} (it has {len(heads)}), float64, "
                       f"{t_used:.1f} s ({t_used / done * 1e3:.0f} ms per slice)"}
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # The GPU raises its clock only after some tens of ms of sustained work:
-    # the default warm-up runs a few hundred steps (~50 ms) so that the timed
-    # steps see the steady state.
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=400)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10,
+                    help="untimed calls before the timed ones (plus at least 50 ms of sustained calls: "
+                         "the clock ramps up over tens of ms)")
+    ap.add_argument("--workload", default="prefill_2k_d128_bf16_causal",
+                    help="the workload of the headline line (default: the 2k D128 bf16 causal prefill)")
     ap.add_argument("--path", default="auto", choices=["auto", "fused", "twopass"])
+    ap.add_argument("--no-flush", action="store_true", help="no cache flush before each timed call")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp16", action="store_true", help="skip the same-shape fp16 line")
     ap.add_argument("--no-configs", action="store_true", help="skip the table over every seeded workload")
@@ -347,29 +416,29 @@ def main():
         print(json.dumps(probe_copy(args.probe_copy_mib, args.steps, args.warmup)), flush=True)
         return
 
-    w = W.BY_NAME["prefill_2k_d128_bf16_causal"]
-    log(f"[bench] {w.describe()} steps={args.steps} warmup={args.warmup}")
-    r = time_gpu(w, args.steps, args.warmup, args.path)
-    flops = algorithmic_flops(w.B, w.Hq, w.Sq, w.Skv, w.D, w.dv, w.causal)
-    by = algorithmic_bytes(w, r["mask_bytes"])
-    tflops = flops / (r["ms"] * 1e-3) / 1e12
-    achieved = by["total"] / (r["ms"] * 1e-3) / 1e9
-    p_gbps = by["p"] / (r["ms"] * 1e-3) / 1e9
-    log(f"[bench] bf16: {r['ms']:.4f} ms/step, {tflops:.1f} TFLOPS, {achieved:.0f} GB/s, P {p_gbps:.0f} GB/s")
+    w = W.BY_NAME[args.workload]
+    log(f"[bench] {w.describe()} steps={args.steps} warmup={args.warmup} flush={not args.no_flush}")
+    r = time_gpu(w, args.steps, args.warmup, args.path, flush=not args.no_flush)
+    row = workload_row(w, r)
+    sec = r["ms"] * 1e-3  # mean per-call time: the roofline's average launch duration
+    tflops = row["flops"] / sec / 1e12
+    achieved = row["bytes"] / sec / 1e9
+    p_gbps = algorithmic_bytes(w, r["mask_bytes"])["p"] / sec / 1e9
+    log(f"[bench] {w.dtype}: {r['ms']:.4f} ms mean, {r['ms_median']:.4f} median per call (flushed); "
+        f"{tflops:.1f} TFLOPS, {achieved:.0f} GB/s, P {p_gbps:.0f} GB/s; back to back {r['ms_back_to_back']:.4f} ms")
 
     extra = {}
-    if not args.no_fp16:
+    if not args.no_fp16 and w.name == "prefill_2k_d128_bf16_causal":
         w16 = W.Workload("prefill_2k_d128_f16_causal", "f16", 2, 16, 16, 2048, 2048, 128, True, "none", 3)
-        r16 = time_gpu(w16, args.steps, args.warmup, args.path)
-        extra["fp16_same_shape"] = {"ms": round(r16["ms"], 5),
-                                    "tflops": round(flops / (r16["ms"] * 1e-3) / 1e12, 2),
-                                    "p_write_gbps": round(by["p"] / (r16["ms"] * 1e-3) / 1e9, 1)}
-        log(f"[bench] fp16: {r16['ms']:.4f} ms/step")
+        r16 = time_gpu(w16, args.steps, args.warmup, args.path, flush=not args.no_flush)
+        extra["fp16_same_shape"] = {"ms": round(r16["ms"], 5), "ms_median": round(r16["ms_median"], 5),
+                                    "tflops": round(row["flops"] / (r16["ms"] * 1e-3) / 1e12, 2),
+                                    "p_write_gbps": round(algorithmic_bytes(w16)["p"] / (r16["ms"] * 1e-3) / 1e9, 1)}
+        log(f"[bench] fp16: {r16['ms']:.4f} ms mean per call")
 
     if not args.no_configs:
-        extra["configs"] = all_configs(min(args.steps, 50), min(args.warmup, 100), args.path)
-        extra["extra_configs"] = all_configs(min(args.steps, 50), min(args.warmup, 100), args.path,
-                                             W.EXTRA_WORKLOADS)
+        extra["configs"] = all_configs(args.path)
+        extra["extra_configs"] = all_configs(args.path, W.EXTRA_WORKLOADS)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -377,20 +446,27 @@ def main():
         cpu = cpu_baseline(w)
         log(f"[bench] cpu baseline: {cpu}")
 
+    kernel = "sdpa_twopass_kernel" if r["path"] == "twopass" else "sdpa_fused_kernel"
     line = {
         "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOPS", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["ms"], 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Sq": w.Sq, "Skv": w.Skv,
-                   "D": w.D, "causal": w.causal, "path": r["path"], "tiles_per_bh": r["tiles_per_bh"],
-                   "tiles64_per_bh": r["tiles64_per_bh"]},
+                   "D": w.D, "causal": w.causal, "mask": w.mask, "path": r["path"],
+                   "tiles_per_bh": r["tiles_per_bh"], "tiles64_per_bh": r["tiles64_per_bh"]},
+        "timing": {"per_call": "hip events on the launch stream around each call, caches flushed before it "
+                               "(512 MiB write, outside the interval)" if r["flushed"] else
+                               "hip events on the launch stream around each call, no flush",
+                   "ms_mean": round(r["ms"], 5), "ms_median": round(r["ms_median"], 5),
+                   "ms_min": round(r["ms_min"], 5),
+                   "ms_back_to_back_secondary": round(r["ms_back_to_back"], 5)},
         "p_write_gbps": round(p_gbps, 1),
         "effective_tflops_frac_of_mfma_peak": round(tflops / MFMA_PEAK_TFLOPS[w.dtype], 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": stored_traffic(),
-                     "kernel": "sdpa_twopass_kernel" if r["path"] == "twopass" else "sdpa_fused_kernel",
-                     "bytes_per_launch": by["total"]},
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": stored_traffic() if w.name == "prefill_2k_d128_bf16_causal" else None,
+                     "kernel": kernel, "bytes_per_launch": row["bytes"]},
         "cpu_baseline": cpu,
         "wall_ms_per_step": round(r["wall_ms"], 5),
     }

@@ -29,9 +29,12 @@
  * records in its merge-log notes.
  *
  * Numerics: scores, row statistics and the P·V accumulation run in float32;
- * P is rounded to the output dtype with round-to-nearest-even and O is
- * accumulated from exactly those rounded values (O = P_stored · V up to
- * float32 summation), then rounded the same way.
+ * P is rounded to the output dtype with round-to-nearest-even. O accumulates
+ * the float32 probabilities, carried into the 16-bit matrix products as the
+ * stored rounded value plus its rounded residual (twice the dtype's
+ * precision), so O is the float32 sum of P·V rounded once to the dtype: the
+ * FlagOS-OP page's Validation section reports worst errors of half a unit of
+ * the output dtype, which only a correctly rounded O reaches.
  */
 #ifndef SDPA_MATH_H
 #define SDPA_MATH_H
@@ -121,9 +124,14 @@ sdpa_status_t sdpa_math_fwd(const sdpa_tensor_t* q, const sdpa_tensor_t* k,
 
 /*
  * sdpa_math_fwd_path — sdpa_math_fwd with the path forced (SDPA_PATH_AUTO
- * behaves exactly like sdpa_math_fwd). A forced path the shape cannot take
+ * behaves exactly like sdpa_math_fwd): the per-call form of the forced
+ * on/off/auto switch of the FlagOS-OP page's single-kernel fusion update
+ * (an experiment knob there, as here). A forced path the shape cannot take
  * (the fused path needs every processed key row of a query block to fit on
- * chip) returns SDPA_ERR_UNSUPPORTED. Both paths compute the same values.
+ * chip) returns SDPA_ERR_UNSUPPORTED with nothing launched; any other path
+ * value is SDPA_ERR_INVALID_ARG. Both paths compute the same values within
+ * the stated tolerances; arguments, layout, ownership and errors otherwise
+ * as sdpa_math_fwd.
  */
 sdpa_status_t sdpa_math_fwd_path(const sdpa_tensor_t* q, const sdpa_tensor_t* k,
                                  const sdpa_tensor_t* v, const sdpa_tensor_t* mask,
@@ -181,11 +189,15 @@ sdpa_status_t sdpa_math_plan(const sdpa_tensor_t* q, const sdpa_tensor_t* k,
                              int is_causal, int enable_gqa,
                              int32_t* path, int64_t* tiles_per_bh, int64_t* tiles_64);
 
-/* Message of the last failed call on this thread ("" if none). Valid until
- * the next call on the same thread. */
+/* Message of the last failed call on this thread ("" if none): the text
+ * behind the status codes above, which map the FlagOS-OP page's
+ * Implementation-section error rules (heads that do not divide, causal with
+ * a mask). The string is owned by the library and valid until the next call
+ * on the same thread; never NULL. */
 const char* sdpa_math_last_error(void);
 
-/* SDPA_MATH_VERSION of the loaded library. */
+/* SDPA_MATH_VERSION of the loaded library (the C ABI above; a caller built
+ * against another version should not use the library). Never fails. */
 int sdpa_math_version(void);
 
 #ifdef __cplusplus

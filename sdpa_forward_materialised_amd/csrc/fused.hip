@@ -215,6 +215,10 @@ void sdpa_fused_kernel(const FwdArgs a) {
             if constexpr (sizeof(T) == 2) {
 #pragma unroll
                 for (int c2 = 0; c2 < 2; ++c2) {
+                    // the rounded probabilities plus their rounded residual:
+                    // O accumulates P to twice the dtype's precision
+                    const vec pl = TR::lo8(p + 8 * c2, pv[kb][c2]);
+                    vec va[ND];
 #pragma unroll
                     for (int d = 0; d < ND; ++d) {
                         u32x2 h2[2];
@@ -224,9 +228,12 @@ void sdpa_fused_kernel(const FwdArgs a) {
                             const int col = 32 * d + tr_col;
                             h2[r] = lds_tr16(vblk + pos_v(row, col * SZ / 16) * 16 + ((col * SZ) & 15));
                         }
-                        const vec va = __builtin_bit_cast(vec, u32x4{h2[0][0], h2[0][1], h2[1][0], h2[1][1]});
-                        oacc[d] = TR::mfma(va, pv[kb][c2], oacc[d]);
+                        va[d] = __builtin_bit_cast(vec, u32x4{h2[0][0], h2[0][1], h2[1][0], h2[1][1]});
                     }
+#pragma unroll
+                    for (int d = 0; d < ND; ++d) oacc[d] = TR::mfma(va[d], pv[kb][c2], oacc[d]);
+#pragma unroll
+                    for (int d = 0; d < ND; ++d) oacc[d] = TR::mfma(va[d], pl, oacc[d]);
                 }
             } else {
 #pragma unroll

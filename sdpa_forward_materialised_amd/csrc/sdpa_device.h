@@ -92,6 +92,20 @@ template <> struct Tr<__bf16> {
         return __builtin_convertvector(f, vec);  // round to nearest even
     }
     static __device__ __forceinline__ float to_f(uint32_t bits16) { return __builtin_bit_cast(float, bits16 << 16); }
+    // Residual of the rounding hi = cvt8(x), itself rounded: x - hi is exact
+    // in float32 (hi is within half a unit of x), so hi + lo carries x to
+    // 16 significant bits where hi alone carries 8.
+    static __device__ __forceinline__ vec lo8(const float* x, vec hi) {
+        const u32x4 b = __builtin_bit_cast(u32x4, hi);
+        f32x8 r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t w = b[e];
+            r[2 * e] = x[2 * e] - __builtin_bit_cast(float, w << 16);
+            r[2 * e + 1] = x[2 * e + 1] - __builtin_bit_cast(float, w & 0xffff0000u);
+        }
+        return __builtin_convertvector(r, vec);
+    }
 };
 
 template <> struct Tr<_Float16> {
@@ -106,6 +120,14 @@ template <> struct Tr<_Float16> {
     }
     static __device__ __forceinline__ float to_f(uint32_t bits16) {
         return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+    }
+    // Residual of the rounding hi = cvt8(x), itself rounded (exact in
+    // float32, as for bf16): hi + lo carries x to 22 significant bits.
+    static __device__ __forceinline__ vec lo8(const float* x, vec hi) {
+        f32x8 r;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[e] = x[e] - (float)hi[e];
+        return __builtin_convertvector(r, vec);
     }
 };
 

@@ -262,8 +262,6 @@ bool fused_config(const Shape& sh, bool causal, int64_t coff, int* waves, int* k
     return false;
 }
 
-bool fused_available() { return true; }
-
 // True when the 16-byte variant of the two-pass kernel can run: probability
 // and output rows 16-byte aligned (null: the default dense outputs), Skv a
 // multiple of 8, and a mask (if any) contiguous along the keys with 16-byte
@@ -323,7 +321,7 @@ sdpa_status_t make_plan(const Shape& sh, bool causal, int64_t coff, int forced, 
                         bool allow_split = false) {
     p->tiles_64 = count_tiles(sh.Sq, sh.Skv, causal, 64, coff);
     int fw = 0, fk = 0;
-    const bool fused_ok = fused_available() && fused_config(sh, causal, coff, &fw, &fk);
+    const bool fused_ok = fused_config(sh, causal, coff, &fw, &fk);
     int path = forced;
     if (path == SDPA_PATH_AUTO) path = env_path();
     // An additive mask over more than 64 query rows goes to the two-pass path
@@ -468,7 +466,9 @@ sdpa_status_t run(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_ten
     a.sched = is_causal ? ((pairs_ok && plan.grid > kResidentWorkgroups) ? 3 : 2) : 0;
     if (const char* e = std::getenv("SDPA_MATH_SCHED")) {
         a.sched = 0;
-        if (*e == '1' && is_causal && per_xcd > 0 && per_xcd % plan.n_qblk == 0 && per_xcd % 2 == 0) a.sched = 1;
+        // order 1 splits each XCD's range into a heavy and a light half of
+        // whole heads' blocks: a permutation only with an even block count
+        if (*e == '1' && is_causal && per_xcd > 0 && per_xcd % plan.n_qblk == 0 && plan.n_qblk % 2 == 0) a.sched = 1;
         if (*e == '2' && is_causal) a.sched = 2;
         if (*e == '3' && pairs_ok) a.sched = 3;
     }

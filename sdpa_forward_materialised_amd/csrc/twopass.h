@@ -702,7 +702,10 @@ void sdpa_twopass_kernel(const FwdArgs a) {
                     for (int d = 0; d < ND; ++d) va[c2][d] = v_operand(vbuf(buf), 32 * kb + 16 * c2, d);
 #pragma unroll
                 for (int c2 = 0; c2 < 2; ++c2) {
+                    // the rounded probabilities (stored) and their rounded
+                    // residual: O accumulates P to twice the dtype's precision
                     const vec pv = TR::cvt8(p + 8 * c2);
+                    const vec pl = TR::lo8(p + 8 * c2, pv);
                     if constexpr (C::PSTAGE) {
                         const int chunk = (32 * kb + 16 * c2 + 8 * hf) * SZ / 16;
                         *reinterpret_cast<u32x4*>(pst + C::pos_p(n, chunk) * 16) = __builtin_bit_cast(u32x4, pv);
@@ -711,6 +714,8 @@ void sdpa_twopass_kernel(const FwdArgs a) {
                     }
 #pragma unroll
                     for (int d = 0; d < ND; ++d) oacc[d] = TR::mfma(va[c2][d], pv, oacc[d]);
+#pragma unroll
+                    for (int d = 0; d < ND; ++d) oacc[d] = TR::mfma(va[c2][d], pl, oacc[d]);
                 }
             } else {
                 if constexpr (C::PSTAGE) {
@@ -776,34 +781,41 @@ void sdpa_twopass_kernel(const FwdArgs a) {
                 p0[e] = fast_exp2(__builtin_fmaf(acc0[e], a.scale_log2, -lse2));
             __builtin_amdgcn_sched_barrier(0);
         }
-        vec pv0[2], pv1[2];
+        vec pv0[2], pv1[2], pl0[2], pl1[2];
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2) {
             pv0[c2] = TR::cvt8(p0 + 8 * c2);
+            pl0[c2] = TR::lo8(p0 + 8 * c2, pv0[c2]);
             *reinterpret_cast<u32x4*>(pst + C::pos_p(n, (16 * c2 + 8 * hf) * SZ / 16) * 16) =
                 __builtin_bit_cast(u32x4, pv0[c2]);
         }
         __builtin_amdgcn_sched_barrier(0);
+        // O^T += V^T (P_hi + P_lo)^T of block 0 under block 1's exp2, in the
+        // order of sweep2_tile: per 16-key half, the hi products then the lo
 #pragma unroll
-        for (int i = 0; i < 2 * ND; ++i) {  // O^T += V^T P^T of block 0 under block 1's exp2
-            const int c2 = i / ND, d = i % ND;
-            oacc[d] = TR::mfma(va0[c2][d], pv0[c2], oacc[d]);
-            va1[c2][d] = v_operand(vt, 32 + 16 * c2, d);
+        for (int i = 0; i < 4 * ND; ++i) {
+            const int c2 = i / (2 * ND), part = (i / ND) & 1, d = i % ND;
+            oacc[d] = TR::mfma(va0[c2][d], part ? pl0[c2] : pv0[c2], oacc[d]);
+            if (part == 0) va1[c2][d] = v_operand(vt, 32 + 16 * c2, d);
 #pragma unroll
-            for (int e = i * 16 / (2 * ND); e < (i + 1) * 16 / (2 * ND); ++e)
+            for (int e = i * 16 / (4 * ND); e < (i + 1) * 16 / (4 * ND); ++e)
                 p1[e] = fast_exp2(__builtin_fmaf(acc1[e], a.scale_log2, -lse2));
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2) {
             pv1[c2] = TR::cvt8(p1 + 8 * c2);
+            pl1[c2] = TR::lo8(p1 + 8 * c2, pv1[c2]);
             *reinterpret_cast<u32x4*>(pst + C::pos_p(n, (32 + 16 * c2 + 8 * hf) * SZ / 16) * 16) =
                 __builtin_bit_cast(u32x4, pv1[c2]);
         }
 #pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2)
+        for (int c2 = 0; c2 < 2; ++c2) {
 #pragma unroll
             for (int d = 0; d < ND; ++d) oacc[d] = TR::mfma(va1[c2][d], pv1[c2], oacc[d]);
+#pragma unroll
+            for (int d = 0; d < ND; ++d) oacc[d] = TR::mfma(va1[c2][d], pl1[c2], oacc[d]);
+        }
         if constexpr (!NL) store_staged(t * BN, false);
       }
     };

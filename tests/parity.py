@@ -23,13 +23,23 @@ def ulp(x, dtype):
     return np.ldexp(1.0, e - 1 - MANT_BITS[dtype])
 
 
-def bound(ref, dtype):
-    """Element-wise max-abs bound: the stated per-dtype tolerance, or one unit
-    in the last place of the output dtype at the oracle value, whichever is
-    larger. The stated bounds are one ulp of the dtype at magnitude 1-2
-    (bf16) and 2-4 (fp16); P never exceeds 1, so for P they apply as stated,
-    while an O element beyond that range cannot be rounded to within them."""
-    return np.maximum(TOL_OP[dtype], ulp(ref, dtype))
+# Error of the kernels' float32 O before its final rounding, per unit of the
+# largest |V| the row reads: P is carried as its rounded value plus the
+# rounded residual (relative error at most 2^-16 in bf16, 2^-22 in fp16 per
+# term), exp2 and its argument in float32 (a few 2^-24 relative), and the
+# float32 accumulation of the products. 2^-13 covers all three with margin.
+PRE_ROUND_SLACK = 2.0 ** -13
+
+
+def bound(ref, dtype, vmax):
+    """Element-wise max-abs bound on O: the stated per-dtype tolerance wherever
+    a correctly rounded output can meet it (half an ulp of the dtype at the
+    oracle value is at most the tolerance: bf16 |O| < 4, fp16 |O| < 8, fp32
+    |O| < 256); elsewhere half an ulp plus the pre-rounding slack times the
+    largest |V|. P never exceeds 1, so its bound is always the stated one."""
+    tol = TOL_OP[dtype]
+    half = 0.5 * ulp(ref, dtype)
+    return np.where(half <= tol, tol, half + PRE_ROUND_SLACK * vmax)
 
 
 # An oracle probability this small may legitimately come back as 0: below half
@@ -46,11 +56,18 @@ def poisoned_outputs(B, Hq, Sq, Skv, Dv, dtype, device):
     return O, P, L
 
 
-def compare(O, P, L, ref, dtype, label=""):
+def compare(O, P, L, ref, dtype, label="", v=None):
     """Element-by-element comparison against the float64 oracle.
 
-    Returns a dict of the observed errors; raises AssertionError on failure.
+    ``v`` is the value tensor the call read (its largest magnitude scales the
+    pre-rounding slack of the O bound where the stated tolerance is out of a
+    correctly rounded output's reach). Returns a dict of the observed errors
+    (``o_elems_relaxed``: O elements whose bound exceeds the stated one);
+    raises AssertionError on failure.
     """
+    if v is None:
+        raise ValueError("compare needs the value tensor v")
+    vmax = float(v.detach().abs().max()) if v.numel() else 0.0
     ro, rp, rl = ref
     o = O.detach().cpu().double().numpy()
     p = P.detach().cpu().double().numpy()
@@ -62,7 +79,7 @@ def compare(O, P, L, ref, dtype, label=""):
     err_o = float(np.abs(o - ro).max()) if o.size else 0.0
     err_p = float(np.abs(p - rp).max()) if p.size else 0.0
     tol = TOL_OP[dtype]
-    bo = bound(ro, dtype)
+    bo = bound(ro, dtype, vmax)
     bad = np.abs(o - ro) > bo
     assert not bad.any(), (f"{label}: {int(bad.sum())} O elements beyond the bound; max|dO| = {err_o:.3e} "
                            f"(max|O_ref| = {np.abs(ro).max():.3f})")
@@ -86,7 +103,7 @@ def compare(O, P, L, ref, dtype, label=""):
         assert np.array_equal(zero_bits & ref_zero, ref_zero), f"{label}: a removed position is not +0.0"
         unexpected = zero_bits & ~ref_zero & (rp >= UNDERFLOW[dtype])
         assert not unexpected.any(), f"{label}: {int(unexpected.sum())} live positions came back as 0"
-    return {"err_o": err_o, "err_p": err_p, "err_lse": err_l, "o_elems_past_unit_range": relaxed,
+    return {"err_o": err_o, "err_p": err_p, "err_lse": err_l, "o_elems_relaxed": relaxed,
             "max_abs_o_ref": float(np.abs(ro).max()) if ro.size else 0.0}
 
 
