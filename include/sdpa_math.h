@@ -169,6 +169,29 @@ sdpa_status_t sdpa_math_fwd_ws(const sdpa_tensor_t* q, const sdpa_tensor_t* k,
                                void* workspace, size_t workspace_bytes, void* hip_stream, int path);
 
 /*
+ * sdpa_math_fwd_noalloc — sdpa_math_fwd_ws for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation): no workspace argument and nothing allocated. A
+ * call whose keys the planner splits into ranges keeps the ranges' row
+ * statistics and float32 partial outputs in a static scratch array of
+ * SDPA_MATH_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it
+ * runs on, until the process ends (its device address is looked up once per
+ * device, on the first call there). A call that would need more than that
+ * returns SDPA_ERR_UNSUPPORTED before any launch (sdpa_math_fwd_ws with a
+ * caller workspace takes it); no part of the scratch needs to start at zero.
+ * Every call on one GPU shares that GPU's scratch, which keeps the last
+ * call's contents: calls that may overlap on one GPU (different streams,
+ * threads) race and must be ordered by the caller. Arguments, layout,
+ * outputs and the other errors as sdpa_math_fwd_path.
+ */
+#define SDPA_MATH_NOALLOC_SCRATCH_BYTES (32u << 20)
+sdpa_status_t sdpa_math_fwd_noalloc(const sdpa_tensor_t* q, const sdpa_tensor_t* k,
+                                    const sdpa_tensor_t* v, const sdpa_tensor_t* mask,
+                                    int is_causal, float scale, int enable_gqa,
+                                    sdpa_tensor_t* out, sdpa_tensor_t* probs, sdpa_tensor_t* lse,
+                                    void* hip_stream, int path);
+
+/*
  * sdpa_math_plan — validate the shapes exactly as sdpa_math_fwd would and
  * report, without launching anything:
  *   *path         the path SDPA_PATH_AUTO resolves to

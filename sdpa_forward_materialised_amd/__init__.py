@@ -7,7 +7,7 @@ the float32 row log-sum-exp, computed by hand-written gfx950 HIP kernels in
 is argument marshalling only; torch supplies device memory and streams.
 """
 
-from ._binding import (EXPORTS, LIB_PATH, PATHS, fwd, last_error, load_library, plan,  # noqa: F401
+from ._binding import (EXPORTS, LIB_PATH, PATHS, fwd, fwd_noalloc, last_error, load_library, plan,  # noqa: F401
                        probe_copy, probe_fill, version)
 
-__all__ = ["fwd", "plan", "version", "last_error", "load_library", "LIB_PATH", "PATHS", "EXPORTS"]
+__all__ = ["fwd", "fwd_noalloc", "plan", "version", "last_error", "load_library", "LIB_PATH", "PATHS", "EXPORTS"]

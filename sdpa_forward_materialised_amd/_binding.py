@@ -29,7 +29,7 @@ _DTYPES = {torch.float32: SDPA_F32, torch.float16: SDPA_F16, torch.bfloat16: SDP
            torch.bool: SDPA_BOOL}
 
 EXPORTS = ("sdpa_math_fwd", "sdpa_math_fwd_path", "sdpa_math_fwd_ws", "sdpa_math_workspace_bytes",
-           "sdpa_math_plan", "sdpa_math_last_error",
+           "sdpa_math_fwd_noalloc", "sdpa_math_plan", "sdpa_math_last_error",
            "sdpa_math_version", "sdpa_probe_fill", "sdpa_probe_copy")
 
 
@@ -66,6 +66,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sdpa_math_fwd_ws.restype = ctypes.c_int
     lib.sdpa_math_fwd_ws.argtypes = [T, T, T, T, ctypes.c_int, ctypes.c_float, ctypes.c_int, T, T, T,
                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int]
+    lib.sdpa_math_fwd_noalloc.restype = ctypes.c_int
+    lib.sdpa_math_fwd_noalloc.argtypes = lib.sdpa_math_fwd.argtypes + [ctypes.c_int]
     lib.sdpa_math_workspace_bytes.restype = ctypes.c_int
     lib.sdpa_math_workspace_bytes.argtypes = [T, T, T, T, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
     lib.sdpa_math_plan.restype = ctypes.c_int
@@ -209,6 +211,35 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, attn_mask: Optional[t
     if rc != 0:
         _raise(rc, lib)
     return O, P, L
+
+
+def fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                out: Tuple[torch.Tensor, torch.Tensor, torch.Tensor],
+                attn_mask: Optional[torch.Tensor] = None, is_causal: bool = False, scale: Optional[float] = None,
+                enable_gqa: bool = False, path: str = "auto", causal_alignment: str = "top_left") -> None:
+    """``sdpa_math_fwd_noalloc``: the forward into caller-provided (O, P, LSE)
+    buffers with nothing allocated, neither by the library (its key-range
+    scratch is a static per-device array) nor here. Calls that may overlap on
+    one GPU share that scratch and must be ordered by the caller."""
+    lib = load_library()
+    O, P, L = out
+    dev = _check_devices(q, k, v, attn_mask, O, P, L)
+    causal = _causal_code(is_causal, causal_alignment)
+    if path not in PATHS:
+        raise ValueError(f"path must be one of {sorted(PATHS)}")
+    if q.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, S, D]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[3]) if q.shape[3] > 0 else 1.0
+    args = (_desc(q, 4), _desc(k, 4), _desc(v, 4), _desc(attn_mask, 4), causal, float(scale),
+            int(bool(enable_gqa)), _desc(O, 4), _desc(P, 4), _desc(L, 3))
+    if dev.index == torch.cuda.current_device():
+        rc = lib.sdpa_math_fwd_noalloc(*args, ctypes.c_void_p(_current_stream(dev)), PATHS[path])
+    else:
+        with torch.cuda.device(dev):
+            rc = lib.sdpa_math_fwd_noalloc(*args, ctypes.c_void_p(_current_stream(dev)), PATHS[path])
+    if rc != 0:
+        _raise(rc, lib)
 
 
 def plan(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, attn_mask: Optional[torch.Tensor] = None,

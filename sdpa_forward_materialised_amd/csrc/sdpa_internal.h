@@ -2,6 +2,7 @@
 // the gfx950 kernels. Not installed; the public interface is include/sdpa_math.h.
 #pragma once
 
+#include <cstddef>
 #include <cstdint>
 
 namespace sdpa {
@@ -75,6 +76,13 @@ int launch_fused(int dtype, int D, int mask_kind, int waves, bool vec, const Fwd
 bool twopass_nl_ok_f32(int D, int mask_kind);
 bool twopass_nl_ok_f16(int D, int mask_kind);
 bool twopass_nl_ok_bf16(int D, int mask_kind);
+
+// Bytes of the per-device static scratch behind sdpa_math_fwd_noalloc (the
+// key-range workspace: per range and query row a (max, sum) pair and a
+// float32 partial output row). Must match SDPA_MATH_NOALLOC_SCRATCH_BYTES.
+constexpr size_t STATIC_SCRATCH_BYTES = size_t(32) << 20;
+// Device address of the current device's static scratch (hipError_t as int).
+int static_scratch(void** ptr);
 
 // Largest key range the fused path keeps on chip per wave (scores held in
 // registers: 32 rows x keys / 64 lanes floats per lane), by head dim.

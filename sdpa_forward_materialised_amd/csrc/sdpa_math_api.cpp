@@ -393,9 +393,14 @@ void fill_strides3(const sdpa_tensor_t* t, int64_t* s) {
     s[2] = t->sizes[2] == 1 ? t->sizes[3] : t->strides[2];
 }
 
+// Where a call's key-range workspace comes from: the caller's buffer (NULL:
+// none, run unsplit) or the library's per-device static scratch.
+enum WsMode { WS_CALLER = 0, WS_STATIC = 1 };
+
 sdpa_status_t run(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_tensor_t* v, const sdpa_tensor_t* mask,
                   int is_causal, float scale, int enable_gqa, sdpa_tensor_t* out, sdpa_tensor_t* probs,
-                  sdpa_tensor_t* lse, void* stream, int path, void* ws = nullptr, size_t ws_bytes = 0) {
+                  sdpa_tensor_t* lse, void* stream, int path, void* ws = nullptr, size_t ws_bytes = 0,
+                  WsMode ws_mode = WS_CALLER) {
     g_last_error.clear();
     if (path < SDPA_PATH_AUTO || path > SDPA_PATH_TWOPASS) return fail(SDPA_ERR_INVALID_ARG, "unknown path %d", path);
     Shape sh;
@@ -406,7 +411,22 @@ sdpa_status_t run(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_ten
     if (sh.B * sh.Hq * sh.Sq == 0) return SDPA_OK;
     const bool vec = staged_layout(sh, mask, out, probs);
     sdpa::Plan plan;
-    if ((st = make_plan(sh, is_causal != 0, causal_offset(sh, is_causal), path, vec, &plan, ws != nullptr))) return st;
+    if ((st = make_plan(sh, is_causal != 0, causal_offset(sh, is_causal), path, vec, &plan,
+                        ws_mode == WS_STATIC || ws != nullptr)))
+        return st;
+    if (ws_mode == WS_STATIC && plan.n_splits > 1) {
+        // the static scratch: a plan that needs more is rejected, never shrunk
+        const size_t need = split_ws_bytes(sh, plan.n_splits);
+        if (need > sdpa::STATIC_SCRATCH_BYTES)
+            return fail(SDPA_ERR_UNSUPPORTED,
+                        "this call needs %zu bytes of key-range scratch; the static scratch holds %zu "
+                        "(use sdpa_math_fwd_ws with a caller workspace)",
+                        need, sdpa::STATIC_SCRATCH_BYTES);
+        const int e = sdpa::static_scratch(&ws);
+        if (e != 0)
+            return fail(SDPA_ERR_HIP, "static scratch lookup failed: %s", hipGetErrorString(static_cast<hipError_t>(e)));
+        ws_bytes = sdpa::STATIC_SCRATCH_BYTES;
+    }
     if (plan.n_splits > 1 && (reinterpret_cast<uintptr_t>(ws) % 256 != 0 || ws_bytes < split_ws_bytes(sh, plan.n_splits)))
         if ((st = make_plan(sh, is_causal != 0, causal_offset(sh, is_causal), path, vec, &plan))) return st;  // no room: unsplit
 
@@ -554,6 +574,13 @@ sdpa_status_t sdpa_math_fwd_ws(const sdpa_tensor_t* q, const sdpa_tensor_t* k, c
                                size_t workspace_bytes, void* hip_stream, int path) {
     return run(q, k, v, mask, is_causal, scale, enable_gqa, out, probs, lse, hip_stream, path, workspace,
                workspace_bytes);
+}
+
+sdpa_status_t sdpa_math_fwd_noalloc(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_tensor_t* v,
+                                    const sdpa_tensor_t* mask, int is_causal, float scale, int enable_gqa,
+                                    sdpa_tensor_t* out, sdpa_tensor_t* probs, sdpa_tensor_t* lse, void* hip_stream,
+                                    int path) {
+    return run(q, k, v, mask, is_causal, scale, enable_gqa, out, probs, lse, hip_stream, path, nullptr, 0, WS_STATIC);
 }
 
 sdpa_status_t sdpa_math_workspace_bytes(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_tensor_t* v,

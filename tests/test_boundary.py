@@ -261,3 +261,26 @@ def test_slice_extent_limit():
     lse = _fake_desc((1, 1, n), B.SDPA_F32, 1 << 23)
     rc = lib.sdpa_math_fwd(q, q, q, None, 0, 0.088, 0, o, p, lse, None)
     assert rc == 2 and "1 GiB" in S.last_error()
+
+
+def test_noalloc_rejects_plans_beyond_its_scratch(monkeypatch):
+    """sdpa_math_fwd_noalloc keeps key-range statistics in a static scratch of
+    SDPA_MATH_NOALLOC_SCRATCH_BYTES; a plan that needs more (here 512 forced
+    ranges over 8192 query rows: about 2 GB) is rejected on the host, before
+    any launch (fake device addresses: nothing is touched)."""
+    monkeypatch.setenv("SDPA_MATH_SPLITS", "512")
+    lib = S.load_library()
+    hdr = open(os.path.join(ROOT, "include", "sdpa_math.h")).read()
+    m = re.search(r"#define SDPA_MATH_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", hdr)
+    limit = int(m.group(1)) << int(m.group(2))
+    n = 65536
+    q = _fake_desc((1, 128, 64, 128), B.SDPA_BF16, 1 << 20)
+    k = _fake_desc((1, 128, n, 128), B.SDPA_BF16, 1 << 30)
+    o = _fake_desc((1, 128, 64, 128), B.SDPA_BF16, 1 << 21)
+    p = _fake_desc((1, 128, 64, n), B.SDPA_BF16, 1 << 31)
+    lse = _fake_desc((1, 128, 64), B.SDPA_F32, 1 << 22)
+    ws = ctypes.c_size_t(0)
+    assert lib.sdpa_math_workspace_bytes(q, k, k, None, 0, 0, ctypes.byref(ws)) == 0
+    assert ws.value > limit
+    rc = lib.sdpa_math_fwd_noalloc(q, k, k, None, 0, 0.088, 0, o, p, lse, None, 0)
+    assert rc == 2 and "scratch" in S.last_error()
