@@ -26,8 +26,12 @@ LSE layout):
     error; Hq != Hkv without ``enable_gqa`` is an error;
   * a row with every key removed has P = 0, O = 0 and LSE = -inf.
 
-Every function here is pinned by ``tests/test_oracle.py`` (brute force, closed
-forms, invariants, equivalences, torch's CPU math backend on float masks).
+Every function here is pinned: the forward by ``tests/test_oracle.py`` (brute
+force, closed forms, invariants, equivalences, torch's CPU math backend on
+float masks, planted mistakes), the backward ``sdpa_backward_reference`` by
+``tests/test_oracle_bwd.py`` (brute force with the full softmax Jacobian,
+finite differences of the forward, gradient identities, closed forms,
+planted mistakes).
 """
 
 from __future__ import annotations
@@ -71,6 +75,10 @@ def load(path: str = _LIB) -> ctypes.CDLL:
     lib.oracle_sdpa_fwd.argtypes = [dp, dp, dp, i64, i64, i64, i64, i64, i64, i64,
                                     ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(i64),
                                     ctypes.c_int, ctypes.c_double, dp, dp, dp]
+    lib.oracle_sdpa_bwd.restype = ctypes.c_int
+    lib.oracle_sdpa_bwd.argtypes = [dp, dp, dp, i64, i64, i64, i64, i64, i64, i64,
+                                    ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(i64),
+                                    ctypes.c_int, ctypes.c_double, dp, dp, dp, dp, dp]
     lib.oracle_sdpa_threads.restype = ctypes.c_int
     lib.oracle_sdpa_threads.argtypes = []
     _lib_cache[path] = lib
@@ -164,3 +172,66 @@ def sdpa_reference(q, k, v, attn_mask=None, is_causal: bool = False,
     if rc != 0:
         raise ValueError(f"oracle rejected the call (code {rc})")
     return out, probs, lse
+
+
+def sdpa_backward_reference(q, k, v, attn_mask=None, is_causal: bool = False,
+                            scale: Optional[float] = None, enable_gqa: bool = False,
+                            dout=None, dprobs=None, lib_path: str = _LIB,
+                            causal_alignment: str = "top_left"
+                            ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Return (dq [B,Hq,Sq,D], dk [B,Hkv,Skv,D], dv [B,Hkv,Skv,Dv]) in float64:
+    the gradients of a loss whose gradients with respect to the forward's
+    outputs are ``dout`` (dL/dO, required) and ``dprobs`` (dL/dP, or None).
+
+    The plain chain rule through P = softmax(scale * Q K^T + mask) and
+    O = P V (``oracle_sdpa_bwd`` in ``sdpa_oracle.c``), following the FlagOS-OP
+    page's Implementation section (an autograd.Function with gradients from
+    both outputs) and its "P800 fused backward" update (softmax Jacobian from
+    the probability map; query-head gradients reduced back to the key/value
+    heads). Removed keys and dead rows receive no gradient.
+    """
+    causal = causal_code(is_causal, causal_alignment)
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, S, D]")
+    B, Hq, Sq, D = q.shape
+    Bk, Hkv, Skv, Dk = k.shape
+    Bv, Hv, Sv, Dv = v.shape
+    if (Bk, Dk) != (B, D) or (Bv, Hv, Sv) != (B, Hkv, Skv):
+        raise ValueError("q, k, v shapes disagree")
+    if Hkv == 0 or Hq % Hkv != 0:
+        raise ValueError(f"query heads {Hq} are not a multiple of key/value heads {Hkv}")
+    if Hq != Hkv and not enable_gqa:
+        raise ValueError("Hq != Hkv requires enable_gqa")
+    if is_causal and attn_mask is not None:
+        raise ValueError("is_causal and attn_mask are mutually exclusive")
+    if dout is None:
+        raise ValueError("dout is required")
+    do = _f64(dout)
+    if do.shape != (B, Hq, Sq, Dv):
+        raise ValueError("dout must be [B, Hq, Sq, Dv]")
+    dpr = None
+    if dprobs is not None:
+        dpr = _f64(dprobs)
+        if dpr.shape != (B, Hq, Sq, Skv):
+            raise ValueError("dprobs must be [B, Hq, Sq, Skv]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    kind, marr, mstr = MASK_NONE, None, [0, 0, 0, 0]
+    if attn_mask is not None:
+        kind, marr, mstr = _mask_array(attn_mask, (B, Hq, Sq, Skv))
+    dq = np.empty((B, Hq, Sq, D), np.float64)
+    dk = np.empty((B, Hkv, Skv, D), np.float64)
+    dv = np.empty((B, Hkv, Skv, Dv), np.float64)
+    dp = ctypes.POINTER(ctypes.c_double)
+    st = (ctypes.c_int64 * 4)(*mstr)
+    lib = load(lib_path)
+    rc = lib.oracle_sdpa_bwd(q.ctypes.data_as(dp), k.ctypes.data_as(dp), v.ctypes.data_as(dp),
+                             B, Hq, Hkv, Sq, Skv, D, Dv, kind,
+                             None if marr is None else marr.ctypes.data_as(ctypes.c_void_p),
+                             st, causal, float(scale), do.ctypes.data_as(dp),
+                             None if dpr is None else dpr.ctypes.data_as(dp),
+                             dq.ctypes.data_as(dp), dk.ctypes.data_as(dp), dv.ctypes.data_as(dp))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the call (code {rc})")
+    return dq, dk, dv

@@ -88,3 +88,51 @@ def sdpa_brute(q, k, v, attn_mask=None, is_causal: bool = False,
                 for d in range(Dv):
                     out[b, h, i, d] = math.fsum(p[j] * float(v[b, hk, j, d]) for j in range(Skv))
     return out, probs, lse
+
+
+def sdpa_backward_brute(q, k, v, attn_mask=None, is_causal: bool = False,
+                        scale: Optional[float] = None, enable_gqa: bool = False,
+                        dout=None, dprobs=None, causal_alignment: str = "top_left"):
+    """Gradients (dq, dk, dv) of a loss with dL/dO = ``dout`` and dL/dP =
+    ``dprobs`` (None: zero), by brute force: the probabilities from
+    ``sdpa_brute``, then the full softmax Jacobian of each row,
+    dP_ik/dS_ij = P_ik (delta_kj - P_ij), applied term by term with exact
+    summation, and the key/value gradients of every query head added to the
+    key/value head it reads (repeat_interleave expansion, summed back)."""
+    _, probs, _ = sdpa_brute(q, k, v, attn_mask, is_causal, scale, enable_gqa, causal_alignment)
+    q = _array(q).astype(np.float64)
+    k = _array(k).astype(np.float64)
+    v = _array(v).astype(np.float64)
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv, Dv = k.shape[1], k.shape[2], v.shape[3]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    do = _array(dout).astype(np.float64)
+    dpr = None if dprobs is None else _array(dprobs).astype(np.float64)
+    kv_head = [h * Hkv // Hq for h in range(Hq)]
+    dq = np.zeros((B, Hq, Sq, D))
+    dk_terms = [[[[[] for _ in range(D)] for _ in range(Skv)] for _ in range(Hkv)] for _ in range(B)]
+    dv_terms = [[[[[] for _ in range(Dv)] for _ in range(Skv)] for _ in range(Hkv)] for _ in range(B)]
+    for b in range(B):
+        for h in range(Hq):
+            hk = kv_head[h]
+            for i in range(Sq):
+                p = probs[b, h, i]
+                # dL/dP_ik: through O (dout . v_k) plus the direct gradient on P
+                g = [math.fsum(float(do[b, h, i, d]) * float(v[b, hk, kk, d]) for d in range(Dv))
+                     + (0.0 if dpr is None else float(dpr[b, h, i, kk])) for kk in range(Skv)]
+                # dL/dS_ij = sum_k g_k P_ik (delta_kj - P_ij)
+                ds = [math.fsum(g[kk] * float(p[kk]) * ((1.0 if kk == j else 0.0) - float(p[j]))
+                                for kk in range(Skv)) for j in range(Skv)]
+                for d in range(D):
+                    dq[b, h, i, d] = scale * math.fsum(ds[j] * float(k[b, hk, j, d]) for j in range(Skv))
+                for j in range(Skv):
+                    for d in range(D):
+                        dk_terms[b][hk][j][d].append(scale * ds[j] * float(q[b, h, i, d]))
+                    for d in range(Dv):
+                        dv_terms[b][hk][j][d].append(float(p[j]) * float(do[b, h, i, d]))
+    dk = np.array([[[[math.fsum(dk_terms[b][hk][j][d]) for d in range(D)] for j in range(Skv)]
+                    for hk in range(Hkv)] for b in range(B)]).reshape(B, Hkv, Skv, D)
+    dv = np.array([[[[math.fsum(dv_terms[b][hk][j][d]) for d in range(Dv)] for j in range(Skv)]
+                    for hk in range(Hkv)] for b in range(B)]).reshape(B, Hkv, Skv, Dv)
+    return dq, dk, dv
