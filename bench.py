@@ -334,6 +334,54 @@ def all_configs(path, workloads=None, reps=100, warmup=10):
     return rows
 
 
+def time_backward(w, reps=50, warmup=10):
+    """The backward (sdpa_math_bwd) on workload ``w`` with dL/dO and dL/dP
+    both given: flushed per-call event time (median), effective TFLOPS over
+    its four algorithmic products (dV, dP, dQ, dK: twice the forward's
+    flops) and HBM bytes (q, k, v, dout, dprobs, lse read; dq, dk, dv
+    written)."""
+    import statistics
+
+    import torch
+
+    import sdpa_forward_materialised_amd as S
+    import sdpa_workloads as W
+
+    dev = torch.device("cuda:0")
+    inp = W.make_inputs(w)
+    q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
+    m = None if inp["mask"] is None else inp["mask"].to(dev)
+    O, P, L = S.fwd(q, k, v, m, w.causal, w.scale, w.gqa, causal_alignment=w.align)
+    g = torch.Generator(device="cpu").manual_seed(w.seed)
+    dout = torch.randn(O.shape, generator=g).to(dev, q.dtype)
+    dprobs = torch.randn(P.shape, generator=g).to(dev, q.dtype)
+    out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+
+    def call():
+        S.bwd(q, k, v, L, dout, dprobs, m, w.causal, w.scale, w.gqa, w.align, out=out)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    st = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    en = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    for i in range(reps):
+        flush_caches()
+        st[i].record()
+        call()
+        en[i].record()
+    torch.cuda.synchronize()
+    ms = statistics.median(a.elapsed_time(b) for a, b in zip(st, en))
+    fl = 2 * algorithmic_flops(w.B, w.Hq, w.Sq, w.Skv, w.D, w.dv, w.causal)
+    e = ELT[w.dtype]
+    nbytes = (2 * (q.numel() + k.numel() + v.numel()) + dout.numel() + dprobs.numel()) * e + L.numel() * 4 \
+        + (0 if m is None else m.numel() * m.element_size())
+    return {"workload": w.name, "ms": round(ms, 5), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+            "hbm_gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "mfma_frac": round(fl / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[w.dtype], 4), "bytes": nbytes}
+
+
 def cpu_baseline(w, budget_s=12.0):
     """The float64 oracle on whole (batch, head) slices of the same workload,
     taken in order (and again from the start once all were done) until about
@@ -439,6 +487,13 @@ def main():
     if not args.no_configs:
         extra["configs"] = all_configs(args.path)
         extra["extra_configs"] = all_configs(args.path, W.EXTRA_WORKLOADS)
+
+    if not args.no_configs:
+        extra["backward"] = []
+        for name in ("prefill_2k_d128_bf16_causal", "gqa_1k_d128_f16_keypad"):
+            rb = time_backward(W.BY_NAME[name])
+            extra["backward"].append(rb)
+            log(f"[bench] backward {name}: {rb['ms']:.4f} ms, {rb['tflops']} TFLOPS, {rb['hbm_frac'] * 100:.1f}% HBM")
 
     cpu = None
     if not args.no_cpu_baseline:

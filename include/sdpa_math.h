@@ -39,6 +39,7 @@
 #ifndef SDPA_MATH_H
 #define SDPA_MATH_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -211,6 +212,55 @@ sdpa_status_t sdpa_math_plan(const sdpa_tensor_t* q, const sdpa_tensor_t* k,
                              const sdpa_tensor_t* v, const sdpa_tensor_t* mask,
                              int is_causal, int enable_gqa,
                              int32_t* path, int64_t* tiles_per_bh, int64_t* tiles_64);
+
+/*
+ * sdpa_math_bwd — the backward of sdpa_math_fwd: gradients of q, k and v
+ * for a loss whose gradients with respect to the two outputs are `dout`
+ * (dL/dO) and `dprobs` (dL/dP; NULL when no gradient reaches P). This is the
+ * two-output gradient of the FlagOS-OP page's Implementation section (its
+ * autograd.Function takes both) and of its "P800 fused backward" update (the
+ * softmax Jacobian taken from the probabilities; the gradients of the query
+ * heads that share a key/value head summed back onto it):
+ *   P_ij  = exp(S_ij - LSE_i)        (S as in sdpa_math_fwd; recomputed from
+ *                                     the saved LSE, not read back)
+ *   dP_ij = dout_i . v_j + dprobs_ij
+ *   dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik)
+ *   dq_i  = scale sum_j dS_ij k_j,  dk_j = scale sum_i dS_ij q_i,
+ *   dv_j  = sum_i P_ij dout_i        (i over every query head of the group)
+ * Removed keys and dead rows receive no gradient; no gradient is returned for
+ * an additive mask.
+ *
+ * q, k, v, mask, is_causal, scale, enable_gqa: exactly as passed to the
+ *        forward (same values: the probabilities are recomputed from them)
+ * lse    [B, Hq, Sq] f32, the forward's LSE
+ * dout   [B, Hq, Sq, Dv] q dtype; dprobs [B, Hq, Sq, Skv] q dtype or NULL
+ * dq     [B, Hq, Sq, D], dk [B, Hkv, Skv, D], dv [B, Hkv, Skv, Dv]: q dtype,
+ *        written in full (may be uninitialised)
+ * workspace  device memory of at least sdpa_math_bwd_workspace_bytes bytes,
+ *        16-byte aligned, owned by the caller, scratch for this call only
+ *        (calls sharing one must be ordered on a stream)
+ * Layout: last dims contiguous; q, k, v, dout, dq, dk, dv need 16-byte
+ * aligned bases and row strides. Errors as sdpa_math_fwd, plus
+ * SDPA_ERR_INVALID_ARG for a missing or short workspace; nothing is enqueued
+ * on error. Enqueued on `hip_stream` without synchronising; deterministic
+ * (no atomics). The library allocates nothing.
+ */
+sdpa_status_t sdpa_math_bwd(const sdpa_tensor_t* q, const sdpa_tensor_t* k,
+                            const sdpa_tensor_t* v, const sdpa_tensor_t* mask,
+                            int is_causal, float scale, int enable_gqa,
+                            const sdpa_tensor_t* lse, const sdpa_tensor_t* dout,
+                            const sdpa_tensor_t* dprobs, sdpa_tensor_t* dq, sdpa_tensor_t* dk,
+                            sdpa_tensor_t* dv, void* workspace, size_t workspace_bytes,
+                            void* hip_stream);
+
+/*
+ * sdpa_math_bwd_workspace_bytes — bytes of workspace sdpa_math_bwd needs for
+ * these inputs (4 * B * Hq * Sq: one float32 per query row). Validates the
+ * inputs like sdpa_math_plan; *bytes is 0 on error.
+ */
+sdpa_status_t sdpa_math_bwd_workspace_bytes(const sdpa_tensor_t* q, const sdpa_tensor_t* k,
+                                            const sdpa_tensor_t* v, const sdpa_tensor_t* mask,
+                                            int is_causal, int enable_gqa, size_t* bytes);
 
 /* Message of the last failed call on this thread ("" if none): the text
  * behind the status codes above, which map the FlagOS-OP page's

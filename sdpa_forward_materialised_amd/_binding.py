@@ -29,7 +29,8 @@ _DTYPES = {torch.float32: SDPA_F32, torch.float16: SDPA_F16, torch.bfloat16: SDP
            torch.bool: SDPA_BOOL}
 
 EXPORTS = ("sdpa_math_fwd", "sdpa_math_fwd_path", "sdpa_math_fwd_ws", "sdpa_math_workspace_bytes",
-           "sdpa_math_fwd_noalloc", "sdpa_math_plan", "sdpa_math_last_error",
+           "sdpa_math_fwd_noalloc", "sdpa_math_bwd", "sdpa_math_bwd_workspace_bytes", "sdpa_math_plan",
+           "sdpa_math_last_error",
            "sdpa_math_version", "sdpa_probe_fill", "sdpa_probe_copy")
 
 
@@ -68,6 +69,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int]
     lib.sdpa_math_fwd_noalloc.restype = ctypes.c_int
     lib.sdpa_math_fwd_noalloc.argtypes = lib.sdpa_math_fwd.argtypes + [ctypes.c_int]
+    lib.sdpa_math_bwd.restype = ctypes.c_int
+    lib.sdpa_math_bwd.argtypes = [T, T, T, T, ctypes.c_int, ctypes.c_float, ctypes.c_int, T, T, T, T, T, T,
+                                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.sdpa_math_bwd_workspace_bytes.restype = ctypes.c_int
+    lib.sdpa_math_bwd_workspace_bytes.argtypes = [T, T, T, T, ctypes.c_int, ctypes.c_int,
+                                                  ctypes.POINTER(ctypes.c_size_t)]
     lib.sdpa_math_workspace_bytes.restype = ctypes.c_int
     lib.sdpa_math_workspace_bytes.argtypes = [T, T, T, T, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
     lib.sdpa_math_plan.restype = ctypes.c_int
@@ -240,6 +247,78 @@ def fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             rc = lib.sdpa_math_fwd_noalloc(*args, ctypes.c_void_p(_current_stream(dev)), PATHS[path])
     if rc != 0:
         _raise(rc, lib)
+
+
+def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor,
+        dprobs: Optional[torch.Tensor] = None, attn_mask: Optional[torch.Tensor] = None, is_causal: bool = False,
+        scale: Optional[float] = None, enable_gqa: bool = False, causal_alignment: str = "top_left",
+        out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None
+        ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """``sdpa_math_bwd``: (dq, dk, dv) for upstream gradients ``dout`` (dL/dO)
+    and ``dprobs`` (dL/dP, or None). The other arguments are those of the
+    forward call and its LSE. ``out`` may pass preallocated (dq, dk, dv)."""
+    lib = load_library()
+    dev = _check_devices(q, k, v, attn_mask, lse, dout, dprobs)
+    causal = _causal_code(is_causal, causal_alignment)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, S, D]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[3]) if q.shape[3] > 0 else 1.0
+    if out is None:
+        dq, dk, dv = torch.empty_like(q, memory_format=torch.contiguous_format), \
+            torch.empty_like(k, memory_format=torch.contiguous_format), \
+            torch.empty_like(v, memory_format=torch.contiguous_format)
+    else:
+        dq, dk, dv = out
+        _check_devices(q, dq, dk, dv)
+    dq_, dk_, dv_ = _desc(q, 4), _desc(k, 4), _desc(v, 4)
+    dm = _desc(attn_mask, 4)
+    n = ctypes.c_size_t(0)
+    rc = lib.sdpa_math_bwd_workspace_bytes(dq_, dk_, dv_, dm, causal, int(bool(enable_gqa)), ctypes.byref(n))
+    if rc != 0:
+        _raise(rc, lib)
+    ws = torch.empty(max(n.value, 16), dtype=torch.uint8, device=dev)
+    args = (dq_, dk_, dv_, dm, causal, float(scale), int(bool(enable_gqa)), _desc(lse, 3), _desc(dout, 4),
+            _desc(dprobs, 4), _desc(dq, 4), _desc(dk, 4), _desc(dv, 4), ctypes.c_void_p(ws.data_ptr()), n.value)
+    if dev.index == torch.cuda.current_device():
+        rc = lib.sdpa_math_bwd(*args, ctypes.c_void_p(_current_stream(dev)))
+    else:
+        with torch.cuda.device(dev):
+            rc = lib.sdpa_math_bwd(*args, ctypes.c_void_p(_current_stream(dev)))
+    if rc != 0:
+        _raise(rc, lib)
+    return dq, dk, dv
+
+
+class SdpaMathFunction(torch.autograd.Function):
+    """(O, P) = sdpa_math(q, k, v, ...) with gradients from both outputs
+    (the FlagOS-OP page's autograd.Function, Implementation section): the
+    forward saves q, k, v, the mask and LSE; the backward calls
+    ``sdpa_math_bwd`` with dL/dO and dL/dP. The mask gets no gradient."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, attn_mask, is_causal, scale, enable_gqa, causal_alignment):
+        O, P, L = fwd(q, k, v, attn_mask, is_causal, scale, enable_gqa, causal_alignment=causal_alignment)
+        ctx.save_for_backward(q, k, v, attn_mask, L)
+        ctx.args = (is_causal, scale, enable_gqa, causal_alignment)
+        ctx.mark_non_differentiable(L)
+        return O, P, L
+
+    @staticmethod
+    def backward(ctx, dO, dP, dL):
+        q, k, v, m, L = ctx.saved_tensors
+        is_causal, scale, gqa, align = ctx.args
+        if dO is None:
+            dO = torch.zeros(q.shape[:3] + (v.shape[3],), dtype=q.dtype, device=q.device)
+        dq, dk, dv = bwd(q, k, v, L, dO.contiguous(), None if dP is None else dP.contiguous(), m, is_causal, scale,
+                         gqa, align)
+        return dq, dk, dv, None, None, None, None, None
+
+
+def sdpa_math(q, k, v, attn_mask=None, is_causal=False, scale=None, enable_gqa=False, causal_alignment="top_left"):
+    """Differentiable (O, P, LSE): ``fwd`` with ``sdpa_math_bwd`` as its
+    backward (gradients reach q, k and v through both O and P)."""
+    return SdpaMathFunction.apply(q, k, v, attn_mask, is_causal, scale, enable_gqa, causal_alignment)
 
 
 def plan(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, attn_mask: Optional[torch.Tensor] = None,

@@ -23,8 +23,8 @@ LIB = os.path.join(PKG, "libsdpa_math.so")
 
 ARCH = os.environ.get("SDPA_MATH_ARCH", "gfx950")
 
-SOURCES = ["twopass_bf16.hip", "twopass_f16.hip", "twopass_f32.hip", "fused.hip", "probes.hip", "noalloc.hip",
-           "sdpa_math_api.cpp"]
+SOURCES = ["twopass_bf16.hip", "twopass_f16.hip", "twopass_f32.hip", "fused.hip", "backward.hip", "probes.hip",
+           "noalloc.hip", "sdpa_math_api.cpp"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC",

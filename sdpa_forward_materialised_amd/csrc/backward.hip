@@ -1,0 +1,527 @@
+// Backward of the materialised-probability SDPA forward: dq, dk, dv from
+// the gradients of both outputs, dout = dL/dO and dprobs = dL/dP.
+//
+// Math (FlagOS-OP pull request "feat: add sdpa_math operator (Ascend Triton +
+// P800 exact-P/A1)": Implementation section, an autograd.Function taking
+// both output gradients; "P800 fused backward" update, the softmax Jacobian
+// from the probability map and the query-head gradients summed back to the
+// key/value heads):
+//   P_ij   = exp(S_ij - LSE_i)  (recomputed exactly from the saved LSE, the
+//            identity of the page's "P800 exact-P fast path" update)
+//   dP_ij  = dout_i . v_j + dprobs_ij
+//   D_i    = sum_j P_ij dP_ij
+//   dS_ij  = P_ij (dP_ij - D_i)
+//   dq_i   = scale sum_j dS_ij k_j,   dk_j = scale sum_i dS_ij q_i,
+//   dv_j   = sum_i P_ij dout_i        (i over every query head of the group)
+//
+// Two launches, no atomics (every output element has one owner, so results
+// are deterministic):
+//  * sdpa_bwd_q_kernel: a wave owns 32 query rows; K and V tiles of 32 keys
+//    are staged in LDS. Sweep 1 recomputes S^T = K Q^T and dP^T = V dout^T
+//    on MFMA (the same keys x queries layout as the forward: each lane holds
+//    two runs of 8 consecutive keys of one query row), adds dprobs and folds
+//    D_i, which also goes to the workspace; sweep 2 recomputes them, forms
+//    dS and accumulates dq^T += K^T dS^T.
+//  * sdpa_bwd_kv_kernel: a wave owns 32 keys of one (batch, key/value head)
+//    and walks every query head of its group and every query tile (Q, dout,
+//    LSE and D staged in LDS): S = Q K^T and dP = dout V^T with queries x
+//    keys accumulators (each lane: runs of 8 consecutive queries of one key),
+//    then dv^T += dout^T P and dk^T += Q^T dS.
+// P and dS enter the 16-bit products as the rounded value plus its rounded
+// residual (as in the forward), so the products carry them to twice the
+// dtype's precision; scores, row terms and accumulation are float32.
+
+#include <type_traits>
+
+#include "sdpa_device.h"
+
+namespace sdpa {
+
+namespace {
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+__device__ __forceinline__ u32x2 lds_tr16(const void* p) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p));
+}
+
+constexpr int BW = 2;  // waves per workgroup in both kernels
+
+// An LDS tile of rows of D elements: row-major, 16-byte chunks of a row
+// permuted in groups of four (chunk c of row r at r * CPR + (c ^ f(r))), so
+// that transposing reads of four-row groups stay free of bank conflicts.
+template <typename T, int D>
+struct Tile {
+    static constexpr int SZ = (int)sizeof(T);
+    static constexpr int ROWB = D * SZ;
+    static constexpr int CPR = ROWB / 16;
+    static constexpr int RPB = ROWB >= 256 ? 1 : 256 / ROWB;
+    static constexpr int BYTES32 = 32 * ROWB;  // bytes of a 32-row tile
+    static_assert(CPR % 4 == 0, "tile rows must hold a multiple of 4 chunks");
+    static __device__ __forceinline__ int f(int row) { return 4 * ((row / RPB) & (CPR / 4 - 1)); }
+    static __device__ __forceinline__ int pos(int row, int chunk) { return row * CPR + (chunk ^ f(row)); }
+};
+
+// Copy rows [row0, row0 + 32) of a slice (row pitch in bytes, rows at or past
+// `limit` read as zeros) into a 32-row LDS tile; threads tid, tid + nt, ...
+template <typename T, int D>
+__device__ __forceinline__ void load_tile32(uint8_t* dst, rsrc_t src, uint32_t pitch, int row0, int limit, int tid,
+                                            int nt) {
+    using TL = Tile<T, D>;
+    for (int i = tid; i < 32 * TL::CPR; i += nt) {
+        const int row = i / TL::CPR, c = i - row * TL::CPR;
+        const int g = row0 + row;
+        const u32x4 x = ld128(src, pred(g < limit, (uint32_t)g * pitch + (uint32_t)(c * 16)));
+        *reinterpret_cast<u32x4*>(dst + TL::pos(row, c) * 16) = x;
+    }
+}
+
+// A operand of an MFMA whose rows are tile rows: lane (m, h) reads tile row
+// `row` (the caller passes base + swap23(m)), elements c*KSTEP + h*KH .. +KH.
+template <typename T, int D>
+__device__ __forceinline__ typename Tr<T>::vec row_operand(const uint8_t* t, int row, int c, int hf) {
+    using TL = Tile<T, D>;
+    constexpr int KH = Tr<T>::KH;
+    const int elem = c * 2 * KH + hf * KH;
+    const uint8_t* p = t + TL::pos(row, elem * TL::SZ / 16) * 16 + ((elem * TL::SZ) & 15);
+    if constexpr (sizeof(T) == 2) return as_vec<T>(*reinterpret_cast<const u32x4*>(p));
+    else return *reinterpret_cast<const float*>(p);
+}
+
+// One element of a tile (float32 tiles: the transposed A operand).
+template <typename T, int D>
+__device__ __forceinline__ float tile_elem(const uint8_t* t, int row, int col) {
+    using TL = Tile<T, D>;
+    return *reinterpret_cast<const float*>(t + TL::pos(row, col * TL::SZ / 16) * 16 + ((col * TL::SZ) & 15));
+}
+
+// 16-bit A operand of the transposed tile (A[m][k] = tile[row0 + k][col(m)],
+// k over 16 rows, head-dim chunk dd): the gfx950 transposing LDS read; output
+// lane i receives column 32 dd + swap23(i % 32), so the product's accumulator
+// holds runs of 8 consecutive columns per lane.
+template <typename T, int D>
+__device__ __forceinline__ typename Tr<T>::vec tr_operand(const uint8_t* t, int row0, int dd, int lane) {
+    using TL = Tile<T, D>;
+    const int trg = lane >> 4, trs = lane & 15;
+    const int sig = ((trs & 1) << 1) | ((trs >> 1) & 1);
+    const int trow = 8 * (trg >> 1) + (trs >> 2);
+    const int tcol = 16 * (trg & 1) + 4 * sig;
+    u32x2 half[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int row = row0 + trow + 4 * r;
+        const int col = 32 * dd + tcol;
+        half[r] = lds_tr16(t + TL::pos(row, col * TL::SZ / 16) * 16 + ((col * TL::SZ) & 15));
+    }
+    return __builtin_bit_cast(typename Tr<T>::vec, u32x4{half[0][0], half[0][1], half[1][0], half[1][1]});
+}
+
+// acc^T += tile^T x W for a 32-row block of the tile starting at row0: W is
+// the lane's 16 values (two runs of 8 consecutive rows, the accumulator
+// layout of a keys x queries or queries x keys product), carried as the
+// rounded value plus its rounded residual for 16-bit types.
+// `pre` multiplies W before it is split (an exact power of two; the caller
+// divides the accumulator by it): fp16 probabilities, at most 1, are lifted
+// by 2^12 so that small ones stay out of fp16's subnormal range, where the
+// split would carry them only to an absolute 2^-25.
+template <typename T, int D>
+__device__ __forceinline__ void acc_tr_product(f32x16* acc, const uint8_t* t, int row0, const float* w, int lane,
+                                               float pre = 1.0f) {
+    using TR = Tr<T>;
+    constexpr int ND = D / 32;
+    const int n = lane & 31, hf = lane >> 5;
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+            typename TR::vec a[ND];
+#pragma unroll
+            for (int dd = 0; dd < ND; ++dd) a[dd] = tr_operand<T, D>(t, row0 + 16 * c2, dd, lane);
+            float ws[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ws[e] = w[8 * c2 + e] * pre;
+            const typename TR::vec hi = TR::cvt8(ws);
+            const typename TR::vec lo = TR::lo8(ws, hi);
+#pragma unroll
+            for (int dd = 0; dd < ND; ++dd) acc[dd] = TR::mfma(a[dd], hi, acc[dd]);
+#pragma unroll
+            for (int dd = 0; dd < ND; ++dd) acc[dd] = TR::mfma(a[dd], lo, acc[dd]);
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = row0 + kk(hf, r);
+#pragma unroll
+            for (int dd = 0; dd < ND; ++dd)
+                acc[dd] = TR::mfma(tile_elem<T, D>(t, row, 32 * dd + swap23(n)), w[r], acc[dd]);
+        }
+    }
+}
+
+// Store a lane's D-column accumulator (runs of 8 consecutive columns) to
+// row `row_off` of a descriptor, times `mul`, rounded to T.
+template <typename T, int D>
+__device__ __forceinline__ void store_acc_row(rsrc_t r, uint32_t row_off, bool ok, const f32x16* acc, float mul, int hf) {
+#pragma unroll
+    for (int dd = 0; dd < D / 32; ++dd) {
+        float x[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x[e] = acc[dd][e] * mul;
+        store8<T, true>(r, row_off, ok, 32 * dd + 8 * hf, D, x);
+        store8<T, true>(r, row_off, ok, 32 * dd + 16 + 8 * hf, D, x + 8);
+    }
+}
+
+// B operand held by a lane for row n of a slice: elements c*KSTEP + h*KH ..
+template <typename T, int D>
+__device__ __forceinline__ void load_frags(typename Tr<T>::vec* f, rsrc_t r, uint32_t row_off, bool ok, int hf) {
+    constexpr int KH = Tr<T>::KH;
+#pragma unroll
+    for (int c = 0; c < D / (2 * KH); ++c) {
+        const uint32_t off = pred(ok, row_off + (uint32_t)((c * 2 * KH + hf * KH) * (int)sizeof(T)));
+        if constexpr (sizeof(T) == 2) f[c] = as_vec<T>(ld128(r, off));
+        else f[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+    }
+}
+
+// dprobs of lane (n, h) in a keys x queries block: row `row_off`, keys
+// jb + kk(h, r) (past Skv: 0).
+template <typename T>
+__device__ __forceinline__ void load_dprobs16(const BwdArgs& a, rsrc_t r, uint32_t row_off, bool row_ok, int jb, int hf,
+                                              float* out) {
+    constexpr int SZ = (int)sizeof(T);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const int j = jb + 16 * c + 8 * hf;
+        if (a.dp_vec) {
+            const uint32_t off = pred(row_ok && j < a.f.Skv, row_off + (uint32_t)(j * SZ));
+            if constexpr (SZ == 2) {
+                const u32x4 w = ld128(r, off);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) out[8 * c + e] = Tr<T>::to_f((w[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+            } else {
+                const u32x4 w0 = ld128(r, off);
+                const u32x4 w1 = ld128(r, off == OOB ? OOB : off + 16);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t b0 = w0[e], b1 = w1[e];
+                    out[8 * c + e] = __builtin_bit_cast(float, b0);
+                    out[8 * c + 4 + e] = __builtin_bit_cast(float, b1);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t off = pred(row_ok && j + e < a.f.Skv, row_off + (uint32_t)((j + e) * SZ));
+                if constexpr (SZ == 2) out[8 * c + e] = Tr<T>::to_f(__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+                else out[8 * c + e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+            }
+        }
+    }
+}
+
+// One mask element (base-2 additive term: a bool mask gives 0 where it keeps
+// the key, -inf where it removes it).
+template <typename T, int MASK>
+__device__ __forceinline__ float mask_elem(const FwdArgs& f, rsrc_t mr, int qi, int j) {
+    constexpr int ME = MASK == MASK_BOOL ? 1 : (int)sizeof(T);
+    const uint32_t off = (uint32_t)(((int64_t)qi * f.m_s[2] + (int64_t)j * f.m_s[3]) * ME);
+    if constexpr (MASK == MASK_BOOL) {
+        return __builtin_amdgcn_raw_buffer_load_b8(mr, off, 0, 0) ? 0.0f : -INFINITY;
+    } else if constexpr (sizeof(T) == 2) {
+        return Tr<T>::to_f(__builtin_amdgcn_raw_buffer_load_b16(mr, off, 0, 0)) * LOG2E;
+    } else {
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(mr, off, 0, 0)) * LOG2E;
+    }
+}
+
+// ====================================================================== dq
+
+template <typename T, int D, int MASK, bool HAS_DP>
+__global__ __launch_bounds__(BW * 64) void sdpa_bwd_q_kernel(const BwdArgs a) {
+    using TR = Tr<T>;
+    using vec = typename TR::vec;
+    using TL = Tile<T, D>;
+    constexpr int SZ = (int)sizeof(T);
+    constexpr int KH = TR::KH;
+    constexpr int NKS = D / (2 * KH);
+    constexpr int ND = D / 32;
+    constexpr int ME = MASK == MASK_BOOL ? 1 : SZ;
+    const FwdArgs& f = a.f;
+
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TL::BYTES32];
+    uint8_t* kt = smem;
+    uint8_t* vt = smem + TL::BYTES32;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 31, hf = lane >> 5;
+    const int nqb = (f.Sq + 32 * BW - 1) / (32 * BW);
+    const int bh = blockIdx.x / nqb;
+    const int qblk = blockIdx.x - bh * nqb;
+    const int b = bh / f.Hq, h = bh - (bh / f.Hq) * f.Hq;
+    const int hk = h / f.group;
+    const int q0 = qblk * 32 * BW;
+    const int qw = q0 + 32 * wave;
+    const int qi = qw + n;
+    const bool row_ok = qi < f.Sq;
+    const int kend = f.causal ? min(f.Skv, max(0, q0 + 32 * BW + f.coff)) : f.Skv;
+    const int ntiles = (kend + 31) / 32;
+
+    const rsrc_t qr = make_rsrc(static_cast<const T*>(f.q) + b * f.q_s[0] + h * f.q_s[1], f.q_ext);
+    const rsrc_t kr = make_rsrc(static_cast<const T*>(f.k) + b * f.k_s[0] + hk * f.k_s[1], f.k_ext);
+    const rsrc_t vr = make_rsrc(static_cast<const T*>(f.v) + b * f.v_s[0] + hk * f.v_s[1], f.v_ext);
+    const rsrc_t dor = make_rsrc(static_cast<const T*>(a.dout) + b * a.do_s[0] + h * a.do_s[1], a.do_ext);
+    const rsrc_t dqr = make_rsrc(static_cast<T*>(a.dq) + b * a.dq_s[0] + h * a.dq_s[1], a.dq_ext);
+    rsrc_t dpr = qr, mr = qr;
+    if constexpr (HAS_DP) dpr = make_rsrc(static_cast<const T*>(a.dprobs) + b * a.dp_s[0] + h * a.dp_s[1], a.dp_ext);
+    if constexpr (MASK != MASK_NONE)
+        mr = make_rsrc(static_cast<const uint8_t*>(f.mask) + (b * f.m_s[0] + h * f.m_s[1]) * ME, f.m_ext);
+
+    vec qf[NKS], df[NKS];
+    load_frags<T, D>(qf, qr, (uint32_t)(row_ok ? qi : 0) * (uint32_t)(f.q_s[2] * SZ), row_ok, hf);
+    load_frags<T, D>(df, dor, (uint32_t)(row_ok ? qi : 0) * (uint32_t)(a.do_s[2] * SZ), row_ok, hf);
+    float lse2 = INFINITY;  // dead or absent rows: every probability exp2(-inf) = 0
+    if (row_ok) {
+        const float l = f.lse[b * f.l_s[0] + h * f.l_s[1] + (int64_t)qi * f.l_s[2]];
+        lse2 = l == -INFINITY ? INFINITY : l * LOG2E;
+    }
+    const uint32_t dp_row = (uint32_t)(row_ok ? qi : 0) * (uint32_t)(a.dp_s[2] * SZ);
+    const uint32_t m_row = (uint32_t)((int64_t)(row_ok ? qi : 0) * f.m_s[2] * ME);
+    const uint32_t krow = (uint32_t)(f.k_s[2] * SZ), vrow = (uint32_t)(f.v_s[2] * SZ);
+
+    // probabilities and gradient-at-P of this lane's 16 (query, key) pairs of
+    // 32-key tile t (staged); removed keys give P = 0
+    auto block = [&](int t, float* p, float* dp) __attribute__((always_inline)) {
+        const int jb = t * 32;
+        f32x16 s = {}, g = {};
+#pragma unroll
+        for (int c = 0; c < NKS; ++c) s = TR::mfma(row_operand<T, D>(kt, swap23(n), c, hf), qf[c], s);
+#pragma unroll
+        for (int c = 0; c < NKS; ++c) g = TR::mfma(row_operand<T, D>(vt, swap23(n), c, hf), df[c], g);
+        float mv[16];
+        if constexpr (MASK != MASK_NONE) load_mask16<T, MASK, false>(f, mr, m_row, jb, hf, mv);
+        float dpv[16];
+        if constexpr (HAS_DP) load_dprobs16<T>(a, dpr, dp_row, row_ok, jb, hf, dpv);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int j = jb + kk(hf, r);
+            float x = MASK != MASK_NONE ? __builtin_fmaf(s[r], f.scale_log2, mv[r]) : s[r] * f.scale_log2;
+            if (j >= f.Skv || (f.causal && j > qi + f.coff)) x = -INFINITY;
+            p[r] = fast_exp2(x - lse2);
+            dp[r] = HAS_DP ? g[r] + dpv[r] : g[r];
+        }
+    };
+    auto stage = [&](int t) __attribute__((always_inline)) {
+        __syncthreads();  // the previous tile's reads are done
+        load_tile32<T, D>(kt, kr, krow, t * 32, f.Skv, tid, BW * 64);
+        load_tile32<T, D>(vt, vr, vrow, t * 32, f.Skv, tid, BW * 64);
+        __syncthreads();
+    };
+
+    // ---------------- sweep 1: D_i = sum_j P_ij dP_ij
+    float dsum = 0.0f;
+    for (int t = 0; t < ntiles; ++t) {
+        stage(t);
+        float p[16], dp[16];
+        block(t, p, dp);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dsum = __builtin_fmaf(p[r], dp[r], dsum);
+    }
+    dsum += __shfl_xor(dsum, 32);
+    if (row_ok && hf == 0) a.dsum[((int64_t)b * f.Hq + h) * f.Sq + qi] = dsum;
+
+    // ---------------- sweep 2: dS = P (dP - D); dq^T += K^T dS^T
+    f32x16 acc[ND];
+#pragma unroll
+    for (int dd = 0; dd < ND; ++dd) acc[dd] = f32x16{};
+    for (int t = 0; t < ntiles; ++t) {
+        stage(t);
+        float p[16], dp[16], ds[16];
+        block(t, p, dp);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ds[r] = p[r] * (dp[r] - dsum);
+        acc_tr_product<T, D>(acc, kt, 0, ds, lane);
+    }
+    store_acc_row<T, D>(dqr, (uint32_t)(row_ok ? qi : 0) * (uint32_t)(a.dq_s[2] * SZ), row_ok, acc, a.scale, hf);
+}
+
+// ====================================================================== dk, dv
+
+template <typename T, int D, int MASK, bool HAS_DP>
+__global__ __launch_bounds__(BW * 64) void sdpa_bwd_kv_kernel(const BwdArgs a) {
+    using TR = Tr<T>;
+    using TL = Tile<T, D>;
+    constexpr int SZ = (int)sizeof(T);
+    constexpr int KH = TR::KH;
+    constexpr int NKS = D / (2 * KH);
+    constexpr int ND = D / 32;
+    constexpr int ME = MASK == MASK_BOOL ? 1 : SZ;
+    constexpr float P_LIFT = std::is_same<T, _Float16>::value ? 4096.0f : 1.0f;
+    const FwdArgs& f = a.f;
+
+    // Q and dout tiles of the current 32 query rows, their log2-domain LSE and
+    // D, then per wave its 32 key rows of K and V and its dprobs tile
+    constexpr int DPB = 32 * 32 * SZ;  // dprobs tile: 32 queries x 32 keys
+    constexpr int WAVEB = 2 * TL::BYTES32 + DPB;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TL::BYTES32 + 2 * 32 * 4 + BW * WAVEB];
+    uint8_t* qt = smem;
+    uint8_t* dot = smem + TL::BYTES32;
+    float* lse_s = reinterpret_cast<float*>(smem + 2 * TL::BYTES32);
+    float* dsum_s = lse_s + 32;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 31, hf = lane >> 5;
+    uint8_t* kw = smem + 2 * TL::BYTES32 + 2 * 32 * 4 + wave * WAVEB;
+    uint8_t* vw = kw + TL::BYTES32;
+    uint8_t* dpw = vw + TL::BYTES32;
+
+    const int nkb = (f.Skv + 32 * BW - 1) / (32 * BW);
+    const int bk = blockIdx.x / nkb;
+    const int kblk = blockIdx.x - bk * nkb;
+    const int b = bk / f.Hkv, hk = bk - (bk / f.Hkv) * f.Hkv;
+    const int k0 = kblk * 32 * BW;
+    const int kw0 = k0 + 32 * wave;
+    const int kj = kw0 + n;  // this lane's key
+    const bool key_ok = kj < f.Skv;
+
+    const rsrc_t kr = make_rsrc(static_cast<const T*>(f.k) + b * f.k_s[0] + hk * f.k_s[1], f.k_ext);
+    const rsrc_t vr = make_rsrc(static_cast<const T*>(f.v) + b * f.v_s[0] + hk * f.v_s[1], f.v_ext);
+    const rsrc_t dkr = make_rsrc(static_cast<T*>(a.dk) + b * a.dk_s[0] + hk * a.dk_s[1], a.dk_ext);
+    const rsrc_t dvr = make_rsrc(static_cast<T*>(a.dv) + b * a.dv_s[0] + hk * a.dv_s[1], a.dv_ext);
+
+    // this wave's key rows (B operands of both products)
+    load_tile32<T, D>(kw, kr, (uint32_t)(f.k_s[2] * SZ), kw0, f.Skv, lane, 64);
+    load_tile32<T, D>(vw, vr, (uint32_t)(f.v_s[2] * SZ), kw0, f.Skv, lane, 64);
+
+    f32x16 dk[ND], dv[ND];
+#pragma unroll
+    for (int dd = 0; dd < ND; ++dd) {
+        dk[dd] = f32x16{};
+        dv[dd] = f32x16{};
+    }
+    // causal: query i sees key j iff j <= i + coff, so queries below
+    // k0 - coff see none of this workgroup's keys
+    const int qstart = f.causal ? max(0, k0 - f.coff) / 32 * 32 : 0;
+
+    for (int hh = 0; hh < f.group; ++hh) {
+        const int h = hk * f.group + hh;
+        const rsrc_t qr = make_rsrc(static_cast<const T*>(f.q) + b * f.q_s[0] + h * f.q_s[1], f.q_ext);
+        const rsrc_t dor = make_rsrc(static_cast<const T*>(a.dout) + b * a.do_s[0] + h * a.do_s[1], a.do_ext);
+        rsrc_t dpr = qr, mr = qr;
+        if constexpr (HAS_DP)
+            dpr = make_rsrc(static_cast<const T*>(a.dprobs) + b * a.dp_s[0] + h * a.dp_s[1], a.dp_ext);
+        if constexpr (MASK != MASK_NONE)
+            mr = make_rsrc(static_cast<const uint8_t*>(f.mask) + (b * f.m_s[0] + h * f.m_s[1]) * ME, f.m_ext);
+        const float* lse_h = f.lse + b * f.l_s[0] + h * f.l_s[1];
+        const float* dsum_h = a.dsum + ((int64_t)b * f.Hq + h) * f.Sq;
+
+        for (int i0 = qstart; i0 < f.Sq; i0 += 32) {
+            __syncthreads();  // the previous tile's reads are done
+            load_tile32<T, D>(qt, qr, (uint32_t)(f.q_s[2] * SZ), i0, f.Sq, tid, BW * 64);
+            load_tile32<T, D>(dot, dor, (uint32_t)(a.do_s[2] * SZ), i0, f.Sq, tid, BW * 64);
+            if (tid < 32) {
+                const int i = i0 + tid;
+                float l = i < f.Sq ? lse_h[(int64_t)i * f.l_s[2]] : -INFINITY;
+                lse_s[tid] = l == -INFINITY ? INFINITY : l * LOG2E;
+                dsum_s[tid] = i < f.Sq ? dsum_h[i] : 0.0f;
+            }
+            if constexpr (HAS_DP) {
+                // dprobs rows i0 .. i0+31, this wave's 32 keys, staged row-major
+                for (int e = lane; e < 32 * 32; e += 64) {
+                    const int rr = e >> 5, cc = e & 31;
+                    const int i = i0 + rr, j = kw0 + cc;
+                    const uint32_t off = pred(i < f.Sq && j < f.Skv,
+                                              (uint32_t)i * (uint32_t)(a.dp_s[2] * SZ) + (uint32_t)(j * SZ));
+                    if constexpr (SZ == 2)
+                        reinterpret_cast<uint16_t*>(dpw)[rr * 32 + cc] = __builtin_amdgcn_raw_buffer_load_b16(dpr, off, 0, 0);
+                    else
+                        reinterpret_cast<uint32_t*>(dpw)[rr * 32 + cc] = __builtin_amdgcn_raw_buffer_load_b32(dpr, off, 0, 0);
+                }
+            }
+            __syncthreads();
+
+            // S = Q K^T and dP = dout V^T: lane (n, h) holds queries
+            // i0 + kk(h, r) of key kj
+            f32x16 s = {}, g = {};
+#pragma unroll
+            for (int c = 0; c < NKS; ++c)
+                s = TR::mfma(row_operand<T, D>(qt, swap23(n), c, hf), row_operand<T, D>(kw, n, c, hf), s);
+#pragma unroll
+            for (int c = 0; c < NKS; ++c)
+                g = TR::mfma(row_operand<T, D>(dot, swap23(n), c, hf), row_operand<T, D>(vw, n, c, hf), g);
+            float p[16], ds[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int ql = kk(hf, r);
+                const int i = i0 + ql;
+                float x = s[r] * f.scale_log2;
+                if constexpr (MASK != MASK_NONE) {
+                    if (i < f.Sq && key_ok) x = __builtin_fmaf(s[r], f.scale_log2, mask_elem<T, MASK>(f, mr, i, kj));
+                }
+                if (!key_ok || (f.causal && kj > i + f.coff)) x = -INFINITY;
+                p[r] = fast_exp2(x - lse_s[ql]);
+                float dp = g[r];
+                if constexpr (HAS_DP) {
+                    if constexpr (SZ == 2) dp += Tr<T>::to_f(reinterpret_cast<const uint16_t*>(dpw)[ql * 32 + n]);
+                    else dp += reinterpret_cast<const float*>(dpw)[ql * 32 + n];
+                }
+                ds[r] = p[r] * (dp - dsum_s[ql]);
+            }
+            acc_tr_product<T, D>(dv, dot, 0, p, lane, P_LIFT);
+            acc_tr_product<T, D>(dk, qt, 0, ds, lane);
+        }
+    }
+    const uint32_t krow_off = (uint32_t)(key_ok ? kj : 0);
+    store_acc_row<T, D>(dkr, krow_off * (uint32_t)(a.dk_s[2] * SZ), key_ok, dk, a.scale, hf);
+    store_acc_row<T, D>(dvr, krow_off * (uint32_t)(a.dv_s[2] * SZ), key_ok, dv, 1.0f / P_LIFT, hf);
+}
+
+template <typename T, int D, int MASK>
+int launch_bwd_t(const BwdArgs& a, hipStream_t s) {
+    const int64_t nq = (int64_t)a.f.B * a.f.Hq * ((a.f.Sq + 32 * BW - 1) / (32 * BW));
+    const int64_t nk = (int64_t)a.f.B * a.f.Hkv * ((a.f.Skv + 32 * BW - 1) / (32 * BW));
+    if (a.dprobs) {
+        if (nq > 0) hipLaunchKernelGGL((sdpa_bwd_q_kernel<T, D, MASK, true>), dim3((unsigned)nq), dim3(BW * 64), 0, s, a);
+        if (nk > 0) hipLaunchKernelGGL((sdpa_bwd_kv_kernel<T, D, MASK, true>), dim3((unsigned)nk), dim3(BW * 64), 0, s, a);
+    } else {
+        if (nq > 0) hipLaunchKernelGGL((sdpa_bwd_q_kernel<T, D, MASK, false>), dim3((unsigned)nq), dim3(BW * 64), 0, s, a);
+        if (nk > 0) hipLaunchKernelGGL((sdpa_bwd_kv_kernel<T, D, MASK, false>), dim3((unsigned)nk), dim3(BW * 64), 0, s, a);
+    }
+    return (int)hipGetLastError();
+}
+
+template <typename T, int D>
+int launch_bwd_d(int mask_kind, const BwdArgs& a, hipStream_t s) {
+    switch (mask_kind) {
+        case MASK_NONE: return launch_bwd_t<T, D, MASK_NONE>(a, s);
+        case MASK_BOOL: return launch_bwd_t<T, D, MASK_BOOL>(a, s);
+        case MASK_ADD: return launch_bwd_t<T, D, MASK_ADD>(a, s);
+        default: return (int)hipErrorInvalidValue;
+    }
+}
+
+template <typename T>
+int launch_bwd_dt(int D, int mask_kind, const BwdArgs& a, hipStream_t s) {
+    switch (D) {
+        case 32: return launch_bwd_d<T, 32>(mask_kind, a, s);
+        case 64: return launch_bwd_d<T, 64>(mask_kind, a, s);
+        case 128: return launch_bwd_d<T, 128>(mask_kind, a, s);
+        default: return (int)hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+int launch_backward(int dtype, int D, int mask_kind, const BwdArgs& a, void* stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    switch (dtype) {
+        case DT_F32: return launch_bwd_dt<float>(D, mask_kind, a, s);
+        case DT_F16: return launch_bwd_dt<_Float16>(D, mask_kind, a, s);
+        case DT_BF16: return launch_bwd_dt<__bf16>(D, mask_kind, a, s);
+        default: return (int)hipErrorInvalidValue;
+    }
+}
+
+}  // namespace sdpa

@@ -49,6 +49,25 @@ struct FwdArgs {
     uint32_t q_ext, k_ext, v_ext, o_ext, p_ext, m_ext, l_ext;
 };
 
+// Backward: the forward's arguments (q, k, v, mask, lse, shapes, strides,
+// causal offset, base-2 scale; o and p unused) plus the upstream gradients
+// dout [B,Hq,Sq,Dv] and dprobs [B,Hq,Sq,Skv] (may be null), the outputs dq,
+// dk, dv, and the per-row sum D_i = sum_j P_ij dP_ij in a float32 workspace
+// [B*Hq*Sq]. Strides (batch, head, row) in elements, like FwdArgs.
+struct BwdArgs {
+    FwdArgs f;
+    const void* dout;
+    const void* dprobs;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* dsum;
+    int64_t do_s[3], dp_s[3], dq_s[3], dk_s[3], dv_s[3];
+    float scale;       // multiplier of Q K^T (the gradients of q and k carry it)
+    int dp_vec;        // dprobs rows: aligned 16-byte loads, Skv a multiple of 8
+    uint32_t do_ext, dp_ext, dq_ext, dk_ext, dv_ext;
+};
+
 // Launch configuration chosen on the host for one call.
 struct Plan {
     int path;        // 1 fused, 2 two-pass
@@ -71,6 +90,9 @@ int launch_twopass_f32(int D, int mask_kind, int waves, bool vec, const FwdArgs&
 int launch_twopass_f16(int D, int mask_kind, int waves, bool vec, const FwdArgs& a, void* stream);
 int launch_twopass_bf16(int D, int mask_kind, int waves, bool vec, const FwdArgs& a, void* stream);
 int launch_fused(int dtype, int D, int mask_kind, int waves, bool vec, const FwdArgs& a, void* stream);
+// Backward launches (query-side kernel, then key/value-side kernel) on the
+// stream; hipError_t as int.
+int launch_backward(int dtype, int D, int mask_kind, const BwdArgs& a, void* stream);
 // Whether the two-pass kernel can run four compute waves without a loader
 // wave (16-byte layouts) for this head dim and mask kind.
 bool twopass_nl_ok_f32(int D, int mask_kind);

@@ -534,6 +534,121 @@ sdpa_status_t run(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_ten
     return SDPA_OK;
 }
 
+// Byte extent of one (batch, head) slice: `rows` rows of `cols` elements at
+// a row pitch of `pitch` elements (0 rows: 0).
+int64_t slice_extent(int64_t rows, int64_t pitch, int64_t cols, int64_t es) {
+    return rows > 0 && cols > 0 ? ((rows - 1) * pitch + cols) * es : 0;
+}
+
+// Backward workspace: the per-row sum D_i = sum_j P_ij dP_ij in float32.
+size_t bwd_ws_bytes(const Shape& sh) { return (size_t)(sh.B * sh.Hq * sh.Sq) * 4; }
+
+sdpa_status_t check_grad(const sdpa_tensor_t* t, const char* name, int dtype, const int64_t* want, int ndim,
+                         bool aligned) {
+    sdpa_status_t st;
+    if ((st = check_tensor(t, name, ndim))) return st;
+    if (t->dtype != dtype)
+        return fail(SDPA_ERR_INVALID_ARG, "%s must have dtype %s, got %s", name, dtype_name(dtype), dtype_name(t->dtype));
+    if ((st = check_dims(t, name, want, ndim))) return st;
+    if (aligned && numel(t) > 0 && !rows_aligned(t, 16))
+        return fail(SDPA_ERR_UNSUPPORTED, "%s needs a 16-byte aligned base and 16-byte multiple strides", name);
+    return SDPA_OK;
+}
+
+sdpa_status_t run_bwd(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_tensor_t* v,
+                      const sdpa_tensor_t* mask, int is_causal, float scale, int enable_gqa, const sdpa_tensor_t* lse,
+                      const sdpa_tensor_t* dout, const sdpa_tensor_t* dprobs, sdpa_tensor_t* dq, sdpa_tensor_t* dk,
+                      sdpa_tensor_t* dv, void* ws, size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    Shape sh;
+    sdpa_status_t st = validate_inputs(q, k, v, mask, is_causal, enable_gqa, &sh);
+    if (st) return st;
+    const int64_t wl[3] = {sh.B, sh.Hq, sh.Sq};
+    const int64_t wo[4] = {sh.B, sh.Hq, sh.Sq, sh.Dv};
+    const int64_t wp[4] = {sh.B, sh.Hq, sh.Sq, sh.Skv};
+    const int64_t wq[4] = {sh.B, sh.Hq, sh.Sq, sh.D};
+    const int64_t wk[4] = {sh.B, sh.Hkv, sh.Skv, sh.D};
+    const int64_t wv[4] = {sh.B, sh.Hkv, sh.Skv, sh.Dv};
+    if ((st = check_grad(lse, "lse", SDPA_F32, wl, 3, false)) || (st = check_grad(dout, "dout", sh.dtype, wo, 4, true)) ||
+        (dprobs && (st = check_grad(dprobs, "dprobs", sh.dtype, wp, 4, false))) ||
+        (st = check_grad(dq, "dq", sh.dtype, wq, 4, true)) || (st = check_grad(dk, "dk", sh.dtype, wk, 4, true)) ||
+        (st = check_grad(dv, "dv", sh.dtype, wv, 4, true)))
+        return st;
+    if (!std::isfinite(scale)) return fail(SDPA_ERR_INVALID_ARG, "scale must be finite");
+    if (sh.B * sh.Hkv == 0) return SDPA_OK;
+    const size_t need = bwd_ws_bytes(sh);
+    if (need > 0 && (!ws || reinterpret_cast<uintptr_t>(ws) % 16 != 0 || ws_bytes < need))
+        return fail(SDPA_ERR_INVALID_ARG, "the backward needs a 16-byte aligned workspace of %zu bytes "
+                                          "(sdpa_math_bwd_workspace_bytes)", need);
+
+    sdpa::BwdArgs a;
+    std::memset(&a, 0, sizeof a);
+    sdpa::FwdArgs& f = a.f;
+    f.q = q->data;
+    f.k = k->data;
+    f.v = v->data;
+    f.mask = mask ? mask->data : nullptr;
+    f.lse = static_cast<float*>(lse->data);
+    fill_strides3(q, f.q_s);
+    fill_strides3(k, f.k_s);
+    fill_strides3(v, f.v_s);
+    for (int d = 0; d < 3; ++d) f.l_s[d] = eff_stride(lse, d);
+    if (mask)
+        for (int d = 0; d < 4; ++d) f.m_s[d] = eff_stride(mask, d);
+    f.B = (int)sh.B;
+    f.Hq = (int)sh.Hq;
+    f.Hkv = (int)sh.Hkv;
+    f.Sq = (int)sh.Sq;
+    f.Skv = (int)sh.Skv;
+    f.group = (int)(sh.Hq / sh.Hkv);
+    f.causal = is_causal ? 1 : 0;
+    f.coff = (int)causal_offset(sh, is_causal);
+    f.scale_log2 = scale * 1.4426950408889634f;
+    a.scale = scale;
+    a.dout = dout->data;
+    a.dprobs = dprobs ? dprobs->data : nullptr;
+    a.dq = dq->data;
+    a.dk = dk->data;
+    a.dv = dv->data;
+    a.dsum = static_cast<float*>(ws);
+    fill_strides3(dout, a.do_s);
+    if (dprobs) fill_strides3(dprobs, a.dp_s);
+    fill_strides3(dq, a.dq_s);
+    fill_strides3(dk, a.dk_s);
+    fill_strides3(dv, a.dv_s);
+    const int64_t es = elt_size(sh.dtype);
+    const int64_t me = sh.mask_kind == sdpa::MASK_BOOL ? 1 : es;
+    a.dp_vec = dprobs && rows_aligned(dprobs, 16) && sh.Skv % 8 == 0;
+    int64_t ext[10];
+    ext[0] = slice_extent(sh.Sq, f.q_s[2], sh.D, es);
+    ext[1] = slice_extent(sh.Skv, f.k_s[2], sh.D, es);
+    ext[2] = slice_extent(sh.Skv, f.v_s[2], sh.Dv, es);
+    ext[3] = (mask && sh.Skv > 0 && sh.Sq > 0) ? ((sh.Sq - 1) * f.m_s[2] + (sh.Skv - 1) * f.m_s[3] + 1) * me : 0;
+    ext[4] = slice_extent(sh.Sq, f.l_s[2], 1, 4);
+    ext[5] = slice_extent(sh.Sq, a.do_s[2], sh.Dv, es);
+    ext[6] = dprobs ? slice_extent(sh.Sq, a.dp_s[2], sh.Skv, es) : 0;
+    ext[7] = slice_extent(sh.Sq, a.dq_s[2], sh.D, es);
+    ext[8] = slice_extent(sh.Skv, a.dk_s[2], sh.D, es);
+    ext[9] = slice_extent(sh.Skv, a.dv_s[2], sh.Dv, es);
+    for (int i = 0; i < 10; ++i)
+        if (ext[i] < 0 || ext[i] >= (int64_t(1) << 30))
+            return fail(SDPA_ERR_UNSUPPORTED, "one (batch, head) slice spans 1 GiB or more");
+    f.q_ext = (uint32_t)ext[0];
+    f.k_ext = (uint32_t)ext[1];
+    f.v_ext = (uint32_t)ext[2];
+    f.m_ext = (uint32_t)ext[3];
+    f.l_ext = (uint32_t)ext[4];
+    a.do_ext = (uint32_t)ext[5];
+    a.dp_ext = (uint32_t)ext[6];
+    a.dq_ext = (uint32_t)ext[7];
+    a.dk_ext = (uint32_t)ext[8];
+    a.dv_ext = (uint32_t)ext[9];
+    const int err = sdpa::launch_backward(sh.dtype, (int)sh.D, sh.mask_kind, a, stream);
+    if (err != 0)
+        return fail(SDPA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(static_cast<hipError_t>(err)));
+    return SDPA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -598,6 +713,27 @@ sdpa_status_t sdpa_math_workspace_bytes(const sdpa_tensor_t* q, const sdpa_tenso
         return st;
     *bytes = split_ws_bytes(sh, plan.n_splits);
     return SDPA_OK;
+}
+
+sdpa_status_t sdpa_math_bwd_workspace_bytes(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_tensor_t* v,
+                                            const sdpa_tensor_t* mask, int is_causal, int enable_gqa, size_t* bytes) {
+    g_last_error.clear();
+    if (!bytes) return fail(SDPA_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = 0;
+    Shape sh;
+    sdpa_status_t st = validate_inputs(q, k, v, mask, is_causal, enable_gqa, &sh);
+    if (st) return st;
+    *bytes = bwd_ws_bytes(sh);
+    return SDPA_OK;
+}
+
+sdpa_status_t sdpa_math_bwd(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_tensor_t* v,
+                            const sdpa_tensor_t* mask, int is_causal, float scale, int enable_gqa,
+                            const sdpa_tensor_t* lse, const sdpa_tensor_t* dout, const sdpa_tensor_t* dprobs,
+                            sdpa_tensor_t* dq, sdpa_tensor_t* dk, sdpa_tensor_t* dv, void* workspace,
+                            size_t workspace_bytes, void* hip_stream) {
+    return run_bwd(q, k, v, mask, is_causal, scale, enable_gqa, lse, dout, dprobs, dq, dk, dv, workspace,
+                   workspace_bytes, hip_stream);
 }
 
 const char* sdpa_math_last_error(void) { return g_last_error.c_str(); }

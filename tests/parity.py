@@ -17,9 +17,17 @@ TOL_LSE = {torch.float32: 1e-5, torch.float16: 1e-4, torch.bfloat16: 1e-4}
 MANT_BITS = {torch.float32: 23, torch.float16: 10, torch.bfloat16: 7}
 
 
+# frexp exponent of the smallest normal number of each dtype (x = m 2^e,
+# m in [0.5, 1)): below it the spacing stays that of the subnormals
+EMIN = {torch.float32: -125, torch.float16: -13, torch.bfloat16: -125}
+
+
 def ulp(x, dtype):
-    """Spacing of ``dtype`` at |x| (its unit in the last place there)."""
-    _, e = np.frexp(np.abs(x))
+    """Spacing of ``dtype`` at |x| (its unit in the last place there; the
+    subnormal spacing below the smallest normal number, and at zero)."""
+    x = np.abs(np.asarray(x, dtype=np.float64))
+    _, e = np.frexp(x)
+    e = np.where(x == 0, EMIN[dtype], np.maximum(e, EMIN[dtype]))
     return np.ldexp(1.0, e - 1 - MANT_BITS[dtype])
 
 
@@ -128,3 +136,70 @@ def head_slice(q, k, v, mask, b, h):
 
 def default_scale(D):
     return 1.0 / math.sqrt(D)
+
+
+# Backward bound: per element, half an ulp of the dtype at the oracle
+# gradient plus BWD_SLACK times the gradient's envelope, the sum of absolute
+# values of the terms it adds up (float32 accumulation, exp2 of the
+# recomputed probabilities, and the rounded residuals of P and dS in the
+# 16-bit products all scale with it).
+BWD_SLACK = 2.0 ** -12
+
+
+# fp16 has subnormals below 2^-14: there the split of dS into rounded value
+# plus rounded residual carries a term only to an absolute 2^-25, so fp16
+# gradients built from dS (dq, dk) get a floor of 2^-24 per kept term.
+BWD_FP16_FLOOR = 2.0 ** -24
+
+
+def backward_envelopes(q, k, v, mask, causal, scale, gqa, dout, dprobs, causal_alignment="top_left"):
+    """(env_dq, env_dk, env_dv) in float64 from the oracle's probabilities:
+    env_dq_i = |scale| sum_j P_ij (|dP_ij| + |D_i|) |k_j|, env_dk_j the same
+    summed over queries with |q_i|, env_dv_j = sum_i P_ij |dout_i|; for fp16
+    inputs the dq and dk envelopes also carry the subnormal floor,
+    BWD_FP16_FLOOR / BWD_SLACK * |scale| * sum over kept terms of |k_j| or
+    |q_i|."""
+    _, p, _ = oracle.sdpa_reference(q, k, v, mask, causal, scale, gqa, causal_alignment=causal_alignment)
+    q, k, v = (x.double().numpy() for x in (q, k, v))
+    do = dout.double().numpy()
+    B, Hq, Sq, D = q.shape
+    Hkv = k.shape[1]
+    g = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    kr = np.repeat(k, g, axis=1)
+    vr = np.repeat(v, g, axis=1)
+    dp = do @ vr.transpose(0, 1, 3, 2)
+    if dprobs is not None:
+        dp = dp + dprobs.double().numpy()
+    dsum = (p * dp).sum(-1, keepdims=True)
+    w = p * (np.abs(dp) + np.abs(dsum))
+    env_dq = abs(scale) * (w @ np.abs(kr))
+    env_dk = abs(scale) * (w.transpose(0, 1, 3, 2) @ np.abs(q))
+    env_dv = p.transpose(0, 1, 3, 2) @ np.abs(do)
+    if dout.dtype == torch.float16:
+        kept = (p > 0).astype(np.float64)
+        f = BWD_FP16_FLOOR / BWD_SLACK * abs(scale)
+        env_dq = env_dq + f * (kept @ np.abs(kr))
+        env_dk = env_dk + f * (kept.transpose(0, 1, 3, 2) @ np.abs(q))
+    env_dk = env_dk.reshape(B, Hkv, g, *env_dk.shape[2:]).sum(2)
+    env_dv = env_dv.reshape(B, Hkv, g, *env_dv.shape[2:]).sum(2)
+    return env_dq, env_dk, env_dv
+
+
+def compare_backward(got, ref, env, dtype, label=""):
+    """Element-by-element check of (dq, dk, dv) against the oracle."""
+    out = {}
+    for name, g, r, e in zip(("dq", "dk", "dv"), got, ref, env):
+        x = g.detach().cpu().double().numpy()
+        assert x.shape == r.shape, (label, name)
+        assert not np.isnan(x).any(), f"{label}: NaN in {name}"
+        err = np.abs(x - r)
+        bound = 0.5 * ulp(r, dtype) + BWD_SLACK * e
+        bad = err > bound
+        assert not bad.any(), (f"{label}: {int(bad.sum())} {name} elements beyond the bound; "
+                               f"max|d{name}| = {float(err.max()):.3e}, worst ratio "
+                               f"{float((err / np.maximum(bound, 1e-300)).max()):.2f}")
+        out["err_" + name] = float(err.max()) if err.size else 0.0
+        out["ratio_" + name] = float((err / np.maximum(bound, 1e-300)).max()) if err.size else 0.0
+    return out

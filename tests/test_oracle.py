@@ -418,9 +418,11 @@ MUTANTS = [
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_pins_catch_planted_mistakes(tmp_path, name, old, new):
     src = open(ORACLE_SRC).read()
-    assert src.count(old) == 1, name
+    cut = src.index("int oracle_sdpa_bwd(")  # plant it in the forward only
+    fwd, rest = src[:cut], src[cut:]
+    assert fwd.count(old) == 1, name
     mutant_src = tmp_path / "mutant.c"
-    mutant_src.write_text(src.replace(old, new))
+    mutant_src.write_text(fwd.replace(old, new) + rest)
     lib = str(tmp_path / "libmutant.so")
     oracle.build(force=True, src=str(mutant_src), out=lib)
     assert not _pins_pass(lib), f"planted mistake '{name}' went unnoticed"

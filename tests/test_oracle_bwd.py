@@ -232,9 +232,11 @@ BWD_MUTANTS = [
 @pytest.mark.parametrize("name,old,new", BWD_MUTANTS, ids=[m[0] for m in BWD_MUTANTS])
 def test_backward_pins_catch_planted_mistakes(tmp_path, name, old, new):
     src = open(ORACLE_SRC).read()
-    assert src.count(old) == 1, name
+    cut = src.index("int oracle_sdpa_bwd(")  # plant it in the backward only
+    fwd, rest = src[:cut], src[cut:]
+    assert rest.count(old) == 1, name
     mutant_src = tmp_path / "mutant.c"
-    mutant_src.write_text(src.replace(old, new))
+    mutant_src.write_text(fwd + rest.replace(old, new))
     lib = str(tmp_path / "libmutant.so")
     oracle.build(force=True, src=str(mutant_src), out=lib)
     assert not _bwd_pins_pass(lib), f"planted mistake '{name}' went unnoticed"

@@ -13,6 +13,12 @@ def test_ulp_values():
     assert ulp(np.array([3.0]), torch.bfloat16)[0] == 2.0 ** -6
     assert ulp(np.array([5.0]), torch.float16)[0] == 2.0 ** -8
     assert ulp(np.array([0.75]), torch.float32)[0] == 2.0 ** -24
+    # subnormals and zero: the subnormal spacing of the dtype
+    assert ulp(np.array([2.4e-5]), torch.float16)[0] == 2.0 ** -24
+    assert ulp(np.array([0.0]), torch.float16)[0] == 2.0 ** -24
+    assert ulp(np.array([6.2e-5]), torch.float16)[0] == 2.0 ** -24   # smallest normal binade
+    assert ulp(np.array([1e-39]), torch.bfloat16)[0] == 2.0 ** -133
+    assert ulp(np.array([0.0]), torch.float32)[0] == 2.0 ** -149
 
 
 def test_stated_bound_where_rounding_can_meet_it():
