@@ -74,7 +74,9 @@ def load(path: str = _LIB) -> ctypes.CDLL:
     lib.oracle_sdpa_fwd.restype = ctypes.c_int
     lib.oracle_sdpa_fwd.argtypes = [dp, dp, dp, i64, i64, i64, i64, i64, i64, i64,
                                     ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(i64),
-                                    ctypes.c_int, ctypes.c_double, dp, dp, dp]
+                                    ctypes.c_int, ctypes.c_double,
+                                    ctypes.c_void_p, ctypes.POINTER(i64), ctypes.c_double, ctypes.c_int,
+                                    dp, dp, dp]
     lib.oracle_sdpa_bwd.restype = ctypes.c_int
     lib.oracle_sdpa_bwd.argtypes = [dp, dp, dp, i64, i64, i64, i64, i64, i64, i64,
                                     ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(i64),
@@ -133,11 +135,20 @@ def causal_code(is_causal, causal_alignment: str = "top_left") -> int:
     return 2 if causal_alignment == "bottom_right" else 1
 
 
+DROPOUT_RULES = {"explicit": 0, "random": 1}
+
+
 def sdpa_reference(q, k, v, attn_mask=None, is_causal: bool = False,
                    scale: Optional[float] = None, enable_gqa: bool = False,
-                   lib_path: str = _LIB, causal_alignment: str = "top_left"
+                   lib_path: str = _LIB, causal_alignment: str = "top_left",
+                   dropout_p: float = 0.0, dropout_mask=None, dropout_rule: str = "explicit"
                    ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
-    """Return (O [B,Hq,Sq,Dv], P [B,Hq,Sq,Skv], LSE [B,Hq,Sq]) in float64."""
+    """Return (O [B,Hq,Sq,Dv], P [B,Hq,Sq,Skv], LSE [B,Hq,Sq]) in float64.
+
+    ``dropout_mask`` (bool, True keeps; broadcastable to [B,Hq,Sq,Skv]) with
+    ``dropout_p`` applies the FlagOS-OP page's dropout rules: "explicit"
+    returns keep * P and O = (keep * P) V / (1 - p); "random" returns
+    keep * P / (1 - p) and O = that times V. LSE is the undropped one."""
     causal = causal_code(is_causal, causal_alignment)
     q, k, v = _f64(q), _f64(k), _f64(v)
     if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
@@ -158,16 +169,28 @@ def sdpa_reference(q, k, v, attn_mask=None, is_causal: bool = False,
     kind, marr, mstr = MASK_NONE, None, [0, 0, 0, 0]
     if attn_mask is not None:
         kind, marr, mstr = _mask_array(attn_mask, (B, Hq, Sq, Skv))
+    karr, kstr = None, [0, 0, 0, 0]
+    if dropout_mask is not None:
+        kkind, karr, kstr = _mask_array(dropout_mask, (B, Hq, Sq, Skv))
+        if kkind != MASK_BOOL:
+            raise ValueError("dropout_mask must be bool")
+        if dropout_rule not in DROPOUT_RULES:
+            raise ValueError(f"dropout_rule must be one of {sorted(DROPOUT_RULES)}")
+        if not 0.0 <= dropout_p < 1.0:
+            raise ValueError("dropout_p must be in [0, 1)")
     out = np.empty((B, Hq, Sq, Dv), np.float64)
     probs = np.empty((B, Hq, Sq, Skv), np.float64)
     lse = np.empty((B, Hq, Sq), np.float64)
     dp = ctypes.POINTER(ctypes.c_double)
     st = (ctypes.c_int64 * 4)(*mstr)
+    kst = (ctypes.c_int64 * 4)(*kstr)
     lib = load(lib_path)
     rc = lib.oracle_sdpa_fwd(q.ctypes.data_as(dp), k.ctypes.data_as(dp), v.ctypes.data_as(dp),
                              B, Hq, Hkv, Sq, Skv, D, Dv, kind,
                              None if marr is None else marr.ctypes.data_as(ctypes.c_void_p),
                              st, causal, float(scale),
+                             None if karr is None else karr.ctypes.data_as(ctypes.c_void_p), kst,
+                             float(dropout_p), DROPOUT_RULES.get(dropout_rule, 0),
                              out.ctypes.data_as(dp), probs.ctypes.data_as(dp), lse.ctypes.data_as(dp))
     if rc != 0:
         raise ValueError(f"oracle rejected the call (code {rc})")

@@ -33,7 +33,12 @@ def _array(x):
 
 def sdpa_brute(q, k, v, attn_mask=None, is_causal: bool = False,
                scale: Optional[float] = None, enable_gqa: bool = False,
-               causal_alignment: str = "top_left"):
+               causal_alignment: str = "top_left", dropout_p: float = 0.0, dropout_mask=None,
+               dropout_rule: str = "explicit"):
+    """Brute-force (O, P, LSE). With ``dropout_mask`` (True keeps): rule
+    "explicit" returns the kept probabilities as they are and divides O by
+    (1 - p); rule "random" divides the kept probabilities by (1 - p) and O
+    is their product with V."""
     q = _array(q).astype(np.float64)
     k = _array(k).astype(np.float64)
     v = _array(v).astype(np.float64)
@@ -52,6 +57,9 @@ def sdpa_brute(q, k, v, attn_mask=None, is_causal: bool = False,
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     mask = None if attn_mask is None else _array(attn_mask)
+    keep = None if dropout_mask is None else _array(dropout_mask)
+    if keep is not None and dropout_rule not in ("explicit", "random"):
+        raise ValueError(f"unknown dropout rule {dropout_rule!r}")
     # KV heads expanded the way repeat_interleave(Hq // Hkv, dim=1) would.
     kv_head = [h * Hkv // Hq for h in range(Hq)]
 
@@ -84,9 +92,16 @@ def sdpa_brute(q, k, v, attn_mask=None, is_causal: bool = False,
                 z = math.fsum(e)
                 lse[b, h, i] = m + math.log(z)
                 p = [x / z for x in e]
+                oscale = 1.0
+                if keep is not None:
+                    p = [x if bool(_lookup(keep, b, h, i, j)) else 0.0 for j, x in enumerate(p)]
+                    if dropout_rule == "random":
+                        p = [x / (1.0 - dropout_p) for x in p]
+                    else:
+                        oscale = 1.0 / (1.0 - dropout_p)
                 probs[b, h, i, :] = p
                 for d in range(Dv):
-                    out[b, h, i, d] = math.fsum(p[j] * float(v[b, hk, j, d]) for j in range(Skv))
+                    out[b, h, i, d] = oscale * math.fsum(p[j] * float(v[b, hk, j, d]) for j in range(Skv))
     return out, probs, lse
 
 

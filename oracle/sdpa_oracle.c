@@ -45,7 +45,8 @@
  * Outputs (contiguous float64): out [B,Hq,Sq,Dv], probs [B,Hq,Sq,Skv],
  *   lse [B,Hq,Sq].
  * Returns 0 on success, 1 when Hq is not a multiple of Hkv, 2 when causal is
- * combined with a mask, 3 for a bad mask kind, 4 for a bad is_causal.
+ * combined with a mask, 3 for a bad mask kind, 4 for a bad is_causal, 5 for
+ * a bad dropout probability or rule.
  *
  * oracle_sdpa_bwd (at the end of this file) is the backward of the same
  * definition: dq, dk, dv from dL/dO and dL/dP by the plain chain rule.
@@ -71,13 +72,26 @@ int oracle_sdpa_threads(void)
 #endif
 }
 
+/*
+ * Dropout (FlagOS-OP page, Implementation section: the explicit and the
+ * random dropout rule; Intentional divergences: with dropout_p > 0 the
+ * output is the product of the dropped probabilities with V). keep is a
+ * uint8 keep-mask over [B,Hq,Sq,Skv] addressed with keep_strides (NULL: no
+ * dropout), drop_p the dropout probability, keep_rule 0 or 1:
+ *   rule 0 (explicit mask): P_out = keep * P,         O = (keep * P) V / (1 - p)
+ *   rule 1 (random):        P_out = keep * P / (1-p), O = P_out V
+ * LSE is that of the undropped softmax.
+ */
 int oracle_sdpa_fwd(const double* q, const double* k, const double* v,
                     int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv,
                     int64_t D, int64_t Dv,
                     int mask_kind, const void* mask, const int64_t* mask_strides,
                     int is_causal, double scale,
+                    const uint8_t* keep, const int64_t* keep_strides, double drop_p, int keep_rule,
                     double* out, double* probs, double* lse)
 {
+    if (keep && (!(drop_p >= 0.0 && drop_p < 1.0) || (keep_rule != 0 && keep_rule != 1)))
+        return 5;
     if (Hkv <= 0 || Hq % Hkv != 0)
         return 1;
     if (is_causal < 0 || is_causal > 2)
@@ -147,11 +161,26 @@ int oracle_sdpa_fwd(const double* q, const double* k, const double* v,
         for (int64_t j = 0; j < Skv; ++j)
             p[j] = exp(p[j] - L);
 
+        double oscale = 1.0;
+        if (keep) { /* drop the removed probabilities, then the rule's scaling */
+            const double inv = 1.0 / (1.0 - drop_p);
+            for (int64_t j = 0; j < Skv; ++j) {
+                const int64_t off = b * keep_strides[0] + h * keep_strides[1] +
+                                    i * keep_strides[2] + j * keep_strides[3];
+                if (keep[off] == 0)
+                    p[j] = 0.0;
+                else if (keep_rule == 1)
+                    p[j] *= inv;
+            }
+            if (keep_rule == 0)
+                oscale = inv;
+        }
+
         for (int64_t d = 0; d < Dv; ++d) {
             double acc = 0.0;
             for (int64_t j = 0; j < Skv; ++j)
                 acc += p[j] * vh[j * Dv + d];
-            o[d] = acc;
+            o[d] = acc * oscale;
         }
     }
     return 0;

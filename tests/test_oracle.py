@@ -407,7 +407,7 @@ MUTANTS = [
     ("GQA head index", "const int64_t hk = h / group;", "const int64_t hk = h % Hkv;"),
     ("causal diagonal", "if (is_causal && j > i + coff)", "if (is_causal && j >= i + coff)"),
     ("bottom-right offset sign", "is_causal == 2 ? Skv - Sq : 0;", "is_causal == 2 ? Sq - Skv : 0;"),
-    ("bool polarity", "[off] == 0)", "[off] != 0)"),
+    ("bool polarity", "((const uint8_t*)mask)[off] == 0)", "((const uint8_t*)mask)[off] != 0)"),
     ("additive sign", "s += ((const double*)mask)[off];", "s -= ((const double*)mask)[off];"),
     ("LSE missing log-sum", "const double L = m + log(l);", "const double L = m;"),
     ("dead-row LSE", "lse[row] = -INFINITY;", "lse[row] = 0.0;"),
