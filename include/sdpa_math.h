@@ -170,6 +170,31 @@ sdpa_status_t sdpa_math_fwd_ws(const sdpa_tensor_t* q, const sdpa_tensor_t* k,
                                void* workspace, size_t workspace_bytes, void* hip_stream, int path);
 
 /*
+ * sdpa_math_fwd_dropout — sdpa_math_fwd with dropout applied to P under one
+ * of the two rules the FlagOS-OP page fixes (Implementation section: the
+ * explicit and the random dropout rule; Intentional divergences: with
+ * dropout_p > 0 the output is the dropped probabilities times V; single-
+ * kernel fusion update: dropout always takes the two-stage path):
+ *   rule 0 (explicit keep-mask): probs = keep * P,            out = (keep * P) V / (1 - dropout_p)
+ *   rule 1 (random):             probs = keep * P / (1 - p),  out = probs V
+ * with P, LSE (of the undropped softmax) and the masking as sdpa_math_fwd.
+ * keep   bool, broadcastable to [B, Hq, Sq, Skv] (True keeps the entry): the
+ *        random numbers of the call, drawn by the caller (for rule 1, keep
+ *        with probability 1 - dropout_p); read only
+ * dropout_p  in [0, 1), else SDPA_ERR_INVALID_ARG; rule 0 or 1, else
+ *        SDPA_ERR_INVALID_ARG
+ * Runs the two-pass kernel (two compute waves and a loader wave), never the
+ * fused path nor key ranges. Other arguments, layout, ownership and errors as
+ * sdpa_math_fwd.
+ */
+sdpa_status_t sdpa_math_fwd_dropout(const sdpa_tensor_t* q, const sdpa_tensor_t* k,
+                                    const sdpa_tensor_t* v, const sdpa_tensor_t* mask,
+                                    int is_causal, float scale, int enable_gqa,
+                                    float dropout_p, const sdpa_tensor_t* keep, int rule,
+                                    sdpa_tensor_t* out, sdpa_tensor_t* probs, sdpa_tensor_t* lse,
+                                    void* hip_stream);
+
+/*
  * sdpa_math_fwd_noalloc — sdpa_math_fwd_ws for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, hosts
  * that forbid allocation): no workspace argument and nothing allocated. A

@@ -29,7 +29,7 @@ _DTYPES = {torch.float32: SDPA_F32, torch.float16: SDPA_F16, torch.bfloat16: SDP
            torch.bool: SDPA_BOOL}
 
 EXPORTS = ("sdpa_math_fwd", "sdpa_math_fwd_path", "sdpa_math_fwd_ws", "sdpa_math_workspace_bytes",
-           "sdpa_math_fwd_noalloc", "sdpa_math_bwd", "sdpa_math_bwd_workspace_bytes", "sdpa_math_plan",
+           "sdpa_math_fwd_noalloc", "sdpa_math_fwd_dropout", "sdpa_math_bwd", "sdpa_math_bwd_workspace_bytes", "sdpa_math_plan",
            "sdpa_math_last_error",
            "sdpa_math_version", "sdpa_probe_fill", "sdpa_probe_copy")
 
@@ -67,6 +67,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sdpa_math_fwd_ws.restype = ctypes.c_int
     lib.sdpa_math_fwd_ws.argtypes = [T, T, T, T, ctypes.c_int, ctypes.c_float, ctypes.c_int, T, T, T,
                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int]
+    lib.sdpa_math_fwd_dropout.restype = ctypes.c_int
+    lib.sdpa_math_fwd_dropout.argtypes = [T, T, T, T, ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_float, T,
+                                          ctypes.c_int, T, T, T, ctypes.c_void_p]
     lib.sdpa_math_fwd_noalloc.restype = ctypes.c_int
     lib.sdpa_math_fwd_noalloc.argtypes = lib.sdpa_math_fwd.argtypes + [ctypes.c_int]
     lib.sdpa_math_bwd.restype = ctypes.c_int
@@ -147,10 +150,14 @@ def _causal_code(is_causal, causal_alignment: str) -> int:
     return CAUSAL_ALIGNMENTS[causal_alignment] if is_causal else 0
 
 
+DROPOUT_RULES = {"explicit": 0, "random": 1}
+
+
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, attn_mask: Optional[torch.Tensor] = None,
         is_causal: bool = False, scale: Optional[float] = None, enable_gqa: bool = False,
         path: str = "auto", out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
-        causal_alignment: str = "top_left") -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+        causal_alignment: str = "top_left", dropout_p: float = 0.0,
+        dropout_mask: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """Return (O [B,Hq,Sq,Dv], P [B,Hq,Sq,Skv], LSE [B,Hq,Sq] float32).
 
     ``scale=None`` means 1/sqrt(D). ``path`` is "auto", "fused" or "twopass".
@@ -159,6 +166,9 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, attn_mask: Optional[t
     when j > i + Skv - Sq.
     ``out`` may pass preallocated (O, P, LSE) buffers (any strides with a
     contiguous last dim); by default P and O share one allocation.
+    ``dropout_p > 0``: with ``dropout_mask`` (bool, True keeps) the explicit
+    rule (P = keep * P, O divided by 1 - p); without one, the random rule on a
+    keep-mask drawn here with torch's generator (P = keep * P / (1 - p)).
     """
     lib = load_library()
     dev = _check_devices(q, k, v, attn_mask)
@@ -185,6 +195,26 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, attn_mask: Optional[t
     dq, dk, dv = _desc(q, 4), _desc(k, 4), _desc(v, 4)
     dm = _desc(attn_mask, 4)
     do, dp, dl = _desc(O, 4), _desc(P, 4), _desc(L, 3)
+    if dropout_p > 0 or dropout_mask is not None:
+        if path == "fused":
+            raise NotImplementedError("dropout runs on the two-pass path only")
+        rule = DROPOUT_RULES["explicit"] if dropout_mask is not None else DROPOUT_RULES["random"]
+        if dropout_mask is None:  # the random rule's keep draws
+            dropout_mask = torch.rand((B, q.shape[1], Sq, Skv), device=dev) >= dropout_p
+        _check_devices(q, dropout_mask)
+
+        def launch_drop():
+            return lib.sdpa_math_fwd_dropout(dq, dk, dv, dm, causal, float(scale), int(bool(enable_gqa)),
+                                             float(dropout_p), _desc(dropout_mask, 4), rule, do, dp, dl,
+                                             ctypes.c_void_p(_current_stream(dev)))
+        if dev.index == torch.cuda.current_device():
+            rc = launch_drop()
+        else:
+            with torch.cuda.device(dev):
+                rc = launch_drop()
+        if rc != 0:
+            _raise(rc, lib)
+        return O, P, L
     # workspace for key ranges, when the library would split this call
     # (the byte count depends on dtypes, shapes, mask layout and flags only:
     # remembered per signature, the descriptors' bytes past the data pointer)

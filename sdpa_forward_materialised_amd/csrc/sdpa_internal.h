@@ -47,6 +47,16 @@ struct FwdArgs {
     // Byte extent of one (batch, head) slice of each tensor (< 2^31); the
     // kernels address every tensor through a buffer descriptor of this size.
     uint32_t q_ext, k_ext, v_ext, o_ext, p_ext, m_ext, l_ext;
+    // Dropout (kernels built with it only): a bool keep-mask over the logical
+    // [B, Hq, Sq, Skv] index (strides in elements, 0 on broadcast dims); the
+    // stored probability is keep * P * drop_pscale and the output product
+    // takes keep * P * drop_oscale.
+    const uint8_t* keep;
+    int64_t kp_s[4];
+    uint32_t kp_ext;
+    int keep_vec;       // keep rows: 8-byte aligned, contiguous, Skv a multiple of 8
+    float drop_pscale;  // 1 (explicit rule) or 1 / (1 - p) (random rule)
+    float drop_oscale;  // 1 / (1 - p)
 };
 
 // Backward: the forward's arguments (q, k, v, mask, lse, shapes, strides,
@@ -86,9 +96,10 @@ struct Plan {
 // variant with 16-byte row stores and vector mask loads (rows aligned, Skv a
 // multiple of 8, mask contiguous in its last dim); the other variant handles
 // any layout element by element. Return a hipError_t as int.
-int launch_twopass_f32(int D, int mask_kind, int waves, bool vec, const FwdArgs& a, void* stream);
-int launch_twopass_f16(int D, int mask_kind, int waves, bool vec, const FwdArgs& a, void* stream);
-int launch_twopass_bf16(int D, int mask_kind, int waves, bool vec, const FwdArgs& a, void* stream);
+// `drop`: the dropout variant (two compute waves and a loader wave only).
+int launch_twopass_f32(int D, int mask_kind, int waves, bool vec, bool drop, const FwdArgs& a, void* stream);
+int launch_twopass_f16(int D, int mask_kind, int waves, bool vec, bool drop, const FwdArgs& a, void* stream);
+int launch_twopass_bf16(int D, int mask_kind, int waves, bool vec, bool drop, const FwdArgs& a, void* stream);
 int launch_fused(int dtype, int D, int mask_kind, int waves, bool vec, const FwdArgs& a, void* stream);
 // Backward launches (query-side kernel, then key/value-side kernel) on the
 // stream; hipError_t as int.

@@ -397,10 +397,33 @@ void fill_strides3(const sdpa_tensor_t* t, int64_t* s) {
 // none, run unsplit) or the library's per-device static scratch.
 enum WsMode { WS_CALLER = 0, WS_STATIC = 1 };
 
+// Dropout of one call: the caller's keep-mask, p and rule.
+struct DropSpec {
+    const sdpa_tensor_t* keep;
+    float p;
+    int rule;  // 0 explicit, 1 random
+};
+
+sdpa_status_t validate_dropout(const Shape& sh, const DropSpec& d) {
+    if (!(d.p >= 0.0f && d.p < 1.0f)) return fail(SDPA_ERR_INVALID_ARG, "dropout_p must be in [0, 1), got %g", d.p);
+    if (d.rule != 0 && d.rule != 1) return fail(SDPA_ERR_INVALID_ARG, "dropout rule must be 0 (explicit) or 1 (random)");
+    const sdpa_tensor_t* m = d.keep;
+    if (!m) return fail(SDPA_ERR_INVALID_ARG, "dropout needs a keep-mask");
+    if (m->ndim != 4) return fail(SDPA_ERR_INVALID_ARG, "the keep-mask must be passed with 4 dims (right-aligned)");
+    if (m->dtype != SDPA_BOOL) return fail(SDPA_ERR_INVALID_ARG, "the keep-mask must be bool");
+    const int64_t full[4] = {sh.B, sh.Hq, sh.Sq, sh.Skv};
+    for (int dd = 0; dd < 4; ++dd)
+        if (m->sizes[dd] < 0 || (m->sizes[dd] != 1 && m->sizes[dd] != full[dd]))
+            return fail(SDPA_ERR_INVALID_ARG, "keep-mask dim %d (%lld) does not broadcast to %lld", dd,
+                        (long long)m->sizes[dd], (long long)full[dd]);
+    if (numel(m) > 0 && !m->data) return fail(SDPA_ERR_INVALID_ARG, "the keep-mask has no data pointer");
+    return SDPA_OK;
+}
+
 sdpa_status_t run(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_tensor_t* v, const sdpa_tensor_t* mask,
                   int is_causal, float scale, int enable_gqa, sdpa_tensor_t* out, sdpa_tensor_t* probs,
                   sdpa_tensor_t* lse, void* stream, int path, void* ws = nullptr, size_t ws_bytes = 0,
-                  WsMode ws_mode = WS_CALLER) {
+                  WsMode ws_mode = WS_CALLER, const DropSpec* drop = nullptr) {
     g_last_error.clear();
     if (path < SDPA_PATH_AUTO || path > SDPA_PATH_TWOPASS) return fail(SDPA_ERR_INVALID_ARG, "unknown path %d", path);
     Shape sh;
@@ -408,6 +431,14 @@ sdpa_status_t run(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_ten
     if (st) return st;
     if ((st = validate_outputs(sh, out, probs, lse))) return st;
     if (!std::isfinite(scale)) return fail(SDPA_ERR_INVALID_ARG, "scale must be finite");
+    if (drop) {
+        if ((st = validate_dropout(sh, *drop))) return st;
+        // [FlagOS] single-kernel fusion update: dropout always takes the two-stage path
+        if (path == SDPA_PATH_FUSED) return fail(SDPA_ERR_UNSUPPORTED, "dropout runs on the two-pass path only");
+        path = SDPA_PATH_TWOPASS;
+        ws = nullptr;
+        ws_mode = WS_CALLER;
+    }
     if (sh.B * sh.Hq * sh.Sq == 0) return SDPA_OK;
     const bool vec = staged_layout(sh, mask, out, probs);
     sdpa::Plan plan;
@@ -429,6 +460,13 @@ sdpa_status_t run(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_ten
     }
     if (plan.n_splits > 1 && (reinterpret_cast<uintptr_t>(ws) % 256 != 0 || ws_bytes < split_ws_bytes(sh, plan.n_splits)))
         if ((st = make_plan(sh, is_causal != 0, causal_offset(sh, is_causal), path, vec, &plan))) return st;  // no room: unsplit
+    if (drop) {  // the dropout kernels: two compute waves and a loader wave
+        plan.waves = 2;
+        plan.q_rows = 64;
+        plan.n_qblk = (int)cdiv(sh.Sq, 64);
+        plan.grid = sh.B * sh.Hq * plan.n_qblk;
+        plan.tiles_per_bh = count_tiles(sh.Sq, sh.Skv, is_causal != 0, 64, causal_offset(sh, is_causal));
+    }
 
     sdpa::FwdArgs a;
     std::memset(&a, 0, sizeof a);
@@ -470,6 +508,17 @@ sdpa_status_t run(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_ten
         a.ws_o = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + (split_ws_ml_bytes(sh, plan.n_splits) + 255) / 256 * 256);
     }
     a.keys_per_wave = plan.keys_per_wave;
+    if (drop) {
+        a.keep = static_cast<const uint8_t*>(drop->keep->data);
+        for (int dd = 0; dd < 4; ++dd) a.kp_s[dd] = eff_stride(drop->keep, dd);
+        const int64_t kext = sh.Skv > 0 ? (sh.Sq - 1) * a.kp_s[2] + (sh.Skv - 1) * a.kp_s[3] + 1 : 0;
+        if (kext >= (int64_t(1) << 30)) return fail(SDPA_ERR_UNSUPPORTED, "one (batch, head) slice spans 1 GiB or more");
+        a.kp_ext = (uint32_t)kext;
+        a.keep_vec = a.kp_s[3] == 1 && sh.Skv % 8 == 0 && reinterpret_cast<uintptr_t>(a.keep) % 8 == 0 &&
+                     (a.kp_s[0] % 8) == 0 && (a.kp_s[1] % 8) == 0 && (a.kp_s[2] % 8) == 0;
+        a.drop_oscale = (float)(1.0 / (1.0 - (double)drop->p));
+        a.drop_pscale = drop->rule == 1 ? a.drop_oscale : 1.0f;
+    }
     // Workgroup order (decode_block). Non-causal: head-major, each XCD taking
     // consecutive blocks (shared K/V in its L2). Causal: when the grid is
     // more than one round of resident workgroups (two per CU on 256 CUs),
@@ -518,11 +567,11 @@ sdpa_status_t run(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_ten
     if (plan.path == SDPA_PATH_FUSED) {
         err = sdpa::launch_fused(sh.dtype, D, sh.mask_kind, plan.waves, vec, a, stream);
     } else if (sh.dtype == SDPA_BF16) {
-        err = sdpa::launch_twopass_bf16(D, sh.mask_kind, plan.waves, vec, a, stream);
+        err = sdpa::launch_twopass_bf16(D, sh.mask_kind, plan.waves, vec, drop != nullptr, a, stream);
     } else if (sh.dtype == SDPA_F16) {
-        err = sdpa::launch_twopass_f16(D, sh.mask_kind, plan.waves, vec, a, stream);
+        err = sdpa::launch_twopass_f16(D, sh.mask_kind, plan.waves, vec, drop != nullptr, a, stream);
     } else {
-        err = sdpa::launch_twopass_f32(D, sh.mask_kind, plan.waves, vec, a, stream);
+        err = sdpa::launch_twopass_f32(D, sh.mask_kind, plan.waves, vec, drop != nullptr, a, stream);
     }
     if (err != 0)
         return fail(SDPA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(static_cast<hipError_t>(err)));
@@ -689,6 +738,15 @@ sdpa_status_t sdpa_math_fwd_ws(const sdpa_tensor_t* q, const sdpa_tensor_t* k, c
                                size_t workspace_bytes, void* hip_stream, int path) {
     return run(q, k, v, mask, is_causal, scale, enable_gqa, out, probs, lse, hip_stream, path, workspace,
                workspace_bytes);
+}
+
+sdpa_status_t sdpa_math_fwd_dropout(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_tensor_t* v,
+                                    const sdpa_tensor_t* mask, int is_causal, float scale, int enable_gqa,
+                                    float dropout_p, const sdpa_tensor_t* keep, int rule, sdpa_tensor_t* out,
+                                    sdpa_tensor_t* probs, sdpa_tensor_t* lse, void* hip_stream) {
+    const DropSpec d{keep, dropout_p, rule};
+    return run(q, k, v, mask, is_causal, scale, enable_gqa, out, probs, lse, hip_stream, SDPA_PATH_AUTO, nullptr, 0,
+               WS_CALLER, &d);
 }
 
 sdpa_status_t sdpa_math_fwd_noalloc(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_tensor_t* v,

@@ -114,11 +114,15 @@ struct TwoPassCfg {
 // sweep 1 over this workgroup's range and writes its rows' (max, sum), 2
 // folds every range's statistics into the LSE, runs sweep 2 over its range
 // (final P) and writes a float32 partial O.
-template <typename T, int D, int NW, int MASK, bool VEC, int TN, bool NL, int SPL = 0>
+// DROP: dropout with a caller keep-mask in sweep 2 (loader-wave kernels,
+// whole calls): the stored probability is keep * P * drop_pscale and the
+// output product takes keep * P * drop_oscale.
+template <typename T, int D, int NW, int MASK, bool VEC, int TN, bool NL, int SPL = 0, bool DROP = false>
 __global__ __attribute__((amdgpu_flat_work_group_size((NL ? NW : NW + 1) * 64, (NL ? NW : NW + 1) * 64),
                           amdgpu_waves_per_eu(NL ? 2 : SDPA_TP_WPE(NW))))
 void sdpa_twopass_kernel(const FwdArgs a) {
     static_assert(SPL == 0 || !NL, "key ranges run on the loader-wave kernels");
+    static_assert(!DROP || (SPL == 0 && !NL), "dropout runs on the whole-call loader-wave kernels");
     using C = TwoPassCfg<T, D, NW, MASK, VEC, TN, NL>;
     static_assert(!NL || C::PSTAGE, "without a loader wave the probability stores must be staged");
     static_assert(C::LDS_BYTES <= 160 * 1024, "tile buffers exceed the 160 KB LDS of a compute unit");
@@ -257,6 +261,31 @@ void sdpa_twopass_kernel(const FwdArgs a) {
     const rsrc_t lr = make_rsrc(a.lse + w.b * a.l_s[0] + w.hq * a.l_s[1], a.l_ext);
     // byte offset of this lane's P row (past the descriptor when the row is out of range)
     const uint32_t prow = pred(row_ok, (uint32_t)((int64_t)(row_ok ? qi : 0) * a.p_s[2] * SZ));
+
+    // dropout keep bits of this lane's 16 keys of block kb: 1 keeps, 0 drops
+    [[maybe_unused]] rsrc_t kpr = qr;
+    [[maybe_unused]] uint32_t kp_row = 0;
+    if constexpr (DROP) {
+        kpr = make_rsrc(a.keep + w.b * a.kp_s[0] + w.hq * a.kp_s[1], a.kp_ext);
+        kp_row = (uint32_t)((int64_t)(row_ok ? qi : 0) * a.kp_s[2]);
+    }
+    auto keep16 = [&](int k0, int kb, float* kv) SDPA_INLINE {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int j = k0 + 32 * kb + 16 * c + 8 * hf;
+            if (a.keep_vec) {
+                const u32x2 wv = ld64(kpr, pred(row_ok && j < a.Skv, kp_row + (uint32_t)j));
+#pragma unroll
+                for (int e = 0; e < 8; ++e) kv[8 * c + e] = ((wv[e >> 2] >> (8 * (e & 3))) & 0xffu) ? 1.0f : 0.0f;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    kv[8 * c + e] = __builtin_amdgcn_raw_buffer_load_b8(
+                                        kpr, pred(row_ok && j + e < a.Skv, kp_row + (uint32_t)((int64_t)(j + e) * a.kp_s[3])),
+                                        0, 0) ? 1.0f : 0.0f;
+            }
+        }
+    };
 
     // Q fragments (B operand): lane (n, h) holds Q[qi][c*KSTEP + h*KH .. +KH)
     vec qf[NKS];
@@ -694,6 +723,18 @@ void sdpa_twopass_kernel(const FwdArgs a) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) p[r] = fast_exp2(tt[r] - lse2);
             }
+            // dropout: ps = what is stored, p = what the output product takes
+            [[maybe_unused]] float ps[16];
+            if constexpr (DROP) {
+                float kv[16];
+                keep16(k0, kb, kv);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float pd = p[r] * kv[r];
+                    ps[r] = pd * a.drop_pscale;
+                    p[r] = pd * a.drop_oscale;
+                }
+            }
             if constexpr (sizeof(T) == 2) {
                 vec va[2][ND];  // V^T operands of both 16-key halves, read ahead of the MFMAs
 #pragma unroll
@@ -706,11 +747,13 @@ void sdpa_twopass_kernel(const FwdArgs a) {
                     // residual: O accumulates P to twice the dtype's precision
                     const vec pv = TR::cvt8(p + 8 * c2);
                     const vec pl = TR::lo8(p + 8 * c2, pv);
+                    const float* stored = DROP ? ps + 8 * c2 : p + 8 * c2;
                     if constexpr (C::PSTAGE) {
                         const int chunk = (32 * kb + 16 * c2 + 8 * hf) * SZ / 16;
-                        *reinterpret_cast<u32x4*>(pst + C::pos_p(n, chunk) * 16) = __builtin_bit_cast(u32x4, pv);
+                        *reinterpret_cast<u32x4*>(pst + C::pos_p(n, chunk) * 16) =
+                            __builtin_bit_cast(u32x4, DROP ? TR::cvt8(stored) : pv);
                     } else {
-                        store_run(k0, kb, c2, edge, p + 8 * c2);
+                        store_run(k0, kb, c2, edge, stored);
                     }
 #pragma unroll
                     for (int d = 0; d < ND; ++d) oacc[d] = TR::mfma(va[c2][d], pv, oacc[d]);
@@ -718,20 +761,21 @@ void sdpa_twopass_kernel(const FwdArgs a) {
                     for (int d = 0; d < ND; ++d) oacc[d] = TR::mfma(va[c2][d], pl, oacc[d]);
                 }
             } else {
+                const float* stored = DROP ? ps : p;
                 if constexpr (C::PSTAGE) {
 #pragma unroll
                     for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
                         for (int h2 = 0; h2 < 2; ++h2) {
                             const int chunk = (32 * kb + 16 * c2 + 8 * hf) * SZ / 16 + h2;
-                            const float* x = p + 8 * c2 + 4 * h2;
+                            const float* x = stored + 8 * c2 + 4 * h2;
                             *reinterpret_cast<u32x4*>(pst + C::pos_p(n, chunk) * 16) =
                                 u32x4{__builtin_bit_cast(uint32_t, x[0]), __builtin_bit_cast(uint32_t, x[1]),
                                       __builtin_bit_cast(uint32_t, x[2]), __builtin_bit_cast(uint32_t, x[3])};
                         }
                 } else {
-                    store_run(k0, kb, 0, edge, p);
-                    store_run(k0, kb, 1, edge, p + 8);
+                    store_run(k0, kb, 0, edge, stored);
+                    store_run(k0, kb, 1, edge, stored + 8);
                 }
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
@@ -820,7 +864,7 @@ void sdpa_twopass_kernel(const FwdArgs a) {
       }
     };
     // (not without a loader wave: its deferred stores leave too few registers)
-    constexpr bool PIPE2 = sizeof(T) == 2 && NKB == 2 && MASK == MASK_NONE && C::PSTAGE && !NL;
+    constexpr bool PIPE2 = sizeof(T) == 2 && NKB == 2 && MASK == MASK_NONE && C::PSTAGE && !NL && !DROP;
     // Without a loader wave a tile's probability stores are issued at the
     // start of the next tile (from the staged copy), so the wait before the
     // next barrier finds them a whole tile old rather than just issued.
@@ -923,14 +967,15 @@ void sdpa_twopass_kernel(const FwdArgs a) {
 template <int MK>
 constexpr int tile_keys() { return MK == MASK_BOOL ? 32 : 64; }
 
-template <typename T, int D, int NW, bool VEC, bool NL>
+template <typename T, int D, int NW, bool VEC, bool NL, bool DROP = false>
 static int launch_twopass_mask(int mask_kind, const FwdArgs& a, hipStream_t s) {
     dim3 grid(a.n_blocks), block((NL ? NW : NW + 1) * 64);
     switch (mask_kind) {
 #define SDPA_TP_CASE(MK)                                                                                          \
     case MK:                                                                                                      \
         if constexpr (!NL || TwoPassCfg<T, D, NW, MK, VEC, tile_keys<MK>(), true>::PSTAGE) {                       \
-            hipLaunchKernelGGL((sdpa_twopass_kernel<T, D, NW, MK, VEC, tile_keys<MK>(), NL>), grid, block, 0, s, a); \
+            hipLaunchKernelGGL((sdpa_twopass_kernel<T, D, NW, MK, VEC, tile_keys<MK>(), NL, 0, DROP>), grid, block, \
+                               0, s, a);                                                                          \
             break;                                                                                                \
         } else {                                                                                      \
             return (int)hipErrorInvalidValue;                                                         \
@@ -1027,8 +1072,20 @@ static bool twopass_nl_ok_t(int D, int mask_kind) {
 // float32 takes at most two compute waves at D = 128 (its tiles are twice
 // as large: two waves keep them within LDS).
 template <typename T>
-static int launch_twopass_t(int D, int mask_kind, int waves, bool vec, const FwdArgs& a, void* stream) {
+static int launch_twopass_t(int D, int mask_kind, int waves, bool vec, bool drop, const FwdArgs& a, void* stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (drop) {  // dropout: two compute waves and a loader wave, whole calls
+        if (waves != 2 || a.n_splits > 1) return (int)hipErrorInvalidValue;
+        switch (D) {
+            case 32: return vec ? launch_twopass_mask<T, 32, 2, true, false, true>(mask_kind, a, s)
+                                : launch_twopass_mask<T, 32, 2, false, false, true>(mask_kind, a, s);
+            case 64: return vec ? launch_twopass_mask<T, 64, 2, true, false, true>(mask_kind, a, s)
+                                : launch_twopass_mask<T, 64, 2, false, false, true>(mask_kind, a, s);
+            case 128: return vec ? launch_twopass_mask<T, 128, 2, true, false, true>(mask_kind, a, s)
+                                 : launch_twopass_mask<T, 128, 2, false, false, true>(mask_kind, a, s);
+            default: return (int)hipErrorInvalidValue;
+        }
+    }
     if (a.n_splits > 1) {
         if (!vec || waves != 2) return (int)hipErrorInvalidValue;
         switch (D) {

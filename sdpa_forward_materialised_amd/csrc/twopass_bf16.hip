@@ -3,8 +3,8 @@
 
 namespace sdpa {
 
-int launch_twopass_bf16(int D, int mask_kind, int waves, bool vec, const FwdArgs& a, void* stream) {
-    return launch_twopass_t<__bf16>(D, mask_kind, waves, vec, a, stream);
+int launch_twopass_bf16(int D, int mask_kind, int waves, bool vec, bool drop, const FwdArgs& a, void* stream) {
+    return launch_twopass_t<__bf16>(D, mask_kind, waves, vec, drop, a, stream);
 }
 
 bool twopass_nl_ok_bf16(int D, int mask_kind) { return twopass_nl_ok_t<__bf16>(D, mask_kind); }
