@@ -195,6 +195,35 @@ sdpa_status_t sdpa_math_fwd_dropout(const sdpa_tensor_t* q, const sdpa_tensor_t*
                                     void* hip_stream);
 
 /*
+ * sdpa_math_fwd_varlen — the forward over packed variable-length sequences
+ * (the THD layout with cumulative sequence offsets that the cudnn-frontend
+ * pull request "[SDPA] SM80 fwd: TemplateParams kernels, plan-time compile,
+ * sym_int THD extents" serves: token-major (T, H, D) tensors plus
+ * cu_seqlens). Sequence b holds query tokens cu_seqlens_q[b] ..
+ * cu_seqlens_q[b+1] and key/value tokens cu_seqlens_kv[b] ..
+ * cu_seqlens_kv[b+1]; it attends only within itself, with the semantics of
+ * sdpa_math_fwd (is_causal 1: top-left, 2: bottom-right, per sequence).
+ * q    [Tq, Hq, D];  k [Tkv, Hkv, D];  v [Tkv, Hkv, Dv]   (3 dims, last contiguous)
+ * cu_seqlens_q, cu_seqlens_kv  device int32 arrays of n_seqs + 1 offsets,
+ *      non-decreasing from 0 (read on the device only: the host never reads
+ *      them; offsets outside [0, T] are clamped to the tensors)
+ * max_seqlen_q, max_seqlen_kv  upper bounds of the sequences' lengths (the
+ *      launch grid covers max_seqlen_q query rows per sequence; longer
+ *      sequences are cut to the bounds)
+ * out   [Tq, Hq, Dv] q dtype; probs [Tq, Hq, max_seqlen_kv] q dtype: row t of
+ *      head h holds the probabilities over its own sequence's keys in entries
+ *      0 .. len_kv - 1 and zeros in the rest; lse [Tq, Hq] f32
+ * No attention mask (causal only), no dropout; the two-pass kernel. Other
+ * arguments, ownership and errors as sdpa_math_fwd.
+ */
+sdpa_status_t sdpa_math_fwd_varlen(const sdpa_tensor_t* q, const sdpa_tensor_t* k,
+                                   const sdpa_tensor_t* v, const int32_t* cu_seqlens_q,
+                                   const int32_t* cu_seqlens_kv, int64_t n_seqs,
+                                   int64_t max_seqlen_q, int64_t max_seqlen_kv, int is_causal,
+                                   float scale, int enable_gqa, sdpa_tensor_t* out,
+                                   sdpa_tensor_t* probs, sdpa_tensor_t* lse, void* hip_stream);
+
+/*
  * sdpa_math_fwd_noalloc — sdpa_math_fwd_ws for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, hosts
  * that forbid allocation): no workspace argument and nothing allocated. A

@@ -258,3 +258,40 @@ def sdpa_backward_reference(q, k, v, attn_mask=None, is_causal: bool = False,
     if rc != 0:
         raise ValueError(f"oracle rejected the call (code {rc})")
     return dq, dk, dv
+
+
+def sdpa_varlen_reference(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_kv: int, is_causal: bool = False,
+                          scale: Optional[float] = None, enable_gqa: bool = False,
+                          causal_alignment: str = "top_left") -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Packed variable-length sequences (token-major q [Tq, Hq, D], k/v
+    [Tkv, Hkv, D], cumulative offsets cu_seqlens_*; the THD layout of the
+    cudnn-frontend pull request "[SDPA] SM80 fwd: TemplateParams kernels,
+    plan-time compile, sym_int THD extents"): each sequence is an independent
+    call of ``sdpa_reference`` on its own tokens. Returns O [Tq, Hq, Dv],
+    P [Tq, Hq, max_seqlen_kv] (zeros past each sequence's keys) and
+    LSE [Tq, Hq], float64. A token outside every sequence gets O = 0, P = 0 and
+    LSE = -inf."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    cq = [int(x) for x in np.asarray(cu_seqlens_q.cpu() if hasattr(cu_seqlens_q, "cpu") else cu_seqlens_q)]
+    ck = [int(x) for x in np.asarray(cu_seqlens_kv.cpu() if hasattr(cu_seqlens_kv, "cpu") else cu_seqlens_kv)]
+    if len(cq) != len(ck) or len(cq) < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_kv must hold n_seqs + 1 offsets each")
+    Tq, Hq, _ = q.shape
+    Dv = v.shape[2]
+    out = np.zeros((Tq, Hq, Dv))
+    probs = np.zeros((Tq, Hq, max_seqlen_kv))
+    lse = np.full((Tq, Hq), -np.inf)
+    for b in range(len(cq) - 1):
+        q0, q1, k0, k1 = cq[b], cq[b + 1], ck[b], ck[b + 1]
+        if q1 <= q0:
+            continue
+        if k1 - k0 > max_seqlen_kv:
+            raise ValueError("a sequence has more keys than max_seqlen_kv")
+        qs = q[q0:q1].transpose(1, 0, 2)[None]
+        ks = k[k0:k1].transpose(1, 0, 2)[None]
+        vs = v[k0:k1].transpose(1, 0, 2)[None]
+        o, p, l = sdpa_reference(qs, ks, vs, None, is_causal, scale, enable_gqa, causal_alignment=causal_alignment)
+        out[q0:q1] = o[0].transpose(1, 0, 2)
+        probs[q0:q1, :, :k1 - k0] = p[0].transpose(1, 0, 2)
+        lse[q0:q1] = l[0].T
+    return out, probs, lse

@@ -29,7 +29,7 @@ _DTYPES = {torch.float32: SDPA_F32, torch.float16: SDPA_F16, torch.bfloat16: SDP
            torch.bool: SDPA_BOOL}
 
 EXPORTS = ("sdpa_math_fwd", "sdpa_math_fwd_path", "sdpa_math_fwd_ws", "sdpa_math_workspace_bytes",
-           "sdpa_math_fwd_noalloc", "sdpa_math_fwd_dropout", "sdpa_math_bwd", "sdpa_math_bwd_workspace_bytes", "sdpa_math_plan",
+           "sdpa_math_fwd_noalloc", "sdpa_math_fwd_dropout", "sdpa_math_fwd_varlen", "sdpa_math_bwd", "sdpa_math_bwd_workspace_bytes", "sdpa_math_plan",
            "sdpa_math_last_error",
            "sdpa_math_version", "sdpa_probe_fill", "sdpa_probe_copy")
 
@@ -41,7 +41,7 @@ class SdpaTensor(ctypes.Structure):
 
 # sdpa_tensor_t byte layouts: pointer, dtype, ndim, sizes[4], strides[4]
 # (unused trailing entries zero)
-_PACK = {4: struct.Struct("<Qii4q4q"), 3: struct.Struct("<Qii3q8x3q8x")}
+_PACK = {4: struct.Struct("<Qii4q4q"), 3: struct.Struct("<Qii3q8x3q8x"), 2: struct.Struct("<Qii2q16x2q16x")}
 assert all(p.size == ctypes.sizeof(SdpaTensor) for p in _PACK.values())
 
 _lib = None
@@ -67,6 +67,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sdpa_math_fwd_ws.restype = ctypes.c_int
     lib.sdpa_math_fwd_ws.argtypes = [T, T, T, T, ctypes.c_int, ctypes.c_float, ctypes.c_int, T, T, T,
                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int]
+    lib.sdpa_math_fwd_varlen.restype = ctypes.c_int
+    lib.sdpa_math_fwd_varlen.argtypes = [T, T, T, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                         ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_int, T, T, T,
+                                         ctypes.c_void_p]
     lib.sdpa_math_fwd_dropout.restype = ctypes.c_int
     lib.sdpa_math_fwd_dropout.argtypes = [T, T, T, T, ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_float, T,
                                           ctypes.c_int, T, T, T, ctypes.c_void_p]
@@ -245,6 +249,47 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, attn_mask: Optional[t
     else:
         with torch.cuda.device(dev):
             rc = launch()
+    if rc != 0:
+        _raise(rc, lib)
+    return O, P, L
+
+
+def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
+               cu_seqlens_kv: torch.Tensor, max_seqlen_q: int, max_seqlen_kv: int, is_causal: bool = False,
+               scale: Optional[float] = None, enable_gqa: bool = False, causal_alignment: str = "top_left",
+               out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None
+               ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """``sdpa_math_fwd_varlen``: packed sequences q [Tq, Hq, D], k/v [Tkv, Hkv, D]
+    with int32 cu_seqlens on the device. Returns (O [Tq, Hq, Dv],
+    P [Tq, Hq, max_seqlen_kv] (zeros past each sequence's keys), LSE [Tq, Hq])."""
+    lib = load_library()
+    dev = _check_devices(q, k, v, cu_seqlens_q, cu_seqlens_kv)
+    for name, cu in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_kv", cu_seqlens_kv)):
+        if cu.dtype != torch.int32 or cu.dim() != 1 or not cu.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 1-D int32 tensor")
+    if cu_seqlens_q.numel() != cu_seqlens_kv.numel() or cu_seqlens_q.numel() < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_kv must hold n_seqs + 1 offsets each")
+    causal = _causal_code(is_causal, causal_alignment)
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be 3-D [T, H, D]")
+    Tq, Hq, D = q.shape
+    Dv = v.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D) if D > 0 else 1.0
+    if out is None:
+        O = torch.empty((Tq, Hq, Dv), dtype=q.dtype, device=dev)
+        P = torch.empty((Tq, Hq, max_seqlen_kv), dtype=q.dtype, device=dev)
+        L = torch.empty((Tq, Hq), dtype=torch.float32, device=dev)
+    else:
+        O, P, L = out
+    args = (_desc(q, 3), _desc(k, 3), _desc(v, 3), ctypes.c_void_p(cu_seqlens_q.data_ptr()),
+            ctypes.c_void_p(cu_seqlens_kv.data_ptr()), cu_seqlens_q.numel() - 1, int(max_seqlen_q),
+            int(max_seqlen_kv), causal, float(scale), int(bool(enable_gqa)), _desc(O, 3), _desc(P, 3), _desc(L, 2))
+    if dev.index == torch.cuda.current_device():
+        rc = lib.sdpa_math_fwd_varlen(*args, ctypes.c_void_p(_current_stream(dev)))
+    else:
+        with torch.cuda.device(dev):
+            rc = lib.sdpa_math_fwd_varlen(*args, ctypes.c_void_p(_current_stream(dev)))
     if rc != 0:
         _raise(rc, lib)
     return O, P, L

@@ -57,6 +57,17 @@ struct FwdArgs {
     int keep_vec;       // keep rows: 8-byte aligned, contiguous, Skv a multiple of 8
     float drop_pscale;  // 1 (explicit rule) or 1 / (1 - p) (random rule)
     float drop_oscale;  // 1 / (1 - p)
+    // Packed variable-length sequences (thd != 0): B sequences whose token
+    // ranges are cu_q[b] .. cu_q[b+1] of the Tq packed query tokens and
+    // cu_k[b] .. cu_k[b+1] of the Tkv key tokens (device int32 arrays); Sq and
+    // Skv hold the maximum lengths, the batch strides are 0, and each
+    // probability row has p_cols entries (zeros past its sequence's keys).
+    int thd;
+    int thd_bottom_right;  // causal alignment per sequence: key j removed when j > i + Skv_b - Sq_b
+    const int* cu_q;
+    const int* cu_k;
+    int Tq, Tkv;
+    int p_cols;
 };
 
 // Backward: the forward's arguments (q, k, v, mask, lse, shapes, strides,

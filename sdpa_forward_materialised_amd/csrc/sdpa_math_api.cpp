@@ -698,6 +698,135 @@ sdpa_status_t run_bwd(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa
     return SDPA_OK;
 }
 
+// Packed variable-length sequences (THD): q [Tq, Hq, D], k [Tkv, Hkv, D],
+// v [Tkv, Hkv, Dv], out [Tq, Hq, Dv], probs [Tq, Hq, max_skv], lse [Tq, Hq].
+sdpa_status_t run_varlen(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_tensor_t* v, const int32_t* cu_q,
+                         const int32_t* cu_k, int64_t nseq, int64_t max_sq, int64_t max_skv, int is_causal, float scale,
+                         int enable_gqa, sdpa_tensor_t* out, sdpa_tensor_t* probs, sdpa_tensor_t* lse, void* stream) {
+    g_last_error.clear();
+    sdpa_status_t st;
+    if ((st = check_tensor(q, "q", 3)) || (st = check_tensor(k, "k", 3)) || (st = check_tensor(v, "v", 3)))
+        return st;
+    if (q->dtype != SDPA_F32 && q->dtype != SDPA_F16 && q->dtype != SDPA_BF16)
+        return fail(SDPA_ERR_INVALID_ARG, "q dtype %s is not f32, f16 or bf16", dtype_name(q->dtype));
+    if (k->dtype != q->dtype || v->dtype != q->dtype) return fail(SDPA_ERR_INVALID_ARG, "q, k, v dtypes differ");
+    Shape sh;
+    sh.B = nseq;
+    sh.Hq = q->sizes[1];
+    sh.D = q->sizes[2];
+    sh.Hkv = k->sizes[1];
+    sh.Dv = v->sizes[2];
+    sh.Sq = max_sq;
+    sh.Skv = max_skv;
+    sh.dtype = q->dtype;
+    sh.mask_kind = sdpa::MASK_NONE;
+    const int64_t Tq = q->sizes[0], Tkv = k->sizes[0];
+    if (nseq < 0 || max_sq < 0 || max_skv < 0)
+        return fail(SDPA_ERR_INVALID_ARG, "sequence count and maximum lengths must be non-negative");
+    if (nseq > 0 && (!cu_q || !cu_k)) return fail(SDPA_ERR_INVALID_ARG, "cu_seqlens_q and cu_seqlens_kv are required");
+    if (v->sizes[0] != Tkv || v->sizes[1] != sh.Hkv) return fail(SDPA_ERR_INVALID_ARG, "k and v disagree on tokens or heads");
+    if (k->sizes[2] != sh.D) return fail(SDPA_ERR_INVALID_ARG, "q and k head dims differ");
+    if (sh.Hkv <= 0 || sh.Hq % sh.Hkv != 0)
+        return fail(SDPA_ERR_INVALID_ARG, "query heads (%lld) are not a multiple of key/value heads (%lld)",
+                    (long long)sh.Hq, (long long)sh.Hkv);
+    if (sh.Hq != sh.Hkv && !enable_gqa) return fail(SDPA_ERR_INVALID_ARG, "Hq != Hkv needs enable_gqa");
+    if (is_causal < 0 || is_causal > 2) return fail(SDPA_ERR_INVALID_ARG, "is_causal must be 0, 1 or 2");
+    if (Tq > INT32_MAX || Tkv > INT32_MAX || max_sq > INT32_MAX || max_skv > INT32_MAX || nseq > INT32_MAX)
+        return fail(SDPA_ERR_UNSUPPORTED, "sizes beyond 2^31 are not supported");
+    if (sh.D != 32 && sh.D != 64 && sh.D != 128)
+        return fail(SDPA_ERR_UNSUPPORTED, "head dim %lld is not implemented (32, 64, 128)", (long long)sh.D);
+    if (sh.Dv != sh.D) return fail(SDPA_ERR_UNSUPPORTED, "value head dim != query head dim is not implemented");
+    const sdpa_tensor_t* in[3] = {q, k, v};
+    for (int i = 0; i < 3; ++i)
+        if (numel(in[i]) > 0 && !rows_aligned(in[i], 16))
+            return fail(SDPA_ERR_UNSUPPORTED, "q, k, v need 16-byte aligned bases and 16-byte multiple strides");
+    const int64_t wo[3] = {Tq, sh.Hq, sh.Dv};
+    const int64_t wp[3] = {Tq, sh.Hq, max_skv};
+    if ((st = check_tensor(out, "out", 3)) || (st = check_tensor(probs, "probs", 3))) return st;
+    if ((st = check_tensor(lse, "lse", 2))) return st;
+    if (out->dtype != sh.dtype || probs->dtype != sh.dtype)
+        return fail(SDPA_ERR_INVALID_ARG, "out and probs must have the query dtype");
+    if (lse->dtype != SDPA_F32) return fail(SDPA_ERR_INVALID_ARG, "lse must be f32");
+    const int64_t wl[2] = {Tq, sh.Hq};
+    if ((st = check_dims(out, "out", wo, 3)) || (st = check_dims(probs, "probs", wp, 3)) ||
+        (st = check_dims(lse, "lse", wl, 2)))
+        return st;
+    if (!std::isfinite(scale)) return fail(SDPA_ERR_INVALID_ARG, "scale must be finite");
+    if (nseq == 0 || sh.Hq == 0 || max_sq == 0 || Tq == 0) return SDPA_OK;
+
+    const int64_t es = elt_size(sh.dtype);
+    const bool vec = max_skv % 8 == 0 && rows_aligned(out, 16) && rows_aligned(probs, 16);
+    sdpa::FwdArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.q = q->data;
+    a.k = k->data;
+    a.v = v->data;
+    a.o = out->data;
+    a.p = probs->data;
+    a.lse = static_cast<float*>(lse->data);
+    // (batch, head, row) strides: no batch stride, tokens are the rows
+    auto st3 = [](const sdpa_tensor_t* t, int64_t* s3) {
+        s3[0] = 0;
+        s3[1] = eff_stride(t, 1);
+        s3[2] = t->strides[0];
+    };
+    st3(q, a.q_s);
+    st3(k, a.k_s);
+    st3(v, a.v_s);
+    st3(out, a.o_s);
+    st3(probs, a.p_s);
+    a.l_s[0] = 0;
+    a.l_s[1] = eff_stride(lse, 1);
+    a.l_s[2] = lse->strides[0];
+    a.B = (int)nseq;
+    a.Hq = (int)sh.Hq;
+    a.Hkv = (int)sh.Hkv;
+    a.Sq = (int)max_sq;
+    a.Skv = (int)max_skv;
+    a.group = (int)(sh.Hq / sh.Hkv);
+    a.causal = is_causal ? 1 : 0;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.p_vec = vec;
+    a.o_vec = vec;
+    a.n_qblk = (int)cdiv(max_sq, 64);
+    const int64_t grid = nseq * sh.Hq * a.n_qblk;
+    if (grid > INT32_MAX) return fail(SDPA_ERR_UNSUPPORTED, "grid too large");
+    a.n_blocks = (int)grid;
+    a.sched = 0;
+    a.n_splits = 1;
+    a.thd = 1;
+    a.thd_bottom_right = is_causal == 2;
+    a.cu_q = cu_q;
+    a.cu_k = cu_k;
+    a.Tq = (int)Tq;
+    a.Tkv = (int)Tkv;
+    a.p_cols = (int)max_skv;
+    int64_t ext[6];
+    ext[0] = slice_extent(max_sq, a.q_s[2], sh.D, es);
+    ext[1] = slice_extent(max_skv, a.k_s[2], sh.D, es);
+    ext[2] = slice_extent(max_skv, a.v_s[2], sh.Dv, es);
+    ext[3] = slice_extent(max_sq, a.o_s[2], sh.Dv, es);
+    ext[4] = slice_extent(max_sq, a.p_s[2], max_skv, es);
+    ext[5] = slice_extent(max_sq, a.l_s[2], 1, 4);
+    for (int i = 0; i < 6; ++i)
+        if (ext[i] < 0 || ext[i] >= (int64_t(1) << 30))
+            return fail(SDPA_ERR_UNSUPPORTED, "one (sequence, head) slice spans 1 GiB or more");
+    a.q_ext = (uint32_t)ext[0];
+    a.k_ext = (uint32_t)ext[1];
+    a.v_ext = (uint32_t)ext[2];
+    a.o_ext = (uint32_t)ext[3];
+    a.p_ext = (uint32_t)ext[4];
+    a.l_ext = (uint32_t)ext[5];
+    const int D = (int)sh.D;
+    int err;
+    if (sh.dtype == SDPA_BF16) err = sdpa::launch_twopass_bf16(D, sdpa::MASK_NONE, 2, vec, false, a, stream);
+    else if (sh.dtype == SDPA_F16) err = sdpa::launch_twopass_f16(D, sdpa::MASK_NONE, 2, vec, false, a, stream);
+    else err = sdpa::launch_twopass_f32(D, sdpa::MASK_NONE, 2, vec, false, a, stream);
+    if (err != 0)
+        return fail(SDPA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(static_cast<hipError_t>(err)));
+    return SDPA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -747,6 +876,15 @@ sdpa_status_t sdpa_math_fwd_dropout(const sdpa_tensor_t* q, const sdpa_tensor_t*
     const DropSpec d{keep, dropout_p, rule};
     return run(q, k, v, mask, is_causal, scale, enable_gqa, out, probs, lse, hip_stream, SDPA_PATH_AUTO, nullptr, 0,
                WS_CALLER, &d);
+}
+
+sdpa_status_t sdpa_math_fwd_varlen(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_tensor_t* v,
+                                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, int64_t n_seqs,
+                                   int64_t max_seqlen_q, int64_t max_seqlen_kv, int is_causal, float scale,
+                                   int enable_gqa, sdpa_tensor_t* out, sdpa_tensor_t* probs, sdpa_tensor_t* lse,
+                                   void* hip_stream) {
+    return run_varlen(q, k, v, cu_seqlens_q, cu_seqlens_kv, n_seqs, max_seqlen_q, max_seqlen_kv, is_causal, scale,
+                      enable_gqa, out, probs, lse, hip_stream);
 }
 
 sdpa_status_t sdpa_math_fwd_noalloc(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_tensor_t* v,

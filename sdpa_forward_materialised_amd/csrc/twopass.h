@@ -114,15 +114,47 @@ struct TwoPassCfg {
 // sweep 1 over this workgroup's range and writes its rows' (max, sum), 2
 // folds every range's statistics into the LSE, runs sweep 2 over its range
 // (final P) and writes a float32 partial O.
+// Packed variable-length sequences: rebase a copy of the arguments onto
+// sequence b. The host leaves the batch strides 0 and Sq / Skv at the
+// maximum lengths; the sequence's token range comes from cu_seqlens, clamped
+// to the packed tensors (and its lengths to the maxima), so no access leaves
+// them whatever the offsets hold.
+template <typename T>
+__device__ __forceinline__ void thd_rebase(FwdArgs& a, int b) {
+    const int q0 = min(max(a.cu_q[b], 0), a.Tq);
+    const int q1 = min(max(a.cu_q[b + 1], q0), a.Tq);
+    const int k0 = min(max(a.cu_k[b], 0), a.Tkv);
+    const int k1 = min(max(a.cu_k[b + 1], k0), a.Tkv);
+    a.Sq = min(q1 - q0, a.Sq);
+    a.Skv = min(k1 - k0, a.Skv);
+    a.coff = a.thd_bottom_right ? a.Skv - a.Sq : 0;
+    a.q = static_cast<const T*>(a.q) + (int64_t)q0 * a.q_s[2];
+    a.o = static_cast<T*>(a.o) + (int64_t)q0 * a.o_s[2];
+    a.p = static_cast<T*>(a.p) + (int64_t)q0 * a.p_s[2];
+    a.lse = a.lse + (int64_t)q0 * a.l_s[2];
+    a.k = static_cast<const T*>(a.k) + (int64_t)k0 * a.k_s[2];
+    a.v = static_cast<const T*>(a.v) + (int64_t)k0 * a.v_s[2];
+}
+
+template <bool USE_FIRST>
+__device__ __forceinline__ const FwdArgs& pick_args(const FwdArgs& first, const FwdArgs& second) {
+    if constexpr (USE_FIRST) return first;
+    else return second;
+}
+
 // DROP: dropout with a caller keep-mask in sweep 2 (loader-wave kernels,
 // whole calls): the stored probability is keep * P * drop_pscale and the
 // output product takes keep * P * drop_oscale.
-template <typename T, int D, int NW, int MASK, bool VEC, int TN, bool NL, int SPL = 0, bool DROP = false>
+// THD: packed variable-length sequences (a workgroup rebased onto its
+// sequence; the probability rows run to p_cols, zeros past the sequence's keys).
+template <typename T, int D, int NW, int MASK, bool VEC, int TN, bool NL, int SPL = 0, bool DROP = false,
+          bool THD = false>
 __global__ __attribute__((amdgpu_flat_work_group_size((NL ? NW : NW + 1) * 64, (NL ? NW : NW + 1) * 64),
                           amdgpu_waves_per_eu(NL ? 2 : SDPA_TP_WPE(NW))))
-void sdpa_twopass_kernel(const FwdArgs a) {
+void sdpa_twopass_kernel(const FwdArgs a_in) {
     static_assert(SPL == 0 || !NL, "key ranges run on the loader-wave kernels");
     static_assert(!DROP || (SPL == 0 && !NL), "dropout runs on the whole-call loader-wave kernels");
+    static_assert(!THD || (SPL == 0 && !NL && !DROP && MASK == MASK_NONE), "packed sequences: whole calls, no mask");
     using C = TwoPassCfg<T, D, NW, MASK, VEC, TN, NL>;
     static_assert(!NL || C::PSTAGE, "without a loader wave the probability stores must be staged");
     static_assert(C::LDS_BYTES <= 160 * 1024, "tile buffers exceed the 160 KB LDS of a compute unit");
@@ -149,7 +181,15 @@ void sdpa_twopass_kernel(const FwdArgs a) {
     const int n = lane & 31;
     const int hf = lane >> 5;
 
-    const Work w = decode_block(SPL ? (int)blockIdx.x / a.n_splits : (int)blockIdx.x, a);
+    const Work w = decode_block(SPL ? (int)blockIdx.x / a_in.n_splits : (int)blockIdx.x, a_in);
+    FwdArgs seq_args;
+    if constexpr (THD) {
+        seq_args = a_in;
+        thd_rebase<T>(seq_args, w.b);
+        if (w.qblk * QB >= seq_args.Sq) return;  // past this sequence's queries (uniform)
+    }
+    const FwdArgs& a = pick_args<THD>(seq_args, a_in);
+    const int pcols = THD ? a.p_cols : a.Skv;  // probability row length
     const int hk = w.hq / a.group;
     const int q0 = w.qblk * QB;
     const int kend = a.causal ? min(a.Skv, max(0, q0 + QB + a.coff)) : a.Skv;
@@ -639,7 +679,7 @@ void sdpa_twopass_kernel(const FwdArgs a) {
         const int jrel = 32 * kb + 16 * c + 8 * hf;
         if constexpr (VEC) {
             uint32_t vo = prow + (uint32_t)(jrel * SZ);
-            if (edge) vo = pred(k0 + jrel < a.Skv, vo);
+            if (edge) vo = pred(k0 + jrel < pcols, vo);
             if constexpr (sizeof(T) == 2) {
                 st128s(pr, vo, (uint32_t)(k0 * SZ), __builtin_bit_cast(u32x4, Tr<T>::cvt8(x)));
             } else {
@@ -651,7 +691,7 @@ void sdpa_twopass_kernel(const FwdArgs a) {
                              __builtin_bit_cast(uint32_t, x[6]), __builtin_bit_cast(uint32_t, x[7])});
             }
         } else {
-            store8<T, false>(pr, row_ok ? prow : 0u, row_ok, k0 + jrel, a.Skv, x);
+            store8<T, false>(pr, row_ok ? prow : 0u, row_ok, k0 + jrel, pcols, x);
         }
     };
 
@@ -664,7 +704,7 @@ void sdpa_twopass_kernel(const FwdArgs a) {
             const int chunk = lane % C::ZC;
             const u32x4 bits = *reinterpret_cast<const u32x4*>(pst + C::pos_p(row, chunk) * 16);
             const int grow = qw + row, key = k0 + chunk * (16 / SZ);
-            const bool ok = grow < a.Sq && (!edge || key < a.Skv);
+            const bool ok = grow < a.Sq && (!edge || key < pcols);
             st128_nt(pr, pred(ok, (uint32_t)((int64_t)(grow < a.Sq ? grow : 0) * a.p_s[2] * SZ) + (uint32_t)(key * SZ)),
                   bits);
         }
@@ -680,13 +720,13 @@ void sdpa_twopass_kernel(const FwdArgs a) {
             for (int i = 0; i < 32 * ZC / 64; ++i) {
                 const int row = qw + i * (64 / ZC) + lane / ZC;
                 const int key = t * BN + (lane % ZC) * (16 / SZ);
-                st128_nt(pr, pred(row < a.Sq && key < a.Skv,
+                st128_nt(pr, pred(row < a.Sq && key < pcols,
                                (uint32_t)((int64_t)(row < a.Sq ? row : 0) * a.p_s[2] * SZ) + (uint32_t)(key * SZ)),
                       u32x4{0u, 0u, 0u, 0u});
             }
         } else {
             const float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-            const bool edge = (t + 1) * BN > a.Skv;
+            const bool edge = (t + 1) * BN > pcols;
 #pragma unroll
             for (int q = 0; q < 2 * NKB; ++q) store_run(t * BN, q >> 1, q & 1, edge, z);
         }
@@ -951,7 +991,7 @@ void sdpa_twopass_kernel(const FwdArgs a) {
 
     // ---------------- causal: keys past this workgroup's last row are zero
     // (with key ranges: written by the last range; LSE by the first)
-    if (SPL == 0 || split == a.n_splits - 1) zero_rows<T, VEC>(pr, a.p_s[2], qw, a.Sq, ntiles * BN, a.Skv, lane);
+    if (SPL == 0 || split == a.n_splits - 1) zero_rows<T, VEC>(pr, a.p_s[2], qw, a.Sq, ntiles * BN, pcols, lane);
     if (SPL == 0 || split == 0)
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, dead ? -INFINITY : lse2 * LN2), lr,
                                               pred(row_ok && hf == 0, (uint32_t)((int64_t)(row_ok ? qi : 0) * a.l_s[2] * 4)),
@@ -966,6 +1006,14 @@ void sdpa_twopass_kernel(const FwdArgs a) {
 // decode with an additive mask 32 -> 40 us).
 template <int MK>
 constexpr int tile_keys() { return MK == MASK_BOOL ? 32 : 64; }
+
+// Packed variable-length sequences: two compute waves and a loader wave, no mask.
+template <typename T, int D, bool VEC>
+static int launch_twopass_thd(const FwdArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL((sdpa_twopass_kernel<T, D, 2, MASK_NONE, VEC, tile_keys<MASK_NONE>(), false, 0, false, true>),
+                       dim3(a.n_blocks), dim3(3 * 64), 0, s, a);
+    return (int)hipGetLastError();
+}
 
 template <typename T, int D, int NW, bool VEC, bool NL, bool DROP = false>
 static int launch_twopass_mask(int mask_kind, const FwdArgs& a, hipStream_t s) {
@@ -1074,6 +1122,15 @@ static bool twopass_nl_ok_t(int D, int mask_kind) {
 template <typename T>
 static int launch_twopass_t(int D, int mask_kind, int waves, bool vec, bool drop, const FwdArgs& a, void* stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (a.thd) {  // packed sequences: two compute waves and a loader wave, no mask, whole calls
+        if (waves != 2 || a.n_splits > 1 || drop || mask_kind != MASK_NONE) return (int)hipErrorInvalidValue;
+        switch (D) {
+            case 32: return vec ? launch_twopass_thd<T, 32, true>(a, s) : launch_twopass_thd<T, 32, false>(a, s);
+            case 64: return vec ? launch_twopass_thd<T, 64, true>(a, s) : launch_twopass_thd<T, 64, false>(a, s);
+            case 128: return vec ? launch_twopass_thd<T, 128, true>(a, s) : launch_twopass_thd<T, 128, false>(a, s);
+            default: return (int)hipErrorInvalidValue;
+        }
+    }
     if (drop) {  // dropout: two compute waves and a loader wave, whole calls
         if (waves != 2 || a.n_splits > 1) return (int)hipErrorInvalidValue;
         switch (D) {
