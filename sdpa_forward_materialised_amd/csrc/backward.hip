@@ -46,7 +46,10 @@ __device__ __forceinline__ u32x2 lds_tr16(const void* p) {
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p));
 }
 
-constexpr int BW = 2;  // waves per workgroup in both kernels
+constexpr int BWQ = 4;  // waves per workgroup of the query-side kernel (128 query rows)
+// waves per workgroup of the key-side kernels (64 keys; measured faster than
+// 128, whose larger blocks balance the causal triangle worse)
+constexpr int BW_KV = 2;
 
 // An LDS tile of rows of D elements: row-major, 16-byte chunks of a row
 // permuted in groups of four (chunk c of row r at r * CPR + (c ^ f(r))), so
@@ -76,6 +79,39 @@ __device__ __forceinline__ void load_tile32(uint8_t* dst, rsrc_t src, uint32_t p
         *reinterpret_cast<u32x4*>(dst + TL::pos(row, c) * 16) = x;
     }
 }
+
+// A 32-row tile's 16-byte chunks held in registers by thread tid of nt
+// threads (chunks tid, tid + nt, ...): loaded from global memory one tile
+// ahead, written to LDS once the current tile has been consumed, so the
+// loads' latency hides behind the current tile's arithmetic.
+template <typename T, int D, int NT>
+struct Prefetch32 {
+    using TL = Tile<T, D>;
+    static constexpr int TOTAL = 32 * TL::CPR;
+    static constexpr int N = (TOTAL + NT - 1) / NT;
+    u32x4 r[N];
+    __device__ __forceinline__ void load(rsrc_t src, uint32_t pitch, int row0, int limit, int tid) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int idx = tid + i * NT;
+            if (TOTAL % NT == 0 || idx < TOTAL) {
+                const int row = idx / TL::CPR, c = idx - (idx / TL::CPR) * TL::CPR;
+                const int g = row0 + row;
+                r[i] = ld128(src, pred(g < limit, (uint32_t)g * pitch + (uint32_t)(c * 16)));
+            }
+        }
+    }
+    __device__ __forceinline__ void store(uint8_t* dst, int tid) const {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int idx = tid + i * NT;
+            if (TOTAL % NT == 0 || idx < TOTAL) {
+                const int row = idx / TL::CPR, c = idx - (idx / TL::CPR) * TL::CPR;
+                *reinterpret_cast<u32x4*>(dst + TL::pos(row, c) * 16) = r[i];
+            }
+        }
+    }
+};
 
 // A operand of an MFMA whose rows are tile rows: lane (m, h) reads tile row
 // `row` (the caller passes base + swap23(m)), elements c*KSTEP + h*KH .. +KH.
@@ -238,7 +274,7 @@ __device__ __forceinline__ float mask_elem(const FwdArgs& f, rsrc_t mr, int qi, 
 // ====================================================================== dq
 
 template <typename T, int D, int MASK, bool HAS_DP>
-__global__ __launch_bounds__(BW * 64) void sdpa_bwd_q_kernel(const BwdArgs a) {
+__global__ __launch_bounds__(BWQ * 64) void sdpa_bwd_q_kernel(const BwdArgs a) {
     using TR = Tr<T>;
     using vec = typename TR::vec;
     using TL = Tile<T, D>;
@@ -256,16 +292,16 @@ __global__ __launch_bounds__(BW * 64) void sdpa_bwd_q_kernel(const BwdArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, hf = lane >> 5;
-    const int nqb = (f.Sq + 32 * BW - 1) / (32 * BW);
+    const int nqb = (f.Sq + 32 * BWQ - 1) / (32 * BWQ);
     const int bh = blockIdx.x / nqb;
     const int qblk = blockIdx.x - bh * nqb;
     const int b = bh / f.Hq, h = bh - (bh / f.Hq) * f.Hq;
     const int hk = h / f.group;
-    const int q0 = qblk * 32 * BW;
+    const int q0 = qblk * 32 * BWQ;
     const int qw = q0 + 32 * wave;
     const int qi = qw + n;
     const bool row_ok = qi < f.Sq;
-    const int kend = f.causal ? min(f.Skv, max(0, q0 + 32 * BW + f.coff)) : f.Skv;
+    const int kend = f.causal ? min(f.Skv, max(0, q0 + 32 * BWQ + f.coff)) : f.Skv;
     const int ntiles = (kend + 31) / 32;
 
     const rsrc_t qr = make_rsrc(static_cast<const T*>(f.q) + b * f.q_s[0] + h * f.q_s[1], f.q_ext);
@@ -290,19 +326,26 @@ __global__ __launch_bounds__(BW * 64) void sdpa_bwd_q_kernel(const BwdArgs a) {
     const uint32_t m_row = (uint32_t)((int64_t)(row_ok ? qi : 0) * f.m_s[2] * ME);
     const uint32_t krow = (uint32_t)(f.k_s[2] * SZ), vrow = (uint32_t)(f.v_s[2] * SZ);
 
+    Prefetch32<T, D, BWQ * 64> kp, vp;
+    auto prefetch = [&](int t) __attribute__((always_inline)) {
+        kp.load(kr, krow, t * 32, f.Skv, tid);
+        vp.load(vr, vrow, t * 32, f.Skv, tid);
+    };
+    // the per-lane loads of tile t (mask terms, dprobs): issued before the
+    // next tile's prefetch, so waiting for them does not wait for it
+    auto lane_loads = [&](int t, float* mv, float* dpv) __attribute__((always_inline)) {
+        if constexpr (MASK != MASK_NONE) load_mask16<T, MASK, false>(f, mr, m_row, t * 32, hf, mv);
+        if constexpr (HAS_DP) load_dprobs16<T>(a, dpr, dp_row, row_ok, t * 32, hf, dpv);
+    };
     // probabilities and gradient-at-P of this lane's 16 (query, key) pairs of
-    // 32-key tile t (staged); removed keys give P = 0
-    auto block = [&](int t, float* p, float* dp) __attribute__((always_inline)) {
+    // the staged 32-key tile t; removed keys give P = 0
+    auto block = [&](int t, const float* mv, const float* dpv, float* p, float* dp) __attribute__((always_inline)) {
         const int jb = t * 32;
         f32x16 s = {}, g = {};
 #pragma unroll
         for (int c = 0; c < NKS; ++c) s = TR::mfma(row_operand<T, D>(kt, swap23(n), c, hf), qf[c], s);
 #pragma unroll
         for (int c = 0; c < NKS; ++c) g = TR::mfma(row_operand<T, D>(vt, swap23(n), c, hf), df[c], g);
-        float mv[16];
-        if constexpr (MASK != MASK_NONE) load_mask16<T, MASK, false>(f, mr, m_row, jb, hf, mv);
-        float dpv[16];
-        if constexpr (HAS_DP) load_dprobs16<T>(a, dpr, dp_row, row_ok, jb, hf, dpv);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int j = jb + kk(hf, r);
@@ -312,22 +355,37 @@ __global__ __launch_bounds__(BW * 64) void sdpa_bwd_q_kernel(const BwdArgs a) {
             dp[r] = HAS_DP ? g[r] + dpv[r] : g[r];
         }
     };
-    auto stage = [&](int t) __attribute__((always_inline)) {
-        __syncthreads();  // the previous tile's reads are done
-        load_tile32<T, D>(kt, kr, krow, t * 32, f.Skv, tid, BW * 64);
-        load_tile32<T, D>(vt, vr, vrow, t * 32, f.Skv, tid, BW * 64);
+    // one sweep over the key tiles: the first tile staged, then per tile the
+    // lane loads, the next tile's prefetch, the arithmetic, and the handover
+    auto sweep = [&](auto&& body) __attribute__((always_inline)) {
+        if (ntiles > 0) {
+            prefetch(0);
+            kp.store(kt, tid);
+            vp.store(vt, tid);
+        }
         __syncthreads();
+        for (int t = 0; t < ntiles; ++t) {
+            float mv[16], dpv[16];
+            lane_loads(t, mv, dpv);
+            if (t + 1 < ntiles) prefetch(t + 1);
+            float p[16], dp[16];
+            block(t, mv, dpv, p, dp);
+            body(p, dp);
+            __syncthreads();  // tile t consumed
+            if (t + 1 < ntiles) {
+                kp.store(kt, tid);
+                vp.store(vt, tid);
+            }
+            __syncthreads();
+        }
     };
 
     // ---------------- sweep 1: D_i = sum_j P_ij dP_ij
     float dsum = 0.0f;
-    for (int t = 0; t < ntiles; ++t) {
-        stage(t);
-        float p[16], dp[16];
-        block(t, p, dp);
+    sweep([&](const float* p, const float* dp) __attribute__((always_inline)) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) dsum = __builtin_fmaf(p[r], dp[r], dsum);
-    }
+    });
     dsum += __shfl_xor(dsum, 32);
     if (row_ok && hf == 0) a.dsum[((int64_t)b * f.Hq + h) * f.Sq + qi] = dsum;
 
@@ -335,21 +393,28 @@ __global__ __launch_bounds__(BW * 64) void sdpa_bwd_q_kernel(const BwdArgs a) {
     f32x16 acc[ND];
 #pragma unroll
     for (int dd = 0; dd < ND; ++dd) acc[dd] = f32x16{};
-    for (int t = 0; t < ntiles; ++t) {
-        stage(t);
-        float p[16], dp[16], ds[16];
-        block(t, p, dp);
+    sweep([&](const float* p, const float* dp) __attribute__((always_inline)) {
+        float ds[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) ds[r] = p[r] * (dp[r] - dsum);
         acc_tr_product<T, D>(acc, kt, 0, ds, lane);
-    }
+    });
     store_acc_row<T, D>(dqr, (uint32_t)(row_ok ? qi : 0) * (uint32_t)(a.dq_s[2] * SZ), row_ok, acc, a.scale, hf);
 }
 
 // ====================================================================== dk, dv
 
-template <typename T, int D, int MASK, bool HAS_DP>
-__global__ __launch_bounds__(BW * 64) void sdpa_bwd_kv_kernel(const BwdArgs a) {
+// WHICH: KV_DV accumulates dv only (S, P), KV_DK dk only (S, P, dP, dS),
+// KV_BOTH both. The two single-gradient launches hold half the accumulators,
+// so twice the waves fit per SIMD: faster despite recomputing S once the grid
+// is large enough to fill the chip twice over; below that one launch wins.
+constexpr int KV_DV = 1, KV_DK = 2, KV_BOTH = 3;
+
+template <typename T, int D, int MASK, bool HAS_DP, int WHICH>
+__global__ __launch_bounds__(BW_KV * 64) void sdpa_bwd_kv_kernel(const BwdArgs a) {
+    constexpr int BW = BW_KV;
+    constexpr bool DO_DV = (WHICH & KV_DV) != 0;
+    constexpr bool NEED_DP = (WHICH & KV_DK) != 0;  // dP, dprobs and D: dk only
     using TR = Tr<T>;
     using TL = Tile<T, D>;
     constexpr int SZ = (int)sizeof(T);
@@ -362,8 +427,9 @@ __global__ __launch_bounds__(BW * 64) void sdpa_bwd_kv_kernel(const BwdArgs a) {
 
     // Q and dout tiles of the current 32 query rows, their log2-domain LSE and
     // D, then per wave its 32 key rows of K and V and its dprobs tile
-    constexpr int DPB = 32 * 32 * SZ;  // dprobs tile: 32 queries x 32 keys
-    constexpr int WAVEB = 2 * TL::BYTES32 + DPB;
+    // (the dv pass reads neither V nor dprobs)
+    constexpr int DPB = HAS_DP && NEED_DP ? 32 * 32 * SZ : 0;  // dprobs tile: 32 queries x 32 keys
+    constexpr int WAVEB = (NEED_DP ? 2 : 1) * TL::BYTES32 + DPB;
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TL::BYTES32 + 2 * 32 * 4 + BW * WAVEB];
     uint8_t* qt = smem;
     uint8_t* dot = smem + TL::BYTES32;
@@ -378,8 +444,11 @@ __global__ __launch_bounds__(BW * 64) void sdpa_bwd_kv_kernel(const BwdArgs a) {
     uint8_t* dpw = vw + TL::BYTES32;
 
     const int nkb = (f.Skv + 32 * BW - 1) / (32 * BW);
-    const int bk = blockIdx.x / nkb;
-    const int kblk = blockIdx.x - bk * nkb;
+    // key block major: the early key blocks (the most query tiles under a
+    // causal mask) of every head go first
+    const int nbk = f.B * f.Hkv;
+    const int kblk = blockIdx.x / nbk;
+    const int bk = blockIdx.x - kblk * nbk;
     const int b = bk / f.Hkv, hk = bk - (bk / f.Hkv) * f.Hkv;
     const int k0 = kblk * 32 * BW;
     const int kw0 = k0 + 32 * wave;
@@ -393,75 +462,125 @@ __global__ __launch_bounds__(BW * 64) void sdpa_bwd_kv_kernel(const BwdArgs a) {
 
     // this wave's key rows (B operands of both products)
     load_tile32<T, D>(kw, kr, (uint32_t)(f.k_s[2] * SZ), kw0, f.Skv, lane, 64);
-    load_tile32<T, D>(vw, vr, (uint32_t)(f.v_s[2] * SZ), kw0, f.Skv, lane, 64);
+    if constexpr (NEED_DP) load_tile32<T, D>(vw, vr, (uint32_t)(f.v_s[2] * SZ), kw0, f.Skv, lane, 64);
 
-    f32x16 dk[ND], dv[ND];
+    // dk^T, dv^T of this lane's key (what this launch accumulates)
+    f32x16 dk[NEED_DP ? ND : 1], dv[DO_DV ? ND : 1];
 #pragma unroll
     for (int dd = 0; dd < ND; ++dd) {
-        dk[dd] = f32x16{};
-        dv[dd] = f32x16{};
+        if constexpr (NEED_DP) dk[dd] = f32x16{};
+        if constexpr (DO_DV) dv[dd] = f32x16{};
     }
     // causal: query i sees key j iff j <= i + coff, so queries below
     // k0 - coff see none of this workgroup's keys
     const int qstart = f.causal ? max(0, k0 - f.coff) / 32 * 32 : 0;
+    const int nqt = f.Sq > qstart ? (f.Sq - qstart + 31) / 32 : 0;  // query tiles per head
+    const int nit = f.group * nqt;                                   // (head of the group, query tile) steps
 
-    for (int hh = 0; hh < f.group; ++hh) {
-        const int h = hk * f.group + hh;
+    // the next step's tiles, held in registers until the current one is consumed
+    Prefetch32<T, D, BW * 64> qp, dop;
+    float lse_n = INFINITY, dsum_n = 0.0f;  // thread tid < 32: row i0 + tid of the next step
+    constexpr int DPC = 32 * 32 * SZ / 16 / 64;  // 16-byte chunks of a dprobs tile per lane
+    u32x4 dpn[DPC];
+    auto step_coords = [&](int it, int& h, int& i0) __attribute__((always_inline)) {
+        const int hh = it / nqt;
+        h = hk * f.group + hh;
+        i0 = qstart + (it - hh * nqt) * 32;
+    };
+    auto prefetch = [&](int it) __attribute__((always_inline)) {
+        int h, i0;
+        step_coords(it, h, i0);
         const rsrc_t qr = make_rsrc(static_cast<const T*>(f.q) + b * f.q_s[0] + h * f.q_s[1], f.q_ext);
         const rsrc_t dor = make_rsrc(static_cast<const T*>(a.dout) + b * a.do_s[0] + h * a.do_s[1], a.do_ext);
-        rsrc_t dpr = qr, mr = qr;
-        if constexpr (HAS_DP)
-            dpr = make_rsrc(static_cast<const T*>(a.dprobs) + b * a.dp_s[0] + h * a.dp_s[1], a.dp_ext);
-        if constexpr (MASK != MASK_NONE)
-            mr = make_rsrc(static_cast<const uint8_t*>(f.mask) + (b * f.m_s[0] + h * f.m_s[1]) * ME, f.m_ext);
-        const float* lse_h = f.lse + b * f.l_s[0] + h * f.l_s[1];
-        const float* dsum_h = a.dsum + ((int64_t)b * f.Hq + h) * f.Sq;
-
-        for (int i0 = qstart; i0 < f.Sq; i0 += 32) {
-            __syncthreads();  // the previous tile's reads are done
-            load_tile32<T, D>(qt, qr, (uint32_t)(f.q_s[2] * SZ), i0, f.Sq, tid, BW * 64);
-            load_tile32<T, D>(dot, dor, (uint32_t)(a.do_s[2] * SZ), i0, f.Sq, tid, BW * 64);
-            if (tid < 32) {
-                const int i = i0 + tid;
-                float l = i < f.Sq ? lse_h[(int64_t)i * f.l_s[2]] : -INFINITY;
-                lse_s[tid] = l == -INFINITY ? INFINITY : l * LOG2E;
-                dsum_s[tid] = i < f.Sq ? dsum_h[i] : 0.0f;
-            }
-            if constexpr (HAS_DP) {
-                // dprobs rows i0 .. i0+31, this wave's 32 keys, staged row-major
-                for (int e = lane; e < 32 * 32; e += 64) {
-                    const int rr = e >> 5, cc = e & 31;
-                    const int i = i0 + rr, j = kw0 + cc;
-                    const uint32_t off = pred(i < f.Sq && j < f.Skv,
-                                              (uint32_t)i * (uint32_t)(a.dp_s[2] * SZ) + (uint32_t)(j * SZ));
-                    if constexpr (SZ == 2)
-                        reinterpret_cast<uint16_t*>(dpw)[rr * 32 + cc] = __builtin_amdgcn_raw_buffer_load_b16(dpr, off, 0, 0);
-                    else
-                        reinterpret_cast<uint32_t*>(dpw)[rr * 32 + cc] = __builtin_amdgcn_raw_buffer_load_b32(dpr, off, 0, 0);
+        qp.load(qr, (uint32_t)(f.q_s[2] * SZ), i0, f.Sq, tid);
+        dop.load(dor, (uint32_t)(a.do_s[2] * SZ), i0, f.Sq, tid);
+        if (tid < 32) {
+            const int i = i0 + tid;
+            const float l = i < f.Sq ? f.lse[b * f.l_s[0] + h * f.l_s[1] + (int64_t)i * f.l_s[2]] : -INFINITY;
+            lse_n = l == -INFINITY ? INFINITY : l * LOG2E;
+            if constexpr (NEED_DP) dsum_n = i < f.Sq ? a.dsum[((int64_t)b * f.Hq + h) * f.Sq + i] : 0.0f;
+        }
+        if constexpr (HAS_DP && NEED_DP) {
+            // rows i0 .. i0+31, this wave's 32 keys: 16-byte chunks when the
+            // rows allow it, else element by element (into the same chunks)
+            const rsrc_t dpr = make_rsrc(static_cast<const T*>(a.dprobs) + b * a.dp_s[0] + h * a.dp_s[1], a.dp_ext);
+            constexpr int CPRD = 32 * SZ / 16;  // chunks per tile row
+#pragma unroll
+            for (int u = 0; u < DPC; ++u) {
+                const int idx = lane + 64 * u;
+                const int rr = idx / CPRD, cc = idx - (idx / CPRD) * CPRD;
+                const int i = i0 + rr, j = kw0 + cc * (16 / SZ);
+                const uint32_t row_off = (uint32_t)i * (uint32_t)(a.dp_s[2] * SZ);
+                if (a.dp_vec) {
+                    dpn[u] = ld128(dpr, pred(i < f.Sq && j < f.Skv, row_off + (uint32_t)(j * SZ)));
+                } else {
+                    uint32_t wv[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                    for (int e = 0; e < 16 / SZ; ++e) {
+                        const uint32_t off = pred(i < f.Sq && j + e < f.Skv, row_off + (uint32_t)((j + e) * SZ));
+                        if constexpr (SZ == 2)
+                            wv[e >> 1] |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(dpr, off, 0, 0) << (16 * (e & 1));
+                        else
+                            wv[e] = __builtin_amdgcn_raw_buffer_load_b32(dpr, off, 0, 0);
+                    }
+                    dpn[u] = u32x4{wv[0], wv[1], wv[2], wv[3]};
                 }
             }
-            __syncthreads();
-
-            // S = Q K^T and dP = dout V^T: lane (n, h) holds queries
-            // i0 + kk(h, r) of key kj
-            f32x16 s = {}, g = {};
+        }
+    };
+    auto put = [&]() __attribute__((always_inline)) {
+        qp.store(qt, tid);
+        dop.store(dot, tid);
+        if (tid < 32) {
+            lse_s[tid] = lse_n;
+            dsum_s[tid] = dsum_n;
+        }
+        if constexpr (HAS_DP && NEED_DP) {
 #pragma unroll
-            for (int c = 0; c < NKS; ++c)
-                s = TR::mfma(row_operand<T, D>(qt, swap23(n), c, hf), row_operand<T, D>(kw, n, c, hf), s);
+            for (int u = 0; u < DPC; ++u) reinterpret_cast<u32x4*>(dpw)[lane + 64 * u] = dpn[u];
+        }
+    };
+
+    if (nit > 0) {
+        prefetch(0);
+        put();
+    }
+    __syncthreads();  // (also orders this wave's K and V rows before their first reads)
+    for (int it = 0; it < nit; ++it) {
+        int h, i0;
+        step_coords(it, h, i0);
+        // this step's mask terms (per lane: its key, 16 queries), before the prefetch
+        float mv[16];
+        if constexpr (MASK != MASK_NONE) {
+            const rsrc_t mr = make_rsrc(static_cast<const uint8_t*>(f.mask) + (b * f.m_s[0] + h * f.m_s[1]) * ME, f.m_ext);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = i0 + kk(hf, r);
+                mv[r] = (i < f.Sq && key_ok) ? mask_elem<T, MASK>(f, mr, i, kj) : 0.0f;
+            }
+        }
+        if (it + 1 < nit) prefetch(it + 1);
+
+        // S = Q K^T and dP = dout V^T: lane (n, h) holds queries
+        // i0 + kk(h, r) of key kj
+        f32x16 sacc = {}, g = {};
+#pragma unroll
+        for (int c = 0; c < NKS; ++c)
+            sacc = TR::mfma(row_operand<T, D>(qt, swap23(n), c, hf), row_operand<T, D>(kw, n, c, hf), sacc);
+        if constexpr (NEED_DP) {
 #pragma unroll
             for (int c = 0; c < NKS; ++c)
                 g = TR::mfma(row_operand<T, D>(dot, swap23(n), c, hf), row_operand<T, D>(vw, n, c, hf), g);
-            float p[16], ds[16];
+        }
+        float p[16], ds[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int ql = kk(hf, r);
-                const int i = i0 + ql;
-                float x = s[r] * f.scale_log2;
-                if constexpr (MASK != MASK_NONE) {
-                    if (i < f.Sq && key_ok) x = __builtin_fmaf(s[r], f.scale_log2, mask_elem<T, MASK>(f, mr, i, kj));
-                }
-                if (!key_ok || (f.causal && kj > i + f.coff)) x = -INFINITY;
-                p[r] = fast_exp2(x - lse_s[ql]);
+        for (int r = 0; r < 16; ++r) {
+            const int ql = kk(hf, r);
+            const int i = i0 + ql;
+            float x = MASK != MASK_NONE ? __builtin_fmaf(sacc[r], f.scale_log2, mv[r]) : sacc[r] * f.scale_log2;
+            if (!key_ok || (f.causal && kj > i + f.coff)) x = -INFINITY;
+            p[r] = fast_exp2(x - lse_s[ql]);
+            if constexpr (NEED_DP) {
                 float dp = g[r];
                 if constexpr (HAS_DP) {
                     if constexpr (SZ == 2) dp += Tr<T>::to_f(reinterpret_cast<const uint16_t*>(dpw)[ql * 32 + n]);
@@ -469,25 +588,44 @@ __global__ __launch_bounds__(BW * 64) void sdpa_bwd_kv_kernel(const BwdArgs a) {
                 }
                 ds[r] = p[r] * (dp - dsum_s[ql]);
             }
-            acc_tr_product<T, D>(dv, dot, 0, p, lane, P_LIFT);
-            acc_tr_product<T, D>(dk, qt, 0, ds, lane);
         }
+        if constexpr (DO_DV) acc_tr_product<T, D>(dv, dot, 0, p, lane, P_LIFT);
+        if constexpr (NEED_DP) acc_tr_product<T, D>(dk, qt, 0, ds, lane);
+        __syncthreads();  // step consumed
+        if (it + 1 < nit) put();
+        __syncthreads();
     }
     const uint32_t krow_off = (uint32_t)(key_ok ? kj : 0);
-    store_acc_row<T, D>(dkr, krow_off * (uint32_t)(a.dk_s[2] * SZ), key_ok, dk, a.scale, hf);
-    store_acc_row<T, D>(dvr, krow_off * (uint32_t)(a.dv_s[2] * SZ), key_ok, dv, 1.0f / P_LIFT, hf);
+    if constexpr (NEED_DP) store_acc_row<T, D>(dkr, krow_off * (uint32_t)(a.dk_s[2] * SZ), key_ok, dk, a.scale, hf);
+    if constexpr (DO_DV) store_acc_row<T, D>(dvr, krow_off * (uint32_t)(a.dv_s[2] * SZ), key_ok, dv, 1.0f / P_LIFT, hf);
+}
+
+// Key-side launches: split into a dk and a dv pass once each pass alone has
+// at least two waves per SIMD of the chip (256 CUs x 4 SIMDs), one combined
+// pass below that.
+constexpr int64_t KV_SPLIT_MIN_WAVES = 2 * 256 * 4;
+
+template <typename T, int D, int MASK, bool HAS_DP>
+void launch_bwd_kv(const BwdArgs& a, int64_t nk, hipStream_t s) {
+    if (nk <= 0) return;
+    if (nk * BW_KV >= KV_SPLIT_MIN_WAVES) {
+        hipLaunchKernelGGL((sdpa_bwd_kv_kernel<T, D, MASK, HAS_DP, KV_DK>), dim3((unsigned)nk), dim3(BW_KV * 64), 0, s, a);
+        hipLaunchKernelGGL((sdpa_bwd_kv_kernel<T, D, MASK, HAS_DP, KV_DV>), dim3((unsigned)nk), dim3(BW_KV * 64), 0, s, a);
+    } else {
+        hipLaunchKernelGGL((sdpa_bwd_kv_kernel<T, D, MASK, HAS_DP, KV_BOTH>), dim3((unsigned)nk), dim3(BW_KV * 64), 0, s, a);
+    }
 }
 
 template <typename T, int D, int MASK>
 int launch_bwd_t(const BwdArgs& a, hipStream_t s) {
-    const int64_t nq = (int64_t)a.f.B * a.f.Hq * ((a.f.Sq + 32 * BW - 1) / (32 * BW));
-    const int64_t nk = (int64_t)a.f.B * a.f.Hkv * ((a.f.Skv + 32 * BW - 1) / (32 * BW));
+    const int64_t nq = (int64_t)a.f.B * a.f.Hq * ((a.f.Sq + 32 * BWQ - 1) / (32 * BWQ));
+    const int64_t nk = (int64_t)a.f.B * a.f.Hkv * ((a.f.Skv + 32 * BW_KV - 1) / (32 * BW_KV));
     if (a.dprobs) {
-        if (nq > 0) hipLaunchKernelGGL((sdpa_bwd_q_kernel<T, D, MASK, true>), dim3((unsigned)nq), dim3(BW * 64), 0, s, a);
-        if (nk > 0) hipLaunchKernelGGL((sdpa_bwd_kv_kernel<T, D, MASK, true>), dim3((unsigned)nk), dim3(BW * 64), 0, s, a);
+        if (nq > 0) hipLaunchKernelGGL((sdpa_bwd_q_kernel<T, D, MASK, true>), dim3((unsigned)nq), dim3(BWQ * 64), 0, s, a);
+        launch_bwd_kv<T, D, MASK, true>(a, nk, s);
     } else {
-        if (nq > 0) hipLaunchKernelGGL((sdpa_bwd_q_kernel<T, D, MASK, false>), dim3((unsigned)nq), dim3(BW * 64), 0, s, a);
-        if (nk > 0) hipLaunchKernelGGL((sdpa_bwd_kv_kernel<T, D, MASK, false>), dim3((unsigned)nk), dim3(BW * 64), 0, s, a);
+        if (nq > 0) hipLaunchKernelGGL((sdpa_bwd_q_kernel<T, D, MASK, false>), dim3((unsigned)nq), dim3(BWQ * 64), 0, s, a);
+        launch_bwd_kv<T, D, MASK, false>(a, nk, s);
     }
     return (int)hipGetLastError();
 }
