@@ -142,8 +142,12 @@ def time_gpu(w, steps, warmup, path="auto", warm_ms=50.0, flush=True):
 
 
 # Sources whose change invalidates a stored counter measurement of the kernel.
-KERNEL_SOURCES = ["sdpa_device.h", "sdpa_internal.h", "twopass.h", "twopass_bf16.hip", "sdpa_math_api.cpp"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sdpa_twopass_kernel.prefill_2k_d128_bf16_causal.traffic.txt")
+KERNEL_SOURCES = ["sdpa_device.h", "sdpa_internal.h", "twopass.h", "twopass_bf16.hip", "twopass_f16.hip",
+                  "twopass_f32.hip", "fused.hip", "sdpa_math_api.cpp"]
+
+
+def profile_file(kernel, workload):
+    return os.path.join(ROOT, "profiles", f"{kernel}.{workload}.txt")
 
 
 def kernel_source_hash():
@@ -156,18 +160,21 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def stored_traffic():
-    """HBM bytes per launch from the committed counter summary, or None when
-    it is missing or was taken on other kernel sources."""
+def stored_traffic(kernel, workload):
+    """HBM bytes per launch of ``kernel`` on ``workload`` from the committed
+    rocprofv3 summary (FETCH_SIZE + WRITE_SIZE, each scaled by the copy-kernel
+    calibration), or None when it is missing or was taken on other kernel
+    sources."""
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(profile_file(kernel, workload)) as fh:
             kv = dict(ln.split(":", 1) for ln in fh if ":" in ln and not ln.startswith("#"))
     except OSError:
         return None
     kv = {k.strip(): v.strip() for k, v in kv.items()}
     if kv.get("kernel_source_sha256") != kernel_source_hash():
         return None
-    return int(kv["traffic_bytes_per_launch"])
+    val = kv.get(f"traffic_bytes_{kernel}")
+    return int(val.split()[0]) if val else None
 
 
 def probe_copy(mib, steps, warmup):
@@ -443,6 +450,8 @@ def main():
                     help="fused vs two-pass (2 and 3 compute waves) on masked short-query shapes, then exit")
     ap.add_argument("--threshold-sweep", action="store_true",
                     help="only time both paths over a grid of shapes (fused/two-pass switch)")
+    ap.add_argument("--backward", action="store_true",
+                    help="only time the backward (sdpa_math_bwd) of --workload and print its JSON line")
     ap.add_argument("--probe-copy-mib", type=int, default=0,
                     help="only time the streaming copy kernel over this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -465,6 +474,9 @@ def main():
         return
 
     w = W.BY_NAME[args.workload]
+    if args.backward:
+        print(json.dumps(time_backward(w, reps=args.steps, warmup=args.warmup)), flush=True)
+        return
     log(f"[bench] {w.describe()} steps={args.steps} warmup={args.warmup} flush={not args.no_flush}")
     r = time_gpu(w, args.steps, args.warmup, args.path, flush=not args.no_flush)
     row = workload_row(w, r)
@@ -520,7 +532,7 @@ def main():
         "effective_tflops_frac_of_mfma_peak": round(tflops / MFMA_PEAK_TFLOPS[w.dtype], 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": stored_traffic() if w.name == "prefill_2k_d128_bf16_causal" else None,
+                     "traffic": stored_traffic(kernel, w.name),
                      "kernel": kernel, "bytes_per_launch": row["bytes"]},
         "cpu_baseline": cpu,
         "wall_ms_per_step": round(r["wall_ms"], 5),
