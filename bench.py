@@ -247,57 +247,63 @@ def threshold_sweep(reps=15, warmup=3):
                     print(json.dumps(res), flush=True)
 
 
-def mask_sweep(reps=50, warmup=20):
-    """Masked short-query shapes (fp16, B=16, H=8, non-causal, full [B,H,Sq,Skv]
-    masks with 10 % of keys removed at random; Sq 32..128, Skv 512..2048, D 64/128,
-    additive or bool): event time per call of the fused path and of the two-pass
-    path with 2 and 3 compute waves (forced), best of 3 x ``reps`` calls; one
-    text line per shape, with the path the planner picks."""
+def mask_sweep(reps=30, warmup=5):
+    """Short-query shapes (fp16, B=16, H=8, non-causal; no mask, or a full
+    [B,H,Sq,Skv] additive or bool mask removing 10 % of keys at random; Sq
+    32..256, Skv 256..2048, D 64/128): flushed per-call median of the fused
+    path's wide variant, its one-row-group kernel (SDPA_MATH_FUSED_WIDE=0)
+    and the two-pass path; one text line per shape, with the path the
+    planner picks ("-" where a variant cannot take the shape)."""
+    import statistics
+
     import torch
 
     import sdpa_forward_materialised_amd as S
 
     dev = "cuda:0"
     g = torch.Generator(device="cpu").manual_seed(0)
-    variants = (("fused", None), ("twopass", "2"), ("twopass", "3"))
-    print("B H Sq Skv D mask | fused tp2 tp3 (us) | auto-plan", flush=True)
-    for Sq in (32, 64, 100, 128):
-        for Skv in (512, 1152, 2048):
+    variants = (("fused", None), ("fused", "0"), ("twopass", None))
+    print("B H Sq Skv D mask | fused-wide fused-1group twopass (us) | auto-plan", flush=True)
+    for Sq in (32, 64, 100, 128, 256):
+        for Skv in (256, 512, 1152, 2048):
             for D in (64, 128):
-                for mk in ("add", "bool"):
+                for mk in ("none", "add", "bool"):
                     B, H = 16, 8
                     q = torch.randn(B, H, Sq, D, generator=g).half().to(dev)
                     k = torch.randn(B, H, Skv, D, generator=g).half().to(dev)
                     v = torch.randn(B, H, Skv, D, generator=g).half().to(dev)
                     drop = torch.rand(B, H, Sq, Skv, generator=g) < 0.1
-                    m = (torch.where(drop, float("-inf"), 0.0).half() if mk == "add" else ~drop).to(dev)
+                    m = None if mk == "none" else \
+                        (torch.where(drop, float("-inf"), 0.0).half() if mk == "add" else ~drop).to(dev)
                     out = (torch.empty(B, H, Sq, D, dtype=q.dtype, device=dev),
                            torch.empty(B, H, Sq, Skv, dtype=q.dtype, device=dev),
                            torch.empty(B, H, Sq, dtype=torch.float32, device=dev))
                     res = []
-                    for path, waves in variants:
-                        os.environ.pop("SDPA_MATH_TP_WAVES", None)
-                        if waves:
-                            os.environ["SDPA_MATH_TP_WAVES"] = waves
+                    for path, wide in variants:
+                        os.environ.pop("SDPA_MATH_FUSED_WIDE", None)
+                        if wide is not None:
+                            os.environ["SDPA_MATH_FUSED_WIDE"] = wide
+                        elif path == "fused":
+                            os.environ["SDPA_MATH_FUSED_WIDE"] = "1"
                         try:
                             for _ in range(warmup):
                                 S.fwd(q, k, v, m, False, None, False, path=path, out=out)
                         except NotImplementedError:
-                            res.append(float("nan"))
+                            res.append(None)
                             continue
                         torch.cuda.synchronize()
-                        best = 1e9
-                        for _ in range(3):
-                            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                            e0.record()
-                            for _ in range(reps):
-                                S.fwd(q, k, v, m, False, None, False, path=path, out=out)
-                            e1.record()
-                            torch.cuda.synchronize()
-                            best = min(best, e0.elapsed_time(e1) / reps * 1e3)
-                        res.append(best)
-                    os.environ.pop("SDPA_MATH_TP_WAVES", None)
-                    print(f"{B} {H} {Sq} {Skv} {D} {mk} | " + " ".join(f"{x:7.2f}" for x in res) +
+                        st = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+                        en = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+                        for i in range(reps):
+                            flush_caches()
+                            st[i].record()
+                            S.fwd(q, k, v, m, False, None, False, path=path, out=out)
+                            en[i].record()
+                        torch.cuda.synchronize()
+                        res.append(statistics.median(x.elapsed_time(y) * 1e3 for x, y in zip(st, en)))
+                    os.environ.pop("SDPA_MATH_FUSED_WIDE", None)
+                    print(f"{B} {H} {Sq} {Skv} {D} {mk} | " +
+                          " ".join("      -" if x is None else f"{x:7.2f}" for x in res) +
                           f" | {S.plan(q, k, v, m)[0]}", flush=True)
 
 

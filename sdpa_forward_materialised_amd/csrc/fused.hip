@@ -324,13 +324,400 @@ void sdpa_fused_kernel(const FwdArgs a) {
     }
 }
 
+// ---------------------------------------------------------------- wide variant
+//
+// Workgroup = RG row groups of 32 query rows (a.fused_rg) x KG key groups;
+// wave w = (row group w / KG, key group w % KG) scores 32 rows against
+// a.keys_per_wave keys, held in registers as above. The V rows of the
+// workgroup's whole key range are staged in LDS by whole-row buffer-to-LDS
+// loads and shared by the row groups (the two-level split lets a short-query
+// shape fill the chip with half as many workgroups); V rows then replace
+// them, landing while the row statistics are combined. Whole-row loads cost
+// the memory pipeline about a quarter of what the MFMA-layout accesses (32
+// rows x 32 bytes per instruction) cost. Row maximum and sum are combined
+// over the KG waves of a row group through LDS; once V has landed no load is
+// left in flight, so each block's probabilities are stored as soon as they
+// are made.
+
+// Bytes of dynamic LDS of the wide kernel: the staged V rows (or, after
+// them, the partial O^T of every wave), then the row max and sum of every wave.
+template <typename T, int D>
+constexpr int fused_wide_lds_bytes(int nw, int vrows) {
+    const int v = vrows * D * (int)sizeof(T), o = nw * 32 * (D + 4) * 4;
+    return (v > o ? v : o) + 2 * nw * 32 * 4;
+}
+
+template <typename T, int D>
+constexpr int fused_wide_max_blocks() {
+    return fused_wide_max_keys(sizeof(T) == 4 ? DT_F32 : DT_F16, D) / 32;
+}
+
+template <typename T, int D, int MASK, bool VEC>
+__global__ __launch_bounds__(FUSED_MAX_WAVES * 64) void sdpa_fused_wide_kernel(const FwdArgs a) {
+    using TR = Tr<T>;
+    using vec = typename TR::vec;
+    constexpr int SZ = (int)sizeof(T);
+    constexpr int KH = TR::KH;
+    constexpr int KSTEP = 2 * KH;
+    constexpr int NKS = D / KSTEP;
+    constexpr int ND = D / 32;
+    constexpr int ME = MASK == MASK_BOOL ? 1 : SZ;
+    constexpr int ROWB = D * SZ;
+    constexpr int CPR = ROWB / 16;
+    constexpr int NBMAX = fused_wide_max_blocks<T, D>();
+    constexpr int OPITCH = D + 4;
+    static_assert(CPR % 4 == 0, "V block layout needs a multiple of 4 chunks per row");
+
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int nw = (int)(blockDim.x >> 6);
+    const int RG = a.fused_rg;
+    const int KG = nw / RG;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n = lane & 31;
+    const int hf = lane >> 5;
+    const int rg = wave / KG, kg = wave - (wave / KG) * KG;
+    const int kpw = a.keys_per_wave;
+    const int vrows = KG * kpw;  // staged V rows: keys 0 .. vrows-1 (zeros past Skv)
+    const int vbytes = vrows * ROWB > nw * 32 * OPITCH * 4 ? vrows * ROWB : nw * 32 * OPITCH * 4;
+    float* red_m = reinterpret_cast<float*>(smem + vbytes);
+    float* red_l = red_m + nw * 32;
+
+    // workgroup -> (batch, head, row block); each XCD (ids handed out in
+    // turn) takes a contiguous range, so the row blocks of a head, and the
+    // heads of a KV group, read K and V through one L2
+    int L = blockIdx.x;
+    if ((a.n_blocks & 7) == 0) {
+        const int per = a.n_blocks >> 3;
+        L = (L & 7) * per + (L >> 3);
+    }
+    const int bh = L / a.n_qblk;
+    const int rb = L - bh * a.n_qblk;
+    const int b = bh / a.Hq, hq = bh - (bh / a.Hq) * a.Hq;
+    const int hk = hq / a.group;
+    const int q0 = (rb * RG + rg) * 32;
+    const int qi = q0 + n;
+    const bool row_ok = qi < a.Sq;
+    // keys the rows of this row group (and of the whole workgroup) may keep
+    const int kend = a.causal ? min(a.Skv, max(0, q0 + 32 + a.coff)) : a.Skv;
+    const int kend_wg = a.causal ? min(a.Skv, max(0, (rb + 1) * RG * 32 + a.coff)) : a.Skv;
+    const int kbase = kg * kpw;
+    const int nb = max(0, min((kend - kbase + 31) / 32, kpw / 32));
+
+    const rsrc_t qr = make_rsrc(static_cast<const T*>(a.q) + b * a.q_s[0] + hq * a.q_s[1], a.q_ext);
+    const rsrc_t kr = make_rsrc(static_cast<const T*>(a.k) + b * a.k_s[0] + hk * a.k_s[1], a.k_ext);
+    const rsrc_t vr = make_rsrc(static_cast<const T*>(a.v) + b * a.v_s[0] + hk * a.v_s[1], a.v_ext);
+    const rsrc_t pr = make_rsrc(static_cast<T*>(a.p) + b * a.p_s[0] + hq * a.p_s[1], a.p_ext);
+    const rsrc_t orr = make_rsrc(static_cast<T*>(a.o) + b * a.o_s[0] + hq * a.o_s[1], a.o_ext);
+    const rsrc_t lr = make_rsrc(a.lse + b * a.l_s[0] + hq * a.l_s[1], a.l_ext);
+    rsrc_t mr = kr;
+    if constexpr (MASK != MASK_NONE)
+        mr = make_rsrc(static_cast<const uint8_t*>(a.mask) + (b * a.m_s[0] + hq * a.m_s[1]) * ME, a.m_ext);
+    const uint32_t krow_bytes = (uint32_t)(a.k_s[2] * SZ);
+    const uint32_t vrow_bytes = (uint32_t)(a.v_s[2] * SZ);
+    const uint32_t prow = pred(row_ok, (uint32_t)((int64_t)(row_ok ? qi : 0) * a.p_s[2] * SZ));
+
+    // ---------------- K rows of the workgroup's keys into LDS (V replaces them
+    // once the scores are made): buffer-to-LDS loads of whole rows.
+    // K layout: row-major, chunk c of row r at r * CPR + (c ^ fk(r)), so that
+    // the operand reads (16 consecutive rows, one chunk each) are free of
+    // bank conflicts; instruction i fills chunk positions [64 i, 64 i + 64).
+    // V layout: 16-row x 4-chunk bricks, read by the transposing LDS read.
+    constexpr int RPI = 64 / CPR;  // rows per buffer-to-LDS instruction
+    constexpr int RPB = ROWB >= 256 ? 1 : 256 / ROWB;
+    auto fk = [](int row) -> int { return (row / RPB) & (CPR - 1); };
+    auto pos_k = [&](int row, int chunk) -> int { return row * CPR + (chunk ^ fk(row)); };
+    auto pos_v = [](int row, int chunk) -> int {
+        return (row >> 4) * (16 * CPR) + (chunk >> 2) * 64 + 4 * (row & 15) + (chunk & 3);
+    };
+    const int nstage = (min(kend_wg, vrows) + 31) / 32 * 32;  // staged rows (whole 32-key blocks)
+    {
+        const int nki = nstage / RPI;
+        for (int i = wave; i < nki; i += nw) {
+            const int row = i * RPI + lane / CPR;
+            const int chunk = (lane % CPR) ^ fk(row);
+            const uint32_t ko = pred(row < a.Skv, (uint32_t)row * krow_bytes + (uint32_t)(chunk * 16));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(smem + i * 1024), 16, ko, 0, 0, 0);
+        }
+    }
+
+    // Q fragments (B operand): lane (n, h) holds Q[qi][c*KSTEP + h*KH .. +KH)
+    vec qf[NKS];
+    {
+        const uint32_t qoff = (uint32_t)((int64_t)(row_ok ? qi : 0) * a.q_s[2] * SZ);
+#pragma unroll
+        for (int c = 0; c < NKS; ++c) {
+            const uint32_t off = pred(row_ok, qoff + (uint32_t)((c * KSTEP + hf * KH) * SZ));
+            if constexpr (sizeof(T) == 2) qf[c] = as_vec<T>(ld128(qr, off));
+            else qf[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(qr, off, 0, 0));
+        }
+    }
+
+    // ---------------- scores of this wave's keys (base 2, masked), kept in
+    // registers; K operands from LDS. The raw mask words of each 32-key block
+    // are loaded two blocks ahead into a ring of three register sets (loads
+    // past the wave's last block are aimed outside the buffers and return
+    // zeros).
+    const int kr0 = swap23(n);
+    constexpr int MQ = !VEC || MASK == MASK_NONE ? 0 : MASK == MASK_BOOL ? 1 : SZ == 2 ? 2 : 4;
+    constexpr int RING = MQ > 0 ? 3 : 1;
+    u32x4 mring[RING][MQ > 0 ? MQ : 1];
+    const uint32_t mrow = (uint32_t)((int64_t)(row_ok ? qi : 0) * a.m_s[2] * ME);
+    auto issue_mask = [&](int kb, int slot) __attribute__((always_inline)) {
+        if constexpr (MQ > 0) {
+            const bool live = kb < nb;
+            const int jb = kbase + 32 * kb;
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const int j = jb + 16 * c + 8 * hf;
+                const uint32_t off = pred(live && j < a.Skv, mrow + (uint32_t)j * ME);
+                if constexpr (MASK == MASK_BOOL) {
+                    const u32x2 w = ld64(mr, off);
+                    mring[slot][0][2 * c] = w[0];
+                    mring[slot][0][2 * c + 1] = w[1];
+                } else if constexpr (SZ == 2) {
+                    mring[slot][c] = ld128(mr, off);
+                } else {
+                    mring[slot][2 * c] = ld128(mr, off);
+                    mring[slot][2 * c + 1] = ld128(mr, off == OOB ? OOB : off + 16);
+                }
+            }
+        }
+    };
+    // base-2 mask terms of a block from its raw words (the vector layouts of load_mask16)
+    auto mask_terms = [&](int slot, float* mv) __attribute__((always_inline)) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            if constexpr (MASK == MASK_BOOL) {
+                const uint32_t w0 = mring[slot][0][2 * c], w1 = mring[slot][0][2 * c + 1];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    mv[8 * c + e] = (((e < 4 ? w0 : w1) >> (8 * (e & 3))) & 0xffu) ? 0.0f : -INFINITY;
+            } else if constexpr (SZ == 2) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t w = mring[slot][c][e >> 1];
+                    mv[8 * c + e] = Tr<T>::to_f((w >> (16 * (e & 1))) & 0xffffu) * LOG2E;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t b0 = mring[slot][2 * c][e], b1 = mring[slot][2 * c + 1][e];
+                    mv[8 * c + e] = __builtin_bit_cast(float, b0) * LOG2E;
+                    mv[8 * c + 4 + e] = __builtin_bit_cast(float, b1) * LOG2E;
+                }
+            }
+        }
+    };
+    if constexpr (RING > 1) {
+#pragma unroll
+        for (int kb = 0; kb < RING - 1 && kb < NBMAX; ++kb) issue_mask(kb, kb);
+    }
+    // every wave's K rows have landed (this wave's by the wait, the others' by
+    // the barrier after theirs)
+    wait_vmem();
+    __syncthreads();
+    f32x16 s[NBMAX];
+    float m_loc = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NBMAX; ++kb) {
+        if constexpr (RING > 1) {
+            if (kb + RING - 1 < NBMAX) issue_mask(kb + RING - 1, (kb + RING - 1) % RING);
+        }
+        s[kb] = f32x16{};
+        if (kb < nb) {
+            const int jb = kbase + 32 * kb;
+            // K operand (A), k-step c: lane (m, h) reads row jb + swap23(m),
+            // elements c*KSTEP + h*KH .. +KH; all reads of the block before its chain
+            vec ka[NKS];
+#pragma unroll
+            for (int c = 0; c < NKS; ++c) {
+                const int elem = c * KSTEP + hf * KH;
+                const uint8_t* kp = smem + pos_k(jb + kr0, elem * SZ / 16) * 16 + ((elem * SZ) & 15);
+                if constexpr (sizeof(T) == 2) ka[c] = as_vec<T>(*reinterpret_cast<const u32x4*>(kp));
+                else ka[c] = *reinterpret_cast<const float*>(kp);
+            }
+            f32x16 acc = {};
+#pragma unroll
+            for (int c = 0; c < NKS; ++c) acc = TR::mfma(ka[c], qf[c], acc);
+            float mv[16];
+            if constexpr (MQ > 0) mask_terms(kb % RING, mv);
+            else if constexpr (MASK != MASK_NONE) load_mask16<T, MASK, VEC>(a, mr, mrow, jb, hf, mv);
+            const bool edge = (jb + 32 > a.Skv) || (a.causal && jb + 31 > q0 + a.coff);
+            float t[16];
+            scores16<MASK>(a, acc, mv, jb, hf, qi, edge, t);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                s[kb][r] = t[r];
+                m_loc = fmaxf(m_loc, t[r]);
+            }
+        }
+    }
+
+    // ---------------- row maximum and sum across the key groups of the row group
+    m_loc = fmaxf(m_loc, __shfl_xor(m_loc, 32));
+    if (hf == 0) red_m[wave * 32 + n] = m_loc;
+    __syncthreads();  // (every wave is also done reading the staged K rows)
+    // ---------------- V rows into the same LDS region, landing while the row
+    // statistics are combined
+    {
+        const int nvi = nstage / 32 * (CPR / 2);
+        for (int i = wave; i < nvi; i += nw) {
+            const int vb = i / (CPR / 2), j = i - (i / (CPR / 2)) * (CPR / 2);
+            const int row = 32 * vb + 16 * (j / (CPR / 4)) + (lane >> 2);
+            const int chunk = 4 * (j % (CPR / 4)) + (lane & 3);
+            const uint32_t vo = pred(row < a.Skv, (uint32_t)row * vrow_bytes + (uint32_t)(chunk * 16));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(smem + vb * 32 * ROWB + j * 1024), 16, vo, 0, 0, 0);
+        }
+    }
+    float M = -INFINITY;
+    for (int i = 0; i < KG; ++i) M = fmaxf(M, red_m[(rg * KG + i) * 32 + n]);
+    float l_loc = 0.0f;
+    if (M != -INFINITY) {
+#pragma unroll
+        for (int kb = 0; kb < NBMAX; ++kb)
+            if (kb < nb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) l_loc += fast_exp2(s[kb][r] - M);
+            }
+    }
+    l_loc += __shfl_xor(l_loc, 32);
+    if (hf == 0) red_l[wave * 32 + n] = l_loc;
+    // every wave's V loads have landed (this wave's by the wait; the others'
+    // by the barrier after theirs)
+    wait_vmem();
+    __syncthreads();
+    float Lsum = 0.0f;
+    for (int i = 0; i < KG; ++i) Lsum += red_l[(rg * KG + i) * 32 + n];
+    const bool dead = (M == -INFINITY);
+    const float lse2 = dead ? INFINITY : M + __log2f(Lsum);
+
+    // ---------------- probabilities (rounded to the dtype), stored as made, and O^T += V^T P^T
+    f32x16 oacc[ND];
+#pragma unroll
+    for (int d = 0; d < ND; ++d) oacc[d] = f32x16{};
+    const int trg = lane >> 4, trs = lane & 15;
+    const int tr_sig = ((trs & 1) << 1) | ((trs >> 1) & 1);
+    const int tr_row = 8 * (trg >> 1) + (trs >> 2);
+    const int tr_col = 16 * (trg & 1) + 4 * tr_sig;
+#pragma unroll
+    for (int kb = 0; kb < NBMAX; ++kb) {
+        if (kb < nb) {
+            const int jb = kbase + 32 * kb;
+            float p[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) p[r] = fast_exp2(s[kb][r] - lse2);
+            if constexpr (sizeof(T) == 2) {
+#pragma unroll
+                for (int c2 = 0; c2 < 2; ++c2) {
+                    const vec pv = TR::cvt8(p + 8 * c2);
+                    const int j = jb + 16 * c2 + 8 * hf;
+                    const u32x4 bits = __builtin_bit_cast(u32x4, pv);
+                    if constexpr (VEC) {
+                        st128(pr, pred(j < a.Skv, prow + (uint32_t)(j * SZ)), bits);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(bits[e >> 1] >> (16 * (e & 1))), pr,
+                                                                  pred(row_ok && j + e < a.Skv, prow + (uint32_t)((j + e) * SZ)),
+                                                                  0, 0);
+                    }
+                    // the rounded probabilities plus their rounded residual:
+                    // O accumulates P to twice the dtype's precision
+                    const vec pl = TR::lo8(p + 8 * c2, pv);
+                    vec va[ND];
+#pragma unroll
+                    for (int d = 0; d < ND; ++d) {
+                        u32x2 h2[2];
+#pragma unroll
+                        for (int r = 0; r < 2; ++r) {
+                            const int row = jb + 16 * c2 + tr_row + 4 * r;
+                            const int col = 32 * d + tr_col;
+                            h2[r] = lds_tr16(smem + pos_v(row, col * SZ / 16) * 16 + ((col * SZ) & 15));
+                        }
+                        va[d] = __builtin_bit_cast(vec, u32x4{h2[0][0], h2[0][1], h2[1][0], h2[1][1]});
+                    }
+#pragma unroll
+                    for (int d = 0; d < ND; ++d) oacc[d] = TR::mfma(va[d], pv, oacc[d]);
+#pragma unroll
+                    for (int d = 0; d < ND; ++d) oacc[d] = TR::mfma(va[d], pl, oacc[d]);
+                }
+            } else {
+#pragma unroll
+                for (int c2 = 0; c2 < 2; ++c2)
+                    store8<T, VEC>(pr, row_ok ? prow : 0u, row_ok, jb + 16 * c2 + 8 * hf, a.Skv, p + 8 * c2);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = jb + kk(hf, r);
+#pragma unroll
+                    for (int d = 0; d < ND; ++d) {
+                        const int col = 32 * d + swap23(n);
+                        const float va = *reinterpret_cast<const float*>(
+                            smem + pos_v(row, col * SZ / 16) * 16 + ((col * SZ) & 15));
+                        oacc[d] = TR::mfma(va, p[r], oacc[d]);
+                    }
+                }
+            }
+        }
+    }
+
+    // ---------------- zeros past this wave's keys, LSE
+    {
+        const int c0 = min(a.Skv, kbase + 32 * nb);
+        const int c1 = kg == KG - 1 ? a.Skv : min(a.Skv, kbase + kpw);
+        zero_rows<T, VEC>(pr, a.p_s[2], q0, a.Sq, c0, c1, lane);
+    }
+    if (kg == 0)
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, dead ? -INFINITY : lse2 * LN2), lr,
+                                              pred(row_ok && hf == 0, (uint32_t)((int64_t)(row_ok ? qi : 0) * a.l_s[2] * 4)),
+                                              0, 0);
+
+    // ---------------- O: the KG partial O^T of each row group summed through LDS
+    if (KG == 1) {
+        const uint32_t orow = (uint32_t)((int64_t)(row_ok ? qi : 0) * a.o_s[2] * SZ);
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+            float x[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) x[r] = oacc[d][r];
+            store8<T, VEC>(orr, orow, row_ok, 32 * d + 8 * hf, D, x);
+            store8<T, VEC>(orr, orow, row_ok, 32 * d + 16 + 8 * hf, D, x + 8);
+        }
+        return;
+    }
+    __syncthreads();  // every wave is done reading the staged V rows
+    float* opart = reinterpret_cast<float*>(smem) + wave * 32 * OPITCH;
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) opart[n * OPITCH + 32 * d + kk(hf, r)] = oacc[d][r];
+    __syncthreads();
+    const float* obase = reinterpret_cast<const float*>(smem);
+    for (int i = threadIdx.x; i < RG * 32 * (D / 8); i += nw * 64) {
+        const int rr = i / (D / 8), c8 = i - (i / (D / 8)) * (D / 8);
+        const int g = rr >> 5, row = rr & 31;
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+        for (int ww = 0; ww < KG; ++ww) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] += obase[((g * KG + ww) * 32 + row) * OPITCH + 8 * c8 + e];
+        }
+        const int orow_i = (rb * RG + g) * 32 + row;
+        const bool ok = orow_i < a.Sq;
+        store8<T, VEC>(orr, (uint32_t)((int64_t)(ok ? orow_i : 0) * a.o_s[2] * SZ), ok, 8 * c8, D, x);
+    }
+}
+
 template <typename T, int D, bool VEC>
 int launch_fused_t(int mask_kind, int waves, const FwdArgs& a, hipStream_t s) {
     const dim3 grid(a.n_blocks), block(waves * 64);
-    const size_t lds = (size_t)fused_lds_bytes<T, D>(waves);
+    const bool wide = a.fused_rg > 0;
+    const size_t lds = wide ? (size_t)fused_wide_lds_bytes<T, D>(waves, waves / a.fused_rg * a.keys_per_wave)
+                            : (size_t)fused_lds_bytes<T, D>(waves);
 #define SDPA_FUSED_LAUNCH(MK)                                                                               \
     {                                                                                                       \
-        auto* k = sdpa_fused_kernel<T, D, MK, VEC>;                                                        \
+        auto* k = wide ? sdpa_fused_wide_kernel<T, D, MK, VEC> : sdpa_fused_kernel<T, D, MK, VEC>;         \
         if (lds > 64 * 1024) {                                                                              \
             const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),                     \
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
@@ -365,8 +752,15 @@ int launch_fused(int dtype, int D, int mask_kind, int waves, bool vec, const Fwd
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (waves < 1 || waves > FUSED_MAX_WAVES || a.keys_per_wave % 32 != 0 || a.keys_per_wave <= 0)
         return (int)hipErrorInvalidValue;
-    const int maxk = D == 128 ? FUSED_MAX_KEYS_PER_WAVE_D128 : FUSED_MAX_KEYS_PER_WAVE;
-    if (a.keys_per_wave > maxk) return (int)hipErrorInvalidValue;
+    if (a.fused_rg > 0) {
+        // wide variant: RG row groups x KG key groups, every staged V row in LDS
+        if (waves % a.fused_rg != 0 || a.keys_per_wave > fused_wide_max_keys(dtype, D) ||
+            fused_wide_lds_bytes_rt(dtype, D, waves, waves / a.fused_rg * a.keys_per_wave) > FUSED_LDS_MAX)
+            return (int)hipErrorInvalidValue;
+    } else {
+        const int maxk = D == 128 ? FUSED_MAX_KEYS_PER_WAVE_D128 : FUSED_MAX_KEYS_PER_WAVE;
+        if (a.keys_per_wave > maxk) return (int)hipErrorInvalidValue;
+    }
     switch (dtype) {
         case DT_F32: return launch_fused_dt<float>(D, mask_kind, waves, vec, a, s);
         case DT_F16: return launch_fused_dt<_Float16>(D, mask_kind, waves, vec, a, s);

@@ -34,6 +34,8 @@ struct FwdArgs {
     int n_qblk;      // query blocks per (batch, head)
     int n_blocks;    // workgroups in the grid
     int keys_per_wave;  // fused path: key range of one wave
+    int fused_rg;       // fused path: 0 one row group per workgroup; else the
+                        // wide variant with this many 32-row groups
     int sched;       // workgroup order (causal: 1, 2, 3), see decode_block
     // Key ranges (split over workgroups): n_splits ranges of split_tiles
     // tiles (an even count) per query block; the two-pass kernels then run as
@@ -97,6 +99,7 @@ struct Plan {
     int n_qblk;
     int64_t grid;
     int keys_per_wave;  // fused only
+    int fused_rg = 0;   // fused only: row groups of the wide variant (0: the one-group kernel)
     int64_t tiles_per_bh;
     int64_t tiles_64;
     int n_splits = 1;     // key ranges per query block (two-pass, with a workspace)
@@ -133,6 +136,17 @@ int static_scratch(void** ptr);
 constexpr int FUSED_MAX_KEYS_PER_WAVE = 256;       // D = 32, 64
 constexpr int FUSED_MAX_KEYS_PER_WAVE_D128 = 128;  // D = 128
 constexpr int FUSED_MAX_WAVES = 8;
+// Wide fused variant: keys per wave, and the LDS it may take for the staged V
+// rows of all its keys (or the partial outputs), plus the row statistics.
+// Keys per wave: D = 32, 64: 320; D = 128: 160 (float32: 128).
+constexpr int fused_wide_max_keys(int dtype, int D) { return D == 128 ? (dtype == DT_F32 ? 128 : 160) : 320; }
+constexpr int FUSED_LDS_MAX = 160 * 1024;
+// Bytes of dynamic LDS of the wide variant for `nw` waves staging `vrows` V rows.
+inline int fused_wide_lds_bytes_rt(int dtype, int D, int nw, int vrows) {
+    const int esz = dtype == DT_F32 ? 4 : 2;
+    const int v = vrows * D * esz, o = nw * 32 * (D + 4) * 4;
+    return (v > o ? v : o) + 2 * nw * 32 * 4;
+}
 constexpr int TILE_N = 64;  // keys per score tile
 
 }  // namespace sdpa

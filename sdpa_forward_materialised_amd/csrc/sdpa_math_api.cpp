@@ -262,6 +262,47 @@ bool fused_config(const Shape& sh, bool causal, int64_t coff, int* waves, int* k
     return false;
 }
 
+// Wide fused variant: workgroups of rg row groups of 32 rows x kg key groups
+// (rg * kg <= 8 waves), the K, then V, rows of all their keys staged in LDS.
+// rg: the largest of 4, 2, 1 that still gives a workgroup per CU (256); kg:
+// the fewest key groups whose per-wave key range and staged rows fit, then
+// doubled while a wave holds more than 128 keys and wave slots are left
+// (more waves in flight: measured faster for 32- and 64-row calls).
+// SDPA_MATH_FUSED_WIDE=0 keeps the fused path on its one-row-group kernel;
+// =1 makes the fused path take the wide variant only (an error where it
+// cannot take the shape).
+bool fused_wide_config(const Shape& sh, bool causal, int64_t coff, int* waves, int* keys_per_wave, int* rg_out) {
+    if (const char* e = std::getenv("SDPA_MATH_FUSED_WIDE"))
+        if (!std::strcmp(e, "0")) return false;
+    const int64_t keys = causal ? std::min(sh.Skv, sh.Sq + coff) : sh.Skv;  // the last row's keys
+    if (keys <= 0) return false;
+    const int64_t n32 = cdiv(sh.Sq, 32), bh = sh.B * sh.Hq;
+    const int dt = sh.dtype == SDPA_F32 ? sdpa::DT_F32 : sdpa::DT_F16;
+    const int64_t limit = sdpa::fused_wide_max_keys(dt, (int)sh.D);
+    for (int rg = 4; rg >= 1; rg /= 2) {
+        if (rg > 1 && (rg > n32 || bh * cdiv(n32, rg) < 256)) continue;
+        for (int kg = 1; rg * kg <= sdpa::FUSED_MAX_WAVES; kg *= 2) {
+            const int64_t kpw = cdiv(cdiv(keys, kg), 32) * 32;
+            if (kpw > limit) continue;
+            if (sdpa::fused_wide_lds_bytes_rt(dt, (int)sh.D, rg * kg, (int)(kg * kpw)) > sdpa::FUSED_LDS_MAX) continue;
+            int k2 = kg;
+            int64_t kp2 = kpw;
+            while (kp2 > 128 && rg * k2 * 2 <= sdpa::FUSED_MAX_WAVES) {
+                const int64_t nk = cdiv(cdiv(keys, 2 * k2), 32) * 32;
+                if (sdpa::fused_wide_lds_bytes_rt(dt, (int)sh.D, rg * 2 * k2, (int)(2 * k2 * nk)) > sdpa::FUSED_LDS_MAX)
+                    break;
+                k2 *= 2;
+                kp2 = nk;
+            }
+            *waves = rg * k2;
+            *keys_per_wave = (int)kp2;
+            *rg_out = rg;
+            return true;
+        }
+    }
+    return false;
+}
+
 // True when the 16-byte variant of the two-pass kernel can run: probability
 // and output rows 16-byte aligned (null: the default dense outputs), Skv a
 // multiple of 8, and a mask (if any) contiguous along the keys with 16-byte
@@ -320,8 +361,15 @@ size_t split_ws_bytes(const Shape& sh, int n_splits) {
 sdpa_status_t make_plan(const Shape& sh, bool causal, int64_t coff, int forced, bool vec, sdpa::Plan* p,
                         bool allow_split = false) {
     p->tiles_64 = count_tiles(sh.Sq, sh.Skv, causal, 64, coff);
-    int fw = 0, fk = 0;
-    const bool fused_ok = fused_config(sh, causal, coff, &fw, &fk);
+    int fw = 0, fk = 0, frg = 0;
+    int ww = 0, wk = 0, wrg = 0;
+    const bool wide_ok = fused_wide_config(sh, causal, coff, &ww, &wk, &wrg);
+    const bool fused_ok = fused_config(sh, causal, coff, &fw, &fk) || wide_ok;
+    if (wide_ok) {
+        fw = ww;
+        fk = wk;
+        frg = wrg;
+    }
     int path = forced;
     if (path == SDPA_PATH_AUTO) path = env_path();
     // An additive mask over more than 64 query rows goes to the two-pass path
@@ -329,10 +377,24 @@ sdpa_status_t make_plan(const Shape& sh, bool causal, int64_t coff, int forced, 
     // and 128, Skv 512 / 1152 / 2048, D = 64: equal or up to 9 % faster; with
     // a bool mask the fused path stays faster, by up to 2.5x).
     const bool add_rows = sh.mask_kind == sdpa::MASK_ADD && sh.Sq > 64;
+    // Where the wide variant can take the shape it replaces that rule: with a
+    // mask (read once instead of once per sweep) from 512 keys and up to 256
+    // query rows, without one from 1024 keys and up to 128 rows (measured,
+    // fp16, 16 x 8 heads, Sq 32..256, Skv 256..2048, D 64 / 128: e.g. 100
+    // queries x 1152 keys, D 64, additive mask 30 vs 39 us; bool mask, 256 x
+    // 1152 55 vs 68 us; no mask, 128 x 512 19 vs 18 us, left to two-pass).
+    const bool masked = sh.mask_kind != sdpa::MASK_NONE;
+    const bool wide_pick = wide_ok && !causal && sh.Skv >= (masked ? 512 : 1024) && sh.Sq <= (masked ? 256 : 128);
+    // (causal calls keep the tile-count rule whichever kernel takes them)
+    const bool tile_rule = fused_ok && p->tiles_64 <= env_max_tiles() && sh.Sq <= env_max_rows() &&
+                           (causal || sh.Skv >= env_min_keys()) && !add_rows;
     if (path == SDPA_PATH_AUTO)
-        path = (fused_ok && p->tiles_64 <= env_max_tiles() && sh.Sq <= env_max_rows() &&
-                (causal || sh.Skv >= env_min_keys()) && !add_rows) ? SDPA_PATH_FUSED
-                                                                   : SDPA_PATH_TWOPASS;
+        path = (wide_ok && !causal ? wide_pick : tile_rule) ? SDPA_PATH_FUSED : SDPA_PATH_TWOPASS;
+    if (path == SDPA_PATH_FUSED && !wide_ok) {
+        const char* e = std::getenv("SDPA_MATH_FUSED_WIDE");
+        if (e && !std::strcmp(e, "1"))
+            return fail(SDPA_ERR_UNSUPPORTED, "the wide fused variant cannot take this shape (SDPA_MATH_FUSED_WIDE=1)");
+    }
     if (path == SDPA_PATH_FUSED && !fused_ok)
         return fail(SDPA_ERR_UNSUPPORTED, "the fused path cannot take this shape (more than %d keys per wave x %d waves)",
                     sh.D == 128 ? sdpa::FUSED_MAX_KEYS_PER_WAVE_D128 : sdpa::FUSED_MAX_KEYS_PER_WAVE,
@@ -341,7 +403,8 @@ sdpa_status_t make_plan(const Shape& sh, bool causal, int64_t coff, int forced, 
     if (path == SDPA_PATH_FUSED) {
         p->waves = fw;
         p->keys_per_wave = fk;
-        p->q_rows = 32;
+        p->fused_rg = frg;
+        p->q_rows = 32 * (frg > 0 ? frg : 1);
     } else {
         // Workgroups of four waves take one wave slot per SIMD, so two of
         // them share a CU with the SIMDs evenly loaded (a five-wave group
@@ -508,6 +571,7 @@ sdpa_status_t run(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_ten
         a.ws_o = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + (split_ws_ml_bytes(sh, plan.n_splits) + 255) / 256 * 256);
     }
     a.keys_per_wave = plan.keys_per_wave;
+    a.fused_rg = plan.fused_rg;
     if (drop) {
         a.keep = static_cast<const uint8_t*>(drop->keep->data);
         for (int dd = 0; dd < 4; ++dd) a.kp_s[dd] = eff_stride(drop->keep, dd);

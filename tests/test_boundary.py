@@ -118,16 +118,20 @@ def test_plan_reports_paths_and_tiles():
 
 def test_plan_picks_fused_for_few_tiles():
     # decode-like: 100 queries x 1152 keys is 36 tiles of 64x64 per (b, h);
-    # a bool mask takes the fused path (32-row blocks x 64-key tiles), an
-    # additive one over more than 64 rows the two-pass path with 64-row
-    # blocks (96-row blocks would leave 92 of 192 rows empty)
+    # with a bool or an additive mask the wide fused kernel takes it, two
+    # 32-row groups per workgroup (2 x 18 tiles of 64 rows x 64 keys)
     q, k = _z(16, 8, 100, 64), _z(16, 8, 1152, 64)
     mb = torch.ones(16, 8, 100, 1152, dtype=torch.bool)
-    assert S.plan(q, k, k, mb) == ("fused", 4 * 18, 36)
+    assert S.plan(q, k, k, mb) == ("fused", 2 * 18, 36)
     m = torch.zeros(16, 8, 100, 1152, dtype=torch.float16)
-    assert S.plan(q, k, k, m) == ("twopass", 2 * 18, 36)
+    assert S.plan(q, k, k, m) == ("fused", 2 * 18, 36)
+    # 64 queries: one row group per workgroup (two would leave the grid at
+    # 128 workgroups), 32-row blocks
     q64 = _z(16, 8, 64, 64)
     assert S.plan(q64, k, k, m[:, :, :64]) == ("fused", 2 * 18, 18)
+    # no mask, 512 keys: two-pass
+    k512 = _z(16, 8, 512, 64)
+    assert S.plan(q, k512, k512)[0] == "twopass"
     q = _z(1, 2, 64, 32, dtype=torch.float32)
     assert S.plan(q, q, q, is_causal=True)[0] == "fused"
     # many tiles: two-pass

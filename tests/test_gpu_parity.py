@@ -7,6 +7,7 @@ removed position, LSE = -inf exactly on dead rows).
 """
 
 import math
+import os
 
 import numpy as np
 import pytest
@@ -18,13 +19,30 @@ from parity import TOL_OP, compare, head_slice, poisoned_outputs, run_oracle
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
-PATHS = ["twopass", "fused"]
+# "fused": the fused path as the planner configures it (its wide kernel
+# wherever that fits); "fused1": the fused path held to its one-row-group
+# kernel; "fusedw": held to the wide kernel (skipped where it cannot fit)
+PATHS = ["twopass", "fused", "fused1"]
+_FUSED_ENV = {"fused1": "0", "fusedw": "1"}
 
 
 def _lib():
     import sdpa_forward_materialised_amd as S
     S.load_library()
     return S
+
+
+def _fwd(path, *args, **kw):
+    """S.fwd with a test path name ("fused1" / "fusedw" hold the fused path to one kernel)."""
+    S = _lib()
+    env = _FUSED_ENV.get(path)
+    if env is not None:
+        os.environ["SDPA_MATH_FUSED_WIDE"] = env
+    try:
+        return S.fwd(*args, path="fused" if path.startswith("fused") else path, **kw)
+    finally:
+        if env is not None:
+            os.environ.pop("SDPA_MATH_FUSED_WIDE", None)
 
 
 def _run(c, path, scale=None, gqa=None, label=""):
@@ -38,13 +56,20 @@ def _run(c, path, scale=None, gqa=None, label=""):
     print(f"[case] {label} path={path} shape={tuple(q.shape)}x{tuple(k.shape)} mask="
           f"{None if m is None else (tuple(m.shape), m.dtype)} causal={c['causal']}", flush=True)
     gm = None if m is None else m.to(DEV)
+    env = _FUSED_ENV.get(path)
+    if env is not None:
+        os.environ["SDPA_MATH_FUSED_WIDE"] = env
     try:
-        O, P, L = S.fwd(q.to(DEV), k.to(DEV), v.to(DEV), gm, c["causal"], scale, gqa, path=path, out=out,
+        O, P, L = S.fwd(q.to(DEV), k.to(DEV), v.to(DEV), gm, c["causal"], scale, gqa,
+                        path="fused" if path.startswith("fused") else path, out=out,
                         causal_alignment=c.get("align", "top_left"))
     except NotImplementedError as e:
-        if path == "fused":
+        if path.startswith("fused"):
             pytest.skip(f"the fused path cannot take this shape: {e}")
         raise
+    finally:
+        if env is not None:
+            os.environ.pop("SDPA_MATH_FUSED_WIDE", None)
     torch.cuda.synchronize()
     return O, P, L
 
@@ -90,6 +115,29 @@ SMALL = [
 def test_small_cases(label, spec, path):
     c = W.make_case(**spec)
     _check(c, path, label=label)
+
+
+# The wide fused kernel with two and four 32-row groups per workgroup (grids
+# of at least 256 workgroups), causal and GQA, ragged row groups, masks of
+# each kind, and a layout without 16-byte rows (element loads and stores).
+WIDE = [
+    ("wide-rg2-f16-d64-add", dict(seed=201, dtype="f16", B=32, Hq=8, Hkv=8, Sq=64, Skv=300, D=64, mask="add", p=0.1)),
+    ("wide-rg2-f16-d64-add-ragged", dict(seed=202, dtype="f16", B=16, Hq=8, Hkv=8, Sq=100, Skv=520, D=64,
+                                         mask="neginf", p=0.1)),
+    ("wide-rg4-bf16-d128", dict(seed=203, dtype="bf16", B=64, Hq=8, Hkv=8, Sq=128, Skv=160, D=128)),
+    ("wide-rg2-f32-d32-causal", dict(seed=204, dtype="f32", B=32, Hq=8, Hkv=8, Sq=64, Skv=64, D=32, causal=True)),
+    ("wide-rg2-bf16-d64-gqa-bool", dict(seed=205, dtype="bf16", B=16, Hq=32, Hkv=8, Sq=40, Skv=256, D=64,
+                                        mask="bool", p=0.2)),
+    ("wide-rg2-f16-d32-oddskv", dict(seed=206, dtype="f16", B=32, Hq=8, Hkv=8, Sq=50, Skv=97, D=32, mask="bool")),
+    ("wide-rg2-f32-d64-add", dict(seed=207, dtype="f32", B=32, Hq=8, Hkv=8, Sq=64, Skv=200, D=64, mask="add",
+                                  p=0.2)),
+]
+
+
+@pytest.mark.parametrize("label,spec", WIDE, ids=[s[0] for s in WIDE])
+def test_fused_wide_row_groups(label, spec):
+    c = W.make_case(**spec)
+    _check(c, "fusedw", label=label)
 
 
 # Bool key-padding masks whose tails remove whole 64-key tiles for every row a
@@ -323,9 +371,9 @@ def test_gqa_matches_repeated_kv_bitwise(path):
     c = W.make_case(122, "f16", 2, 8, 2, 70, 130, 64, mask="bool", mask_shape=(2, 1, 70, 130))
     S = _lib()
     q, k, v, m = (c[x].to(DEV) for x in ("q", "k", "v", "mask"))
-    a = S.fwd(q, k, v, m, False, None, True, path=path)
-    b = S.fwd(q, k.repeat_interleave(4, 1).contiguous(), v.repeat_interleave(4, 1).contiguous(), m, False, None,
-              False, path=path)
+    a = _fwd(path, q, k, v, m, False, None, True)
+    b = _fwd(path, q, k.repeat_interleave(4, 1).contiguous(), v.repeat_interleave(4, 1).contiguous(), m, False,
+             None, False)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
 
@@ -335,8 +383,8 @@ def test_deterministic(path):
     c = W.make_case(123, "bf16", 1, 4, 4, 200, 200, 128, causal=True)
     S = _lib()
     q, k, v = (c[x].to(DEV) for x in ("q", "k", "v"))
-    a = S.fwd(q, k, v, None, True, path=path)
-    b = S.fwd(q, k, v, None, True, path=path)
+    a = _fwd(path, q, k, v, None, True)
+    b = _fwd(path, q, k, v, None, True)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
 
