@@ -102,6 +102,14 @@ def time_gpu(w, steps, warmup, path="auto", warm_ms=50.0, flush=True):
     L = torch.empty(B, Hq, Sq, dtype=torch.float32, device=dev)
     out = (O, P, L)
     chosen, tiles, tiles64 = S.plan(q, k, v, m, w.causal, w.gqa, causal_alignment=w.align)
+    # the kernel doing the call's bulk (a forced path goes through the planner's override)
+    if path != "auto":
+        os.environ["SDPA_MATH_PATH"] = path
+    try:
+        kernel = S.kernel_name(q, k, v, m, w.causal, w.gqa, causal_alignment=w.align)
+    finally:
+        if path != "auto":
+            os.environ.pop("SDPA_MATH_PATH", None)
 
     def call():
         S.fwd(q, k, v, m, w.causal, w.scale, w.gqa, path=path, out=out, causal_alignment=w.align)
@@ -138,7 +146,8 @@ def time_gpu(w, steps, warmup, path="auto", warm_ms=50.0, flush=True):
     return {"ms": statistics.fmean(per_call), "ms_median": statistics.median(per_call), "ms_min": min(per_call),
             "ms_back_to_back": e0.elapsed_time(e1) / steps, "wall_ms": wall * 1e3 / steps,
             "mask_bytes": mask_bytes, "flushed": flush,
-            "path": path if path != "auto" else chosen, "tiles_per_bh": tiles, "tiles64_per_bh": tiles64}
+            "path": path if path != "auto" else chosen, "kernel": kernel, "tiles_per_bh": tiles,
+            "tiles64_per_bh": tiles64}
 
 
 # Sources whose change invalidates a stored counter measurement of the kernel.
@@ -325,7 +334,7 @@ def workload_row(w, r):
         fl = 2.0 * w.B * w.Hq * kept_pairs(w.Sq, w.Skv, w.align) * (w.D + w.dv)
     else:
         fl = algorithmic_flops(w.B, w.Hq, w.Sq, w.Skv, w.D, w.dv, w.causal)
-    return {"workload": w.name, "dtype": w.dtype, "path": r["path"], "ms": round(r["ms_median"], 5),
+    return {"workload": w.name, "dtype": w.dtype, "path": r["path"], "kernel": r["kernel"], "ms": round(r["ms_median"], 5),
             "ms_mean": round(r["ms"], 5), "ms_back_to_back": round(r["ms_back_to_back"], 5),
             "tflops": round(fl / sec / 1e12, 2), "p_write_gbps": round(by["p"] / sec / 1e9, 1),
             "hbm_gbps": round(by["total"] / sec / 1e9, 1),
@@ -519,7 +528,7 @@ def main():
         cpu = cpu_baseline(w)
         log(f"[bench] cpu baseline: {cpu}")
 
-    kernel = "sdpa_twopass_kernel" if r["path"] == "twopass" else "sdpa_fused_kernel"
+    kernel = r["kernel"]
     line = {
         "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOPS", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["ms"], 5),

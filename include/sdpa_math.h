@@ -79,7 +79,9 @@ typedef enum {
 typedef enum {
     SDPA_PATH_AUTO = 0,    /* choose by the number of score tiles (see sdpa_math_plan) */
     SDPA_PATH_FUSED = 1,   /* one sweep over the keys; scores stay on chip */
-    SDPA_PATH_TWOPASS = 2  /* row statistics sweep, then a probability/output sweep */
+    SDPA_PATH_TWOPASS = 2, /* row statistics sweep, then a probability/output sweep */
+    SDPA_PATH_FUSED_WIDE = 3 /* reported by sdpa_math_plan only: the fused path on its
+                                wide kernel (several 32-row groups per workgroup) */
 } sdpa_path_t;
 
 /*
@@ -249,18 +251,24 @@ sdpa_status_t sdpa_math_fwd_noalloc(const sdpa_tensor_t* q, const sdpa_tensor_t*
 /*
  * sdpa_math_plan — validate the shapes exactly as sdpa_math_fwd would and
  * report, without launching anything:
- *   *path         the path SDPA_PATH_AUTO resolves to
+ *   *path         the path SDPA_PATH_AUTO resolves to (SDPA_PATH_FUSED_WIDE
+ *                 when that is the fused path on its wide kernel)
  *   *tiles_per_bh score tiles one (batch, head) processes with this
  *                 library's tiling, after causal truncation
  *   *tiles_64     the same count in 64x64 tiles (the unit of the FlagOS-OP
  *                 page's fused-vs-two-stage rule, single-kernel fusion update)
  * out/probs/lse may be NULL here. Any output pointer may be NULL.
- * SDPA_PATH_AUTO takes the fused path when that path can hold the keys,
- * Sq <= 128, tiles_64 <= 64 and (is_causal or Skv >= 512) (thresholds
- * measured on MI355X), else the two-pass path. The environment variable
+ * SDPA_PATH_AUTO (thresholds measured on MI355X): where the fused path's
+ * wide kernel can hold the keys of a non-causal call, the fused path when
+ * the call has a mask, Skv >= 512 and Sq <= 256, or no mask, Skv >= 1024
+ * and Sq <= 128; otherwise the fused path when it can hold the keys,
+ * Sq <= 128, tiles_64 <= 64, (is_causal or Skv >= 512) and no additive mask
+ * over more than 64 rows; else the two-pass path. The environment variable
  * SDPA_MATH_PATH=auto|fused|twopass forces the choice;
  * SDPA_MATH_FUSED_MAX_ROWS=<n>, SDPA_MATH_FUSED_MAX_TILES=<n> and
- * SDPA_MATH_FUSED_MIN_KEYS=<n> move the three thresholds.
+ * SDPA_MATH_FUSED_MIN_KEYS=<n> move the three thresholds of the second
+ * rule; SDPA_MATH_FUSED_WIDE=0 keeps the fused path off its wide kernel,
+ * =1 on it (SDPA_ERR_UNSUPPORTED where it cannot hold the keys).
  */
 sdpa_status_t sdpa_math_plan(const sdpa_tensor_t* q, const sdpa_tensor_t* k,
                              const sdpa_tensor_t* v, const sdpa_tensor_t* mask,

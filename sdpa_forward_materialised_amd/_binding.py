@@ -22,7 +22,10 @@ LIB_PATH = os.path.join(_PKG, "libsdpa_math.so")
 SDPA_F32, SDPA_F16, SDPA_BF16, SDPA_BOOL = 0, 1, 2, 3
 PATH_AUTO, PATH_FUSED, PATH_TWOPASS = 0, 1, 2
 PATHS = {"auto": PATH_AUTO, "fused": PATH_FUSED, "twopass": PATH_TWOPASS}
-PATH_NAMES = {v: k for k, v in PATHS.items()}
+PATH_FUSED_WIDE = 3  # reported by sdpa_math_plan: the fused path on its wide kernel
+PATH_NAMES = {**{v: k for k, v in PATHS.items()}, PATH_FUSED_WIDE: "fused"}
+KERNEL_NAMES = {PATH_FUSED: "sdpa_fused_kernel", PATH_FUSED_WIDE: "sdpa_fused_wide_kernel",
+                PATH_TWOPASS: "sdpa_twopass_kernel"}
 CAUSAL_ALIGNMENTS = {"top_left": 1, "bottom_right": 2}  # the C ABI's is_causal codes
 
 _DTYPES = {torch.float32: SDPA_F32, torch.float16: SDPA_F16, torch.bfloat16: SDPA_BF16,
@@ -413,6 +416,19 @@ def plan(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, attn_mask: Optional[
     if rc != 0:
         _raise(rc, lib)
     return PATH_NAMES[path.value], tiles.value, tiles64.value
+
+
+def kernel_name(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, attn_mask: Optional[torch.Tensor] = None,
+                is_causal: bool = False, enable_gqa: bool = False, causal_alignment: str = "top_left") -> str:
+    """Name of the kernel that does the bulk of a call planned like ``plan``."""
+    lib = load_library()
+    path = ctypes.c_int32(-1)
+    rc = lib.sdpa_math_plan(_desc(q, 4), _desc(k, 4), _desc(v, 4), _desc(attn_mask, 4),
+                            _causal_code(is_causal, causal_alignment), int(bool(enable_gqa)),
+                            ctypes.byref(path), None, None)
+    if rc != 0:
+        _raise(rc, lib)
+    return KERNEL_NAMES[path.value]
 
 
 def probe_fill(dst: torch.Tensor, value: int = 0) -> None:

@@ -919,7 +919,7 @@ sdpa_status_t sdpa_math_plan(const sdpa_tensor_t* q, const sdpa_tensor_t* k, con
     if ((st = make_plan(sh, is_causal != 0, causal_offset(sh, is_causal), SDPA_PATH_AUTO,
                         staged_layout(sh, mask, nullptr, nullptr), &plan)))
         return st;
-    if (path) *path = plan.path;
+    if (path) *path = plan.path == SDPA_PATH_FUSED && plan.fused_rg > 0 ? SDPA_PATH_FUSED_WIDE : plan.path;
     if (tiles_per_bh) *tiles_per_bh = plan.tiles_per_bh;
     if (tiles_64) *tiles_64 = plan.tiles_64;
     return SDPA_OK;
