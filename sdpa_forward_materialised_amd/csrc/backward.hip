@@ -285,7 +285,16 @@ __global__ __launch_bounds__(BWQ * 64) void sdpa_bwd_q_kernel(const BwdArgs a) {
     constexpr int ME = MASK == MASK_BOOL ? 1 : SZ;
     const FwdArgs& f = a.f;
 
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TL::BYTES32];
+    // 16-bit, D = 128: each wave's q and dout rows live in LDS (read as B
+    // operands per tile) instead of 64 registers, where that lets two waves
+    // share a SIMD: no mask, or an additive one without dprobs (2k causal
+    // bf16: 816 -> 700 us). With a bool mask, or a mask and dprobs, the
+    // per-lane mask and dprobs loads keep the wave at one per SIMD either way
+    // and the extra LDS reads only cost (GQA key padding 2070 -> 2136 us);
+    // smaller head dims already run two or more per SIMD (1k D = 64: 183 ->
+    // 193 us).
+    constexpr bool DO_LDS = sizeof(T) == 2 && D == 128 && (MASK == MASK_NONE || (MASK == MASK_ADD && !HAS_DP));
+    __shared__ __attribute__((aligned(16))) uint8_t smem[(2 + (DO_LDS ? 2 * BWQ : 0)) * TL::BYTES32];
     uint8_t* kt = smem;
     uint8_t* vt = smem + TL::BYTES32;
 
@@ -314,9 +323,24 @@ __global__ __launch_bounds__(BWQ * 64) void sdpa_bwd_q_kernel(const BwdArgs a) {
     if constexpr (MASK != MASK_NONE)
         mr = make_rsrc(static_cast<const uint8_t*>(f.mask) + (b * f.m_s[0] + h * f.m_s[1]) * ME, f.m_ext);
 
-    vec qf[NKS], df[NKS];
-    load_frags<T, D>(qf, qr, (uint32_t)(row_ok ? qi : 0) * (uint32_t)(f.q_s[2] * SZ), row_ok, hf);
-    load_frags<T, D>(df, dor, (uint32_t)(row_ok ? qi : 0) * (uint32_t)(a.do_s[2] * SZ), row_ok, hf);
+    vec qf[DO_LDS ? 1 : NKS], df[DO_LDS ? 1 : NKS];
+    uint8_t* qtw = smem + (2 + wave) * TL::BYTES32;        // this wave's q rows (16-bit)
+    uint8_t* dtw = smem + (2 + BWQ + wave) * TL::BYTES32;  // and dout rows
+    if constexpr (DO_LDS) {
+        // the lane's fragments, written where row_operand(.., n, c, hf) reads them
+        vec fr[NKS];
+        load_frags<T, D>(fr, qr, (uint32_t)(row_ok ? qi : 0) * (uint32_t)(f.q_s[2] * SZ), row_ok, hf);
+#pragma unroll
+        for (int c = 0; c < NKS; ++c)
+            *reinterpret_cast<u32x4*>(qtw + TL::pos(n, 2 * c + hf) * 16) = __builtin_bit_cast(u32x4, fr[c]);
+        load_frags<T, D>(fr, dor, (uint32_t)(row_ok ? qi : 0) * (uint32_t)(a.do_s[2] * SZ), row_ok, hf);
+#pragma unroll
+        for (int c = 0; c < NKS; ++c)
+            *reinterpret_cast<u32x4*>(dtw + TL::pos(n, 2 * c + hf) * 16) = __builtin_bit_cast(u32x4, fr[c]);
+    } else {
+        load_frags<T, D>(qf, qr, (uint32_t)(row_ok ? qi : 0) * (uint32_t)(f.q_s[2] * SZ), row_ok, hf);
+        load_frags<T, D>(df, dor, (uint32_t)(row_ok ? qi : 0) * (uint32_t)(a.do_s[2] * SZ), row_ok, hf);
+    }
     float lse2 = INFINITY;  // dead or absent rows: every probability exp2(-inf) = 0
     if (row_ok) {
         const float l = f.lse[b * f.l_s[0] + h * f.l_s[1] + (int64_t)qi * f.l_s[2]];
@@ -343,9 +367,15 @@ __global__ __launch_bounds__(BWQ * 64) void sdpa_bwd_q_kernel(const BwdArgs a) {
         const int jb = t * 32;
         f32x16 s = {}, g = {};
 #pragma unroll
-        for (int c = 0; c < NKS; ++c) s = TR::mfma(row_operand<T, D>(kt, swap23(n), c, hf), qf[c], s);
+        for (int c = 0; c < NKS; ++c) {
+            if constexpr (DO_LDS) s = TR::mfma(row_operand<T, D>(kt, swap23(n), c, hf), row_operand<T, D>(qtw, n, c, hf), s);
+            else s = TR::mfma(row_operand<T, D>(kt, swap23(n), c, hf), qf[c], s);
+        }
 #pragma unroll
-        for (int c = 0; c < NKS; ++c) g = TR::mfma(row_operand<T, D>(vt, swap23(n), c, hf), df[c], g);
+        for (int c = 0; c < NKS; ++c) {
+            if constexpr (DO_LDS) g = TR::mfma(row_operand<T, D>(vt, swap23(n), c, hf), row_operand<T, D>(dtw, n, c, hf), g);
+            else g = TR::mfma(row_operand<T, D>(vt, swap23(n), c, hf), df[c], g);
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int j = jb + kk(hf, r);
