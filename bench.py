@@ -316,6 +316,45 @@ def mask_sweep(reps=30, warmup=5):
                           f" | {S.plan(q, k, v, m)[0]}", flush=True)
 
 
+def host_path(n=2000):
+    """Host time per call on the tiny workload (1x2 heads, 64x64, D=32, fp32
+    causal): through the Python binding's fwd, through a prepared call (one C
+    call per launch), and the GPU time per call back to back. Calls are issued
+    without synchronising; the host time is the issuing loop's wall time."""
+    import torch
+
+    import sdpa_forward_materialised_amd as S
+    import sdpa_workloads as W
+
+    w = W.BY_NAME["tiny_f32_causal"]
+    inp = W.make_inputs(w)
+    q, k, v = (inp[x].to("cuda:0") for x in ("q", "k", "v"))
+    out = S.fwd(q, k, v, None, True)
+    call = S.prepare_fwd(q, k, v, None, True, out=out)
+
+    def host(fn):
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            fn()
+        t1 = time.perf_counter()
+        torch.cuda.synchronize()
+        return (t1 - t0) / n * 1e6
+
+    r = {"workload": w.name, "fwd_host_us": round(host(lambda: S.fwd(q, k, v, None, True, out=out)), 2),
+         "prepared_host_us": round(host(call.run), 2)}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(n):
+        call.run()
+    e1.record()
+    torch.cuda.synchronize()
+    r["gpu_us_per_call_back_to_back"] = round(e0.elapsed_time(e1) / n * 1e3, 2)
+    return r
+
+
 def kept_pairs(Sq, Skv, align):
     """(query, key) pairs a causal mask keeps: query i keeps keys j <= i + c
     (c = 0 top-left, Skv - Sq bottom-right)."""
@@ -516,6 +555,8 @@ def main():
         extra["extra_configs"] = all_configs(args.path, W.EXTRA_WORKLOADS)
 
     if not args.no_configs:
+        extra["host_path"] = host_path()
+        log(f"[bench] host path: {extra['host_path']}")
         extra["backward"] = []
         for name in ("prefill_2k_d128_bf16_causal", "gqa_1k_d128_f16_keypad"):
             rb = time_backward(W.BY_NAME[name])

@@ -8,7 +8,7 @@ is argument marshalling only; torch supplies device memory and streams.
 """
 
 from ._binding import (EXPORTS, LIB_PATH, PATHS, SdpaMathFunction, bwd, fwd, fwd_noalloc, fwd_varlen,  # noqa: F401
-                       kernel_name, last_error, load_library, plan, probe_copy, probe_fill, sdpa_math, version)
+                       PreparedFwd, kernel_name, last_error, load_library, plan, prepare_fwd, probe_copy, probe_fill, sdpa_math, version)
 
-__all__ = ["fwd", "fwd_noalloc", "fwd_varlen", "bwd", "sdpa_math", "SdpaMathFunction", "plan", "kernel_name", "version", "last_error",
+__all__ = ["fwd", "fwd_noalloc", "fwd_varlen", "bwd", "sdpa_math", "SdpaMathFunction", "plan", "kernel_name", "prepare_fwd", "PreparedFwd", "version", "last_error",
            "load_library", "LIB_PATH", "PATHS", "EXPORTS"]

@@ -257,6 +257,65 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, attn_mask: Optional[t
     return O, P, L
 
 
+class PreparedFwd:
+    """A forward call bound to fixed tensors: ``prepare_fwd`` validates the
+    arguments, packs the tensor descriptors and sizes the key-range workspace
+    once; each ``run()`` then launches with one C call (about a torch op
+    launch of host time, where ``fwd`` also spends some microseconds on
+    argument handling), for loops that refill the same buffers in place.
+    The tensors must keep their storage, shapes and strides between runs
+    (they are held here, so they stay alive)."""
+
+    def __init__(self, q, k, v, attn_mask, is_causal, scale, enable_gqa, path, out, causal_alignment):
+        self._lib = load_library()
+        self._dev = _check_devices(q, k, v, attn_mask)
+        if path not in PATHS:
+            raise ValueError(f"path must be one of {sorted(PATHS)}")
+        if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+            raise ValueError("q, k, v must be 4-D [B, H, S, D]")
+        B, Hq, Sq, D = q.shape
+        Skv, Dv = k.shape[2], v.shape[3]
+        if out is None:
+            out = (torch.empty((B, Hq, Sq, Dv), dtype=q.dtype, device=self._dev),
+                   torch.empty((B, Hq, Sq, Skv), dtype=q.dtype, device=self._dev),
+                   torch.empty((B, Hq, Sq), dtype=torch.float32, device=self._dev))
+        _check_devices(q, *out)
+        self.out = tuple(out)
+        self._keep = (q, k, v, attn_mask)
+        causal = _causal_code(is_causal, causal_alignment)
+        dq, dk, dv, dm = _desc(q, 4), _desc(k, 4), _desc(v, 4), _desc(attn_mask, 4)
+        n = ctypes.c_size_t(0)
+        rc = self._lib.sdpa_math_workspace_bytes(dq, dk, dv, dm, causal, int(bool(enable_gqa)), ctypes.byref(n))
+        if rc != 0:
+            _raise(rc, self._lib)
+        self._ws = torch.empty(n.value, dtype=torch.uint8, device=self._dev) if n.value > 0 else None
+        if scale is None:
+            scale = 1.0 / math.sqrt(D) if D > 0 else 1.0
+        self._args = (dq, dk, dv, dm, causal, float(scale), int(bool(enable_gqa)),
+                      _desc(self.out[0], 4), _desc(self.out[1], 4), _desc(self.out[2], 3),
+                      None if self._ws is None else ctypes.c_void_p(self._ws.data_ptr()), n.value)
+        self._path = PATHS[path]
+        # validate everything once, on the current stream
+        self.run()
+
+    def run(self, stream: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+        """Launch on ``stream`` (a raw HIP stream handle; default: the
+        current stream of the tensors' device, which must be current)."""
+        st = _current_stream(self._dev) if stream is None else stream
+        rc = self._lib.sdpa_math_fwd_ws(*self._args, ctypes.c_void_p(st), self._path)
+        if rc != 0:
+            _raise(rc, self._lib)
+        return self.out
+
+
+def prepare_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, attn_mask: Optional[torch.Tensor] = None,
+                is_causal: bool = False, scale: Optional[float] = None, enable_gqa: bool = False,
+                path: str = "auto", out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
+                causal_alignment: str = "top_left") -> PreparedFwd:
+    """``fwd`` bound to these tensors (see PreparedFwd); runs it once."""
+    return PreparedFwd(q, k, v, attn_mask, is_causal, scale, enable_gqa, path, out, causal_alignment)
+
+
 def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
                cu_seqlens_kv: torch.Tensor, max_seqlen_q: int, max_seqlen_kv: int, is_causal: bool = False,
                scale: Optional[float] = None, enable_gqa: bool = False, causal_alignment: str = "top_left",
