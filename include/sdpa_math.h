@@ -150,8 +150,13 @@ sdpa_status_t sdpa_math_fwd_path(const sdpa_tensor_t* q, const sdpa_tensor_t* k,
  * keys are cut into ranges whose row statistics and float32 partial outputs
  * go to the workspace, combined into the same O, P and LSE (the FlagOS-OP
  * "P800 exact-P fast path" update: P = exp(S - LSE) with the row LSE folded
- * from the ranges' statistics). Validates like sdpa_math_plan; *bytes is set
- * to 0 on error.
+ * from the ranges' statistics). Where fewer bytes move that way (roughly: 8
+ * times the query rows per key head below D times the element size), the
+ * ranges run in one sweep over the keys on the wide fused kernel and the
+ * workspace also holds every probability as float32, relative to its
+ * range's row maximum, until a combine launch scales it into P; otherwise
+ * the two-pass kernel runs a statistics and a probability launch per range.
+ * Validates like sdpa_math_plan; *bytes is set to 0 on error.
  */
 sdpa_status_t sdpa_math_workspace_bytes(const sdpa_tensor_t* q, const sdpa_tensor_t* k,
                                         const sdpa_tensor_t* v, const sdpa_tensor_t* mask,
@@ -233,9 +238,11 @@ sdpa_status_t sdpa_math_fwd_varlen(const sdpa_tensor_t* q, const sdpa_tensor_t* 
  * statistics and float32 partial outputs in a static scratch array of
  * SDPA_MATH_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it
  * runs on, until the process ends (its device address is looked up once per
- * device, on the first call there). A call that would need more than that
- * returns SDPA_ERR_UNSUPPORTED before any launch (sdpa_math_fwd_ws with a
- * caller workspace takes it); no part of the scratch needs to start at zero.
+ * device, on the first call there). One-sweep ranges that would need more
+ * than that run as the two-pass split instead; a two-pass split that would
+ * need more returns SDPA_ERR_UNSUPPORTED before any launch (sdpa_math_fwd_ws
+ * with a caller workspace takes it); no part of the scratch needs to start
+ * at zero.
  * Every call on one GPU shares that GPU's scratch, which keeps the last
  * call's contents: calls that may overlap on one GPU (different streams,
  * threads) race and must be ordered by the caller. Arguments, layout,
@@ -251,8 +258,11 @@ sdpa_status_t sdpa_math_fwd_noalloc(const sdpa_tensor_t* q, const sdpa_tensor_t*
 /*
  * sdpa_math_plan — validate the shapes exactly as sdpa_math_fwd would and
  * report, without launching anything:
- *   *path         the path SDPA_PATH_AUTO resolves to (SDPA_PATH_FUSED_WIDE
- *                 when that is the fused path on its wide kernel)
+ *   *path         the path SDPA_PATH_AUTO resolves to in a call with its
+ *                 workspace (sdpa_math_fwd_ws; SDPA_PATH_FUSED_WIDE when that
+ *                 is the fused path on its wide kernel, key ranges included;
+ *                 a call that the planner splits over key ranges runs
+ *                 unsplit without a workspace)
  *   *tiles_per_bh score tiles one (batch, head) processes with this
  *                 library's tiling, after causal truncation
  *   *tiles_64     the same count in 64x64 tiles (the unit of the FlagOS-OP

@@ -160,6 +160,11 @@ def _causal_code(is_causal, causal_alignment: str) -> int:
 DROPOUT_RULES = {"explicit": 0, "random": 1}
 
 
+# planner overrides the workspace size depends on
+_PLAN_ENV = ("SDPA_MATH_PATH", "SDPA_MATH_SPLITS", "SDPA_MATH_TP_WAVES", "SDPA_MATH_RANGES", "SDPA_MATH_RANGE_KEYS",
+             "SDPA_MATH_RANGE_WAVES")
+
+
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, attn_mask: Optional[torch.Tensor] = None,
         is_causal: bool = False, scale: Optional[float] = None, enable_gqa: bool = False,
         path: str = "auto", out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
@@ -226,7 +231,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, attn_mask: Optional[t
     # (the byte count depends on dtypes, shapes, mask layout and flags only:
     # remembered per signature, the descriptors' bytes past the data pointer)
     sig = (dq[8:], dk[8:], None if dm is None else dm[8:], causal, bool(enable_gqa),
-           os.environ.get("SDPA_MATH_SPLITS"), os.environ.get("SDPA_MATH_TP_WAVES"))
+           tuple(os.environ.get(e) for e in _PLAN_ENV))
     nbytes = _WS_BYTES.get(sig)
     if nbytes is None:
         n = ctypes.c_size_t(0)

@@ -352,8 +352,14 @@ constexpr int fused_wide_max_blocks() {
     return fused_wide_max_keys(sizeof(T) == 4 ? DT_F32 : DT_F16, D) / 32;
 }
 
-template <typename T, int D, int MASK, bool VEC>
-__global__ __launch_bounds__(FUSED_MAX_WAVES * 64) void sdpa_fused_wide_kernel(const FwdArgs a) {
+// RANGE: the workgroup takes one key range of a long-key call (range r of
+// a.n_splits: keys [r * R, r * R + R), R = KG * a.keys_per_wave) as a call of
+// its own, and writes, instead of P, O and LSE: its probabilities relative
+// to its own row maximum (float32, ws_e), its rows' (max, sum) (ws_ml) and
+// its float32 partial O (ws_o); sdpa_range_combine_kernel folds them.
+template <typename T, int D, int MASK, bool VEC, bool RANGE>
+__global__ __launch_bounds__(FUSED_MAX_WAVES * 64) void sdpa_fused_wide_kernel(const FwdArgs a_in) {
+    static_assert(!RANGE || VEC, "key ranges take the 16-byte layouts");
     using TR = Tr<T>;
     using vec = typename TR::vec;
     constexpr int SZ = (int)sizeof(T);
@@ -369,6 +375,8 @@ __global__ __launch_bounds__(FUSED_MAX_WAVES * 64) void sdpa_fused_wide_kernel(c
     static_assert(CPR % 4 == 0, "V block layout needs a multiple of 4 chunks per row");
 
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    FwdArgs ra = a_in;  // RANGE: rebased onto the workgroup's key range below
+    const FwdArgs& a = RANGE ? ra : a_in;
     const int nw = (int)(blockDim.x >> 6);
     const int RG = a.fused_rg;
     const int KG = nw / RG;
@@ -391,6 +399,34 @@ __global__ __launch_bounds__(FUSED_MAX_WAVES * 64) void sdpa_fused_wide_kernel(c
         const int per = a.n_blocks >> 3;
         L = (L & 7) * per + (L >> 3);
     }
+    int range = 0, koff = 0;
+    if constexpr (RANGE) {
+        // workgroup order: the query heads of a KV group fastest, then the
+        // ranges, so that a group's heads read each range's K and V rows
+        // through L2 at about the same time; L becomes (batch, head, row block)
+        const int g = L % a_in.group;
+        L /= a_in.group;
+        range = L % a_in.n_splits;
+        L /= a_in.n_splits;
+        const int rb0 = L % a_in.n_qblk, bk = L / a_in.n_qblk;  // bk = batch * Hkv + KV head
+        L = ((bk / a_in.Hkv) * a_in.Hq + (bk % a_in.Hkv) * a_in.group + g) * a_in.n_qblk + rb0;
+        // the range's keys as a call of its own: K, V and mask columns from
+        // koff on (the descriptors shrink by as much), Skv the range's keys,
+        // the causal offset moved with them
+        koff = range * vrows;
+        ra.Skv = min(vrows, a_in.Skv - koff);
+        ra.coff = a_in.coff - koff;
+        const int64_t kadv = (int64_t)koff * a_in.k_s[2], vadv = (int64_t)koff * a_in.v_s[2];
+        ra.k = static_cast<const T*>(a_in.k) + kadv;
+        ra.v = static_cast<const T*>(a_in.v) + vadv;
+        ra.k_ext = a_in.k_ext - (uint32_t)(kadv * SZ);
+        ra.v_ext = a_in.v_ext - (uint32_t)(vadv * SZ);
+        if constexpr (MASK != MASK_NONE) {
+            const int64_t madv = (int64_t)koff * a_in.m_s[3] * ME;
+            ra.mask = static_cast<const uint8_t*>(a_in.mask) + madv;
+            ra.m_ext = a_in.m_ext - (uint32_t)madv;
+        }
+    }
     const int bh = L / a.n_qblk;
     const int rb = L - bh * a.n_qblk;
     const int b = bh / a.Hq, hq = bh - (bh / a.Hq) * a.Hq;
@@ -407,15 +443,31 @@ __global__ __launch_bounds__(FUSED_MAX_WAVES * 64) void sdpa_fused_wide_kernel(c
     const rsrc_t qr = make_rsrc(static_cast<const T*>(a.q) + b * a.q_s[0] + hq * a.q_s[1], a.q_ext);
     const rsrc_t kr = make_rsrc(static_cast<const T*>(a.k) + b * a.k_s[0] + hk * a.k_s[1], a.k_ext);
     const rsrc_t vr = make_rsrc(static_cast<const T*>(a.v) + b * a.v_s[0] + hk * a.v_s[1], a.v_ext);
-    const rsrc_t pr = make_rsrc(static_cast<T*>(a.p) + b * a.p_s[0] + hq * a.p_s[1], a.p_ext);
-    const rsrc_t orr = make_rsrc(static_cast<T*>(a.o) + b * a.o_s[0] + hq * a.o_s[1], a.o_ext);
+    // RANGE: float32 probability rows of this (batch, head) in ws_e (pitch
+    // Skv of the whole call, from the range's first key), partial O rows in
+    // ws_o (pitch D)
+    const int64_t wsrow0 = (int64_t)(b * a.Hq + hq) * a.Sq;  // first workspace row of this (batch, head)
+    const rsrc_t pr = RANGE ? make_rsrc(a_in.ws_e + wsrow0 * a_in.Skv + koff,
+                                        (uint32_t)(((int64_t)a.Sq * a_in.Skv - koff) * 4))
+                            : make_rsrc(static_cast<T*>(a.p) + b * a.p_s[0] + hq * a.p_s[1], a.p_ext);
+    const rsrc_t orr = RANGE ? make_rsrc(a_in.ws_o + ((int64_t)range * a.B * a.Hq * a.Sq + wsrow0) * D,
+                                         (uint32_t)((int64_t)a.Sq * D * 4))
+                             : make_rsrc(static_cast<T*>(a.o) + b * a.o_s[0] + hq * a.o_s[1], a.o_ext);
     const rsrc_t lr = make_rsrc(a.lse + b * a.l_s[0] + hq * a.l_s[1], a.l_ext);
     rsrc_t mr = kr;
     if constexpr (MASK != MASK_NONE)
         mr = make_rsrc(static_cast<const uint8_t*>(a.mask) + (b * a.m_s[0] + hq * a.m_s[1]) * ME, a.m_ext);
     const uint32_t krow_bytes = (uint32_t)(a.k_s[2] * SZ);
     const uint32_t vrow_bytes = (uint32_t)(a.v_s[2] * SZ);
-    const uint32_t prow = pred(row_ok, (uint32_t)((int64_t)(row_ok ? qi : 0) * a.p_s[2] * SZ));
+    const uint32_t prow = RANGE ? pred(row_ok, (uint32_t)((int64_t)(row_ok ? qi : 0) * a_in.Skv * 4))
+                                : pred(row_ok, (uint32_t)((int64_t)(row_ok ? qi : 0) * a.p_s[2] * SZ));
+    // one run of 8 output columns of a row: the dtype, or float32 partials (RANGE)
+    auto store_o8 = [&](uint32_t row_off, bool ok, int col, const float* x) __attribute__((always_inline)) {
+        if constexpr (RANGE) store8<float, true>(orr, row_off, ok, col, D, x);
+        else store8<T, VEC>(orr, row_off, ok, col, D, x);
+    };
+    const int64_t o_pitch = RANGE ? D : a.o_s[2];  // output row pitch, elements
+    constexpr int OSZ = RANGE ? 4 : SZ;
 
     // ---------------- K rows of the workgroup's keys into LDS (V replaces them
     // once the scores are made): buffer-to-LDS loads of whole rows.
@@ -590,7 +642,9 @@ __global__ __launch_bounds__(FUSED_MAX_WAVES * 64) void sdpa_fused_wide_kernel(c
     float Lsum = 0.0f;
     for (int i = 0; i < KG; ++i) Lsum += red_l[(rg * KG + i) * 32 + n];
     const bool dead = (M == -INFINITY);
-    const float lse2 = dead ? INFINITY : M + __log2f(Lsum);
+    // RANGE: probabilities relative to the range's row maximum (the combine
+    // launch scales them by 2^(M - lse2) once every range's sum is known)
+    const float lse2 = dead ? INFINITY : RANGE ? M : M + __log2f(Lsum);
 
     // ---------------- probabilities (rounded to the dtype), stored as made, and O^T += V^T P^T
     f32x16 oacc[ND];
@@ -613,7 +667,9 @@ __global__ __launch_bounds__(FUSED_MAX_WAVES * 64) void sdpa_fused_wide_kernel(c
                     const vec pv = TR::cvt8(p + 8 * c2);
                     const int j = jb + 16 * c2 + 8 * hf;
                     const u32x4 bits = __builtin_bit_cast(u32x4, pv);
-                    if constexpr (VEC) {
+                    if constexpr (RANGE) {
+                        store8<float, true>(pr, row_ok ? prow : 0u, row_ok, j, a.Skv, p + 8 * c2);
+                    } else if constexpr (VEC) {
                         st128(pr, pred(j < a.Skv, prow + (uint32_t)(j * SZ)), bits);
                     } else {
 #pragma unroll
@@ -665,23 +721,28 @@ __global__ __launch_bounds__(FUSED_MAX_WAVES * 64) void sdpa_fused_wide_kernel(c
     {
         const int c0 = min(a.Skv, kbase + 32 * nb);
         const int c1 = kg == KG - 1 ? a.Skv : min(a.Skv, kbase + kpw);
-        zero_rows<T, VEC>(pr, a.p_s[2], q0, a.Sq, c0, c1, lane);
+        if constexpr (RANGE) zero_rows<float, true>(pr, a_in.Skv, q0, a.Sq, c0, c1, lane);
+        else zero_rows<T, VEC>(pr, a.p_s[2], q0, a.Sq, c0, c1, lane);
     }
-    if (kg == 0)
+    if constexpr (RANGE) {
+        if (kg == 0 && hf == 0 && row_ok)
+            a_in.ws_ml[(int64_t)range * a.B * a.Hq * a.Sq + wsrow0 + qi] = float2{M, dead ? 0.0f : Lsum};
+    } else if (kg == 0) {
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, dead ? -INFINITY : lse2 * LN2), lr,
                                               pred(row_ok && hf == 0, (uint32_t)((int64_t)(row_ok ? qi : 0) * a.l_s[2] * 4)),
                                               0, 0);
+    }
 
     // ---------------- O: the KG partial O^T of each row group summed through LDS
     if (KG == 1) {
-        const uint32_t orow = (uint32_t)((int64_t)(row_ok ? qi : 0) * a.o_s[2] * SZ);
+        const uint32_t orow = (uint32_t)((int64_t)(row_ok ? qi : 0) * o_pitch * OSZ);
 #pragma unroll
         for (int d = 0; d < ND; ++d) {
             float x[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) x[r] = oacc[d][r];
-            store8<T, VEC>(orr, orow, row_ok, 32 * d + 8 * hf, D, x);
-            store8<T, VEC>(orr, orow, row_ok, 32 * d + 16 + 8 * hf, D, x + 8);
+            store_o8(orow, row_ok, 32 * d + 8 * hf, x);
+            store_o8(orow, row_ok, 32 * d + 16 + 8 * hf, x + 8);
         }
         return;
     }
@@ -705,19 +766,129 @@ __global__ __launch_bounds__(FUSED_MAX_WAVES * 64) void sdpa_fused_wide_kernel(c
         }
         const int orow_i = (rb * RG + g) * 32 + row;
         const bool ok = orow_i < a.Sq;
-        store8<T, VEC>(orr, (uint32_t)((int64_t)(ok ? orow_i : 0) * a.o_s[2] * SZ), ok, 8 * c8, D, x);
+        store_o8((uint32_t)((int64_t)(ok ? orow_i : 0) * o_pitch * OSZ), ok, 8 * c8, x);
     }
+}
+
+// Output of a call whose keys ran as ranges of the wide kernel: per row, the
+// log-sum-exp from every range's (max, sum); P = RNE(e * c_r) with e the
+// range's float32 probability and c_r = 2^(max_r - lse2); O the sum over
+// ranges of c_r times the range's float32 partial O, rounded once.
+// Workgroup = one row x 2048 keys (8 per thread). The row's statistics are
+// reduced over the workgroup's threads (a fixed tree: the same bits in every
+// workgroup of the row) and the scales c_r kept in LDS; each workgroup also
+// sums the partial outputs of a slice of the head dim (threads split over
+// ranges, then a fixed-order sum through LDS), so that no thread walks every
+// range. Keys past the last range (causal) get P = 0.
+template <bool MAX>
+__device__ __forceinline__ float block_reduce256(float x, float* red) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float y = __shfl_xor(x, o);
+        x = MAX ? fmaxf(x, y) : x + y;
+    }
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+    __syncthreads();
+    x = MAX ? fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])) : (red[0] + red[1]) + (red[2] + red[3]);
+    __syncthreads();
+    return x;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void sdpa_range_combine_kernel(const FwdArgs a, int D, int range_keys, int nchunk) {
+    constexpr int SZ = (int)sizeof(T);
+    __shared__ float cs[RANGE_MAX];
+    __shared__ float red[256];
+    const int tid = (int)threadIdx.x;
+    const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
+    const int64_t row = (int64_t)blockIdx.x / nchunk;
+    const int chunk = (int)((int64_t)blockIdx.x - row * nchunk);
+    const int n = a.n_splits;
+    const float2* st = a.ws_ml + row;  // range r's (max, sum) at st[r * rows]
+    float m = -INFINITY;
+    for (int r = tid; r < n; r += 256) m = fmaxf(m, st[(int64_t)r * rows].x);
+    const float M = block_reduce256<true>(m, red);
+    const bool dead = (M == -INFINITY);
+    float l = 0.0f;
+    if (!dead)
+        for (int r = tid; r < n; r += 256) {
+            const float2 s = st[(int64_t)r * rows];
+            if (s.x != -INFINITY) l += s.y * fast_exp2(s.x - M);
+        }
+    const float lsum = block_reduce256<false>(l, red);
+    const float lse2 = dead ? INFINITY : M + __log2f(lsum);
+    // scale of range r's probabilities and partial output (0 for a range
+    // that keeps no key of the row, and for a dead row)
+    for (int r = tid; r < n; r += 256) {
+        const float mr = st[(int64_t)r * rows].x;
+        cs[r] = mr == -INFINITY ? 0.0f : fast_exp2(mr - lse2);
+    }
+    __syncthreads();
+    const int q = (int)(row % a.Sq);
+    const int64_t bh = row / a.Sq;
+    const int h = (int)(bh % a.Hq), b = (int)(bh / a.Hq);
+    const int j0 = (chunk * 256 + tid) * 8;
+    if (j0 < a.Skv) {
+        const int r = j0 / range_keys;  // a run of 8 keys lies in one range (multiples of 32)
+        float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (r < n) {
+            const float c = cs[r];
+            const float* e = a.ws_e + row * a.Skv + j0;
+            const f32x4 u0 = *reinterpret_cast<const f32x4*>(e);
+            const f32x4 u1 = *reinterpret_cast<const f32x4*>(e + 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[i] = u0[i] * c;
+                x[4 + i] = u1[i] * c;
+            }
+        }
+        T* p = static_cast<T*>(a.p) + b * a.p_s[0] + h * a.p_s[1] + (int64_t)q * a.p_s[2] + j0;
+        if constexpr (SZ == 2) {
+            *reinterpret_cast<u32x4*>(p) = __builtin_bit_cast(u32x4, Tr<T>::cvt8(x));
+        } else {
+            *reinterpret_cast<f32x4*>(p) = f32x4{x[0], x[1], x[2], x[3]};
+            *reinterpret_cast<f32x4*>(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
+        }
+    }
+    // O columns [d0, d0 + dn) of this workgroup: thread (g, col) sums ranges
+    // g, g + G, ... of column d0 + col; then the G partial sums in order
+    const int dpc = (D + nchunk - 1) / nchunk;  // columns per workgroup (<= D <= 256)
+    const int d0 = chunk * dpc;
+    const int dn = min(D, d0 + dpc) - d0;
+    T* orow = static_cast<T*>(a.o) + b * a.o_s[0] + h * a.o_s[1] + (int64_t)q * a.o_s[2];
+    if (dn > 0) {
+        const int G = 256 / dpc;
+        const int col = tid % dpc, g = tid / dpc;
+        float x = 0.0f;
+        if (col < dn && g < G)
+            for (int r = g; r < n; r += G) x += cs[r] * a.ws_o[((int64_t)r * rows + row) * D + d0 + col];
+        red[tid] = x;
+        __syncthreads();
+        if (tid < dn) {
+            float s = 0.0f;
+            for (int gg = 0; gg < G; ++gg) s += red[gg * dpc + tid];
+            if constexpr (SZ == 2) {
+                orow[d0 + tid] = static_cast<T>(s);
+            } else {
+                orow[d0 + tid] = s;
+            }
+        }
+    }
+    if (chunk == 0 && tid == 0) a.lse[b * a.l_s[0] + h * a.l_s[1] + (int64_t)q * a.l_s[2]] = dead ? -INFINITY : lse2 * LN2;
 }
 
 template <typename T, int D, bool VEC>
 int launch_fused_t(int mask_kind, int waves, const FwdArgs& a, hipStream_t s) {
     const dim3 grid(a.n_blocks), block(waves * 64);
     const bool wide = a.fused_rg > 0;
+    const bool ranges = wide && a.n_splits > 1;  // key ranges of the wide kernel, then the combine
+    if (ranges && !VEC) return (int)hipErrorInvalidValue;
     const size_t lds = wide ? (size_t)fused_wide_lds_bytes<T, D>(waves, waves / a.fused_rg * a.keys_per_wave)
                             : (size_t)fused_lds_bytes<T, D>(waves);
 #define SDPA_FUSED_LAUNCH(MK)                                                                               \
     {                                                                                                       \
-        auto* k = wide ? sdpa_fused_wide_kernel<T, D, MK, VEC> : sdpa_fused_kernel<T, D, MK, VEC>;         \
+        auto* k = ranges ? sdpa_fused_wide_kernel<T, D, MK, VEC, VEC>                                      \
+                  : wide ? sdpa_fused_wide_kernel<T, D, MK, VEC, false> : sdpa_fused_kernel<T, D, MK, VEC>;  \
         if (lds > 64 * 1024) {                                                                              \
             const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),                     \
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
@@ -733,6 +904,12 @@ int launch_fused_t(int mask_kind, int waves, const FwdArgs& a, hipStream_t s) {
         default: return (int)hipErrorInvalidValue;
     }
 #undef SDPA_FUSED_LAUNCH
+    if (ranges) {
+        const int range_keys = waves / a.fused_rg * a.keys_per_wave;
+        const int nchunk = (a.Skv + 2047) / 2048;
+        const int64_t nwg = (int64_t)a.B * a.Hq * a.Sq * nchunk;
+        hipLaunchKernelGGL(sdpa_range_combine_kernel<T>, dim3((unsigned)nwg), dim3(256), 0, s, a, D, range_keys, nchunk);
+    }
     return (int)hipGetLastError();
 }
 
@@ -760,6 +937,14 @@ int launch_fused(int dtype, int D, int mask_kind, int waves, bool vec, const Fwd
     } else {
         const int maxk = D == 128 ? FUSED_MAX_KEYS_PER_WAVE_D128 : FUSED_MAX_KEYS_PER_WAVE;
         if (a.keys_per_wave > maxk) return (int)hipErrorInvalidValue;
+    }
+    if (a.n_splits > 1) {
+        // key ranges: the wide kernel on 16-byte layouts, its workspace given,
+        // every range starting inside the keys, whole ranges per row block
+        const int64_t rk = a.fused_rg > 0 ? (int64_t)(waves / a.fused_rg) * a.keys_per_wave : 0;
+        if (a.fused_rg <= 0 || !vec || !a.ws_ml || !a.ws_o || !a.ws_e || (int64_t)(a.n_splits - 1) * rk >= a.Skv ||
+            a.n_blocks % a.n_splits != 0 || a.Skv % 8 != 0 || a.n_splits > RANGE_MAX)
+            return (int)hipErrorInvalidValue;
     }
     switch (dtype) {
         case DT_F32: return launch_fused_dt<float>(D, mask_kind, waves, vec, a, s);

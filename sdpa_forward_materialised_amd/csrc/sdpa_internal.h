@@ -46,6 +46,11 @@ struct FwdArgs {
     int split_tiles;
     float2* ws_ml;
     float* ws_o;
+    // Key ranges of the wide fused kernel (one sweep per range): each range's
+    // probabilities relative to its own row maximum, float32, in
+    // ws_e [B*Hq][Sq][Skv]; a combine launch scales them by the row's final
+    // normaliser into P.
+    float* ws_e;
     // Byte extent of one (batch, head) slice of each tensor (< 2^31); the
     // kernels address every tensor through a buffer descriptor of this size.
     uint32_t q_ext, k_ext, v_ext, o_ext, p_ext, m_ext, l_ext;
@@ -102,8 +107,10 @@ struct Plan {
     int fused_rg = 0;   // fused only: row groups of the wide variant (0: the one-group kernel)
     int64_t tiles_per_bh;
     int64_t tiles_64;
-    int n_splits = 1;     // key ranges per query block (two-pass, with a workspace)
-    int split_tiles = 0;  // kernel tiles per key range (even)
+    int n_splits = 1;     // key ranges per query block (with a workspace)
+    int split_tiles = 0;  // two-pass: kernel tiles per key range (even)
+    // n_splits > 1 on the fused path: key ranges of the wide kernel, one sweep
+    // each (keys_per_wave * waves keys per range), then a combine launch
 };
 
 // Kernel launchers, one translation unit per dtype. `vec` selects the
@@ -148,5 +155,7 @@ inline int fused_wide_lds_bytes_rt(int dtype, int D, int nw, int vrows) {
     return (v > o ? v : o) + 2 * nw * 32 * 4;
 }
 constexpr int TILE_N = 64;  // keys per score tile
+// Most key ranges of one call on the wide kernel (the combine keeps a scale per range in LDS).
+constexpr int RANGE_MAX = 4096;
 
 }  // namespace sdpa

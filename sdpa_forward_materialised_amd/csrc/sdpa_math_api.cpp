@@ -357,9 +357,62 @@ size_t split_ws_bytes(const Shape& sh, int n_splits) {
     const size_t ml = (split_ws_ml_bytes(sh, n_splits) + 255) / 256 * 256;
     return ml + (size_t)n_splits * sh.B * sh.Hq * sh.Sq * sh.Dv * 4;
 }
+// Key ranges of the wide kernel add (256-byte aligned) every row's float32
+// probabilities relative to its range's maximum.
+size_t plan_ws_e_offset(const Shape& sh, int n_splits) { return (split_ws_bytes(sh, n_splits) + 255) / 256 * 256; }
+size_t plan_ws_bytes(const Shape& sh, const sdpa::Plan& p) {
+    if (p.n_splits <= 1) return 0;
+    if (p.path != SDPA_PATH_FUSED) return split_ws_bytes(sh, p.n_splits);
+    return plan_ws_e_offset(sh, p.n_splits) + (size_t)sh.B * sh.Hq * sh.Sq * sh.Skv * 4;
+}
+
+// One-sweep key ranges on the wide fused kernel, for few query rows against
+// many keys: each workgroup scores one range of R keys (K staged in LDS, then
+// V) once, and writes its probabilities relative to its own row maximum as
+// float32, its rows' (max, sum) and its float32 partial O; a combine launch
+// scales each range by 2^(max_r - lse2) into P and O. K and V are read once
+// (the two-pass split reads K in both launches) at the price of the float32
+// probabilities written and read back: 8 bytes per probability against the
+// D * element-size bytes of the K row re-read per key and KV head. Measured
+// (bf16 / f16, D = 64 and 128, 1 to 16 query rows, 8192 to 65536 keys) the
+// ranges win where those 8 bytes times the query rows stay within a quarter
+// of the K row (one or four query rows: 20-30 % faster) and lose at half of
+// it (8 and 16 rows: 5-8 % slower): taken where 32 * Sq <= D * element size.
+// With grouped heads each query head's workgroups stage the group's K and V
+// rows again (four heads per KV head, one query row x 32768 keys: 154 us
+// against 133 for the two-pass split), so grouped calls keep the split.
+// One row group of 32 rows and 4 key
+// groups per workgroup, R = 64 KB of K rows: 256 keys at D = 128 (16-bit;
+// 128 for float32), 512 at D = 64, 1024 at D = 32, so that two workgroups
+// share a CU (one query row x 32768 keys, bf16, D = 128, 32 heads: 118 us,
+// against 134 with 512-key ranges of 8 waves, one workgroup per CU, and 156
+// for the two-pass split).
+// SDPA_MATH_RANGES=0 turns them off, =1 takes them wherever they fit (any
+// row count); SDPA_MATH_RANGE_KEYS=R and SDPA_MATH_RANGE_WAVES=KG override.
+bool range_config(const Shape& sh, bool causal, int64_t coff, int* waves, int* keys_per_wave, int* n_ranges) {
+    const int64_t keys = causal ? std::max<int64_t>(0, std::min(sh.Skv, sh.Sq + coff)) : sh.Skv;
+    const int dt = sh.dtype == SDPA_F32 ? sdpa::DT_F32 : sdpa::DT_F16;
+    const int64_t es = elt_size(sh.dtype);
+    int64_t R = (64 * 1024) / (sh.D * es);
+    int64_t kg = 4;
+    if (const char* e = std::getenv("SDPA_MATH_RANGE_KEYS")) R = std::atoll(e);
+    if (const char* e = std::getenv("SDPA_MATH_RANGE_WAVES")) kg = std::atoll(e);
+    if (kg < 1 || kg > sdpa::FUSED_MAX_WAVES || R < 32 * kg || R % (32 * kg)) return false;
+    const int64_t kpw = R / kg;
+    if (kpw > sdpa::fused_wide_max_keys(dt, (int)sh.D) ||
+        sdpa::fused_wide_lds_bytes_rt(dt, (int)sh.D, (int)kg, (int)R) > sdpa::FUSED_LDS_MAX)
+        return false;
+    // one (batch, head) slice of the float32 probabilities must stay under 1 GiB
+    if (sh.Sq * sh.Skv * 4 >= (int64_t(1) << 30) || keys <= 0) return false;
+    if (cdiv(keys, R) > sdpa::RANGE_MAX) return false;
+    *waves = (int)kg;
+    *keys_per_wave = (int)kpw;
+    *n_ranges = (int)cdiv(keys, R);
+    return true;
+}
 
 sdpa_status_t make_plan(const Shape& sh, bool causal, int64_t coff, int forced, bool vec, sdpa::Plan* p,
-                        bool allow_split = false) {
+                        bool allow_split = false, bool allow_ranges = true) {
     p->tiles_64 = count_tiles(sh.Sq, sh.Skv, causal, 64, coff);
     int fw = 0, fk = 0, frg = 0;
     int ww = 0, wk = 0, wrg = 0;
@@ -372,6 +425,7 @@ sdpa_status_t make_plan(const Shape& sh, bool causal, int64_t coff, int forced, 
     }
     int path = forced;
     if (path == SDPA_PATH_AUTO) path = env_path();
+    const bool auto_path = path == SDPA_PATH_AUTO;
     // An additive mask over more than 64 query rows goes to the two-pass path
     // (it stages the mask tiles in LDS; measured: fp16, 16 x 8 heads, Sq 100
     // and 128, Skv 512 / 1152 / 2048, D = 64: equal or up to 9 % faster; with
@@ -441,8 +495,26 @@ sdpa_status_t make_plan(const Shape& sh, bool causal, int64_t coff, int forced, 
         }
         p->q_rows = 32 * p->waves;
     }
+    // one-sweep key ranges on the wide kernel (range_config) in place of the
+    // two-pass split where they move fewer bytes
+    if (allow_split && allow_ranges && vec && auto_path) {
+        const char* re = std::getenv("SDPA_MATH_RANGES");
+        const bool force = re && *re == '1', off = re && *re == '0';
+        const bool fewer_bytes = sh.Hq == sh.Hkv && 32 * sh.Sq <= sh.D * elt_size(sh.dtype);
+        int rw = 0, rk = 0, rn = 0;
+        if (!off && (force || (p->path == SDPA_PATH_TWOPASS && p->n_splits > 1 && fewer_bytes)) &&
+            range_config(sh, causal, coff, &rw, &rk, &rn) && rn >= 2) {
+            p->path = SDPA_PATH_FUSED;
+            p->waves = rw;
+            p->keys_per_wave = rk;
+            p->fused_rg = 1;
+            p->q_rows = 32;
+            p->n_splits = rn;
+            p->split_tiles = 0;
+        }
+    }
     p->n_qblk = (int)cdiv(sh.Sq, p->q_rows);
-    p->grid = sh.B * sh.Hq * p->n_qblk;
+    p->grid = sh.B * sh.Hq * p->n_qblk * (p->path == SDPA_PATH_FUSED ? p->n_splits : 1);
     p->tiles_per_bh = count_tiles(sh.Sq, sh.Skv, causal, p->q_rows, coff);
     if (p->grid > INT32_MAX) return fail(SDPA_ERR_UNSUPPORTED, "grid too large");
     return SDPA_OK;
@@ -508,9 +580,19 @@ sdpa_status_t run(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_ten
     if ((st = make_plan(sh, is_causal != 0, causal_offset(sh, is_causal), path, vec, &plan,
                         ws_mode == WS_STATIC || ws != nullptr)))
         return st;
+    // the wide kernel's key ranges without room for their workspace: the
+    // two-pass split instead (whose workspace is checked below)
+    if (plan.path == SDPA_PATH_FUSED && plan.n_splits > 1) {
+        const size_t room = ws_mode == WS_STATIC                           ? sdpa::STATIC_SCRATCH_BYTES
+                            : reinterpret_cast<uintptr_t>(ws) % 256 != 0 ? 0
+                                                                          : ws_bytes;
+        if (plan_ws_bytes(sh, plan) > room &&
+            (st = make_plan(sh, is_causal != 0, causal_offset(sh, is_causal), path, vec, &plan, true, false)))
+            return st;
+    }
     if (ws_mode == WS_STATIC && plan.n_splits > 1) {
         // the static scratch: a plan that needs more is rejected, never shrunk
-        const size_t need = split_ws_bytes(sh, plan.n_splits);
+        const size_t need = plan_ws_bytes(sh, plan);
         if (need > sdpa::STATIC_SCRATCH_BYTES)
             return fail(SDPA_ERR_UNSUPPORTED,
                         "this call needs %zu bytes of key-range scratch; the static scratch holds %zu "
@@ -521,7 +603,7 @@ sdpa_status_t run(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_ten
             return fail(SDPA_ERR_HIP, "static scratch lookup failed: %s", hipGetErrorString(static_cast<hipError_t>(e)));
         ws_bytes = sdpa::STATIC_SCRATCH_BYTES;
     }
-    if (plan.n_splits > 1 && (reinterpret_cast<uintptr_t>(ws) % 256 != 0 || ws_bytes < split_ws_bytes(sh, plan.n_splits)))
+    if (plan.n_splits > 1 && (reinterpret_cast<uintptr_t>(ws) % 256 != 0 || ws_bytes < plan_ws_bytes(sh, plan)))
         if ((st = make_plan(sh, is_causal != 0, causal_offset(sh, is_causal), path, vec, &plan))) return st;  // no room: unsplit
     if (drop) {  // the dropout kernels: two compute waves and a loader wave
         plan.waves = 2;
@@ -569,6 +651,8 @@ sdpa_status_t run(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_ten
     if (plan.n_splits > 1) {
         a.ws_ml = static_cast<float2*>(ws);
         a.ws_o = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + (split_ws_ml_bytes(sh, plan.n_splits) + 255) / 256 * 256);
+        if (plan.path == SDPA_PATH_FUSED)
+            a.ws_e = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + plan_ws_e_offset(sh, plan.n_splits));
     }
     a.keys_per_wave = plan.keys_per_wave;
     a.fused_rg = plan.fused_rg;
@@ -916,8 +1000,9 @@ sdpa_status_t sdpa_math_plan(const sdpa_tensor_t* q, const sdpa_tensor_t* k, con
     sdpa_status_t st = validate_inputs(q, k, v, mask, is_causal, enable_gqa, &sh);
     if (st) return st;
     sdpa::Plan plan;
+    // as a call with its workspace (sdpa_math_fwd_ws) runs it
     if ((st = make_plan(sh, is_causal != 0, causal_offset(sh, is_causal), SDPA_PATH_AUTO,
-                        staged_layout(sh, mask, nullptr, nullptr), &plan)))
+                        staged_layout(sh, mask, nullptr, nullptr), &plan, true)))
         return st;
     if (path) *path = plan.path == SDPA_PATH_FUSED && plan.fused_rg > 0 ? SDPA_PATH_FUSED_WIDE : plan.path;
     if (tiles_per_bh) *tiles_per_bh = plan.tiles_per_bh;
@@ -971,7 +1056,7 @@ sdpa_status_t sdpa_math_workspace_bytes(const sdpa_tensor_t* q, const sdpa_tenso
     if ((st = make_plan(sh, is_causal != 0, causal_offset(sh, is_causal), SDPA_PATH_AUTO,
                         staged_layout(sh, mask, nullptr, nullptr), &plan, true)))
         return st;
-    *bytes = split_ws_bytes(sh, plan.n_splits);
+    *bytes = plan_ws_bytes(sh, plan);
     return SDPA_OK;
 }
 

@@ -192,12 +192,20 @@ def test_workspace_query(monkeypatch):
                      causal=1) == (0, 0)
     q, k = _z(16, 8, 100, 64), _z(16, 8, 1152, 64)
     assert _ws_bytes(q, k, torch.zeros(16, 8, 100, 1152, dtype=torch.float16)) == (0, 0)
-    # one query row against 32768 keys, 32 heads: 16 ranges of 32 tiles (towards 512 workgroups)
+    # one query row against 32768 keys, 32 heads: one-sweep ranges of 256 keys
+    # on the wide kernel (128 ranges): per range and row (max, sum) and a float32
+    # partial O, then every probability as float32
     q, k = _z(4, 8, 1, 128, dtype=torch.bfloat16), _z(4, 8, 32768, 128, dtype=torch.bfloat16)
     rc, n = _ws_bytes(q, k)
     rows = 4 * 8 * 1
-    ml = -(-(16 * rows * 8) // 256) * 256
-    assert rc == 0 and n == ml + 16 * rows * 128 * 4
+    up = lambda x: -(-x // 256) * 256  # noqa: E731
+    ml = up(128 * rows * 8)
+    assert rc == 0 and n == up(ml + 128 * rows * 128 * 4) + rows * 32768 * 4
+    # without them: the two-pass split, 16 ranges of 32 tiles (towards 512 workgroups)
+    monkeypatch.setenv("SDPA_MATH_RANGES", "0")
+    rc, n = _ws_bytes(q, k)
+    assert rc == 0 and n == up(16 * rows * 8) + 16 * rows * 128 * 4
+    monkeypatch.delenv("SDPA_MATH_RANGES")
     # forced ranges; a semantic error leaves the count at 0
     monkeypatch.setenv("SDPA_MATH_SPLITS", "3")
     assert _ws_bytes(_z(1, 2, 256, 64), _z(1, 2, 640, 64))[1] > 0  # two-pass shape (the fused path never splits)

@@ -8,6 +8,7 @@ removed position, LSE = -inf exactly on dead rows).
 
 import math
 import os
+import re
 
 import numpy as np
 import pytest
@@ -212,6 +213,80 @@ def test_key_ranges(label, spec, align, splits, monkeypatch):
     if align:
         c["align"] = align
     _check(c, "twopass", label=f"{label} splits={splits}")
+
+
+# Key ranges in one sweep on the wide fused kernel (forced with small ranges so
+# that small calls span several, the last one ragged): each range's float32
+# probabilities relative to its own row maximum, its (max, sum) and its float32
+# partial O, folded into P, O and LSE by the combine launch. The same shapes
+# as the two-pass ranges, plus rows that every key of a range (or of the whole
+# row) removes.
+RANGE_CASES = SPLIT_CASES + [
+    ("f16-d64-neginf-heads", dict(seed=110, dtype="f16", B=1, Hq=4, Hkv=4, Sq=33, Skv=1152, D=64, mask="neginf",
+                                  mask_shape=(1, 4, 33, 1152)), None),
+    ("bf16-d128-bool-dead", dict(seed=179, dtype="bf16", B=2, Hq=2, Hkv=1, Sq=40, Skv=528, D=128, mask="bool",
+                                 mask_shape=(2, 1, 40, 528), p=0.3), None),
+]
+
+
+def _dead_ranges(c):
+    # batch 0 keeps no key past 200 (whole ranges removed), batch 1 rows 3..6
+    # keep no key at all (dead rows: P = O = 0, LSE = -inf)
+    m = c["mask"].clone()
+    m[0, :, :, 200:] = False
+    m[1, :, 3:7, :] = False
+    c["mask"] = m
+    return c
+
+
+def _ran_ranges(capfd):
+    # the launch itself (SDPA_MATH_DEBUG): the fused path over more than one key range
+    err = capfd.readouterr().err
+    m = re.search(r"path=fused .*splits=(\d+)", err)
+    assert m and int(m.group(1)) > 1, err
+
+
+@pytest.mark.parametrize("keys,waves", [(64, 2), (256, 8)])
+@pytest.mark.parametrize("label,spec,align", RANGE_CASES, ids=[s[0] for s in RANGE_CASES])
+def test_one_sweep_key_ranges(label, spec, align, keys, waves, monkeypatch, capfd):
+    monkeypatch.setenv("SDPA_MATH_DEBUG", "1")
+    monkeypatch.setenv("SDPA_MATH_RANGES", "1")
+    monkeypatch.setenv("SDPA_MATH_RANGE_KEYS", str(keys))
+    monkeypatch.setenv("SDPA_MATH_RANGE_WAVES", str(waves))
+    c = W.make_case(**spec)
+    if label.endswith("-dead"):
+        c = _dead_ranges(c)
+    if align:
+        c["align"] = align
+    Sq, Skv = spec["Sq"], spec["Skv"]
+    last = Skv if not spec.get("causal") else min(Skv, Sq + (Skv - Sq if align == "bottom_right" else 0))
+    if last <= keys:
+        pytest.skip(f"the last row keeps {last} keys: one range of {keys}")
+    S = _lib()
+    gqa = c["q"].shape[1] != c["k"].shape[1]
+    assert S.kernel_name(c["q"], c["k"], c["v"], c["mask"], c["causal"], gqa,
+                         causal_alignment=c.get("align", "top_left")) == "sdpa_fused_wide_kernel"
+    _check(c, "auto", label=f"{label} one-sweep ranges of {keys} keys")
+    _ran_ranges(capfd)
+
+
+@pytest.mark.parametrize("spec", [
+    dict(seed=180, dtype="bf16", B=1, Hq=4, Hkv=4, Sq=1, Skv=8192, D=128),
+    dict(seed=181, dtype="f16", B=2, Hq=4, Hkv=4, Sq=2, Skv=4096, D=128, mask="add", p=0.1),
+    dict(seed=182, dtype="f32", B=1, Hq=2, Hkv=2, Sq=3, Skv=3000, D=64),
+], ids=["bf16-decode", "f16-add", "f32-d64"])
+def test_one_sweep_ranges_chosen_by_default(spec, monkeypatch, capfd):
+    # decode rows against long keys: the default plan runs the keys as one-sweep
+    # ranges on the wide kernel
+    for e in ("SDPA_MATH_RANGES", "SDPA_MATH_RANGE_KEYS", "SDPA_MATH_RANGE_WAVES", "SDPA_MATH_SPLITS"):
+        monkeypatch.delenv(e, raising=False)
+    monkeypatch.setenv("SDPA_MATH_DEBUG", "1")
+    c = W.make_case(**spec)
+    S = _lib()
+    gqa = c["q"].shape[1] != c["k"].shape[1]
+    assert S.kernel_name(c["q"], c["k"], c["v"], c["mask"], c["causal"], gqa) == "sdpa_fused_wide_kernel"
+    _check(c, "auto", label="default one-sweep ranges")
+    _ran_ranges(capfd)
 
 
 def test_key_ranges_chosen_by_default(monkeypatch):
