@@ -340,10 +340,12 @@ void sdpa_fused_kernel(const FwdArgs a) {
 // are made.
 
 // Bytes of dynamic LDS of the wide kernel: the staged V rows (or, after
-// them, the partial O^T of every wave), then the row max and sum of every wave.
+// them, the partial O^T of every wave; with `oseq`, one O^T accumulation
+// buffer per row group; none with one key group per row group, whose waves
+// store their outputs directly), then the row max and sum of every wave.
 template <typename T, int D>
-constexpr int fused_wide_lds_bytes(int nw, int vrows) {
-    const int v = vrows * D * (int)sizeof(T), o = nw * 32 * (D + 4) * 4;
+constexpr int fused_wide_lds_bytes(int nw, int rg, int vrows, bool oseq) {
+    const int v = vrows * D * (int)sizeof(T), o = nw == rg ? 0 : (oseq ? rg : nw) * 32 * (D + 4) * 4;
     return (v > o ? v : o) + 2 * nw * 32 * 4;
 }
 
@@ -387,7 +389,8 @@ __global__ __launch_bounds__(FUSED_MAX_WAVES * 64) void sdpa_fused_wide_kernel(c
     const int rg = wave / KG, kg = wave - (wave / KG) * KG;
     const int kpw = a.keys_per_wave;
     const int vrows = KG * kpw;  // staged V rows: keys 0 .. vrows-1 (zeros past Skv)
-    const int vbytes = vrows * ROWB > nw * 32 * OPITCH * 4 ? vrows * ROWB : nw * 32 * OPITCH * 4;
+    const int obytes = KG == 1 ? 0 : (a.fused_oseq ? RG : nw) * 32 * OPITCH * 4;
+    const int vbytes = vrows * ROWB > obytes ? vrows * ROWB : obytes;
     float* red_m = reinterpret_cast<float*>(smem + vbytes);
     float* red_l = red_m + nw * 32;
 
@@ -401,15 +404,21 @@ __global__ __launch_bounds__(FUSED_MAX_WAVES * 64) void sdpa_fused_wide_kernel(c
     }
     int range = 0, koff = 0;
     if constexpr (RANGE) {
-        // workgroup order: the query heads of a KV group fastest, then the
-        // ranges, so that a group's heads read each range's K and V rows
-        // through L2 at about the same time; L becomes (batch, head, row block)
-        const int g = L % a_in.group;
-        L /= a_in.group;
-        range = L % a_in.n_splits;
-        L /= a_in.n_splits;
-        const int rb0 = L % a_in.n_qblk, bk = L / a_in.n_qblk;  // bk = batch * Hkv + KV head
-        L = ((bk / a_in.Hkv) * a_in.Hq + (bk % a_in.Hkv) * a_in.group + g) * a_in.n_qblk + rb0;
+        if (a_in.fused_hg) {
+            // the group's heads are this workgroup's row groups
+            range = L % a_in.n_splits;
+            L /= a_in.n_splits;
+        } else {
+            // workgroup order: the query heads of a KV group fastest, then the
+            // ranges, so that a group's heads read each range's K and V rows
+            // through L2 at about the same time; L becomes (batch, head, row block)
+            const int g = L % a_in.group;
+            L /= a_in.group;
+            range = L % a_in.n_splits;
+            L /= a_in.n_splits;
+            const int rb0 = L % a_in.n_qblk, bk = L / a_in.n_qblk;  // bk = batch * Hkv + KV head
+            L = ((bk / a_in.Hkv) * a_in.Hq + (bk % a_in.Hkv) * a_in.group + g) * a_in.n_qblk + rb0;
+        }
         // the range's keys as a call of its own: K, V and mask columns from
         // koff on (the descriptors shrink by as much), Skv the range's keys,
         // the causal offset moved with them
@@ -427,16 +436,31 @@ __global__ __launch_bounds__(FUSED_MAX_WAVES * 64) void sdpa_fused_wide_kernel(c
             ra.m_ext = a_in.m_ext - (uint32_t)madv;
         }
     }
-    const int bh = L / a.n_qblk;
-    const int rb = L - bh * a.n_qblk;
-    const int b = bh / a.Hq, hq = bh - (bh / a.Hq) * a.Hq;
+    // (batch, query head of this wave, row block). Head row groups
+    // (a.fused_hg): the RG row groups are RG query heads of one KV group, all
+    // on the same 32 rows, so the group's K and V rows are staged once; else
+    // they are consecutive 32-row groups of one head.
+    const bool hgr = a.fused_hg != 0;
+    const int rb = L % a.n_qblk;
+    int b, hq;
+    if (hgr) {
+        const int nset = a.group / RG;  // head sets per KV group
+        const int hs = L / a.n_qblk;    // (batch * Hkv + KV head) * nset + set
+        const int bk = hs / nset;
+        b = bk / a.Hkv;
+        hq = (bk - b * a.Hkv) * a.group + (hs - bk * nset) * RG + rg;
+    } else {
+        const int bh = L / a.n_qblk;
+        b = bh / a.Hq;
+        hq = bh - b * a.Hq;
+    }
     const int hk = hq / a.group;
-    const int q0 = (rb * RG + rg) * 32;
+    const int q0 = hgr ? rb * 32 : (rb * RG + rg) * 32;
     const int qi = q0 + n;
     const bool row_ok = qi < a.Sq;
     // keys the rows of this row group (and of the whole workgroup) may keep
     const int kend = a.causal ? min(a.Skv, max(0, q0 + 32 + a.coff)) : a.Skv;
-    const int kend_wg = a.causal ? min(a.Skv, max(0, (rb + 1) * RG * 32 + a.coff)) : a.Skv;
+    const int kend_wg = a.causal ? min(a.Skv, max(0, (hgr ? rb + 1 : (rb + 1) * RG) * 32 + a.coff)) : a.Skv;
     const int kbase = kg * kpw;
     const int nb = max(0, min((kend - kbase + 31) / 32, kpw / 32));
 
@@ -450,9 +474,15 @@ __global__ __launch_bounds__(FUSED_MAX_WAVES * 64) void sdpa_fused_wide_kernel(c
     const rsrc_t pr = RANGE ? make_rsrc(a_in.ws_e + wsrow0 * a_in.Skv + koff,
                                         (uint32_t)(((int64_t)a.Sq * a_in.Skv - koff) * 4))
                             : make_rsrc(static_cast<T*>(a.p) + b * a.p_s[0] + hq * a.p_s[1], a.p_ext);
-    const rsrc_t orr = RANGE ? make_rsrc(a_in.ws_o + ((int64_t)range * a.B * a.Hq * a.Sq + wsrow0) * D,
-                                         (uint32_t)((int64_t)a.Sq * D * 4))
-                             : make_rsrc(static_cast<T*>(a.o) + b * a.o_s[0] + hq * a.o_s[1], a.o_ext);
+    // output rows of query head h of this workgroup's batch
+    auto o_rsrc = [&](int h) -> rsrc_t {
+        if constexpr (RANGE)
+            return make_rsrc(a_in.ws_o + ((int64_t)range * a.B * a.Hq * a.Sq + (int64_t)(b * a.Hq + h) * a.Sq) * D,
+                             (uint32_t)((int64_t)a.Sq * D * 4));
+        else
+            return make_rsrc(static_cast<T*>(a.o) + b * a.o_s[0] + h * a.o_s[1], a.o_ext);
+    };
+    const rsrc_t orr = o_rsrc(hq);
     const rsrc_t lr = make_rsrc(a.lse + b * a.l_s[0] + hq * a.l_s[1], a.l_ext);
     rsrc_t mr = kr;
     if constexpr (MASK != MASK_NONE)
@@ -462,9 +492,9 @@ __global__ __launch_bounds__(FUSED_MAX_WAVES * 64) void sdpa_fused_wide_kernel(c
     const uint32_t prow = RANGE ? pred(row_ok, (uint32_t)((int64_t)(row_ok ? qi : 0) * a_in.Skv * 4))
                                 : pred(row_ok, (uint32_t)((int64_t)(row_ok ? qi : 0) * a.p_s[2] * SZ));
     // one run of 8 output columns of a row: the dtype, or float32 partials (RANGE)
-    auto store_o8 = [&](uint32_t row_off, bool ok, int col, const float* x) __attribute__((always_inline)) {
-        if constexpr (RANGE) store8<float, true>(orr, row_off, ok, col, D, x);
-        else store8<T, VEC>(orr, row_off, ok, col, D, x);
+    auto store_o8 = [&](rsrc_t r, uint32_t row_off, bool ok, int col, const float* x) __attribute__((always_inline)) {
+        if constexpr (RANGE) store8<float, true>(r, row_off, ok, col, D, x);
+        else store8<T, VEC>(r, row_off, ok, col, D, x);
     };
     const int64_t o_pitch = RANGE ? D : a.o_s[2];  // output row pitch, elements
     constexpr int OSZ = RANGE ? 4 : SZ;
@@ -741,32 +771,58 @@ __global__ __launch_bounds__(FUSED_MAX_WAVES * 64) void sdpa_fused_wide_kernel(c
             float x[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) x[r] = oacc[d][r];
-            store_o8(orow, row_ok, 32 * d + 8 * hf, x);
-            store_o8(orow, row_ok, 32 * d + 16 + 8 * hf, x + 8);
+            store_o8(orr, orow, row_ok, 32 * d + 8 * hf, x);
+            store_o8(orr, orow, row_ok, 32 * d + 16 + 8 * hf, x + 8);
         }
         return;
     }
     __syncthreads();  // every wave is done reading the staged V rows
-    float* opart = reinterpret_cast<float*>(smem) + wave * 32 * OPITCH;
+    // The KG partial O^T of each row group summed in key-group order: every
+    // wave's partial in LDS, then summed by the reading threads; or, with
+    // a.fused_oseq (less LDS: one buffer per row group), accumulated in turn
+    // (key group 0 writes, the others add) -- the same sums either way.
+    const bool oseq = a.fused_oseq != 0;
+    if (oseq) {
+        float* obuf = reinterpret_cast<float*>(smem) + rg * 32 * OPITCH;
+        for (int k2 = 0; k2 < KG; ++k2) {
+            if (kg == k2) {
 #pragma unroll
-    for (int d = 0; d < ND; ++d)
+                for (int d = 0; d < ND; ++d)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) opart[n * OPITCH + 32 * d + kk(hf, r)] = oacc[d][r];
-    __syncthreads();
+                    for (int r = 0; r < 16; ++r) {
+                        float* o = obuf + n * OPITCH + 32 * d + kk(hf, r);
+                        *o = (k2 == 0 ? 0.0f : *o) + oacc[d][r];
+                    }
+            }
+            __syncthreads();
+        }
+    } else {
+        float* opart = reinterpret_cast<float*>(smem) + wave * 32 * OPITCH;
+#pragma unroll
+        for (int d = 0; d < ND; ++d)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) opart[n * OPITCH + 32 * d + kk(hf, r)] = oacc[d][r];
+        __syncthreads();
+    }
     const float* obase = reinterpret_cast<const float*>(smem);
     for (int i = threadIdx.x; i < RG * 32 * (D / 8); i += nw * 64) {
         const int rr = i / (D / 8), c8 = i - (i / (D / 8)) * (D / 8);
         const int g = rr >> 5, row = rr & 31;
         float x[8];
+        if (oseq) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = 0.0f;
-        for (int ww = 0; ww < KG; ++ww) {
+            for (int e = 0; e < 8; ++e) x[e] = obase[(g * 32 + row) * OPITCH + 8 * c8 + e];
+        } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] += obase[((g * KG + ww) * 32 + row) * OPITCH + 8 * c8 + e];
+            for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+            for (int ww = 0; ww < KG; ++ww) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] += obase[((g * KG + ww) * 32 + row) * OPITCH + 8 * c8 + e];
+            }
         }
-        const int orow_i = (rb * RG + g) * 32 + row;
+        const int orow_i = hgr ? rb * 32 + row : (rb * RG + g) * 32 + row;
         const bool ok = orow_i < a.Sq;
-        store_o8((uint32_t)((int64_t)(ok ? orow_i : 0) * o_pitch * OSZ), ok, 8 * c8, x);
+        store_o8(hgr ? o_rsrc(hq - rg + g) : orr, (uint32_t)((int64_t)(ok ? orow_i : 0) * o_pitch * OSZ), ok, 8 * c8, x);
     }
 }
 
@@ -883,7 +939,8 @@ int launch_fused_t(int mask_kind, int waves, const FwdArgs& a, hipStream_t s) {
     const bool wide = a.fused_rg > 0;
     const bool ranges = wide && a.n_splits > 1;  // key ranges of the wide kernel, then the combine
     if (ranges && !VEC) return (int)hipErrorInvalidValue;
-    const size_t lds = wide ? (size_t)fused_wide_lds_bytes<T, D>(waves, waves / a.fused_rg * a.keys_per_wave)
+    const size_t lds = wide ? (size_t)fused_wide_lds_bytes<T, D>(waves, a.fused_rg, waves / a.fused_rg * a.keys_per_wave,
+                                                                  a.fused_oseq != 0)
                             : (size_t)fused_lds_bytes<T, D>(waves);
 #define SDPA_FUSED_LAUNCH(MK)                                                                               \
     {                                                                                                       \
@@ -932,7 +989,9 @@ int launch_fused(int dtype, int D, int mask_kind, int waves, bool vec, const Fwd
     if (a.fused_rg > 0) {
         // wide variant: RG row groups x KG key groups, every staged V row in LDS
         if (waves % a.fused_rg != 0 || a.keys_per_wave > fused_wide_max_keys(dtype, D) ||
-            fused_wide_lds_bytes_rt(dtype, D, waves, waves / a.fused_rg * a.keys_per_wave) > FUSED_LDS_MAX)
+            fused_wide_lds_bytes_rt(dtype, D, waves, a.fused_rg, waves / a.fused_rg * a.keys_per_wave, a.fused_oseq != 0) >
+                FUSED_LDS_MAX ||
+            (a.fused_hg && (a.group % a.fused_rg != 0)))
             return (int)hipErrorInvalidValue;
     } else {
         const int maxk = D == 128 ? FUSED_MAX_KEYS_PER_WAVE_D128 : FUSED_MAX_KEYS_PER_WAVE;

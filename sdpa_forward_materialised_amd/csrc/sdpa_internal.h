@@ -36,6 +36,10 @@ struct FwdArgs {
     int keys_per_wave;  // fused path: key range of one wave
     int fused_rg;       // fused path: 0 one row group per workgroup; else the
                         // wide variant with this many 32-row groups
+    int fused_hg;       // wide variant: its row groups are fused_rg query heads
+                        // of one KV group on the same 32 rows (K, V staged once)
+    int fused_oseq;     // wide variant: partial outputs accumulated in turn in
+                        // one LDS buffer per row group (less LDS)
     int sched;       // workgroup order (causal: 1, 2, 3), see decode_block
     // Key ranges (split over workgroups): n_splits ranges of split_tiles
     // tiles (an even count) per query block; the two-pass kernels then run as
@@ -105,6 +109,8 @@ struct Plan {
     int64_t grid;
     int keys_per_wave;  // fused only
     int fused_rg = 0;   // fused only: row groups of the wide variant (0: the one-group kernel)
+    int fused_hg = 0;   // wide variant: row groups are query heads of one KV group
+    int fused_oseq = 0; // wide variant: partial outputs accumulated in turn (less LDS)
     int64_t tiles_per_bh;
     int64_t tiles_64;
     int n_splits = 1;     // key ranges per query block (with a workspace)
@@ -148,10 +154,11 @@ constexpr int FUSED_MAX_WAVES = 8;
 // Keys per wave: D = 32, 64: 320; D = 128: 160 (float32: 128).
 constexpr int fused_wide_max_keys(int dtype, int D) { return D == 128 ? (dtype == DT_F32 ? 128 : 160) : 320; }
 constexpr int FUSED_LDS_MAX = 160 * 1024;
-// Bytes of dynamic LDS of the wide variant for `nw` waves staging `vrows` V rows.
-inline int fused_wide_lds_bytes_rt(int dtype, int D, int nw, int vrows) {
+// Bytes of dynamic LDS of the wide variant for `nw` waves in `rg` row groups
+// staging `vrows` V rows (`oseq`: partial outputs accumulated in turn).
+inline int fused_wide_lds_bytes_rt(int dtype, int D, int nw, int rg, int vrows, bool oseq) {
     const int esz = dtype == DT_F32 ? 4 : 2;
-    const int v = vrows * D * esz, o = nw * 32 * (D + 4) * 4;
+    const int v = vrows * D * esz, o = nw == rg ? 0 : (oseq ? rg : nw) * 32 * (D + 4) * 4;
     return (v > o ? v : o) + 2 * nw * 32 * 4;
 }
 constexpr int TILE_N = 64;  // keys per score tile

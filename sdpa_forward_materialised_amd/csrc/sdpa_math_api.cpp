@@ -284,12 +284,12 @@ bool fused_wide_config(const Shape& sh, bool causal, int64_t coff, int* waves, i
         for (int kg = 1; rg * kg <= sdpa::FUSED_MAX_WAVES; kg *= 2) {
             const int64_t kpw = cdiv(cdiv(keys, kg), 32) * 32;
             if (kpw > limit) continue;
-            if (sdpa::fused_wide_lds_bytes_rt(dt, (int)sh.D, rg * kg, (int)(kg * kpw)) > sdpa::FUSED_LDS_MAX) continue;
+            if (sdpa::fused_wide_lds_bytes_rt(dt, (int)sh.D, rg * kg, rg, (int)(kg * kpw), false) > sdpa::FUSED_LDS_MAX) continue;
             int k2 = kg;
             int64_t kp2 = kpw;
             while (kp2 > 128 && rg * k2 * 2 <= sdpa::FUSED_MAX_WAVES) {
                 const int64_t nk = cdiv(cdiv(keys, 2 * k2), 32) * 32;
-                if (sdpa::fused_wide_lds_bytes_rt(dt, (int)sh.D, rg * 2 * k2, (int)(2 * k2 * nk)) > sdpa::FUSED_LDS_MAX)
+                if (sdpa::fused_wide_lds_bytes_rt(dt, (int)sh.D, rg * 2 * k2, rg, (int)(2 * k2 * nk), false) > sdpa::FUSED_LDS_MAX)
                     break;
                 k2 *= 2;
                 kp2 = nk;
@@ -378,36 +378,49 @@ size_t plan_ws_bytes(const Shape& sh, const sdpa::Plan& p) {
 // ranges win where those 8 bytes times the query rows stay within a quarter
 // of the K row (one or four query rows: 20-30 % faster) and lose at half of
 // it (8 and 16 rows: 5-8 % slower): taken where 32 * Sq <= D * element size.
-// With grouped heads each query head's workgroups stage the group's K and V
-// rows again (four heads per KV head, one query row x 32768 keys: 154 us
-// against 133 for the two-pass split), so grouped calls keep the split.
-// One row group of 32 rows and 4 key
-// groups per workgroup, R = 64 KB of K rows: 256 keys at D = 128 (16-bit;
-// 128 for float32), 512 at D = 64, 1024 at D = 32, so that two workgroups
-// share a CU (one query row x 32768 keys, bf16, D = 128, 32 heads: 118 us,
-// against 134 with 512-key ranges of 8 waves, one workgroup per CU, and 156
-// for the two-pass split).
+// Ungrouped heads: one row group of 32 rows and 4 key groups per workgroup,
+// R = 64 KB of K rows: 256 keys at D = 128 (16-bit; 128 for float32), 512 at
+// D = 64, 1024 at D = 32, so that two workgroups share a CU (one query row x
+// 32768 keys, bf16, D = 128, 32 heads: 118 us, against 134 with 512-key
+// ranges of 8 waves, one workgroup per CU, and 156 for the two-pass split).
+// Grouped heads: the group's query heads (up to 8) are the row groups of one
+// workgroup, which stages each range's K and V rows once for all of them, one
+// wave per head over the range's keys (R = the most one wave holds: 160 at
+// D = 128, 320 at D = 64): one query row x 32768 keys, bf16, D = 128, 2 x 32
+// heads on 8 KV heads 92 us against 124 with two key groups of 128 keys and
+// 133 for the two-pass split; 4 x 16 on 8: 139 against 199; 64 on 8: 96
+// against 133.
 // SDPA_MATH_RANGES=0 turns them off, =1 takes them wherever they fit (any
 // row count); SDPA_MATH_RANGE_KEYS=R and SDPA_MATH_RANGE_WAVES=KG override.
-bool range_config(const Shape& sh, bool causal, int64_t coff, int* waves, int* keys_per_wave, int* n_ranges) {
+bool range_config(const Shape& sh, bool causal, int64_t coff, int* waves, int* keys_per_wave, int* n_ranges,
+                  int* rg_out) {
     const int64_t keys = causal ? std::max<int64_t>(0, std::min(sh.Skv, sh.Sq + coff)) : sh.Skv;
     const int dt = sh.dtype == SDPA_F32 ? sdpa::DT_F32 : sdpa::DT_F16;
     const int64_t es = elt_size(sh.dtype);
-    int64_t R = (64 * 1024) / (sh.D * es);
-    int64_t kg = 4;
-    if (const char* e = std::getenv("SDPA_MATH_RANGE_KEYS")) R = std::atoll(e);
+    const int64_t group = sh.Hq / sh.Hkv;
+    // grouped heads: the group's heads (up to 8) are the row groups
+    const int64_t rg = group <= sdpa::FUSED_MAX_WAVES ? group : group % sdpa::FUSED_MAX_WAVES == 0 ? sdpa::FUSED_MAX_WAVES : 0;
+    if (rg == 0) return false;
+    int64_t kg = rg > 1 ? 1 : 4;
     if (const char* e = std::getenv("SDPA_MATH_RANGE_WAVES")) kg = std::atoll(e);
-    if (kg < 1 || kg > sdpa::FUSED_MAX_WAVES || R < 32 * kg || R % (32 * kg)) return false;
+    if (kg < 1 || rg * kg > sdpa::FUSED_MAX_WAVES) return false;
+    const int64_t max_kpw = sdpa::fused_wide_max_keys(dt, (int)sh.D);
+    int64_t R = rg > 1 ? max_kpw : std::min<int64_t>((64 * 1024) / (sh.D * es), kg * max_kpw) / (32 * kg) * (32 * kg);
+    if (const char* e = std::getenv("SDPA_MATH_RANGE_KEYS")) R = std::atoll(e);
+    if (R < 32 * kg || R % (32 * kg)) return false;
     const int64_t kpw = R / kg;
-    if (kpw > sdpa::fused_wide_max_keys(dt, (int)sh.D) ||
-        sdpa::fused_wide_lds_bytes_rt(dt, (int)sh.D, (int)kg, (int)R) > sdpa::FUSED_LDS_MAX)
+    // head row groups accumulate their partial outputs in turn (one LDS buffer
+    // per row group), which keeps two workgroups per CU
+    if (kpw > max_kpw ||
+        sdpa::fused_wide_lds_bytes_rt(dt, (int)sh.D, (int)(rg * kg), (int)rg, (int)R, rg > 1) > sdpa::FUSED_LDS_MAX)
         return false;
     // one (batch, head) slice of the float32 probabilities must stay under 1 GiB
     if (sh.Sq * sh.Skv * 4 >= (int64_t(1) << 30) || keys <= 0) return false;
     if (cdiv(keys, R) > sdpa::RANGE_MAX) return false;
-    *waves = (int)kg;
+    *waves = (int)(rg * kg);
     *keys_per_wave = (int)kpw;
     *n_ranges = (int)cdiv(keys, R);
+    *rg_out = (int)rg;
     return true;
 }
 
@@ -500,21 +513,24 @@ sdpa_status_t make_plan(const Shape& sh, bool causal, int64_t coff, int forced, 
     if (allow_split && allow_ranges && vec && auto_path) {
         const char* re = std::getenv("SDPA_MATH_RANGES");
         const bool force = re && *re == '1', off = re && *re == '0';
-        const bool fewer_bytes = sh.Hq == sh.Hkv && 32 * sh.Sq <= sh.D * elt_size(sh.dtype);
-        int rw = 0, rk = 0, rn = 0;
+        const bool fewer_bytes = 32 * sh.Sq <= sh.D * elt_size(sh.dtype);
+        int rw = 0, rk = 0, rn = 0, rrg = 0;
         if (!off && (force || (p->path == SDPA_PATH_TWOPASS && p->n_splits > 1 && fewer_bytes)) &&
-            range_config(sh, causal, coff, &rw, &rk, &rn) && rn >= 2) {
+            range_config(sh, causal, coff, &rw, &rk, &rn, &rrg) && rn >= 2) {
             p->path = SDPA_PATH_FUSED;
             p->waves = rw;
             p->keys_per_wave = rk;
-            p->fused_rg = 1;
+            p->fused_rg = rrg;
+            p->fused_hg = sh.Hq != sh.Hkv;
+            p->fused_oseq = rrg > 1;
             p->q_rows = 32;
             p->n_splits = rn;
             p->split_tiles = 0;
         }
     }
     p->n_qblk = (int)cdiv(sh.Sq, p->q_rows);
-    p->grid = sh.B * sh.Hq * p->n_qblk * (p->path == SDPA_PATH_FUSED ? p->n_splits : 1);
+    // (head row groups: one workgroup per fused_rg query heads)
+    p->grid = sh.B * sh.Hq / (p->fused_hg ? p->fused_rg : 1) * p->n_qblk * (p->path == SDPA_PATH_FUSED ? p->n_splits : 1);
     p->tiles_per_bh = count_tiles(sh.Sq, sh.Skv, causal, p->q_rows, coff);
     if (p->grid > INT32_MAX) return fail(SDPA_ERR_UNSUPPORTED, "grid too large");
     return SDPA_OK;
@@ -656,6 +672,8 @@ sdpa_status_t run(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_ten
     }
     a.keys_per_wave = plan.keys_per_wave;
     a.fused_rg = plan.fused_rg;
+    a.fused_hg = plan.fused_hg;
+    a.fused_oseq = plan.fused_oseq;
     if (drop) {
         a.keep = static_cast<const uint8_t*>(drop->keep->data);
         for (int dd = 0; dd < 4; ++dd) a.kp_s[dd] = eff_stride(drop->keep, dd);

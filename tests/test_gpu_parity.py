@@ -251,8 +251,10 @@ def _ran_ranges(capfd):
 def test_one_sweep_key_ranges(label, spec, align, keys, waves, monkeypatch, capfd):
     monkeypatch.setenv("SDPA_MATH_DEBUG", "1")
     monkeypatch.setenv("SDPA_MATH_RANGES", "1")
+    # grouped heads are the workgroup's row groups: `waves` split into them
+    group = spec["Hq"] // spec["Hkv"]
     monkeypatch.setenv("SDPA_MATH_RANGE_KEYS", str(keys))
-    monkeypatch.setenv("SDPA_MATH_RANGE_WAVES", str(waves))
+    monkeypatch.setenv("SDPA_MATH_RANGE_WAVES", str(max(1, waves // group)))
     c = W.make_case(**spec)
     if label.endswith("-dead"):
         c = _dead_ranges(c)
@@ -274,17 +276,23 @@ def test_one_sweep_key_ranges(label, spec, align, keys, waves, monkeypatch, capf
     dict(seed=180, dtype="bf16", B=1, Hq=4, Hkv=4, Sq=1, Skv=8192, D=128),
     dict(seed=181, dtype="f16", B=2, Hq=4, Hkv=4, Sq=2, Skv=4096, D=128, mask="add", p=0.1),
     dict(seed=182, dtype="f32", B=1, Hq=2, Hkv=2, Sq=3, Skv=3000, D=64),
-], ids=["bf16-decode", "f16-add", "f32-d64"])
+    dict(seed=183, dtype="f16", B=2, Hq=8, Hkv=2, Sq=2, Skv=4096, D=128, mask="add", p=0.1),
+    dict(seed=184, dtype="bf16", B=1, Hq=16, Hkv=2, Sq=3, Skv=4000, D=64, causal=True, align="bottom_right"),
+], ids=["bf16-decode", "f16-add", "f32-d64", "f16-gqa4-add", "bf16-gqa8-causal-br"])
 def test_one_sweep_ranges_chosen_by_default(spec, monkeypatch, capfd):
     # decode rows against long keys: the default plan runs the keys as one-sweep
-    # ranges on the wide kernel
+    # ranges on the wide kernel (grouped heads: the group's heads in one workgroup)
     for e in ("SDPA_MATH_RANGES", "SDPA_MATH_RANGE_KEYS", "SDPA_MATH_RANGE_WAVES", "SDPA_MATH_SPLITS"):
         monkeypatch.delenv(e, raising=False)
     monkeypatch.setenv("SDPA_MATH_DEBUG", "1")
+    spec = dict(spec)
+    align = spec.pop("align", "top_left")
     c = W.make_case(**spec)
+    c["align"] = align
     S = _lib()
     gqa = c["q"].shape[1] != c["k"].shape[1]
-    assert S.kernel_name(c["q"], c["k"], c["v"], c["mask"], c["causal"], gqa) == "sdpa_fused_wide_kernel"
+    assert S.kernel_name(c["q"], c["k"], c["v"], c["mask"], c["causal"], gqa,
+                         causal_alignment=align) == "sdpa_fused_wide_kernel"
     _check(c, "auto", label="default one-sweep ranges")
     _ran_ranges(capfd)
 
