@@ -278,7 +278,9 @@ def test_one_sweep_key_ranges(label, spec, align, keys, waves, monkeypatch, capf
     dict(seed=182, dtype="f32", B=1, Hq=2, Hkv=2, Sq=3, Skv=3000, D=64),
     dict(seed=183, dtype="f16", B=2, Hq=8, Hkv=2, Sq=2, Skv=4096, D=128, mask="add", p=0.1),
     dict(seed=184, dtype="bf16", B=1, Hq=16, Hkv=2, Sq=3, Skv=4000, D=64, causal=True, align="bottom_right"),
-], ids=["bf16-decode", "f16-add", "f32-d64", "f16-gqa4-add", "bf16-gqa8-causal-br"])
+    # batched decode: enough (batch, head) pairs to fill the chip unsplit
+    dict(seed=185, dtype="bf16", B=64, Hq=8, Hkv=2, Sq=1, Skv=1024, D=128),
+], ids=["bf16-decode", "f16-add", "f32-d64", "f16-gqa4-add", "bf16-gqa8-causal-br", "bf16-batched-gqa"])
 def test_one_sweep_ranges_chosen_by_default(spec, monkeypatch, capfd):
     # decode rows against long keys: the default plan runs the keys as one-sweep
     # ranges on the wide kernel (grouped heads: the group's heads in one workgroup)
