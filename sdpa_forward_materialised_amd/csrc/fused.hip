@@ -16,6 +16,10 @@
 // partials are summed through LDS. Every global load (Q, K, mask, V) is
 // issued before the first store, so no wait ever covers a store.
 
+#include <mutex>
+#include <set>
+#include <utility>
+
 #include "sdpa_device.h"
 
 namespace sdpa {
@@ -933,6 +937,22 @@ __global__ __launch_bounds__(256) void sdpa_range_combine_kernel(const FwdArgs a
     if (chunk == 0 && tid == 0) a.lse[b * a.l_s[0] + h * a.l_s[1] + (int64_t)q * a.l_s[2]] = dead ? -INFINITY : lse2 * LN2;
 }
 
+// Allow a kernel the most dynamic LDS any fused launch asks for, once per
+// (device, kernel): a host-side function attribute, so later launches (also
+// those recorded into a graph) make no further runtime call for it.
+int raise_lds_limit(const void* k) {
+    static std::mutex mu;
+    static std::set<std::pair<int, const void*>> done;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return (int)e;
+    std::lock_guard<std::mutex> lock(mu);
+    if (done.count({dev, k})) return 0;
+    e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, FUSED_LDS_MAX);
+    if (e == hipSuccess) done.insert({dev, k});
+    return (int)e;
+}
+
 template <typename T, int D, bool VEC>
 int launch_fused_t(int mask_kind, int waves, const FwdArgs& a, hipStream_t s) {
     const dim3 grid(a.n_blocks), block(waves * 64);
@@ -947,9 +967,8 @@ int launch_fused_t(int mask_kind, int waves, const FwdArgs& a, hipStream_t s) {
         auto* k = ranges ? sdpa_fused_wide_kernel<T, D, MK, VEC, VEC>                                      \
                   : wide ? sdpa_fused_wide_kernel<T, D, MK, VEC, false> : sdpa_fused_kernel<T, D, MK, VEC>;  \
         if (lds > 64 * 1024) {                                                                              \
-            const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),                     \
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
-            if (e != hipSuccess) return (int)e;                                                            \
+            const int e = raise_lds_limit(reinterpret_cast<const void*>(k));                                 \
+            if (e != 0) return e;                                                                           \
         }                                                                                                   \
         hipLaunchKernelGGL(k, grid, block, lds, s, a);                                                      \
         break;                                                                                              \
