@@ -279,6 +279,14 @@ sdpa_status_t sdpa_math_fwd_noalloc(const sdpa_tensor_t* q, const sdpa_tensor_t*
  * SDPA_MATH_FUSED_MIN_KEYS=<n> move the three thresholds of the second
  * rule; SDPA_MATH_FUSED_WIDE=0 keeps the fused path off its wide kernel,
  * =1 on it (SDPA_ERR_UNSUPPORTED where it cannot hold the keys).
+ * With a workspace (sdpa_math_fwd_ws, sdpa_math_fwd_noalloc), under
+ * SDPA_PATH_AUTO: a call of one to four query rows (32 * Sq <= D times the
+ * element size) that the whole-call wide kernel does not take runs its keys
+ * as ranges in one sweep on the wide kernel, then a combine launch (the
+ * query heads of a KV group sharing a workgroup); other calls with few
+ * query blocks against many keys run the two-pass kernel over key ranges.
+ * SDPA_MATH_RANGES=0 keeps the one-sweep ranges off, =1 takes them wherever
+ * they fit; SDPA_MATH_SPLITS=<n> forces n two-pass ranges.
  */
 sdpa_status_t sdpa_math_plan(const sdpa_tensor_t* q, const sdpa_tensor_t* k,
                              const sdpa_tensor_t* v, const sdpa_tensor_t* mask,

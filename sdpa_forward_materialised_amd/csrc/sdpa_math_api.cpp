@@ -519,7 +519,8 @@ sdpa_status_t make_plan(const Shape& sh, bool causal, int64_t coff, int forced, 
     // keeps it.
     if (allow_split && allow_ranges && vec && auto_path) {
         const char* re = std::getenv("SDPA_MATH_RANGES");
-        const bool force = re && *re == '1', off = re && *re == '0';
+        // (a forced two-pass range count, SDPA_MATH_SPLITS, keeps the two-pass ranges)
+        const bool force = re && *re == '1', off = (re && *re == '0') || (!force && std::getenv("SDPA_MATH_SPLITS"));
         const bool fewer_bytes = 32 * sh.Sq <= sh.D * elt_size(sh.dtype);
         const bool whole_wide = p->path == SDPA_PATH_FUSED && p->fused_rg > 0;
         int rw = 0, rk = 0, rn = 0, rrg = 0;
