@@ -82,6 +82,8 @@ EXTRA_WORKLOADS: Sequence[Workload] = (
              align="bottom_right"),
     # one query row per head against a long key cache: the keys are split over workgroups
     Workload("decode_1x32768_d128_bf16", "bf16", 4, 8, 8, 1, 32768, 128, False, "none", 7),
+    # batched decode with grouped heads (4 query heads per KV head) against a 4096-key cache
+    Workload("decode_gqa_16x32x8_1x4096_d128_bf16", "bf16", 16, 32, 8, 1, 4096, 128, False, "none", 8),
 )
 
 BY_NAME: Dict[str, Workload] = {w.name: w for w in (*WORKLOADS, *EXTRA_WORKLOADS)}

@@ -555,8 +555,9 @@ def test_workload_full_size(w, path):
 
 @pytest.mark.parametrize("w", list(W.EXTRA_WORKLOADS), ids=lambda w: w.name)
 def test_extra_workload_full_size(w):
-    """Chunked prefill (bottom-right causal) and long-key decode at full size,
-    with the default plan (key ranges where the planner picks them): sampled
+    """Chunked prefill (bottom-right causal), long-key decode and batched
+    grouped-head decode at full size, with the default plan (key ranges where
+    the planner picks them): sampled
     (batch, head) slices against the oracle, plus whole-output properties."""
     c = _workload_case(w)
     c["align"] = w.align
