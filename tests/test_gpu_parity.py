@@ -6,6 +6,7 @@ the same seeded inputs (max-abs bounds per dtype, +0.0 bit pattern at every
 removed position, LSE = -inf exactly on dead rows).
 """
 
+import contextlib
 import math
 import os
 import re
@@ -22,9 +23,30 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 # "fused": the fused path as the planner configures it (its wide kernel
 # wherever that fits); "fused1": the fused path held to its one-row-group
-# kernel; "fusedw": held to the wide kernel (skipped where it cannot fit)
-PATHS = ["twopass", "fused", "fused1"]
-_FUSED_ENV = {"fused1": "0", "fusedw": "1"}
+# kernel; "fusedw": held to the wide kernel (skipped where it cannot fit);
+# "ranges": the default plan with the wide kernel's one-sweep key ranges
+# forced wherever they fit (64-key ranges, one key group per row group, so
+# that small calls span several ranges)
+PATHS = ["twopass", "fused", "fused1", "ranges"]
+_PATH_ENV = {"fused1": {"SDPA_MATH_FUSED_WIDE": "0"}, "fusedw": {"SDPA_MATH_FUSED_WIDE": "1"},
+             "ranges": {"SDPA_MATH_RANGES": "1", "SDPA_MATH_RANGE_KEYS": "64", "SDPA_MATH_RANGE_WAVES": "1"}}
+_BINDING_PATH = {"fused1": "fused", "fusedw": "fused", "ranges": "auto"}
+
+
+@contextlib.contextmanager
+def _path_env(path):
+    """Environment of a test path name; yields the binding's path argument."""
+    env = _PATH_ENV.get(path, {})
+    saved = {k: os.environ.get(k) for k in env}
+    os.environ.update(env)
+    try:
+        yield _BINDING_PATH.get(path, path)
+    finally:
+        for k, val in saved.items():
+            if val is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = val
 
 
 def _lib():
@@ -34,16 +56,10 @@ def _lib():
 
 
 def _fwd(path, *args, **kw):
-    """S.fwd with a test path name ("fused1" / "fusedw" hold the fused path to one kernel)."""
+    """S.fwd with a test path name (see PATHS)."""
     S = _lib()
-    env = _FUSED_ENV.get(path)
-    if env is not None:
-        os.environ["SDPA_MATH_FUSED_WIDE"] = env
-    try:
-        return S.fwd(*args, path="fused" if path.startswith("fused") else path, **kw)
-    finally:
-        if env is not None:
-            os.environ.pop("SDPA_MATH_FUSED_WIDE", None)
+    with _path_env(path) as p:
+        return S.fwd(*args, path=p, **kw)
 
 
 def _run(c, path, scale=None, gqa=None, label=""):
@@ -57,20 +73,14 @@ def _run(c, path, scale=None, gqa=None, label=""):
     print(f"[case] {label} path={path} shape={tuple(q.shape)}x{tuple(k.shape)} mask="
           f"{None if m is None else (tuple(m.shape), m.dtype)} causal={c['causal']}", flush=True)
     gm = None if m is None else m.to(DEV)
-    env = _FUSED_ENV.get(path)
-    if env is not None:
-        os.environ["SDPA_MATH_FUSED_WIDE"] = env
     try:
-        O, P, L = S.fwd(q.to(DEV), k.to(DEV), v.to(DEV), gm, c["causal"], scale, gqa,
-                        path="fused" if path.startswith("fused") else path, out=out,
-                        causal_alignment=c.get("align", "top_left"))
+        with _path_env(path) as p:
+            O, P, L = S.fwd(q.to(DEV), k.to(DEV), v.to(DEV), gm, c["causal"], scale, gqa, path=p, out=out,
+                            causal_alignment=c.get("align", "top_left"))
     except NotImplementedError as e:
         if path.startswith("fused"):
             pytest.skip(f"the fused path cannot take this shape: {e}")
         raise
-    finally:
-        if env is not None:
-            os.environ.pop("SDPA_MATH_FUSED_WIDE", None)
     torch.cuda.synchronize()
     return O, P, L
 
