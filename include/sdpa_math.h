@@ -287,6 +287,11 @@ sdpa_status_t sdpa_math_fwd_noalloc(const sdpa_tensor_t* q, const sdpa_tensor_t*
  * query blocks against many keys run the two-pass kernel over key ranges.
  * SDPA_MATH_RANGES=0 keeps the one-sweep ranges off, =1 takes them wherever
  * they fit; SDPA_MATH_SPLITS=<n> forces n two-pass ranges.
+ * On the two-pass path, a non-causal grouped-head call (query heads per KV
+ * head a multiple of 4) without a mask or with one that all query heads
+ * share runs four query heads of a KV group per workgroup on 32 shared rows;
+ * SDPA_MATH_HEAD_ROWS=0 keeps one head per workgroup. Outputs do not depend
+ * on either choice.
  */
 sdpa_status_t sdpa_math_plan(const sdpa_tensor_t* q, const sdpa_tensor_t* k,
                              const sdpa_tensor_t* v, const sdpa_tensor_t* mask,

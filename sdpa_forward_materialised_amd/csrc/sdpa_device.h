@@ -162,13 +162,15 @@ struct Work {
 //  2  causal: heaviest first over the whole grid (every head at once);
 //  3  causal: each XCD takes its heads two at a time, the pair's blocks
 //     interleaved heaviest first: the balance of heaviest-first order with
-//     the K/V working set of two heads per L2 (measured fastest).
+//     the K/V working set of two heads per L2 (measured fastest);
+//  4  dispatch order, no remap: consecutive blocks run at the same time on
+//     all eight XCDs (head rows: measured faster than head-major per XCD).
 __device__ __forceinline__ Work decode_block(int L, const FwdArgs& a) {
     const int nb = a.n_blocks;
     const int nfull = nb & ~7;
     const int nq = a.n_qblk;
     Work w;
-    if (L < nfull && a.sched != 2) {
+    if (L < nfull && a.sched != 2 && a.sched != 4) {
         const int per = nfull >> 3;
         const int x = L & 7, i = L >> 3;
         if (a.sched == 1) {
@@ -206,8 +208,11 @@ __device__ __forceinline__ Work decode_block(int L, const FwdArgs& a) {
     const int bh = L / nq;
     const int r = L - bh * nq;
     w.qblk = a.causal ? (nq - 1 - r) : r;
-    w.b = bh / a.Hq;
-    w.hq = bh - w.b * a.Hq;
+    // with head rows, bh counts head sets of a.head_rows query heads (w.hq: the first)
+    const int hs = a.head_rows > 0 ? a.head_rows : 1;
+    const int hpb = a.Hq / hs;
+    w.b = bh / hpb;
+    w.hq = (bh - w.b * hpb) * hs;
     return w;
 }
 

@@ -40,7 +40,10 @@ struct FwdArgs {
                         // of one KV group on the same 32 rows (K, V staged once)
     int fused_oseq;     // wide variant: partial outputs accumulated in turn in
                         // one LDS buffer per row group (less LDS)
-    int sched;       // workgroup order (causal: 1, 2, 3), see decode_block
+    int sched;       // workgroup order (causal: 1, 2, 3; 4: dispatch order), see decode_block
+    int head_rows;   // two-pass, no loader wave: 0, or the number of query heads
+                     // of one KV group a workgroup takes (one per compute wave,
+                     // all on the same 32 rows; the mask, if any, shared by the heads)
     // Key ranges (split over workgroups): n_splits ranges of split_tiles
     // tiles (an even count) per query block; the two-pass kernels then run as
     // a statistics launch, a probability launch and an output combine, with
@@ -113,6 +116,7 @@ struct Plan {
     int fused_oseq = 0; // wide variant: partial outputs accumulated in turn (less LDS)
     int64_t tiles_per_bh;
     int64_t tiles_64;
+    int head_rows = 0;    // two-pass: query heads per workgroup on shared rows (0: one head)
     int n_splits = 1;     // key ranges per query block (with a workspace)
     int split_tiles = 0;  // two-pass: kernel tiles per key range (even)
     // n_splits > 1 on the fused path: key ranges of the wide kernel, one sweep

@@ -70,6 +70,7 @@ struct Shape {
     int64_t B, Hq, Hkv, Sq, Skv, D, Dv;
     int dtype;
     int mask_kind;
+    bool mask_head_shared;  // no mask, or one that every query head shares (size 1 or stride 0)
 };
 
 sdpa_status_t check_tensor(const sdpa_tensor_t* t, const char* name, int ndim) {
@@ -130,6 +131,7 @@ sdpa_status_t validate_inputs(const sdpa_tensor_t* q, const sdpa_tensor_t* k, co
         return fail(SDPA_ERR_INVALID_ARG, "is_causal must be 0 (none), 1 (top-left) or 2 (bottom-right), got %d",
                     is_causal);
     sh->mask_kind = sdpa::MASK_NONE;
+    sh->mask_head_shared = !mask || mask->sizes[1] == 1 || mask->strides[1] == 0;
     if (mask) {
         if (is_causal) return fail(SDPA_ERR_INVALID_ARG, "is_causal and an explicit mask are mutually exclusive");
         if (mask->ndim != 4) return fail(SDPA_ERR_INVALID_ARG, "mask must be passed with 4 dims (right-aligned)");
@@ -507,6 +509,19 @@ sdpa_status_t make_plan(const Shape& sh, bool causal, int64_t coff, int forced, 
             if (p->n_splits > 1) p->waves = 2;  // key ranges run on the two-wave loader kernel
         }
         p->q_rows = 32 * p->waves;
+        // Head rows: a grouped-head call on the four-wave kernel without a
+        // loader wave gives each workgroup four query heads of one KV group
+        // on 32 shared rows (one head per wave) instead of 128 rows of one
+        // head: the same K/V tile loads per workgroup, a quarter of the mask
+        // rows when the heads share the mask (measured: GQA key padding, fp16,
+        // 4 x 32 heads on 8, 1024 x 1024, D = 128: 176.3 -> 165.3 us with
+        // the blocks in dispatch order, 170.2 head-major per XCD).
+        // SDPA_MATH_HEAD_ROWS=0 turns it off.
+        const char* hr = std::getenv("SDPA_MATH_HEAD_ROWS");
+        if (p->waves == 4 && !causal && (sh.Hq / sh.Hkv) % 4 == 0 && sh.mask_head_shared && !(hr && *hr == '0')) {
+            p->head_rows = 4;
+            p->q_rows = 32;
+        }
     }
     // one-sweep key ranges on the wide kernel (range_config) for one to four
     // query rows, in place of the two-pass kernel (split or not) and of the
@@ -529,6 +544,7 @@ sdpa_status_t make_plan(const Shape& sh, bool causal, int64_t coff, int forced, 
             p->path = SDPA_PATH_FUSED;
             p->waves = rw;
             p->keys_per_wave = rk;
+            p->head_rows = 0;
             p->fused_rg = rrg;
             p->fused_hg = sh.Hq != sh.Hkv;
             p->fused_oseq = rrg > 1;
@@ -538,8 +554,9 @@ sdpa_status_t make_plan(const Shape& sh, bool causal, int64_t coff, int forced, 
         }
     }
     p->n_qblk = (int)cdiv(sh.Sq, p->q_rows);
-    // (head row groups: one workgroup per fused_rg query heads)
-    p->grid = sh.B * sh.Hq / (p->fused_hg ? p->fused_rg : 1) * p->n_qblk * (p->path == SDPA_PATH_FUSED ? p->n_splits : 1);
+    // (head rows and head row groups: one workgroup per head_rows / fused_rg query heads)
+    const int64_t heads_per_wg = p->fused_hg ? p->fused_rg : p->head_rows > 0 ? p->head_rows : 1;
+    p->grid = sh.B * sh.Hq / heads_per_wg * p->n_qblk * (p->path == SDPA_PATH_FUSED ? p->n_splits : 1);
     p->tiles_per_bh = count_tiles(sh.Sq, sh.Skv, causal, p->q_rows, coff);
     if (p->grid > INT32_MAX) return fail(SDPA_ERR_UNSUPPORTED, "grid too large");
     return SDPA_OK;
@@ -683,6 +700,7 @@ sdpa_status_t run(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_ten
     a.fused_rg = plan.fused_rg;
     a.fused_hg = plan.fused_hg;
     a.fused_oseq = plan.fused_oseq;
+    a.head_rows = plan.head_rows;
     if (drop) {
         a.keep = static_cast<const uint8_t*>(drop->keep->data);
         for (int dd = 0; dd < 4; ++dd) a.kp_s[dd] = eff_stride(drop->keep, dd);
@@ -702,12 +720,13 @@ sdpa_status_t run(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_ten
     // blocks, 91 us against 103 head-major and 110 grid-wide heaviest-first.
     // Otherwise heaviest first over the whole grid: 1k x 1k D=64, 352
     // blocks, all resident at once, 23.6 us against 26.7 with head pairs.
-    // SDPA_MATH_SCHED=0..3 overrides (1: heavy and light blocks interleaved
-    // per XCD).
+    // Head rows (non-causal): dispatch order, 165 against 170 us head-major
+    // per XCD on the GQA key-padding workload. SDPA_MATH_SCHED=0..4 overrides
+    // (1: heavy and light blocks interleaved per XCD).
     constexpr int64_t kResidentWorkgroups = 2 * 256;
     const int64_t per_xcd = plan.grid % 8 == 0 ? plan.grid / 8 : 0;
     const bool pairs_ok = is_causal && per_xcd > 0 && per_xcd % (2 * plan.n_qblk) == 0;
-    a.sched = is_causal ? ((pairs_ok && plan.grid > kResidentWorkgroups) ? 3 : 2) : 0;
+    a.sched = is_causal ? ((pairs_ok && plan.grid > kResidentWorkgroups) ? 3 : 2) : plan.head_rows > 0 ? 4 : 0;
     if (const char* e = std::getenv("SDPA_MATH_SCHED")) {
         a.sched = 0;
         // order 1 splits each XCD's range into a heavy and a light half of
@@ -715,6 +734,7 @@ sdpa_status_t run(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_ten
         if (*e == '1' && is_causal && per_xcd > 0 && per_xcd % plan.n_qblk == 0 && plan.n_qblk % 2 == 0) a.sched = 1;
         if (*e == '2' && is_causal) a.sched = 2;
         if (*e == '3' && pairs_ok) a.sched = 3;
+        if (*e == '4') a.sched = 4;
     }
 
     // byte extent of one (batch, head) slice of each tensor
@@ -895,6 +915,7 @@ sdpa_status_t run_varlen(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const s
     sh.Skv = max_skv;
     sh.dtype = q->dtype;
     sh.mask_kind = sdpa::MASK_NONE;
+    sh.mask_head_shared = true;
     const int64_t Tq = q->sizes[0], Tkv = k->sizes[0];
     if (nseq < 0 || max_sq < 0 || max_skv < 0)
         return fail(SDPA_ERR_INVALID_ARG, "sequence count and maximum lengths must be non-negative");

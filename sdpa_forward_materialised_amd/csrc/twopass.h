@@ -147,14 +147,19 @@ __device__ __forceinline__ const FwdArgs& pick_args(const FwdArgs& first, const 
 // output product takes keep * P * drop_oscale.
 // THD: packed variable-length sequences (a workgroup rebased onto its
 // sequence; the probability rows run to p_cols, zeros past the sequence's keys).
+// HR: head rows (four-wave kernels without a loader wave, a.head_rows == 4):
+// the compute waves take the query heads w.hq, w.hq + 1, ... of one KV group
+// on the same 32 rows, sharing each K/V tile (and the head-shared mask rows)
+// among the heads.
 template <typename T, int D, int NW, int MASK, bool VEC, int TN, bool NL, int SPL = 0, bool DROP = false,
-          bool THD = false>
+          bool THD = false, bool HR = false>
 __global__ __attribute__((amdgpu_flat_work_group_size((NL ? NW : NW + 1) * 64, (NL ? NW : NW + 1) * 64),
                           amdgpu_waves_per_eu(NL ? 2 : SDPA_TP_WPE(NW))))
 void sdpa_twopass_kernel(const FwdArgs a_in) {
     static_assert(SPL == 0 || !NL, "key ranges run on the loader-wave kernels");
     static_assert(!DROP || (SPL == 0 && !NL), "dropout runs on the whole-call loader-wave kernels");
     static_assert(!THD || (SPL == 0 && !NL && !DROP && MASK == MASK_NONE), "packed sequences: whole calls, no mask");
+    static_assert(!HR || (NL && NW == 4 && SPL == 0 && !DROP && !THD), "head rows: four waves, no loader wave");
     using C = TwoPassCfg<T, D, NW, MASK, VEC, TN, NL>;
     static_assert(!NL || C::PSTAGE, "without a loader wave the probability stores must be staged");
     static_assert(C::LDS_BYTES <= 160 * 1024, "tile buffers exceed the 160 KB LDS of a compute unit");
@@ -190,9 +195,10 @@ void sdpa_twopass_kernel(const FwdArgs a_in) {
     }
     const FwdArgs& a = pick_args<THD>(seq_args, a_in);
     const int pcols = THD ? a.p_cols : a.Skv;  // probability row length
+    constexpr bool hrows = HR;
     const int hk = w.hq / a.group;
-    const int q0 = w.qblk * QB;
-    const int kend = a.causal ? min(a.Skv, max(0, q0 + QB + a.coff)) : a.Skv;
+    const int q0 = hrows ? w.qblk * 32 : w.qblk * QB;
+    const int kend = a.causal ? min(a.Skv, max(0, q0 + (hrows ? 32 : QB) + a.coff)) : a.Skv;
     const int ntiles = (kend + BN - 1) / BN;
     // this workgroup's tiles [t_lo, t_hi) (t_lo even: tile t stays in buffer t & 1)
     const int split = SPL ? (int)blockIdx.x % a.n_splits : 0;
@@ -242,7 +248,7 @@ void sdpa_twopass_kernel(const FwdArgs a_in) {
                     if ((j - j0) % js != 0) continue;
                     const int row = j * C::MRPI + mrow;  // query row q0 + row
                     // whole 16-byte chunks only: Skv is a multiple of the keys per chunk here
-                    const uint32_t vo = pred(q0 + row < a.Sq && t * BN + mch * (16 / ME) < a.Skv,
+                    const uint32_t vo = pred((!hrows || row < 32) && q0 + row < a.Sq && t * BN + mch * (16 / ME) < a.Skv,
                                              (uint32_t)((int64_t)(q0 + row) * a.m_s[2] * ME) + (uint32_t)(mch * 16));
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(mr, (lds_void*)(mbuf(b) + j * 1024), 16, vo,
                                                              (uint32_t)(t * BN * ME), 0, 0);
@@ -291,14 +297,16 @@ void sdpa_twopass_kernel(const FwdArgs a_in) {
     }
 
     // ======================================================== compute waves
-    const int qw = q0 + 32 * wave;
+    const int qw = hrows ? q0 : q0 + 32 * wave;
+    const int hq_w = hrows ? w.hq + wave : w.hq;  // this wave's query head
+    const int mrow0 = hrows ? 0 : 32 * wave;      // its rows in the staged mask tile
     const int qi = qw + n;
     const bool row_ok = qi < a.Sq;
 
-    const rsrc_t qr = make_rsrc(static_cast<const T*>(a.q) + w.b * a.q_s[0] + w.hq * a.q_s[1], a.q_ext);
-    const rsrc_t pr = make_rsrc(static_cast<T*>(a.p) + w.b * a.p_s[0] + w.hq * a.p_s[1], a.p_ext);
-    const rsrc_t orr = make_rsrc(static_cast<T*>(a.o) + w.b * a.o_s[0] + w.hq * a.o_s[1], a.o_ext);
-    const rsrc_t lr = make_rsrc(a.lse + w.b * a.l_s[0] + w.hq * a.l_s[1], a.l_ext);
+    const rsrc_t qr = make_rsrc(static_cast<const T*>(a.q) + w.b * a.q_s[0] + hq_w * a.q_s[1], a.q_ext);
+    const rsrc_t pr = make_rsrc(static_cast<T*>(a.p) + w.b * a.p_s[0] + hq_w * a.p_s[1], a.p_ext);
+    const rsrc_t orr = make_rsrc(static_cast<T*>(a.o) + w.b * a.o_s[0] + hq_w * a.o_s[1], a.o_ext);
+    const rsrc_t lr = make_rsrc(a.lse + w.b * a.l_s[0] + hq_w * a.l_s[1], a.l_ext);
     // byte offset of this lane's P row (past the descriptor when the row is out of range)
     const uint32_t prow = pred(row_ok, (uint32_t)((int64_t)(row_ok ? qi : 0) * a.p_s[2] * SZ));
 
@@ -306,7 +314,7 @@ void sdpa_twopass_kernel(const FwdArgs a_in) {
     [[maybe_unused]] rsrc_t kpr = qr;
     [[maybe_unused]] uint32_t kp_row = 0;
     if constexpr (DROP) {
-        kpr = make_rsrc(a.keep + w.b * a.kp_s[0] + w.hq * a.kp_s[1], a.kp_ext);
+        kpr = make_rsrc(a.keep + w.b * a.kp_s[0] + hq_w * a.kp_s[1], a.kp_ext);
         kp_row = (uint32_t)((int64_t)(row_ok ? qi : 0) * a.kp_s[2]);
     }
     auto keep16 = [&](int k0, int kb, float* kv) SDPA_INLINE {
@@ -370,7 +378,7 @@ void sdpa_twopass_kernel(const FwdArgs a_in) {
         if constexpr (MASK == MASK_NONE) {
             return;
         } else if constexpr (C::MLDS) {
-            const uint8_t* base = mt + (32 * wave + n) * C::MROWB;
+            const uint8_t* base = mt + (mrow0 + n) * C::MROWB;
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
                 const int jrel = 32 * kb + 16 * c + 8 * hf;
@@ -412,7 +420,7 @@ void sdpa_twopass_kernel(const FwdArgs a_in) {
         if constexpr (MASK == MASK_BOOL && C::MLDS) {
             constexpr int NCH = 32 * C::MROWB / 16 / 64;  // 16-byte chunks per lane
             static_assert(NCH >= 1 && 32 * C::MROWB % 1024 == 0, "mask tile rows of a wave must split into lane chunks");
-            const u32x4* c = reinterpret_cast<const u32x4*>(mt + 32 * wave * C::MROWB) + lane * NCH;
+            const u32x4* c = reinterpret_cast<const u32x4*>(mt + mrow0 * C::MROWB) + lane * NCH;
             uint32_t any = 0u, zero_byte = 0u;
 #pragma unroll
             for (int i = 0; i < NCH; ++i) {
@@ -1022,6 +1030,15 @@ static int launch_twopass_mask(int mask_kind, const FwdArgs& a, hipStream_t s) {
 #define SDPA_TP_CASE(MK)                                                                                          \
     case MK:                                                                                                      \
         if constexpr (!NL || TwoPassCfg<T, D, NW, MK, VEC, tile_keys<MK>(), true>::PSTAGE) {                       \
+            if (a.head_rows > 0) {                                                                                \
+                if constexpr (NL && NW == 4 && !DROP) {                                                           \
+                    hipLaunchKernelGGL((sdpa_twopass_kernel<T, D, NW, MK, VEC, tile_keys<MK>(), NL, 0, false, false, \
+                                                            true>), grid, block, 0, s, a);                        \
+                    break;                                                                                        \
+                } else {                                                                                          \
+                    return (int)hipErrorInvalidValue;                                                             \
+                }                                                                                                 \
+            }                                                                                                     \
             hipLaunchKernelGGL((sdpa_twopass_kernel<T, D, NW, MK, VEC, tile_keys<MK>(), NL, 0, DROP>), grid, block, \
                                0, s, a);                                                                          \
             break;                                                                                                \

@@ -167,6 +167,48 @@ def test_key_padding_dead_tiles(D, dtype, waves, monkeypatch):
     _check(c, "twopass", label=f"keypad D={D} {dtype} waves={waves}")
 
 
+# Head rows: grouped heads on the four-wave kernel without a loader wave take
+# four query heads of one KV group per workgroup, on 32 shared rows. Group 4
+# and 8, no mask / head-shared bool and additive masks (with dead tail tiles
+# and dead rows), ragged Sq and Skv; against the oracle and bit for bit
+# against the same call with head rows off (SDPA_MATH_HEAD_ROWS=0). A mask
+# with per-head rows keeps one head per workgroup.
+HEAD_ROWS = [
+    ("f16-d128-g4-keypad", dict(seed=190, dtype="f16", B=2, Hq=8, Hkv=2, Sq=200, Skv=320, D=128), "keypad"),
+    ("bf16-d64-g8-none", dict(seed=191, dtype="bf16", B=1, Hq=16, Hkv=2, Sq=77, Skv=136, D=64), None),
+    ("f16-d32-g4-add", dict(seed=192, dtype="f16", B=2, Hq=4, Hkv=1, Sq=65, Skv=256, D=32, mask="add",
+                            mask_shape=(2, 1, 65, 256), p=0.2), None),
+    ("f32-d64-g4-bool", dict(seed=193, dtype="f32", B=1, Hq=8, Hkv=2, Sq=96, Skv=200, D=64, mask="bool",
+                             mask_shape=(1, 1, 96, 200), p=0.3), None),
+    ("f16-d64-g4-perhead", dict(seed=194, dtype="f16", B=1, Hq=4, Hkv=1, Sq=70, Skv=128, D=64, mask="bool",
+                                mask_shape=(1, 4, 70, 128), p=0.3), None),
+]
+
+
+@pytest.mark.parametrize("label,spec,kind", HEAD_ROWS, ids=[s[0] for s in HEAD_ROWS])
+def test_head_rows(label, spec, kind, monkeypatch):
+    monkeypatch.setenv("SDPA_MATH_TP_WAVES", "4")
+    c = W.make_case(**spec)
+    if kind == "keypad":
+        B, Sq, Skv = spec["B"], spec["Sq"], spec["Skv"]
+        keep = torch.zeros(B, 1, Sq, Skv, dtype=torch.bool)
+        for b, nk in enumerate((100, Skv)):
+            keep[b, :, :, :nk] = True
+        keep[0, :, 30:41, :] = False  # dead rows
+        c["mask"] = keep
+    on = _check(c, "twopass", label=f"{label} head rows")
+    S = _lib()
+    q, k, v = (c[x].to(DEV) for x in ("q", "k", "v"))
+    m = None if c["mask"] is None else c["mask"].to(DEV)
+    a = S.fwd(q, k, v, m, False, None, True, path="twopass")
+    monkeypatch.setenv("SDPA_MATH_HEAD_ROWS", "0")
+    b = S.fwd(q, k, v, m, False, None, True, path="twopass")
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    print(f"[result] {label} {on}", flush=True)
+
+
 # Bottom-right causal (query i keeps keys j <= i + Skv - Sq): a query chunk
 # against a longer key cache, grouped heads, more queries than keys (leading
 # dead rows), ragged float32, square, a few rows against a long cache, and a
