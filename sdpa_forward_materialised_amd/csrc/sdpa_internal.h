@@ -40,7 +40,7 @@ struct FwdArgs {
                         // of one KV group on the same 32 rows (K, V staged once)
     int fused_oseq;     // wide variant: partial outputs accumulated in turn in
                         // one LDS buffer per row group (less LDS)
-    int sched;       // workgroup order (causal: 1, 2, 3; 4: dispatch order), see decode_block
+    int sched;       // workgroup order (causal: 1, 2, 3; 4: dispatch order; 5: heads together), see decode_block
     int head_rows;   // two-pass, no loader wave: 0, or the number of query heads
                      // of one KV group a workgroup takes (one per compute wave,
                      // all on the same 32 rows; the mask, if any, shared by the heads)

@@ -209,6 +209,27 @@ def test_head_rows(label, spec, kind, monkeypatch):
     print(f"[result] {label} {on}", flush=True)
 
 
+def test_head_rows_orders(monkeypatch):
+    """Head rows under every non-causal workgroup order: 16 head sets of 4 query heads, 4 query
+    blocks each (64 workgroups, 8 per XCD: whole head sets per XCD, so order 5 applies); the same
+    bits in each order, and the oracle's values."""
+    monkeypatch.setenv("SDPA_MATH_TP_WAVES", "4")
+    c = W.make_case(195, "f16", 2, 32, 8, 100, 200, 64)
+    keep = torch.zeros(2, 1, 100, 200, dtype=torch.bool)
+    keep[0, :, :, :120] = True
+    keep[1] = True
+    c["mask"] = keep
+    ref = run_oracle(c["q"], c["k"], c["v"], c["mask"], False, None, True)
+    outs = {}
+    for sched in ("0", "4", "5"):
+        monkeypatch.setenv("SDPA_MATH_SCHED", sched)
+        outs[sched] = _run(c, "twopass", label=f"head rows order {sched}")
+        compare(*outs[sched], ref, torch.float16, f"head rows order {sched}", v=c["v"])
+    for sched in ("0", "4"):
+        for x, y in zip(outs["5"], outs[sched]):
+            assert torch.equal(x, y), sched
+
+
 # Bottom-right causal (query i keeps keys j <= i + Skv - Sq): a query chunk
 # against a longer key cache, grouped heads, more queries than keys (leading
 # dead rows), ragged float32, square, a few rows against a long cache, and a
@@ -472,12 +493,12 @@ def test_dispatch_orders_identical(Sq, waves, monkeypatch):
     c = W.make_case(124, "bf16", 2, 8, 8, Sq, Sq, 64, causal=True)
     ref = run_oracle(c["q"], c["k"], c["v"], None, True, None, False)
     outs = {}
-    for sched in ("0", "1", "2", "3"):
+    for sched in ("0", "1", "2", "3", "4", "5"):
         monkeypatch.setenv("SDPA_MATH_SCHED", sched)
         outs[sched] = _run(c, "twopass", label=f"Sq={Sq} order {sched}")
         compare(*outs[sched], ref, torch.bfloat16, f"Sq={Sq} order {sched}", v=c["v"])
     monkeypatch.delenv("SDPA_MATH_SCHED")
-    for sched in ("0", "1", "2"):
+    for sched in ("0", "1", "2", "4", "5"):
         for x, y in zip(outs["3"], outs[sched]):
             assert torch.equal(x, y), sched
 
