@@ -52,7 +52,11 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 
 // NL: no loader wave; the compute waves share the tile loads (and defer
 // each tile's probability stores by one tile, see the kernel).
-template <typename T, int D, int NW, int MASK, bool VEC, int TN, bool NL>
+// CT (head rows with a bool mask): the 32 shared rows of a mask tile are
+// staged in sweep 1 only, in the V buffers that sweep leaves free; sweep 2
+// takes each tile's class from a per-wave record and reads the mask from
+// memory for mixed tiles only. No LDS of its own for the mask.
+template <typename T, int D, int NW, int MASK, bool VEC, int TN, bool NL, bool CT = false>
 struct TwoPassCfg {
     static constexpr int NWAVES = NL ? NW : NW + 1;  // waves per workgroup
     static constexpr int SZ = (int)sizeof(T);
@@ -70,8 +74,10 @@ struct TwoPassCfg {
     static constexpr int MROWB = BN * ME;         // bytes per mask tile row
     static constexpr int MCPR = MROWB / 16;
     static constexpr int MRPI = 64 / MCPR;
-    static constexpr int MNI = QB / MRPI;
-    static constexpr int MTILEB = MLDS ? QB * MROWB : 0;
+    static constexpr int MQ = CT ? 32 : QB;       // mask tile rows
+    static constexpr int MNI = MQ / MRPI;
+    static constexpr int MTILEB = MLDS ? MQ * MROWB : 0;
+    static_assert(!CT || MTILEB <= TILEB, "a mask tile must fit in a V buffer");
     // Probabilities of a tile are staged per wave in LDS and written out as
     // whole rows (the MFMA layout gives each lane two 16-byte runs of one
     // row per 32 keys, i.e. 32-byte pieces of 32 rows per store: the costly
@@ -80,7 +86,7 @@ struct TwoPassCfg {
     static constexpr int ZC = BN * SZ / 16;       // 16-byte chunks per row of a P tile
     static constexpr int ZRPB = ZC * 16 >= 256 ? 1 : 256 / (ZC * 16);  // P rows per 64-bank span
     static constexpr int PSTB = 32 * BN * SZ;     // bytes of one wave's staged P tile
-    static constexpr int KVM_BYTES = 2 * (2 * TILEB + MTILEB);
+    static constexpr int KVM_BYTES = 2 * (2 * TILEB + (CT ? 0 : MTILEB));
     static constexpr bool PSTAGE = VEC && KVM_BYTES + NW * PSTB <= 80 * 1024;
     static constexpr int LDS_BYTES = KVM_BYTES + (PSTAGE ? NW * PSTB : 0);
 
@@ -150,9 +156,9 @@ __device__ __forceinline__ const FwdArgs& pick_args(const FwdArgs& first, const 
 // HR: head rows (four-wave kernels without a loader wave, a.head_rows == 4):
 // the compute waves take the query heads w.hq, w.hq + 1, ... of one KV group
 // on the same 32 rows, sharing each K/V tile (and the head-shared mask rows)
-// among the heads.
+// among the heads. CT: see TwoPassCfg (head rows with a bool mask).
 template <typename T, int D, int NW, int MASK, bool VEC, int TN, bool NL, int SPL = 0, bool DROP = false,
-          bool THD = false, bool HR = false>
+          bool THD = false, bool HR = false, bool CT = false>
 __global__ __attribute__((amdgpu_flat_work_group_size((NL ? NW : NW + 1) * 64, (NL ? NW : NW + 1) * 64),
                           amdgpu_waves_per_eu(NL ? 2 : SDPA_TP_WPE(NW))))
 void sdpa_twopass_kernel(const FwdArgs a_in) {
@@ -160,7 +166,8 @@ void sdpa_twopass_kernel(const FwdArgs a_in) {
     static_assert(!DROP || (SPL == 0 && !NL), "dropout runs on the whole-call loader-wave kernels");
     static_assert(!THD || (SPL == 0 && !NL && !DROP && MASK == MASK_NONE), "packed sequences: whole calls, no mask");
     static_assert(!HR || (NL && NW == 4 && SPL == 0 && !DROP && !THD), "head rows: four waves, no loader wave");
-    using C = TwoPassCfg<T, D, NW, MASK, VEC, TN, NL>;
+    static_assert(!CT || (HR && MASK == MASK_BOOL && VEC), "class records: head rows with a staged bool mask");
+    using C = TwoPassCfg<T, D, NW, MASK, VEC, TN, NL, CT>;
     static_assert(!NL || C::PSTAGE, "without a loader wave the probability stores must be staged");
     static_assert(C::LDS_BYTES <= 160 * 1024, "tile buffers exceed the 160 KB LDS of a compute unit");
     constexpr int BN = C::BN;
@@ -178,7 +185,7 @@ void sdpa_twopass_kernel(const FwdArgs a_in) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS_BYTES];
     auto kbuf = [&](int b) -> uint8_t* { return smem + b * C::TILEB; };
     auto vbuf = [&](int b) -> uint8_t* { return smem + 2 * C::TILEB + b * C::TILEB; };
-    auto mbuf = [&](int b) -> uint8_t* { return smem + 4 * C::TILEB + b * C::MTILEB; };
+    auto mbuf = [&](int b) -> uint8_t* { return CT ? vbuf(b) : smem + 4 * C::TILEB + b * C::MTILEB; };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -439,6 +446,16 @@ void sdpa_twopass_kernel(const FwdArgs a_in) {
             return 0;
         }
     };
+    // CT: the classes sweep 1 found, 2 bits per tile, tile t in lane t / 16
+    // (up to 1024 tiles); the same in every wave of the workgroup (its waves
+    // share the rows)
+    uint32_t cls_rec = 0u;
+    auto record_flags = [&](int t, int flags) SDPA_INLINE {
+        if constexpr (CT) cls_rec |= lane == (t >> 4) ? (uint32_t)flags << (2 * (t & 15)) : 0u;
+    };
+    auto recorded_flags = [&](int t) SDPA_INLINE -> int {
+        return (int)(((uint32_t)__builtin_amdgcn_readlane((int)cls_rec, t >> 4) >> (2 * (t & 15))) & 3u);
+    };
 
     // Base-2 scaled, masked scores t[r] of one block. `edge`: the block may
     // hold keys past Skv or past this wave's causal diagonal.
@@ -479,6 +496,7 @@ void sdpa_twopass_kernel(const FwdArgs a_in) {
         const int k0 = t * BN;
         const int buf = t & 1;
         const int flags = tile_flags(mbuf(buf));
+        record_flags(t, flags);
         if (flags & TILE_DEAD) return;
         const bool plain = MASK == MASK_NONE || (flags & TILE_FULL);  // no key of the tile is masked
 #pragma unroll
@@ -743,7 +761,7 @@ void sdpa_twopass_kernel(const FwdArgs a_in) {
     auto sweep2_tile = [&](int t, auto edge_c, int buf) SDPA_INLINE {
         constexpr bool edge = decltype(edge_c)::value;
         const int k0 = t * BN;
-        const int flags = tile_flags(mbuf(buf));
+        const int flags = CT ? recorded_flags(t) : tile_flags(mbuf(buf));
         const bool plain = MASK == MASK_NONE || (flags & TILE_FULL);  // no key of the tile is masked
         if (flags & TILE_DEAD) {  // P = 0, O unchanged
             if constexpr (C::PSTAGE) {
@@ -765,7 +783,11 @@ void sdpa_twopass_kernel(const FwdArgs a_in) {
                 for (int r = 0; r < 16; ++r) p[r] = fast_exp2(__builtin_fmaf(acc[r], a.scale_log2, -lse2));
             } else {
                 float mv[16];
-                mask_terms(mbuf(buf), k0, kb, mv);
+                if constexpr (CT)  // mixed tiles only: the mask from memory
+                    load_mask16<T, MASK, true>(a, mr, (uint32_t)((int64_t)(row_ok ? qi : 0) * a.m_s[2] * ME),
+                                               k0 + 32 * kb, hf, mv);
+                else
+                    mask_terms(mbuf(buf), k0, kb, mv);
                 float tt[16];
                 scores(acc, mv, kb, k0, edge, tt);
 #pragma unroll
@@ -918,10 +940,12 @@ void sdpa_twopass_kernel(const FwdArgs a_in) {
     // next barrier finds them a whole tile old rather than just issued.
     auto load2 = [&](int t) SDPA_INLINE {
         if constexpr (NL) {
-            if (t < ntiles) {
+            // CT: no mask tiles, and no K/V for a tile every row of the
+            // workgroup drops (its classes are the same in every wave)
+            if (t < ntiles && !(CT && (recorded_flags(t) & TILE_DEAD))) {
                 dma_k(kbuf(t & 1), t, wave, NW);
                 dma_v(vbuf(t & 1), t, wave, NW);
-                dma_m(t, t & 1, wave, NW);
+                if constexpr (!CT) dma_m(t, t & 1, wave, NW);
             }
         }
     };
@@ -1031,6 +1055,14 @@ static int launch_twopass_mask(int mask_kind, const FwdArgs& a, hipStream_t s) {
     case MK:                                                                                                      \
         if constexpr (!NL || TwoPassCfg<T, D, NW, MK, VEC, tile_keys<MK>(), true>::PSTAGE) {                       \
             if (a.head_rows > 0) {                                                                                \
+                if constexpr (NL && NW == 4 && !DROP && MK == MASK_BOOL && VEC &&                                 \
+                              TwoPassCfg<T, D, NW, MK, VEC, 64, true, true>::PSTAGE) {                              \
+                    if (a.Skv <= 64 * 1024) {                                                                     \
+                        hipLaunchKernelGGL((sdpa_twopass_kernel<T, D, NW, MK, VEC, 64, NL, 0, false, false, true, \
+                                                                true>), grid, block, 0, s, a);                    \
+                        break;                                                                                    \
+                    }                                                                                             \
+                }                                                                                                 \
                 if constexpr (NL && NW == 4 && !DROP) {                                                           \
                     hipLaunchKernelGGL((sdpa_twopass_kernel<T, D, NW, MK, VEC, tile_keys<MK>(), NL, 0, false, false, \
                                                             true>), grid, block, 0, s, a);                        \
