@@ -164,12 +164,13 @@ struct Work {
 //     interleaved heaviest first: the balance of heaviest-first order with
 //     the K/V working set of two heads per L2 (measured fastest);
 //  4  dispatch order, no remap: consecutive blocks run at the same time on
-//     all eight XCDs;
+//     all eight XCDs, every XCD takes a share of every head (head rows:
+//     each XCD then carries a share of every batch's key-padding work;
+//     measured fastest, though each XCD's L2 fetches every KV head);
 //  5  each XCD takes a contiguous range of heads (head sets with head rows),
 //     its blocks query-block-major: all of its heads advance together, so
 //     the workgroups that run at once read several heads' K/V tiles instead
-//     of one head's (head rows: as fast as dispatch order, 162 against 165 us
-//     head-major, with each K/V still read through one XCD's L2).
+//     of one, each K/V read through one XCD's L2.
 __device__ __forceinline__ Work decode_block(int L, const FwdArgs& a) {
     const int nb = a.n_blocks;
     const int nfull = nb & ~7;

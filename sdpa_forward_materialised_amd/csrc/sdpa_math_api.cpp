@@ -720,14 +720,16 @@ sdpa_status_t run(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa_ten
     // blocks, 91 us against 103 head-major and 110 grid-wide heaviest-first.
     // Otherwise heaviest first over the whole grid: 1k x 1k D=64, 352
     // blocks, all resident at once, 23.6 us against 26.7 with head pairs.
-    // Head rows (non-causal): each XCD's heads advance together (order 5),
-    // 162 against 165 us head-major per XCD on the GQA key-padding workload.
+    // Head rows (non-causal): dispatch order (order 4), so that every XCD
+    // takes a share of every batch: GQA key padding (per-batch key counts
+    // 601 to 1017) 139.4 us against 157.0 with each XCD's heads advancing
+    // together (order 5) and 151.4 with those heads strided over batches.
     // SDPA_MATH_SCHED=0..5 overrides (1: heavy and light blocks interleaved
-    // per XCD; 4: dispatch order).
+    // per XCD).
     constexpr int64_t kResidentWorkgroups = 2 * 256;
     const int64_t per_xcd = plan.grid % 8 == 0 ? plan.grid / 8 : 0;
     const bool pairs_ok = is_causal && per_xcd > 0 && per_xcd % (2 * plan.n_qblk) == 0;
-    a.sched = is_causal ? ((pairs_ok && plan.grid > kResidentWorkgroups) ? 3 : 2) : plan.head_rows > 0 ? 5 : 0;
+    a.sched = is_causal ? ((pairs_ok && plan.grid > kResidentWorkgroups) ? 3 : 2) : plan.head_rows > 0 ? 4 : 0;
     if (const char* e = std::getenv("SDPA_MATH_SCHED")) {
         a.sched = 0;
         // order 1 splits each XCD's range into a heavy and a light half of
