@@ -123,10 +123,22 @@ template <> struct Tr<_Float16> {
     }
     // Residual of the rounding hi = cvt8(x), itself rounded (exact in
     // float32, as for bf16): hi + lo carries x to 22 significant bits.
+    // x - hi in one mixed-precision fma per element (hi taken from its
+    // packed half as a half-precision operand, times -1, plus x): the same
+    // exact difference as widening hi and subtracting, in one instruction
+    // instead of two.
     static __device__ __forceinline__ vec lo8(const float* x, vec hi) {
+        const u32x4 b = __builtin_bit_cast(u32x4, hi);
         f32x8 r;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) r[e] = x[e] - (float)hi[e];
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t w = b[e];
+            float d0, d1;
+            asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(d0) : "v"(w), "v"(x[2 * e]));
+            asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(d1) : "v"(w), "v"(x[2 * e + 1]));
+            r[2 * e] = d0;
+            r[2 * e + 1] = d1;
+        }
         return __builtin_convertvector(r, vec);
     }
 };
