@@ -52,11 +52,12 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 
 // NL: no loader wave; the compute waves share the tile loads (and defer
 // each tile's probability stores by one tile, see the kernel).
-// CT (head rows with a bool mask): the 32 shared rows of a mask tile are
-// staged in sweep 1 only, in the V buffers that sweep leaves free; sweep 2
-// takes each tile's class from a per-wave record and reads the mask from
-// memory for mixed tiles only. No LDS of its own for the mask.
-template <typename T, int D, int NW, int MASK, bool VEC, int TN, bool NL, bool CT = false>
+// CT (bool masks without a loader wave): mask tiles are staged in sweep 1
+// only, in the V buffers that sweep leaves free; sweep 2 takes each tile's
+// class from a per-wave record and reads the mask from memory for mixed
+// tiles only. No LDS of its own for the mask. HR (head rows): the waves
+// share 32 query rows, so a mask tile has 32 rows.
+template <typename T, int D, int NW, int MASK, bool VEC, int TN, bool NL, bool CT = false, bool HR = false>
 struct TwoPassCfg {
     static constexpr int NWAVES = NL ? NW : NW + 1;  // waves per workgroup
     static constexpr int SZ = (int)sizeof(T);
@@ -74,10 +75,10 @@ struct TwoPassCfg {
     static constexpr int MROWB = BN * ME;         // bytes per mask tile row
     static constexpr int MCPR = MROWB / 16;
     static constexpr int MRPI = 64 / MCPR;
-    static constexpr int MQ = CT ? 32 : QB;       // mask tile rows
+    static constexpr int MQ = HR ? 32 : QB;       // mask tile rows
     static constexpr int MNI = MQ / MRPI;
     static constexpr int MTILEB = MLDS ? MQ * MROWB : 0;
-    static_assert(!CT || MTILEB <= TILEB, "a mask tile must fit in a V buffer");
+    static constexpr bool CT_FITS = MTILEB <= TILEB;  // a mask tile fits in a V buffer
     // Probabilities of a tile are staged per wave in LDS and written out as
     // whole rows (the MFMA layout gives each lane two 16-byte runs of one
     // row per 32 keys, i.e. 32-byte pieces of 32 rows per store: the costly
@@ -166,8 +167,9 @@ void sdpa_twopass_kernel(const FwdArgs a_in) {
     static_assert(!DROP || (SPL == 0 && !NL), "dropout runs on the whole-call loader-wave kernels");
     static_assert(!THD || (SPL == 0 && !NL && !DROP && MASK == MASK_NONE), "packed sequences: whole calls, no mask");
     static_assert(!HR || (NL && NW == 4 && SPL == 0 && !DROP && !THD), "head rows: four waves, no loader wave");
-    static_assert(!CT || (HR && MASK == MASK_BOOL && VEC), "class records: head rows with a staged bool mask");
-    using C = TwoPassCfg<T, D, NW, MASK, VEC, TN, NL, CT>;
+    static_assert(!CT || (NL && MASK == MASK_BOOL && VEC), "class records: no loader wave, a staged bool mask");
+    using C = TwoPassCfg<T, D, NW, MASK, VEC, TN, NL, CT, HR>;
+    static_assert(!CT || C::CT_FITS, "a mask tile must fit in a V buffer");
     static_assert(!NL || C::PSTAGE, "without a loader wave the probability stores must be staged");
     static_assert(C::LDS_BYTES <= 160 * 1024, "tile buffers exceed the 160 KB LDS of a compute unit");
     constexpr int BN = C::BN;
@@ -940,9 +942,9 @@ void sdpa_twopass_kernel(const FwdArgs a_in) {
     // next barrier finds them a whole tile old rather than just issued.
     auto load2 = [&](int t) SDPA_INLINE {
         if constexpr (NL) {
-            // CT: no mask tiles, and no K/V for a tile every row of the
-            // workgroup drops (its classes are the same in every wave)
-            if (t < ntiles && !(CT && (recorded_flags(t) & TILE_DEAD))) {
+            // CT: no mask tiles; with head rows no K/V for a tile every row
+            // of the workgroup drops (its classes are the same in every wave)
+            if (t < ntiles && !(CT && HR && (recorded_flags(t) & TILE_DEAD))) {
                 dma_k(kbuf(t & 1), t, wave, NW);
                 dma_v(vbuf(t & 1), t, wave, NW);
                 if constexpr (!CT) dma_m(t, t & 1, wave, NW);
@@ -1056,7 +1058,7 @@ static int launch_twopass_mask(int mask_kind, const FwdArgs& a, hipStream_t s) {
         if constexpr (!NL || TwoPassCfg<T, D, NW, MK, VEC, tile_keys<MK>(), true>::PSTAGE) {                       \
             if (a.head_rows > 0) {                                                                                \
                 if constexpr (NL && NW == 4 && !DROP && MK == MASK_BOOL && VEC &&                                 \
-                              TwoPassCfg<T, D, NW, MK, VEC, 64, true, true>::PSTAGE) {                              \
+                              TwoPassCfg<T, D, NW, MK, VEC, 64, true, true, true>::PSTAGE) {                        \
                     if (a.Skv <= 64 * 1024) {                                                                     \
                         hipLaunchKernelGGL((sdpa_twopass_kernel<T, D, NW, MK, VEC, 64, NL, 0, false, false, true, \
                                                                 true>), grid, block, 0, s, a);                    \
@@ -1069,6 +1071,15 @@ static int launch_twopass_mask(int mask_kind, const FwdArgs& a, hipStream_t s) {
                     break;                                                                                        \
                 } else {                                                                                          \
                     return (int)hipErrorInvalidValue;                                                             \
+                }                                                                                                 \
+            }                                                                                                     \
+            if constexpr (NL && NW == 4 && !DROP && MK == MASK_BOOL && VEC &&                                     \
+                          TwoPassCfg<T, D, NW, MK, VEC, 64, true, true>::PSTAGE &&                                  \
+                          TwoPassCfg<T, D, NW, MK, VEC, 64, true, true>::CT_FITS) {                                 \
+                if (a.m_s[1] == 0 && a.Skv <= 64 * 1024) { /* a mask all query heads share */                   \
+                    hipLaunchKernelGGL((sdpa_twopass_kernel<T, D, NW, MK, VEC, 64, NL, 0, false, false, false, true>), \
+                                       grid, block, 0, s, a);                                                     \
+                    break;                                                                                        \
                 }                                                                                                 \
             }                                                                                                     \
             hipLaunchKernelGGL((sdpa_twopass_kernel<T, D, NW, MK, VEC, tile_keys<MK>(), NL, 0, DROP>), grid, block, \

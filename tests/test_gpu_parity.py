@@ -214,12 +214,19 @@ def test_head_rows(label, spec, kind, monkeypatch):
     print(f"[result] {label} {on}", flush=True)
 
 
-# Head rows with a bool mask (64-key tiles, tile classes recorded in the
-# statistics sweep, the mask read from memory for mixed tiles in the
-# probability sweep, dead tiles' K/V loads skipped): random masks (every
-# tile mixed), key padding with ragged tails, fully masked rows, more than
-# 16 and more than 64 tiles (the class record spans several lanes).
+# Bool masks that every query head shares, on the four-wave kernel without a
+# loader wave (64-key tiles, tile classes recorded in the statistics sweep,
+# the mask read from memory for mixed tiles in the probability sweep; with
+# head rows also dead tiles' K/V loads skipped): random masks (every tile
+# mixed), key padding with ragged tails, fully masked rows, more than 16 and
+# more than 64 tiles (the class record spans several lanes); grouped heads
+# (head rows) and one KV head per query head.
 CLASS_CASES = [
+    ("mha-random-ragged", dict(seed=186, dtype="bf16", B=2, Hq=3, Hkv=3, Sq=150, Skv=264, D=128, mask="bool",
+                               mask_shape=(2, 1, 150, 264), p=0.3), None),
+    ("mha-keypad-2104", dict(seed=187, dtype="f16", B=2, Hq=2, Hkv=2, Sq=130, Skv=2104, D=64), (900, 2097)),
+    ("mha-broadcast-row", dict(seed=188, dtype="f16", B=1, Hq=2, Hkv=2, Sq=200, Skv=136, D=128, mask="bool",
+                               mask_shape=(1, 1, 1, 136), p=0.5), None),
     ("random-ragged", dict(seed=196, dtype="f16", B=2, Hq=8, Hkv=2, Sq=77, Skv=200, D=64, mask="bool",
                            mask_shape=(2, 1, 77, 200), p=0.3), None),
     ("keypad-2000", dict(seed=197, dtype="bf16", B=2, Hq=4, Hkv=1, Sq=96, Skv=2000, D=128), (700, 1999)),
