@@ -441,7 +441,8 @@ __global__ __launch_bounds__(BWQ * 64) void sdpa_bwd_q_kernel(const BwdArgs a) {
 constexpr int KV_DV = 1, KV_DK = 2, KV_BOTH = 3;
 
 template <typename T, int D, int MASK, bool HAS_DP, int WHICH>
-__global__ __launch_bounds__(BW_KV * 64) void sdpa_bwd_kv_kernel(const BwdArgs a) {
+__global__ __launch_bounds__(BW_KV * 64) __attribute__((amdgpu_waves_per_eu(WHICH != KV_BOTH && sizeof(T) == 2 ? 2 : 1)))
+void sdpa_bwd_kv_kernel(const BwdArgs a) {
     constexpr int BW = BW_KV;
     constexpr bool DO_DV = (WHICH & KV_DV) != 0;
     constexpr bool NEED_DP = (WHICH & KV_DK) != 0;  // dP, dprobs and D: dk only
