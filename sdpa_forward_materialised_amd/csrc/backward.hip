@@ -274,7 +274,8 @@ __device__ __forceinline__ float mask_elem(const FwdArgs& f, rsrc_t mr, int qi, 
 // ====================================================================== dq
 
 template <typename T, int D, int MASK, bool HAS_DP>
-__global__ __launch_bounds__(BWQ * 64) void sdpa_bwd_q_kernel(const BwdArgs a) {
+__global__ __launch_bounds__(BWQ * 64) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 && MASK != MASK_NONE ? 2 : 1)))
+void sdpa_bwd_q_kernel(const BwdArgs a) {
     using TR = Tr<T>;
     using vec = typename TR::vec;
     using TL = Tile<T, D>;
@@ -286,14 +287,13 @@ __global__ __launch_bounds__(BWQ * 64) void sdpa_bwd_q_kernel(const BwdArgs a) {
     const FwdArgs& f = a.f;
 
     // 16-bit, D = 128: each wave's q and dout rows live in LDS (read as B
-    // operands per tile) instead of 64 registers, where that lets two waves
-    // share a SIMD: no mask, or an additive one without dprobs (2k causal
-    // bf16: 816 -> 700 us). With a bool mask, or a mask and dprobs, the
-    // per-lane mask and dprobs loads keep the wave at one per SIMD either way
-    // and the extra LDS reads only cost (GQA key padding 2070 -> 2136 us);
-    // smaller head dims already run two or more per SIMD (1k D = 64: 183 ->
-    // 193 us).
-    constexpr bool DO_LDS = sizeof(T) == 2 && D == 128 && (MASK == MASK_NONE || (MASK == MASK_ADD && !HAS_DP));
+    // operands per tile) instead of 64 registers, which lets two waves share
+    // a SIMD (2k causal bf16: 816 -> 700 us). With a mask the per-lane mask
+    // and dprobs loads need the occupancy request above as well (the
+    // compiler otherwise spends the freed registers on them): GQA key
+    // padding 2077 -> 1845 us. Smaller head dims already run two or more per
+    // SIMD (1k D = 64: 183 -> 193 us with the rows in LDS).
+    constexpr bool DO_LDS = sizeof(T) == 2 && D == 128;
     __shared__ __attribute__((aligned(16))) uint8_t smem[(2 + (DO_LDS ? 2 * BWQ : 0)) * TL::BYTES32];
     uint8_t* kt = smem;
     uint8_t* vt = smem + TL::BYTES32;
