@@ -340,8 +340,11 @@ sdpa_status_t sdpa_math_bwd(const sdpa_tensor_t* q, const sdpa_tensor_t* k,
 
 /*
  * sdpa_math_bwd_workspace_bytes — bytes of workspace sdpa_math_bwd needs for
- * these inputs (4 * B * Hq * Sq: one float32 per query row). Validates the
- * inputs like sdpa_math_plan; *bytes is 0 on error.
+ * these inputs: one float32 per query row (4 * B * Hq * Sq, rounded up to
+ * 256), plus, for a causal call whose key blocks (64 keys) number fewer
+ * than 1024, float32 partial dk and dv for each of up to 4 query ranges
+ * (8 * ranges * B * Hkv * Skv * D). Validates the inputs like
+ * sdpa_math_plan; *bytes is 0 on error.
  */
 sdpa_status_t sdpa_math_bwd_workspace_bytes(const sdpa_tensor_t* q, const sdpa_tensor_t* k,
                                             const sdpa_tensor_t* v, const sdpa_tensor_t* mask,

@@ -476,10 +476,14 @@ void sdpa_bwd_kv_kernel(const BwdArgs a) {
 
     const int nkb = (f.Skv + 32 * BW - 1) / (32 * BW);
     // key block major: the early key blocks (the most query tiles under a
-    // causal mask) of every head go first
+    // causal mask) of every head go first; with query ranges the ranges of
+    // a key block are consecutive
+    const int ns = WHICH == KV_BOTH ? a.kv_splits : 1;
+    const int sidx = ns > 1 ? (int)blockIdx.x % ns : 0;
+    const int lin = ns > 1 ? (int)blockIdx.x / ns : (int)blockIdx.x;
     const int nbk = f.B * f.Hkv;
-    const int kblk = blockIdx.x / nbk;
-    const int bk = blockIdx.x - kblk * nbk;
+    const int kblk = lin / nbk;
+    const int bk = lin - kblk * nbk;
     const int b = bk / f.Hkv, hk = bk - (bk / f.Hkv) * f.Hkv;
     const int k0 = kblk * 32 * BW;
     const int kw0 = k0 + 32 * wave;
@@ -506,7 +510,11 @@ void sdpa_bwd_kv_kernel(const BwdArgs a) {
     // k0 - coff see none of this workgroup's keys
     const int qstart = f.causal ? max(0, k0 - f.coff) / 32 * 32 : 0;
     const int nqt = f.Sq > qstart ? (f.Sq - qstart + 31) / 32 : 0;  // query tiles per head
-    const int nit = f.group * nqt;                                   // (head of the group, query tile) steps
+    const int nit_all = f.group * nqt;                               // (head of the group, query tile) steps
+    // this workgroup's steps [it_lo, nit) (all of them without query ranges)
+    const int per = (nit_all + ns - 1) / ns;
+    const int it_lo = min(nit_all, sidx * per);
+    const int nit = min(nit_all, it_lo + per);
 
     // the next step's tiles, held in registers until the current one is consumed
     Prefetch32<T, D, BW * 64> qp, dop;
@@ -572,12 +580,12 @@ void sdpa_bwd_kv_kernel(const BwdArgs a) {
         }
     };
 
-    if (nit > 0) {
-        prefetch(0);
+    if (nit > it_lo) {
+        prefetch(it_lo);
         put();
     }
     __syncthreads();  // (also orders this wave's K and V rows before their first reads)
-    for (int it = 0; it < nit; ++it) {
+    for (int it = it_lo; it < nit; ++it) {
         int h, i0;
         step_coords(it, h, i0);
         // this step's mask terms (per lane: its key, 16 queries), before the prefetch
@@ -626,9 +634,86 @@ void sdpa_bwd_kv_kernel(const BwdArgs a) {
         if (it + 1 < nit) put();
         __syncthreads();
     }
+    if constexpr (WHICH == KV_BOTH) {
+        if (ns > 1) {  // float32 partials of this query range, unscaled
+            const int64_t plane = (int64_t)nbk * f.Skv * D;
+            float* pk = a.ws_kv + ((int64_t)sidx * nbk + bk) * f.Skv * D + (int64_t)(key_ok ? kj : 0) * D;
+            float* pv = pk + (int64_t)ns * plane;
+            if (key_ok) {
+#pragma unroll
+                for (int dd = 0; dd < ND; ++dd) {
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        const int c0 = 32 * dd + 16 * h2 + 8 * hf;
+#pragma unroll
+                        for (int q4 = 0; q4 < 2; ++q4) {
+                            const int e = 8 * h2 + 4 * q4;
+                            *reinterpret_cast<f32x4*>(pk + c0 + 4 * q4) =
+                                f32x4{dk[dd][e], dk[dd][e + 1], dk[dd][e + 2], dk[dd][e + 3]};
+                            *reinterpret_cast<f32x4*>(pv + c0 + 4 * q4) =
+                                f32x4{dv[dd][e], dv[dd][e + 1], dv[dd][e + 2], dv[dd][e + 3]};
+                        }
+                    }
+                }
+            }
+            return;
+        }
+    }
     const uint32_t krow_off = (uint32_t)(key_ok ? kj : 0);
     if constexpr (NEED_DP) store_acc_row<T, D>(dkr, krow_off * (uint32_t)(a.dk_s[2] * SZ), key_ok, dk, a.scale, hf);
     if constexpr (DO_DV) store_acc_row<T, D>(dvr, krow_off * (uint32_t)(a.dv_s[2] * SZ), key_ok, dv, 1.0f / P_LIFT, hf);
+}
+
+// dk and dv of a key-side launch over query ranges: each row's float32
+// partials summed in range order, then scaled (dk: the score scale; dv: the
+// fp16 probability lift undone) and rounded once. One thread per 8
+// consecutive columns of a (batch, KV head, key) row.
+template <typename T>
+__global__ __launch_bounds__(256) void sdpa_bwd_kv_reduce_kernel(const BwdArgs a, int D) {
+    const FwdArgs& f = a.f;
+    constexpr float P_LIFT = std::is_same<T, _Float16>::value ? 4096.0f : 1.0f;
+    const int nbk = f.B * f.Hkv;
+    const int64_t rows = (int64_t)nbk * f.Skv;
+    const int cpr = D / 8;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= rows * cpr) return;
+    const int64_t row = i / cpr;
+    const int c = (int)(i - row * cpr) * 8;
+    const int bk = (int)(row / f.Skv), key = (int)(row - (int64_t)bk * f.Skv);
+    const int b = bk / f.Hkv, hk = bk - (bk / f.Hkv) * f.Hkv;
+    const int64_t plane = rows * D;
+    float sk[8] = {0, 0, 0, 0, 0, 0, 0, 0}, sv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int s2 = 0; s2 < a.kv_splits; ++s2) {
+        const float* pk = a.ws_kv + (int64_t)s2 * plane + row * D + c;
+        const float* pv = pk + (int64_t)a.kv_splits * plane;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const f32x4 uk = *reinterpret_cast<const f32x4*>(pk + 4 * h);
+            const f32x4 uv = *reinterpret_cast<const f32x4*>(pv + 4 * h);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sk[4 * h + e] += uk[e];
+                sv[4 * h + e] += uv[e];
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        sk[e] *= a.scale;
+        sv[e] *= 1.0f / P_LIFT;
+    }
+    T* dk = static_cast<T*>(a.dk) + b * a.dk_s[0] + hk * a.dk_s[1] + (int64_t)key * a.dk_s[2] + c;
+    T* dv = static_cast<T*>(a.dv) + b * a.dv_s[0] + hk * a.dv_s[1] + (int64_t)key * a.dv_s[2] + c;
+    if constexpr (sizeof(T) == 2) {
+        *reinterpret_cast<u32x4*>(dk) = __builtin_bit_cast(u32x4, Tr<T>::cvt8(sk));
+        *reinterpret_cast<u32x4*>(dv) = __builtin_bit_cast(u32x4, Tr<T>::cvt8(sv));
+    } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            *reinterpret_cast<f32x4*>(dk + 4 * h) = f32x4{sk[4 * h], sk[4 * h + 1], sk[4 * h + 2], sk[4 * h + 3]};
+            *reinterpret_cast<f32x4*>(dv + 4 * h) = f32x4{sv[4 * h], sv[4 * h + 1], sv[4 * h + 2], sv[4 * h + 3]};
+        }
+    }
 }
 
 // Key-side launches: split into a dk and a dv pass once each pass alone has
@@ -643,7 +728,13 @@ void launch_bwd_kv(const BwdArgs& a, int64_t nk, hipStream_t s) {
         hipLaunchKernelGGL((sdpa_bwd_kv_kernel<T, D, MASK, HAS_DP, KV_DK>), dim3((unsigned)nk), dim3(BW_KV * 64), 0, s, a);
         hipLaunchKernelGGL((sdpa_bwd_kv_kernel<T, D, MASK, HAS_DP, KV_DV>), dim3((unsigned)nk), dim3(BW_KV * 64), 0, s, a);
     } else {
-        hipLaunchKernelGGL((sdpa_bwd_kv_kernel<T, D, MASK, HAS_DP, KV_BOTH>), dim3((unsigned)nk), dim3(BW_KV * 64), 0, s, a);
+        const int ns = a.kv_splits > 1 ? a.kv_splits : 1;
+        hipLaunchKernelGGL((sdpa_bwd_kv_kernel<T, D, MASK, HAS_DP, KV_BOTH>), dim3((unsigned)(nk * ns)),
+                           dim3(BW_KV * 64), 0, s, a);
+        if (ns > 1) {
+            const int64_t n = (int64_t)a.f.B * a.f.Hkv * a.f.Skv * (D / 8);
+            hipLaunchKernelGGL(sdpa_bwd_kv_reduce_kernel<T>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a, D);
+        }
     }
 }
 

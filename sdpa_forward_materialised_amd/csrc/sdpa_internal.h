@@ -97,6 +97,11 @@ struct BwdArgs {
     void* dk;
     void* dv;
     float* dsum;
+    // key-side launch over query ranges (kv_splits > 1): float32 partial dk
+    // and dv of each range, [range][b * Hkv + hkv][key][D] (dk, then dv),
+    // summed in range order by a reduce launch
+    float* ws_kv;
+    int kv_splits;
     int64_t do_s[3], dp_s[3], dq_s[3], dk_s[3], dv_s[3];
     float scale;       // multiplier of Q K^T (the gradients of q and k carry it)
     int dp_vec;        // dprobs rows: aligned 16-byte loads, Skv a multiple of 8

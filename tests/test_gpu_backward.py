@@ -99,6 +99,20 @@ def test_backward_scales(scale):
     _check(c, f"scale={scale}", scale=scale)
 
 
+# Causal calls with few key blocks split each key block's query steps over
+# up to four workgroups (float32 partial dk, dv summed by a reduce launch):
+# four ranges with ragged Sq and Skv and grouped heads, two ranges
+# bottom-right with more keys than queries, and fp32.
+@pytest.mark.parametrize("label,spec,align", [
+    ("4-ranges-gqa", dict(seed=215, dtype="bf16", B=1, Hq=2, Hkv=1, Sq=600, Skv=700, D=64, causal=True), "top_left"),
+    ("2-ranges-br", dict(seed=216, dtype="f16", B=1, Hq=2, Hkv=2, Sq=520, Skv=776, D=128, causal=True), "bottom_right"),
+    ("f32-ranges", dict(seed=217, dtype="f32", B=1, Hq=1, Hkv=1, Sq=520, Skv=520, D=32, causal=True), "top_left"),
+], ids=["4-ranges-gqa", "2-ranges-br", "f32-ranges"])
+def test_backward_query_ranges(label, spec, align):
+    c = W.make_case(**spec)
+    _check(c, label, align=align)
+
+
 def test_backward_deterministic():
     S = _lib()
     c = W.make_case(seed=214, dtype="bf16", B=1, Hq=4, Hkv=2, Sq=200, Skv=200, D=128, causal=True)
