@@ -401,9 +401,20 @@ void sdpa_bwd_q_kernel(const BwdArgs a) {
             float mv[16], dpv[16];
             lane_loads(t, mv, dpv);
             if (t + 1 < ntiles) prefetch(t + 1);
-            float p[16], dp[16];
-            block(t, mv, dpv, p, dp);
-            body(p, dp);
+            // a tile whose mask removes every key of this wave's rows adds
+            // nothing (P = 0 there): its products are skipped
+            bool live = true;
+            if constexpr (MASK != MASK_NONE) {
+                bool any = false;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) any |= mv[r] != -INFINITY;
+                live = __builtin_amdgcn_ballot_w64(any && row_ok) != 0;
+            }
+            if (live) {
+                float p[16], dp[16];
+                block(t, mv, dpv, p, dp);
+                body(p, dp);
+            }
             __syncthreads();  // tile t consumed
             if (t + 1 < ntiles) {
                 kp.store(kt, tid);
