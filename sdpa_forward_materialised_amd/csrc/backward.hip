@@ -361,7 +361,10 @@ void sdpa_bwd_q_kernel(const BwdArgs a) {
     // the per-lane loads of tile t (mask terms, dprobs): issued before the
     // next tile's prefetch, so waiting for them does not wait for it
     auto lane_loads = [&](int t, float* mv, float* dpv) __attribute__((always_inline)) {
-        if constexpr (MASK != MASK_NONE) load_mask16<T, MASK, false>(f, mr, m_row, t * 32, hf, mv);
+        if constexpr (MASK != MASK_NONE) {
+            if (f.mask_vec) load_mask16<T, MASK, true>(f, mr, m_row, t * 32, hf, mv);  // one load per 8 keys
+            else load_mask16<T, MASK, false>(f, mr, m_row, t * 32, hf, mv);
+        }
         if constexpr (HAS_DP) load_dprobs16<T>(a, dpr, dp_row, row_ok, t * 32, hf, dpv);
     };
     // probabilities and gradient-at-P of this lane's 16 (query, key) pairs of

@@ -892,6 +892,7 @@ sdpa_status_t run_bwd(const sdpa_tensor_t* q, const sdpa_tensor_t* k, const sdpa
     const int64_t es = elt_size(sh.dtype);
     const int64_t me = sh.mask_kind == sdpa::MASK_BOOL ? 1 : es;
     a.dp_vec = dprobs && rows_aligned(dprobs, 16) && sh.Skv % 8 == 0;
+    f.mask_vec = mask && eff_stride(mask, 3) == 1 && rows_aligned(mask, 16) && sh.Skv % 8 == 0;
     int64_t ext[10];
     ext[0] = slice_extent(sh.Sq, f.q_s[2], sh.D, es);
     ext[1] = slice_extent(sh.Skv, f.k_s[2], sh.D, es);
