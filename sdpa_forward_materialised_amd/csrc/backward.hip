@@ -458,7 +458,7 @@ void sdpa_bwd_q_kernel(const BwdArgs a) {
 constexpr int KV_DV = 1, KV_DK = 2, KV_BOTH = 3;
 
 template <typename T, int D, int MASK, bool HAS_DP, int WHICH>
-__global__ __launch_bounds__(BW_KV * 64) __attribute__((amdgpu_waves_per_eu(WHICH != KV_BOTH && sizeof(T) == 2 ? 2 : 1)))
+__global__ __launch_bounds__(BW_KV * 64) __attribute__((amdgpu_waves_per_eu(WHICH != KV_BOTH && sizeof(T) == 2 && !(D == 128 && MASK != MASK_NONE && HAS_DP) ? 2 : 1)))
 void sdpa_bwd_kv_kernel(const BwdArgs a) {
     constexpr int BW = BW_KV;
     constexpr bool DO_DV = (WHICH & KV_DV) != 0;
@@ -478,7 +478,14 @@ void sdpa_bwd_kv_kernel(const BwdArgs a) {
     // (the dv pass reads neither V nor dprobs)
     constexpr int DPB = HAS_DP && NEED_DP ? 32 * 32 * SZ : 0;  // dprobs tile: 32 queries x 32 keys
     constexpr int WAVEB = (NEED_DP ? 2 : 1) * TL::BYTES32 + DPB;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TL::BYTES32 + 2 * 32 * 4 + BW * WAVEB];
+    // mask tile of a step (aligned contiguous masks): its 32 query rows x the
+    // workgroup's 32 BW keys, staged with Q and dout by whole-row loads and
+    // read back by column (each lane's key)
+    constexpr int MROW = 32 * BW * ME;
+    constexpr int MTB = MASK != MASK_NONE ? 32 * MROW : 0;
+    constexpr int MCH = MTB / 16 / (BW * 64);  // 16-byte chunks per thread
+    static_assert(MTB % (16 * BW * 64) == 0, "mask tile chunks must split evenly over the threads");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TL::BYTES32 + 2 * 32 * 4 + BW * WAVEB + MTB];
     uint8_t* qt = smem;
     uint8_t* dot = smem + TL::BYTES32;
     float* lse_s = reinterpret_cast<float*>(smem + 2 * TL::BYTES32);
@@ -488,6 +495,7 @@ void sdpa_bwd_kv_kernel(const BwdArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, hf = lane >> 5;
     uint8_t* kw = smem + 2 * TL::BYTES32 + 2 * 32 * 4 + wave * WAVEB;
+    uint8_t* mtile = smem + 2 * TL::BYTES32 + 2 * 32 * 4 + BW * WAVEB;
     uint8_t* vw = kw + TL::BYTES32;
     uint8_t* dpw = vw + TL::BYTES32;
 
@@ -538,6 +546,7 @@ void sdpa_bwd_kv_kernel(const BwdArgs a) {
     float lse_n = INFINITY, dsum_n = 0.0f;  // thread tid < 32: row i0 + tid of the next step
     constexpr int DPC = 32 * 32 * SZ / 16 / 64;  // 16-byte chunks of a dprobs tile per lane
     u32x4 dpn[DPC];
+    [[maybe_unused]] u32x4 mpn[MCH > 0 ? MCH : 1];
     auto step_coords = [&](int it, int& h, int& i0) __attribute__((always_inline)) {
         const int hh = it / nqt;
         h = hk * f.group + hh;
@@ -550,6 +559,18 @@ void sdpa_bwd_kv_kernel(const BwdArgs a) {
         const rsrc_t dor = make_rsrc(static_cast<const T*>(a.dout) + b * a.do_s[0] + h * a.do_s[1], a.do_ext);
         qp.load(qr, (uint32_t)(f.q_s[2] * SZ), i0, f.Sq, tid);
         dop.load(dor, (uint32_t)(a.do_s[2] * SZ), i0, f.Sq, tid);
+        if constexpr (MASK != MASK_NONE) {
+            if (f.mask_vec) {
+                const rsrc_t mrh = make_rsrc(static_cast<const uint8_t*>(f.mask) + (b * f.m_s[0] + h * f.m_s[1]) * ME, f.m_ext);
+#pragma unroll
+                for (int u = 0; u < MCH; ++u) {
+                    const int idx = tid + u * BW * 64;
+                    const int rr = idx / (MROW / 16), cc = idx - (idx / (MROW / 16)) * (MROW / 16);
+                    const int i = i0 + rr, j = k0 + cc * (16 / ME);
+                    mpn[u] = ld128(mrh, pred(i < f.Sq && j < f.Skv, (uint32_t)(((int64_t)i * f.m_s[2] + j) * ME)));
+                }
+            }
+        }
         if (tid < 32) {
             const int i = i0 + tid;
             const float l = i < f.Sq ? f.lse[b * f.l_s[0] + h * f.l_s[1] + (int64_t)i * f.l_s[2]] : -INFINITY;
@@ -587,6 +608,12 @@ void sdpa_bwd_kv_kernel(const BwdArgs a) {
     auto put = [&]() __attribute__((always_inline)) {
         qp.store(qt, tid);
         dop.store(dot, tid);
+        if constexpr (MASK != MASK_NONE) {
+            if (f.mask_vec) {
+#pragma unroll
+                for (int u = 0; u < MCH; ++u) reinterpret_cast<u32x4*>(mtile)[tid + u * BW * 64] = mpn[u];
+            }
+        }
         if (tid < 32) {
             lse_s[tid] = lse_n;
             dsum_s[tid] = dsum_n;
@@ -608,11 +635,25 @@ void sdpa_bwd_kv_kernel(const BwdArgs a) {
         // this step's mask terms (per lane: its key, 16 queries), before the prefetch
         float mv[16];
         if constexpr (MASK != MASK_NONE) {
-            const rsrc_t mr = make_rsrc(static_cast<const uint8_t*>(f.mask) + (b * f.m_s[0] + h * f.m_s[1]) * ME, f.m_ext);
+            if (f.mask_vec) {  // from the staged tile: row kk(hf, r), this lane's key
+                const uint8_t* mc = mtile + (kj - k0) * ME;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int i = i0 + kk(hf, r);
-                mv[r] = (i < f.Sq && key_ok) ? mask_elem<T, MASK>(f, mr, i, kj) : 0.0f;
+                for (int r = 0; r < 16; ++r) {
+                    const int i = i0 + kk(hf, r);
+                    const uint8_t* e = mc + kk(hf, r) * MROW;
+                    float x;
+                    if constexpr (MASK == MASK_BOOL) x = *e ? 0.0f : -INFINITY;
+                    else if constexpr (SZ == 2) x = Tr<T>::to_f(*reinterpret_cast<const uint16_t*>(e)) * LOG2E;
+                    else x = *reinterpret_cast<const float*>(e) * LOG2E;
+                    mv[r] = (i < f.Sq && key_ok) ? x : 0.0f;
+                }
+            } else {
+                const rsrc_t mr = make_rsrc(static_cast<const uint8_t*>(f.mask) + (b * f.m_s[0] + h * f.m_s[1]) * ME, f.m_ext);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int i = i0 + kk(hf, r);
+                    mv[r] = (i < f.Sq && key_ok) ? mask_elem<T, MASK>(f, mr, i, kj) : 0.0f;
+                }
             }
         }
         if (it + 1 < nit) prefetch(it + 1);

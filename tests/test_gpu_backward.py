@@ -69,6 +69,11 @@ CASES = [
     ("bf16-d32-single", dict(seed=208, dtype="bf16", B=1, Hq=1, Hkv=1, Sq=1, Skv=1, D=32)),
     ("f16-d64-sq>skv-causal", dict(seed=209, dtype="f16", B=1, Hq=2, Hkv=1, Sq=130, Skv=70, D=64, causal=True)),
     ("f32-d64-add-odd-skv", dict(seed=210, dtype="f32", B=1, Hq=2, Hkv=2, Sq=50, Skv=37, D=64, mask="add", p=0.2)),
+    # aligned masks (Skv a multiple of 8): the key side stages each step's mask tile in LDS
+    ("f16-d128-add-aligned", dict(seed=218, dtype="f16", B=1, Hq=4, Hkv=2, Sq=75, Skv=264, D=128, mask="add", p=0.1)),
+    ("f32-d64-add-aligned", dict(seed=219, dtype="f32", B=2, Hq=2, Hkv=1, Sq=41, Skv=136, D=64, mask="add", p=0.2)),
+    ("bf16-d32-neginf-aligned", dict(seed=220, dtype="bf16", B=1, Hq=3, Hkv=3, Sq=97, Skv=200, D=32, mask="neginf",
+                                     p=0.3)),
 ]
 
 
