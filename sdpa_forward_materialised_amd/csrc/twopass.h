@@ -157,7 +157,8 @@ __device__ __forceinline__ const FwdArgs& pick_args(const FwdArgs& first, const 
 // HR: head rows (four-wave kernels without a loader wave, a.head_rows == 4):
 // the compute waves take the query heads w.hq, w.hq + 1, ... of one KV group
 // on the same 32 rows, sharing each K/V tile (and the head-shared mask rows)
-// among the heads. CT: see TwoPassCfg (head rows with a bool mask).
+// among the heads. CT: see TwoPassCfg (recorded tile classes of a bool mask
+// that all query heads share).
 template <typename T, int D, int NW, int MASK, bool VEC, int TN, bool NL, int SPL = 0, bool DROP = false,
           bool THD = false, bool HR = false, bool CT = false>
 __global__ __attribute__((amdgpu_flat_work_group_size((NL ? NW : NW + 1) * 64, (NL ? NW : NW + 1) * 64),
@@ -448,9 +449,9 @@ void sdpa_twopass_kernel(const FwdArgs a_in) {
             return 0;
         }
     };
-    // CT: the classes sweep 1 found, 2 bits per tile, tile t in lane t / 16
-    // (up to 1024 tiles); the same in every wave of the workgroup (its waves
-    // share the rows)
+    // CT: the classes sweep 1 found for this wave's rows, 2 bits per tile,
+    // tile t in lane t / 16 (up to 1024 tiles); with head rows the same in
+    // every wave of the workgroup (its waves share the rows)
     uint32_t cls_rec = 0u;
     auto record_flags = [&](int t, int flags) SDPA_INLINE {
         if constexpr (CT) cls_rec |= lane == (t >> 4) ? (uint32_t)flags << (2 * (t & 15)) : 0u;

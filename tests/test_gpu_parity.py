@@ -170,12 +170,11 @@ def test_key_padding_dead_tiles(D, dtype, waves, monkeypatch):
 # Head rows: grouped heads on the four-wave kernel without a loader wave take
 # four query heads of one KV group per workgroup, on 32 shared rows. Group 4
 # and 8, no mask / head-shared bool and additive masks (with dead tail tiles
-# and dead rows), ragged Sq and Skv; against the oracle and, where the tiling
-# is the same, bit for bit against the same call with head rows off
-# (SDPA_MATH_HEAD_ROWS=0). With a 16-bit bool mask head rows take 64-key
-# tiles (32 without them), which changes which tiles count as wholly kept,
-# so those calls are held to the oracle only. A mask with per-head rows keeps
-# one head per workgroup.
+# and dead rows), ragged Sq and Skv; against the oracle and bit for bit
+# against the same call with head rows off (SDPA_MATH_HEAD_ROWS=0: with a
+# head-shared 16-bit bool mask both take 64-key tiles with recorded classes,
+# and a wave's classes depend only on its own rows). A mask with per-head
+# rows keeps one head per workgroup.
 HEAD_ROWS = [
     ("f16-d128-g4-keypad", dict(seed=190, dtype="f16", B=2, Hq=8, Hkv=2, Sq=200, Skv=320, D=128), "keypad"),
     ("bf16-d64-g8-none", dict(seed=191, dtype="bf16", B=1, Hq=16, Hkv=2, Sq=77, Skv=136, D=64), None),
@@ -207,10 +206,8 @@ def test_head_rows(label, spec, kind, monkeypatch):
     monkeypatch.setenv("SDPA_MATH_HEAD_ROWS", "0")
     b = S.fwd(q, k, v, m, False, None, True, path="twopass")
     torch.cuda.synchronize()
-    same_tiling = not (spec["dtype"] != "f32" and (kind == "keypad" or spec.get("mask") == "bool"))
-    if same_tiling:
-        for x, y in zip(a, b):
-            assert torch.equal(x, y)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
     print(f"[result] {label} {on}", flush=True)
 
 
