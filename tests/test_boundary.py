@@ -213,6 +213,33 @@ def test_workspace_query(monkeypatch):
     assert rc == 1 and n == 0
 
 
+def _bwd_ws_bytes(q, k, causal=0, gqa=0):
+    lib = S.load_library()
+    n = ctypes.c_size_t(123)
+    rc = lib.sdpa_math_bwd_workspace_bytes(B._desc(q, 4), B._desc(k, 4), B._desc(k, 4), B._desc(None, 4),
+                                           causal, gqa, ctypes.byref(n))
+    return rc, n.value
+
+
+def test_backward_workspace_query():
+    up = lambda x: -(-x // 256) * 256  # noqa: E731
+    # D_i per query row only: large grids, and any call without a causal mask
+    q = _z(2, 16, 2048, 128, dtype=torch.bfloat16)
+    assert _bwd_ws_bytes(q, q, causal=1) == (0, up(2 * 16 * 2048 * 4))
+    q, k = _z(4, 32, 1024, 128), _z(4, 8, 1024, 128)
+    assert _bwd_ws_bytes(q, k, causal=0, gqa=1) == (0, up(4 * 32 * 1024 * 4))
+    # causal with 4 x 8 x 16 = 512 key blocks of 64 keys (under 1024): two query
+    # ranges, each with float32 partial dk and dv
+    q = _z(4, 8, 1024, 64)
+    assert _bwd_ws_bytes(q, q, causal=1) == (0, up(4 * 8 * 1024 * 4) + 2 * 2 * 4 * 8 * 1024 * 64 * 4)
+    # one key block: four ranges (at least 8 steps of 32 rows each: 2 heads x 19 tiles)
+    q, k = _z(1, 2, 600, 64, dtype=torch.bfloat16), _z(1, 1, 64, 64, dtype=torch.bfloat16)
+    assert _bwd_ws_bytes(q, k, causal=2, gqa=1) == (0, up(2 * 600 * 4) + 4 * 2 * 1 * 64 * 64 * 4)
+    # too few steps for a range of 8: none
+    q = _z(1, 1, 200, 32)
+    assert _bwd_ws_bytes(q, q, causal=1) == (0, up(200 * 4))
+
+
 @pytest.mark.parametrize("shape,ndim,view", [
     ((2, 3, 5, 32), 4, None),                 # contiguous 4-D
     ((2, 3, 7), 3, None),                     # LSE-like 3-D
